@@ -1,0 +1,180 @@
+"""f64 CPU oracle for the selective-scan hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, the package smoke check and the CPU-baseline leg of the benchmark
+may import this package.  The product (the HIP library and its binding) never does.
+
+Thin ctypes wrapper over ``liboracle.so`` (built from ``oracle.c`` by ``build.py``).
+Every function takes numpy arrays, converts them to contiguous float64 and returns
+freshly allocated float64 outputs.  What each routine computes, and which page and
+section it follows, is stated in ``oracle.c``.
+
+Parity status: every function here is pinned by the CPU tests (closed forms, finite
+differences, the unrolled form, step/split equivalence, invariants, page formulas and
+hand-derived worked examples under ``tests/golden``); none is "parity unpinned".
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_D = ctypes.POINTER(ctypes.c_double)
+_I = ctypes.c_int64
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        sigs = {
+            "oracle_scan_fwd": [_I] * 4 + [_D] * 9,
+            "oracle_scan_step": [_I] * 3 + [_D] * 8,
+            "oracle_scan_materialized": [_I] * 4 + [_D] * 8,
+            "oracle_scan_bwd": [_I] * 4 + [_D] * 15,
+            "oracle_conv1d_fwd": [_I] * 4 + [_D] * 4,
+            "oracle_conv1d_bwd": [_I] * 4 + [_D] * 6,
+            "oracle_conv1d_step_bwd": [_I] * 2 + [_D] * 6,
+            "oracle_rmsnorm_fwd": [_I] * 2 + [_D, _D, ctypes.c_double, _D, _D],
+            "oracle_rmsnorm_bwd": [_I] * 2 + [_D] * 6,
+        }
+        for name, args in sigs.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = None
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _p(a):
+    if a is None:
+        return ctypes.cast(None, _D)
+    return a.ctypes.data_as(_D)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle uses (OMP_NUM_THREADS or all host cores)."""
+    return int(_load().oracle_num_threads())
+
+
+# ----------------------------------------------------------------------------------
+# selective scan
+# ----------------------------------------------------------------------------------
+
+def scan_fwd(x, delta, A, Bm, Cm, Dv, h0=None):
+    """Returns (y [B,L,D], h_last [B,D,N])."""
+    x, delta, A, Bm, Cm, Dv, h0 = map(_f64, (x, delta, A, Bm, Cm, Dv, h0))
+    Bsz, L, D = x.shape
+    N = A.shape[1]
+    y = np.empty((Bsz, L, D))
+    h_last = np.empty((Bsz, D, N))
+    _load().oracle_scan_fwd(Bsz, L, D, N, _p(x), _p(delta), _p(A), _p(Bm), _p(Cm), _p(Dv),
+                            _p(h0), _p(y), _p(h_last))
+    return y, h_last
+
+
+def scan_step(h, x_t, delta_t, A, B_t, C_t, Dv):
+    """One token: h [B,D,N] -> (h', y_t [B,D]); x_t, delta_t [B,D]; B_t, C_t [B,N]."""
+    h = _f64(h).copy()
+    x_t, delta_t, A, B_t, C_t, Dv = map(_f64, (x_t, delta_t, A, B_t, C_t, Dv))
+    Bsz, D, N = h.shape
+    y = np.empty((Bsz, D))
+    _load().oracle_scan_step(Bsz, D, N, _p(h), _p(x_t), _p(delta_t), _p(A), _p(B_t), _p(C_t),
+                             _p(Dv), _p(y))
+    return h, y
+
+
+def scan_materialized(x, delta, A, Bm, Cm, Dv, h0=None):
+    """O(L^2) unrolled form of the scan output y [B,L,D]."""
+    x, delta, A, Bm, Cm, Dv, h0 = map(_f64, (x, delta, A, Bm, Cm, Dv, h0))
+    Bsz, L, D = x.shape
+    N = A.shape[1]
+    y = np.empty((Bsz, L, D))
+    _load().oracle_scan_materialized(Bsz, L, D, N, _p(x), _p(delta), _p(A), _p(Bm), _p(Cm),
+                                     _p(Dv), _p(h0), _p(y))
+    return y
+
+
+def scan_bwd(x, delta, A, Bm, Cm, Dv, dy, h0=None):
+    """Exact adjoint.  Returns dict dx, ddelta, dA, dB, dC, dD, dh0 (dA, dD from zero)."""
+    x, delta, A, Bm, Cm, Dv, dy, h0 = map(_f64, (x, delta, A, Bm, Cm, Dv, dy, h0))
+    Bsz, L, D = x.shape
+    N = A.shape[1]
+    out = dict(dx=np.empty((Bsz, L, D)), ddelta=np.empty((Bsz, L, D)), dA=np.zeros((D, N)),
+               dB=np.empty((Bsz, L, N)), dC=np.empty((Bsz, L, N)), dD=np.zeros(D),
+               dh0=np.empty((Bsz, D, N)))
+    _load().oracle_scan_bwd(Bsz, L, D, N, _p(x), _p(delta), _p(A), _p(Bm), _p(Cm), _p(Dv),
+                            _p(h0), _p(dy), _p(out["dx"]), _p(out["ddelta"]), _p(out["dA"]),
+                            _p(out["dB"]), _p(out["dC"]), _p(out["dD"]), _p(out["dh0"]))
+    return out
+
+
+# ----------------------------------------------------------------------------------
+# conv1d
+# ----------------------------------------------------------------------------------
+
+def conv1d_fwd(x, W, bias=None):
+    x, W, bias = map(_f64, (x, W, bias))
+    Bsz, L, D = x.shape
+    K = W.shape[1]
+    out = np.empty((Bsz, L, D))
+    _load().oracle_conv1d_fwd(Bsz, L, D, K, _p(x), _p(W), _p(bias), _p(out))
+    return out
+
+
+def conv1d_bwd(x, W, dout):
+    """Returns dict dx [B,L,D], dW [D,K], db [D] (dW, db from zero)."""
+    x, W, dout = map(_f64, (x, W, dout))
+    Bsz, L, D = x.shape
+    K = W.shape[1]
+    out = dict(dx=np.empty((Bsz, L, D)), dW=np.zeros((D, K)), db=np.zeros(D))
+    _load().oracle_conv1d_bwd(Bsz, L, D, K, _p(x), _p(W), _p(dout), _p(out["dx"]),
+                              _p(out["dW"]), _p(out["db"]))
+    return out
+
+
+def conv1d_step_bwd(d_out, window, W, dW=None, db=None):
+    """The per-timestep step backward; dW, db are accumulated (copies returned)."""
+    d_out, window, W = map(_f64, (d_out, window, W))
+    D, K = W.shape
+    dW = np.zeros((D, K)) if dW is None else _f64(dW).copy()
+    db = np.zeros(D) if db is None else _f64(db).copy()
+    dx = np.empty(D)
+    _load().oracle_conv1d_step_bwd(D, K, _p(d_out), _p(window), _p(W), _p(dx), _p(dW), _p(db))
+    return dx, dW, db
+
+
+# ----------------------------------------------------------------------------------
+# RMSNorm
+# ----------------------------------------------------------------------------------
+
+def rmsnorm_fwd(x, scale, eps):
+    x, scale = map(_f64, (x, scale))
+    R, M = x.shape
+    y = np.empty((R, M))
+    rms = np.empty(R)
+    _load().oracle_rmsnorm_fwd(R, M, _p(x), _p(scale), float(eps), _p(y), _p(rms))
+    return y, rms
+
+
+def rmsnorm_bwd(dy, x, scale, rms):
+    """Returns dict dx [R,M], dscale [M] (dscale from zero)."""
+    dy, x, scale, rms = map(_f64, (dy, x, scale, rms))
+    R, M = x.shape
+    out = dict(dx=np.empty((R, M)), dscale=np.zeros(M))
+    _load().oracle_rmsnorm_bwd(R, M, _p(dy), _p(x), _p(scale), _p(rms), _p(out["dx"]),
+                               _p(out["dscale"]))
+    return out
