@@ -1,0 +1,156 @@
+/*
+ * ssm_scan.h -- C ABI of libssmscan.so, the MI355X (gfx950) selective-scan hot path.
+ *
+ * Four operations on already-projected tensors:
+ *   ssm_scan_fwd       selective-SSM scan, forward
+ *   ssm_scan_bwd       its backward (backpropagation through time across the state)
+ *   conv1d_causal_bwd  depthwise causal conv1d backward
+ *   rmsnorm_bwd        batched RMSNorm backward
+ *
+ * Common conventions
+ * ------------------
+ * - Pointers.  Every tensor pointer is a DEVICE pointer to a dense, row-major,
+ *   contiguous buffer; no strides or offsets cross this ABI (a strided view read as
+ *   dense silently gives wrong numbers -- the failure the rustytorch backward_cuda
+ *   commit reports for its matmul path).  Every tensor pointer must be 16-byte
+ *   aligned.  The caller owns every buffer; the library never allocates or frees
+ *   device memory.
+ * - dtype.  ssm_dtype_t selects the storage type of the activations (x, delta, B, C,
+ *   y, dy, dx, ddelta, conv x/dout/dx, norm x/dy/dx): f32 or bf16.  Parameters and
+ *   their gradients (A, D, W, scale, rms, dA, dD, dW, db, dscale), states (h0,
+ *   h_last, dh0, checkpoints) and dB/dC are always f32.  Arithmetic is f32 with f32
+ *   state; bf16 outputs are rounded to nearest even.
+ * - Streams.  `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   Calls only enqueue work: they return before the GPU finishes and never
+ *   synchronize.  Buffers must stay alive until the stream work completes.  Calls
+ *   are re-entrant; the library keeps no state except a per-thread error message.
+ * - Workspace.  Scratch (partial sums, chunk carries) lives in a caller buffer `ws`
+ *   of at least the size the matching *_workspace_bytes() query returns for the
+ *   same arguments; ws may be NULL when that size is 0.  Its content on entry is
+ *   ignored.  Two calls that run concurrently need separate workspaces.
+ * - Accumulation.  Parameter gradients (dA, dD, dW, db, dscale) are ADDED to the
+ *   caller's buffer (as the mamba-rs backward_ops.rs functions accumulate their
+ *   weight and scale gradients); every other output is overwritten.
+ * - Determinism.  No atomics: every sum runs in a fixed order, so repeated calls
+ *   with the same inputs give bit-identical outputs.
+ * - Errors.  Arguments are validated on the host before any HIP call; a rejected
+ *   call enqueues nothing and leaves every output untouched.  The return value is
+ *   SSM_OK or a negative SSM_ERR_* code; ssm_last_error() then describes the
+ *   problem.  Nothing aborts and no exception crosses the ABI.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
+
+enum {
+    SSM_OK = 0,
+    SSM_ERR_ARG = -1,          /* null required pointer, size <= 0, size overflow */
+    SSM_ERR_UNSUPPORTED = -2,  /* N not in {4,8,16}, K not in [1,8], dtype, M too large */
+    SSM_ERR_WORKSPACE = -3,    /* ws_bytes smaller than the query's answer */
+    SSM_ERR_ALIGN = -4,        /* a tensor pointer is not 16-byte aligned */
+    SSM_ERR_HIP = -5           /* the HIP runtime rejected a launch */
+};
+
+/* Message for the last non-OK return on the calling thread ("" if none). */
+const char *ssm_last_error(void);
+
+/* Library version string. */
+const char *ssm_version(void);
+
+/* ---------------------------------------------------------------------------------
+ * Selective scan (Mamba S6).  The pages name this scan and its reverse pass -- the
+ * rustytorch commit "feat(mamba): GPU-accelerated backward pass (backward_cuda)"
+ * (sequential scan, its BPTT reverse pass, the shared forward recompute) and the
+ * mamba-rs 0.5.1 crate summary (training by backpropagation through the SSM
+ * state) -- without printing it.  Per batch row b, channel d, state n:
+ *     a_t[n] = exp(delta[b,t,d] * A[d,n])
+ *     h_t[n] = a_t[n] * h_{t-1}[n] + delta[b,t,d] * Bm[b,t,n] * x[b,t,d]
+ *     y[b,t,d] = sum_n Cm[b,t,n] * h_t[n] + Dv[d] * x[b,t,d]
+ * with h_{-1} = h0[b,d,:] or 0 (the zero-initialised state of the foxhunt ml-alpha
+ * forward-pass commit).  delta is used as given (already softplus'd); A is used as
+ * given (not A_log).
+ *
+ * Shapes: x, delta, y, dy, dx, ddelta [B,L,D]; Bm, Cm [B,L,N] (shared by all
+ * channels); A, dA [D,N]; Dv, dD [D]; h0, h_last, dh0 [B,D,N]; dB, dC [B,L,N] f32.
+ * Supported: N in {4, 8, 16}; B <= 65535; L, D >= 1 (tails handled, no multiple
+ * required).
+ *
+ * Checkpoints.  The forward can save the state before every 16th step into `ckpt`
+ * (ssm_scan_ckpt_bytes() bytes; layout private to this library version) for the
+ * backward to recompute states from.  The backward given ckpt == NULL recomputes
+ * the forward itself into its workspace.
+ * ------------------------------------------------------------------------------- */
+size_t ssm_scan_ckpt_bytes(int64_t B, int64_t L, int64_t D, int64_t N);
+size_t ssm_scan_fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
+                                    ssm_dtype_t dtype);
+/* with_ckpt = 1 if the backward will be given the forward's checkpoints */
+size_t ssm_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
+                                    ssm_dtype_t dtype, int with_ckpt);
+
+/* Forward.  Required: x, delta, A, Bm, Cm, Dv, y.  Optional (NULL to skip): h0
+ * (initial state; zero if NULL), ckpt (out: checkpoints), h_last (out: state after
+ * the last step). */
+int ssm_scan_fwd(void *stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D,
+                 int64_t N, const void *x, const void *delta, const float *A,
+                 const void *Bm, const void *Cm, const float *Dv, const float *h0,
+                 void *y, float *ckpt, float *h_last, void *ws, size_t ws_bytes);
+
+/* Backward for upstream gradient dy [B,L,D].  Required: x, delta, A, Bm, Cm, Dv, dy,
+ * dx, ddelta, dA, dB, dC, dD.  Optional: h0 (the forward's initial state; used only
+ * when ckpt is NULL), ckpt (the forward's checkpoints for these same inputs and h0),
+ * dh0 (out: gradient of the initial state, overwritten).
+ * dx, ddelta, dB, dC, dh0 are overwritten; dA, dD are accumulated. */
+int ssm_scan_bwd(void *stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D,
+                 int64_t N, const void *x, const void *delta, const float *A,
+                 const void *Bm, const void *Cm, const float *Dv, const float *h0,
+                 const void *dy, const float *ckpt, void *dx, void *ddelta, float *dA,
+                 float *dB, float *dC, float *dD, float *dh0, void *ws, size_t ws_bytes);
+
+/* ---------------------------------------------------------------------------------
+ * Depthwise causal conv1d backward.  The mamba-rs 0.5.1 backward_ops.rs section
+ * backward_conv1d_step gives one timestep of it for a shift-register conv (bias grad
+ * = upstream value; weight grad = upstream value times the saved window; input grad
+ * through the newest tap).  Here the whole sequence at once, for the forward
+ *     out[b,t,d] = bias[d] + sum_{k<K} W[d,k] * x[b, t-K+1+k, d]   (x = 0 for t < 0):
+ *     dx[b,s,d] = sum_k dout[b, s+K-1-k, d] * W[d,k]     (terms with s+K-1-k < L)
+ *     dW[d,k]  += sum_{b,t} dout[b,t,d] * x[b, t-K+1+k, d]
+ *     db[d]    += sum_{b,t} dout[b,t,d]
+ * dout is the gradient of the conv output (taken after any activation backward).
+ * Shapes: x, dout, dx [B,L,D] (dtype); W, dW [D,K] f32 (tap K-1 = newest input);
+ * db [D] f32.  Supported: K in [1, 8].
+ * ------------------------------------------------------------------------------- */
+size_t conv1d_causal_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t K,
+                                         ssm_dtype_t dtype);
+int conv1d_causal_bwd(void *stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D,
+                      int64_t K, const void *x, const float *W, const void *dout, void *dx,
+                      float *dW, float *db, void *ws, size_t ws_bytes);
+
+/* ---------------------------------------------------------------------------------
+ * Batched RMSNorm backward given the saved per-row rms (not its inverse), as the
+ * mamba-rs 0.5.1 backward_ops.rs section backward_rms_norm states it, for the
+ * forward y[r,i] = x[r,i] / rms[r] * scale[i], rms[r] = sqrt(mean_i x[r,i]^2 + eps):
+ *     inv = 1/rms[r],  c = inv^2 * (sum_i dy[r,i] scale[i] x[r,i]) / M
+ *     dx[r,i]    = inv * (scale[i] dy[r,i] - x[r,i] * c)      (overwritten)
+ *     dscale[i] += sum_r dy[r,i] * x[r,i] * inv              (accumulated)
+ * Shapes: dy, x, dx [R,M] (dtype); scale, dscale [M] f32; rms [R] f32.
+ * Supported: M <= 8192 when bf16 and M is a multiple of 8, M <= 4096 when f32 and M
+ * is a multiple of 4, otherwise M <= 1024.
+ * ------------------------------------------------------------------------------- */
+size_t rmsnorm_bwd_workspace_bytes(int64_t R, int64_t M, ssm_dtype_t dtype);
+int rmsnorm_bwd(void *stream, ssm_dtype_t dtype, int64_t R, int64_t M, const void *dy,
+                const void *x, const float *scale, const float *rms, void *dx,
+                float *dscale, void *ws, size_t ws_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

@@ -1,1 +1,10 @@
-"""MI355X-native selective-scan hot path (placeholder; binding added with the C ABI)."""
+"""MI355X-native (gfx950) selective-scan hot path.
+
+The product is ``libssmscan.so`` (HIP kernels behind a C ABI, declared in
+``include/ssm_scan.h``); ``binding`` is its thin Python binding.  ``workloads`` and
+``synth`` hold the synthetic workload shapes and seeded input generators.  Importing
+the package does not load the library; the first binding call does, and raises if it
+is missing.
+"""
+from .binding import (SsmError, conv1d_causal_bwd, load, new_ckpt, rmsnorm_bwd,  # noqa: F401
+                      ssm_scan_bwd, ssm_scan_fwd, version)

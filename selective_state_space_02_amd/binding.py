@@ -1,0 +1,271 @@
+"""Thin ctypes binding of libssmscan.so (argument marshalling only).
+
+Each function has the name of the C entry point it calls and takes torch tensors that
+live on the GPU.  It checks what the C ABI cannot see (device, dtype, contiguity --
+a strided view read as dense silently gives wrong numbers), allocates missing outputs
+and the workspace with torch, and calls the library on torch's current stream.  All
+arithmetic runs in the library's HIP kernels; nothing here computes any part of the
+scan, the conv or the norm.  If the library is missing or cannot be loaded, every call
+raises RuntimeError: there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssmscan.so")
+
+SSM_F32, SSM_BF16 = 0, 1
+SSM_OK, SSM_ERR_ARG, SSM_ERR_UNSUPPORTED, SSM_ERR_WORKSPACE, SSM_ERR_ALIGN, SSM_ERR_HIP = (
+    0, -1, -2, -3, -4, -5)
+
+EXPORTS = ("ssm_last_error", "ssm_version", "ssm_scan_ckpt_bytes",
+           "ssm_scan_fwd_workspace_bytes", "ssm_scan_bwd_workspace_bytes", "ssm_scan_fwd",
+           "ssm_scan_bwd", "conv1d_causal_bwd_workspace_bytes", "conv1d_causal_bwd",
+           "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd")
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int64
+_S = ctypes.c_size_t
+_E = ctypes.c_int
+
+
+class SsmError(RuntimeError):
+    """A non-OK status from the library (code in .code)."""
+
+    def __init__(self, code, msg):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+def load():
+    """Load libssmscan.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                           "(run __graft_entry__.build() or selective_state_space_02_amd/build.py)")
+    try:
+        lib = ctypes.CDLL(LIB_PATH)
+    except OSError as e:
+        raise RuntimeError(f"cannot load {LIB_PATH}: {e}") from e
+    lib.ssm_last_error.restype = ctypes.c_char_p
+    lib.ssm_last_error.argtypes = []
+    lib.ssm_version.restype = ctypes.c_char_p
+    lib.ssm_version.argtypes = []
+    lib.ssm_scan_ckpt_bytes.restype = _S
+    lib.ssm_scan_ckpt_bytes.argtypes = [_I] * 4
+    lib.ssm_scan_fwd_workspace_bytes.restype = _S
+    lib.ssm_scan_fwd_workspace_bytes.argtypes = [_I] * 4 + [_E]
+    lib.ssm_scan_bwd_workspace_bytes.restype = _S
+    lib.ssm_scan_bwd_workspace_bytes.argtypes = [_I] * 4 + [_E, _E]
+    lib.ssm_scan_fwd.restype = _E
+    lib.ssm_scan_fwd.argtypes = [_P, _E] + [_I] * 4 + [_P] * 10 + [_P, _S]
+    lib.ssm_scan_bwd.restype = _E
+    lib.ssm_scan_bwd.argtypes = [_P, _E] + [_I] * 4 + [_P] * 16 + [_P, _S]
+    lib.conv1d_causal_bwd_workspace_bytes.restype = _S
+    lib.conv1d_causal_bwd_workspace_bytes.argtypes = [_I] * 4 + [_E]
+    lib.conv1d_causal_bwd.restype = _E
+    lib.conv1d_causal_bwd.argtypes = [_P, _E] + [_I] * 4 + [_P] * 6 + [_P, _S]
+    lib.rmsnorm_bwd_workspace_bytes.restype = _S
+    lib.rmsnorm_bwd_workspace_bytes.argtypes = [_I] * 2 + [_E]
+    lib.rmsnorm_bwd.restype = _E
+    lib.rmsnorm_bwd.argtypes = [_P, _E] + [_I] * 2 + [_P] * 6 + [_P, _S]
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().ssm_last_error().decode()
+
+
+def version() -> str:
+    return load().ssm_version().decode()
+
+
+def _check(rc):
+    if rc != SSM_OK:
+        raise SsmError(rc, last_error())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SSM_F32
+    if t.dtype == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError(f"activation dtype must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t, name, dtype=None, shape=None, device=None):
+    """Device pointer of a dense tensor (None -> NULL), after the checks the ABI needs."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor (got device {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous (strided views are not accepted)")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _workspace(nbytes, device, ws):
+    if nbytes == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"workspace too small: {ws.numel() * ws.element_size()} < {nbytes} bytes")
+    return ws, ws.numel() * ws.element_size()
+
+
+# ----------------------------------------------------------------------------------
+# selective scan
+# ----------------------------------------------------------------------------------
+
+def ssm_scan_ckpt_bytes(B, L, D, N) -> int:
+    return int(load().ssm_scan_ckpt_bytes(B, L, D, N))
+
+
+def ssm_scan_fwd_workspace_bytes(B, L, D, N, dtype_code) -> int:
+    return int(load().ssm_scan_fwd_workspace_bytes(B, L, D, N, dtype_code))
+
+
+def ssm_scan_bwd_workspace_bytes(B, L, D, N, dtype_code, with_ckpt) -> int:
+    return int(load().ssm_scan_bwd_workspace_bytes(B, L, D, N, dtype_code, int(bool(with_ckpt))))
+
+
+def new_ckpt(B, L, D, N, device) -> torch.Tensor:
+    """A buffer for the forward's checkpoints (f32, opaque layout)."""
+    return torch.empty(ssm_scan_ckpt_bytes(B, L, D, N) // 4, dtype=torch.float32, device=device)
+
+
+def ssm_scan_fwd(x, delta, A, Bm, Cm, Dv, h0=None, y=None, ckpt=None, h_last=None, ws=None):
+    """y = scan(x, delta, A, Bm, Cm, Dv; h0).  Returns y (allocated if not given)."""
+    lib = load()
+    Bsz, L, D = x.shape
+    N = A.shape[1]
+    dev = x.device
+    dt = x.dtype
+    code = _dtype_code(x)
+    if y is None:
+        y = torch.empty_like(x)
+    args = [
+        _ptr(x, "x", dt, (Bsz, L, D), dev), _ptr(delta, "delta", dt, (Bsz, L, D), dev),
+        _ptr(A, "A", torch.float32, (D, N), dev), _ptr(Bm, "Bm", dt, (Bsz, L, N), dev),
+        _ptr(Cm, "Cm", dt, (Bsz, L, N), dev), _ptr(Dv, "Dv", torch.float32, (D,), dev),
+        _ptr(h0, "h0", torch.float32, (Bsz, D, N), dev), _ptr(y, "y", dt, (Bsz, L, D), dev),
+        _ptr(ckpt, "ckpt", torch.float32, None, dev),
+        _ptr(h_last, "h_last", torch.float32, (Bsz, D, N), dev),
+    ]
+    if ckpt is not None and ckpt.numel() * 4 < ssm_scan_ckpt_bytes(Bsz, L, D, N):
+        raise ValueError("ckpt buffer too small (use new_ckpt)")
+    need = ssm_scan_fwd_workspace_bytes(Bsz, L, D, N, code)
+    ws, nbytes = _workspace(need, dev, ws)
+    _check(lib.ssm_scan_fwd(_stream(dev), code, Bsz, L, D, N, *args,
+                            _ptr(ws, "ws") if ws is not None else None, nbytes))
+    return y
+
+
+def ssm_scan_bwd(x, delta, A, Bm, Cm, Dv, dy, ckpt=None, h0=None, dx=None, ddelta=None,
+                 dA=None, dB=None, dC=None, dD=None, dh0=None, ws=None):
+    """Backward.  dA and dD are accumulated into (zeros allocated if not given); every
+    other gradient is overwritten.  Returns dict dx, ddelta, dA, dB, dC, dD, dh0."""
+    lib = load()
+    Bsz, L, D = x.shape
+    N = A.shape[1]
+    dev = x.device
+    dt = x.dtype
+    code = _dtype_code(x)
+    f32 = torch.float32
+    dx = torch.empty_like(x) if dx is None else dx
+    ddelta = torch.empty_like(x) if ddelta is None else ddelta
+    dA = torch.zeros((D, N), dtype=f32, device=dev) if dA is None else dA
+    dB = torch.empty((Bsz, L, N), dtype=f32, device=dev) if dB is None else dB
+    dC = torch.empty((Bsz, L, N), dtype=f32, device=dev) if dC is None else dC
+    dD = torch.zeros((D,), dtype=f32, device=dev) if dD is None else dD
+    if ckpt is not None and ckpt.numel() * 4 < ssm_scan_ckpt_bytes(Bsz, L, D, N):
+        raise ValueError("ckpt buffer too small")
+    args = [
+        _ptr(x, "x", dt, (Bsz, L, D), dev), _ptr(delta, "delta", dt, (Bsz, L, D), dev),
+        _ptr(A, "A", f32, (D, N), dev), _ptr(Bm, "Bm", dt, (Bsz, L, N), dev),
+        _ptr(Cm, "Cm", dt, (Bsz, L, N), dev), _ptr(Dv, "Dv", f32, (D,), dev),
+        _ptr(h0, "h0", f32, (Bsz, D, N), dev), _ptr(dy, "dy", dt, (Bsz, L, D), dev),
+        _ptr(ckpt, "ckpt", f32, None, dev),
+        _ptr(dx, "dx", dt, (Bsz, L, D), dev), _ptr(ddelta, "ddelta", dt, (Bsz, L, D), dev),
+        _ptr(dA, "dA", f32, (D, N), dev), _ptr(dB, "dB", f32, (Bsz, L, N), dev),
+        _ptr(dC, "dC", f32, (Bsz, L, N), dev), _ptr(dD, "dD", f32, (D,), dev),
+        _ptr(dh0, "dh0", f32, (Bsz, D, N), dev),
+    ]
+    need = ssm_scan_bwd_workspace_bytes(Bsz, L, D, N, code, ckpt is not None)
+    ws, nbytes = _workspace(need, dev, ws)
+    _check(lib.ssm_scan_bwd(_stream(dev), code, Bsz, L, D, N, *args,
+                            _ptr(ws, "ws") if ws is not None else None, nbytes))
+    return dict(dx=dx, ddelta=ddelta, dA=dA, dB=dB, dC=dC, dD=dD, dh0=dh0)
+
+
+# ----------------------------------------------------------------------------------
+# conv1d / RMSNorm
+# ----------------------------------------------------------------------------------
+
+def conv1d_causal_bwd_workspace_bytes(B, L, D, K, dtype_code) -> int:
+    return int(load().conv1d_causal_bwd_workspace_bytes(B, L, D, K, dtype_code))
+
+
+def conv1d_causal_bwd(x, W, dout, dx=None, dW=None, db=None, ws=None):
+    """Returns dict dx (overwritten), dW, db (accumulated; zeros if not given)."""
+    lib = load()
+    Bsz, L, D = x.shape
+    K = W.shape[1]
+    dev = x.device
+    dt = x.dtype
+    code = _dtype_code(x)
+    f32 = torch.float32
+    dx = torch.empty_like(x) if dx is None else dx
+    dW = torch.zeros((D, K), dtype=f32, device=dev) if dW is None else dW
+    db = torch.zeros((D,), dtype=f32, device=dev) if db is None else db
+    args = [_ptr(x, "x", dt, (Bsz, L, D), dev), _ptr(W, "W", f32, (D, K), dev),
+            _ptr(dout, "dout", dt, (Bsz, L, D), dev), _ptr(dx, "dx", dt, (Bsz, L, D), dev),
+            _ptr(dW, "dW", f32, (D, K), dev), _ptr(db, "db", f32, (D,), dev)]
+    need = conv1d_causal_bwd_workspace_bytes(Bsz, L, D, K, code)
+    ws, nbytes = _workspace(need, dev, ws)
+    _check(lib.conv1d_causal_bwd(_stream(dev), code, Bsz, L, D, K, *args,
+                                 _ptr(ws, "ws") if ws is not None else None, nbytes))
+    return dict(dx=dx, dW=dW, db=db)
+
+
+def rmsnorm_bwd_workspace_bytes(R, M, dtype_code) -> int:
+    return int(load().rmsnorm_bwd_workspace_bytes(R, M, dtype_code))
+
+
+def rmsnorm_bwd(dy, x, scale, rms, dx=None, dscale=None, ws=None):
+    """Returns dict dx (overwritten), dscale (accumulated; zeros if not given)."""
+    lib = load()
+    R, M = x.shape
+    dev = x.device
+    dt = x.dtype
+    code = _dtype_code(x)
+    f32 = torch.float32
+    dx = torch.empty_like(x) if dx is None else dx
+    dscale = torch.zeros((M,), dtype=f32, device=dev) if dscale is None else dscale
+    args = [_ptr(dy, "dy", dt, (R, M), dev), _ptr(x, "x", dt, (R, M), dev),
+            _ptr(scale, "scale", f32, (M,), dev), _ptr(rms, "rms", f32, (R,), dev),
+            _ptr(dx, "dx", dt, (R, M), dev), _ptr(dscale, "dscale", f32, (M,), dev)]
+    need = rmsnorm_bwd_workspace_bytes(R, M, code)
+    ws, nbytes = _workspace(need, dev, ws)
+    _check(lib.rmsnorm_bwd(_stream(dev), code, R, M, *args,
+                           _ptr(ws, "ws") if ws is not None else None, nbytes))
+    return dict(dx=dx, dscale=dscale)

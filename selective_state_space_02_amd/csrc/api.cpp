@@ -1,0 +1,365 @@
+// C ABI of libssmscan.so: host-side validation, workspace sizing and carving, and the
+// launch sequence of each operation.  All validation happens before the first HIP
+// call, so every rejection path runs (and is tested) without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/ssm_scan.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return SSM_OK;
+}
+
+constexpr int64_t kMaxElems = int64_t(1) << 46;  // guards int64 index arithmetic
+constexpr size_t kAlign = 256;                    // workspace sub-buffer alignment
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Carves consecutive 256-byte-aligned regions out of a workspace.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  float* take(size_t nfloats) {
+    float* p = base ? reinterpret_cast<float*>(base + off) : nullptr;
+    off += round_up(nfloats * sizeof(float));
+    return p;
+  }
+};
+
+// ---------------------------------------------------------------------------------
+// scan plans
+// ---------------------------------------------------------------------------------
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Coarse chunking: enough chunks that B * ceil(D/16) * nc wavefronts fill the GPU,
+// chunk lengths a multiple of the checkpoint interval.
+ssm::Chunking choose_chunks(int64_t B, int64_t L, int64_t D, int64_t target_waves) {
+  ssm::Chunking c;
+  c.nf = cdiv(L, ssm::kTc);
+  const int64_t chan_waves = B * cdiv(D, 16);
+  int64_t nc = cdiv(target_waves, chan_waves);
+  if (nc < 1) nc = 1;
+  if (nc > c.nf) nc = c.nf;
+  if (nc > 65535) nc = 65535;
+  c.Lc = cdiv(c.nf, nc) * ssm::kTc;
+  c.nc = int(cdiv(L, c.Lc));
+  return c;
+}
+
+constexpr int64_t kFwdTargetWaves = 4096;
+constexpr int64_t kBwdTargetWaves = 2048;
+
+size_t fwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, ssm::FwdPlan* plan, void* ws) {
+  const ssm::Chunking c = choose_chunks(B, L, D, kFwdTargetWaves);
+  Carver cv(ws);
+  ssm::FwdPlan p{};
+  p.nc = c.nc;
+  p.Lc = c.Lc;
+  p.nf = c.nf;
+  if (c.nc > 1) {
+    p.S = cv.take(size_t(B) * c.nc * D * N);
+    p.SD = cv.take(size_t(B) * c.nc * D);
+    p.hin = cv.take(size_t(B) * c.nc * D * N);
+  }
+  if (plan) *plan = p;
+  return cv.off;
+}
+
+size_t ckpt_floats(int64_t B, int64_t L, int64_t D, int64_t N) {
+  return size_t(B) * size_t(cdiv(L, ssm::kTc)) * size_t(D) * size_t(N);
+}
+
+size_t bwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, bool with_ckpt, ssm::BwdPlan* plan,
+              float** ckpt_out, ssm::FwdPlan* fplan, void* ws) {
+  const ssm::Chunking c = choose_chunks(B, L, D, kBwdTargetWaves);
+  Carver cv(ws);
+  ssm::BwdPlan p{};
+  p.nc = c.nc;
+  p.Lc = c.Lc;
+  p.nf = c.nf;
+  p.ng = cdiv(D, 64);
+  if (c.nc > 1) {
+    p.GS = cv.take(size_t(B) * c.nc * D * N);
+    p.SD = cv.take(size_t(B) * c.nc * D);
+    p.gin = cv.take(size_t(B) * c.nc * D * N);
+  }
+  p.dBp = cv.take(size_t(p.ng) * B * L * N);
+  p.dCp = cv.take(size_t(p.ng) * B * L * N);
+  p.dAp = cv.take(size_t(B) * c.nc * D * N);
+  p.dDp = cv.take(size_t(B) * c.nc * D);
+  if (!with_ckpt) {
+    float* ck = cv.take(ckpt_floats(B, L, D, N));
+    if (ckpt_out) *ckpt_out = ck;
+    // the forward's own workspace follows
+    char* fbase = ws ? static_cast<char*>(ws) + cv.off : nullptr;
+    cv.off += fwd_ws(B, L, D, N, fplan, fbase);
+  }
+  if (plan) *plan = p;
+  return cv.off;
+}
+
+int check_scan_dims(ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D, int64_t N) {
+  if (B <= 0 || L <= 0 || D <= 0 || N <= 0)
+    return fail(SSM_ERR_ARG, "sizes must be positive (B=%lld L=%lld D=%lld N=%lld)",
+                (long long)B, (long long)L, (long long)D, (long long)N);
+  if (dtype != SSM_F32 && dtype != SSM_BF16)
+    return fail(SSM_ERR_UNSUPPORTED, "dtype %d not supported (SSM_F32 or SSM_BF16)", int(dtype));
+  if (N != 4 && N != 8 && N != 16)
+    return fail(SSM_ERR_UNSUPPORTED, "state size N=%lld not supported (4, 8 or 16)", (long long)N);
+  if (B > 65535) return fail(SSM_ERR_UNSUPPORTED, "batch B=%lld exceeds 65535", (long long)B);
+  if (B > kMaxElems / L || B * L > kMaxElems / D || B * L * D > kMaxElems / N)
+    return fail(SSM_ERR_ARG, "tensor sizes overflow");
+  return SSM_OK;
+}
+
+struct Ptr {
+  const void* p;
+  const char* name;
+};
+
+int check_ptrs(std::initializer_list<Ptr> required, std::initializer_list<Ptr> optional) {
+  for (const Ptr& q : required)
+    if (!q.p) return fail(SSM_ERR_ARG, "required pointer '%s' is NULL", q.name);
+  for (const Ptr& q : required)
+    if (!aligned16(q.p)) return fail(SSM_ERR_ALIGN, "pointer '%s' is not 16-byte aligned", q.name);
+  for (const Ptr& q : optional)
+    if (q.p && !aligned16(q.p))
+      return fail(SSM_ERR_ALIGN, "pointer '%s' is not 16-byte aligned", q.name);
+  return SSM_OK;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (ws_bytes < need)
+    return fail(SSM_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", ws_bytes,
+                need);
+  if (need > 0 && !ws) return fail(SSM_ERR_WORKSPACE, "workspace pointer is NULL");
+  if (ws && !aligned16(ws)) return fail(SSM_ERR_ALIGN, "workspace is not 16-byte aligned");
+  return SSM_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// conv plan
+void conv_plan(int64_t B, int64_t L, int64_t D, ssm_dtype_t, ssm::ConvPlan* p) {
+  p->vec = (D % 4 == 0) ? 4 : 1;
+  const int64_t colblocks = cdiv(D / p->vec, 256);
+  // about 2048 blocks; time blocks of at least 64 steps
+  int64_t nTb = cdiv(2048, colblocks * B);
+  int64_t maxTb = cdiv(L, 64);
+  if (nTb > maxTb) nTb = maxTb;
+  if (nTb < 1) nTb = 1;
+  p->Tb = cdiv(L, nTb);
+  p->nTb = cdiv(L, p->Tb);
+}
+
+size_t conv_ws(int64_t B, int64_t L, int64_t D, int64_t K, ssm_dtype_t dt, ssm::ConvPlan* plan,
+               void* ws) {
+  ssm::ConvPlan p{};
+  conv_plan(B, L, D, dt, &p);
+  Carver cv(ws);
+  p.dWp = cv.take(size_t(B) * p.nTb * D * K);
+  p.dbp = cv.take(size_t(B) * p.nTb * D);
+  if (plan) *plan = p;
+  return cv.off;
+}
+
+// rms plan; returns false if M is not supported
+bool rms_plan(int64_t R, int64_t M, ssm_dtype_t dt, ssm::RmsPlan* p) {
+  const int64_t full = (dt == SSM_BF16) ? 8 : 4;
+  p->vec = (M % full == 0) ? full : 1;
+  const int64_t per_pass = 64 * p->vec;
+  const int64_t need = cdiv(M, per_pass);
+  int64_t passes = 1;
+  while (passes < need) passes *= 2;
+  if (passes > 16) return false;
+  p->passes = passes;
+  // about 512 blocks of 4 wavefronts, at least 4 rows per block
+  int64_t rpb = cdiv(R, 512);
+  if (rpb < 4) rpb = 4;
+  p->rows_per_block = rpb;
+  p->nblk = cdiv(R, rpb);
+  return true;
+}
+
+size_t rms_ws(int64_t R, int64_t M, ssm_dtype_t dt, ssm::RmsPlan* plan, void* ws) {
+  ssm::RmsPlan p{};
+  if (!rms_plan(R, M, dt, &p)) return 0;
+  Carver cv(ws);
+  p.dsp = cv.take(size_t(p.nblk) * M);
+  if (plan) *plan = p;
+  return cv.off;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ssm_last_error(void) { return g_err.c_str(); }
+
+const char* ssm_version(void) { return "ssmscan-gfx950 0.1.0"; }
+
+size_t ssm_scan_ckpt_bytes(int64_t B, int64_t L, int64_t D, int64_t N) {
+  if (B <= 0 || L <= 0 || D <= 0 || N <= 0) return 0;
+  return ckpt_floats(B, L, D, N) * sizeof(float);
+}
+
+size_t ssm_scan_fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype_t) {
+  if (B <= 0 || L <= 0 || D <= 0 || N <= 0) return 0;
+  return fwd_ws(B, L, D, N, nullptr, nullptr);
+}
+
+size_t ssm_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype_t,
+                                    int with_ckpt) {
+  if (B <= 0 || L <= 0 || D <= 0 || N <= 0) return 0;
+  return bwd_ws(B, L, D, N, with_ckpt != 0, nullptr, nullptr, nullptr, nullptr);
+}
+
+int ssm_scan_fwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D, int64_t N,
+                 const void* x, const void* delta, const float* A, const void* Bm,
+                 const void* Cm, const float* Dv, const float* h0, void* y, float* ckpt,
+                 float* h_last, void* ws, size_t ws_bytes) {
+  int rc = check_scan_dims(dtype, B, L, D, N);
+  if (rc) return rc;
+  rc = check_ptrs({{x, "x"}, {delta, "delta"}, {A, "A"}, {Bm, "Bm"}, {Cm, "Cm"}, {Dv, "Dv"}, {y, "y"}},
+                  {{h0, "h0"}, {ckpt, "ckpt"}, {h_last, "h_last"}});
+  if (rc) return rc;
+  ssm::FwdPlan p{};
+  const size_t need = fwd_ws(B, L, D, N, &p, nullptr);
+  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  fwd_ws(B, L, D, N, &p, ws);
+  p.ckpt = ckpt;
+  ssm::ScanArgs a{};
+  a.dtype = int(dtype);
+  a.B = B; a.L = L; a.D = D; a.N = N;
+  a.x = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dv = Dv; a.h0 = h0;
+  a.y = y; a.h_last = h_last;
+  return hip_status(ssm::launch_scan_fwd(a, p, static_cast<hipStream_t>(stream)), "ssm_scan_fwd");
+}
+
+int ssm_scan_bwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D, int64_t N,
+                 const void* x, const void* delta, const float* A, const void* Bm,
+                 const void* Cm, const float* Dv, const float* h0, const void* dy,
+                 const float* ckpt, void* dx, void* ddelta, float* dA, float* dB, float* dC,
+                 float* dD, float* dh0, void* ws, size_t ws_bytes) {
+  int rc = check_scan_dims(dtype, B, L, D, N);
+  if (rc) return rc;
+  rc = check_ptrs({{x, "x"}, {delta, "delta"}, {A, "A"}, {Bm, "Bm"}, {Cm, "Cm"}, {Dv, "Dv"},
+                   {dy, "dy"}, {dx, "dx"}, {ddelta, "ddelta"}, {dA, "dA"}, {dB, "dB"},
+                   {dC, "dC"}, {dD, "dD"}},
+                  {{h0, "h0"}, {ckpt, "ckpt"}, {dh0, "dh0"}});
+  if (rc) return rc;
+  const bool with_ckpt = ckpt != nullptr;
+  ssm::BwdPlan p{};
+  ssm::FwdPlan fp{};
+  float* own_ckpt = nullptr;
+  const size_t need = bwd_ws(B, L, D, N, with_ckpt, &p, &own_ckpt, &fp, nullptr);
+  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  bwd_ws(B, L, D, N, with_ckpt, &p, &own_ckpt, &fp, ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  ssm::ScanArgs a{};
+  a.dtype = int(dtype);
+  a.B = B; a.L = L; a.D = D; a.N = N;
+  a.x = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dv = Dv; a.h0 = h0;
+  a.dy = dy; a.dx = dx; a.ddelta = ddelta; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD;
+  a.dh0 = dh0;
+  if (with_ckpt) {
+    p.ckpt = ckpt;
+  } else {
+    // recompute the forward's checkpoints (y is not needed)
+    fp.ckpt = own_ckpt;
+    ssm::ScanArgs f = a;
+    f.y = nullptr;
+    f.h_last = nullptr;
+    hipError_t e = ssm::launch_scan_fwd(f, fp, st);
+    if (e != hipSuccess) return hip_status(e, "ssm_scan_bwd (forward recompute)");
+    p.ckpt = own_ckpt;
+  }
+  return hip_status(ssm::launch_scan_bwd(a, p, st), "ssm_scan_bwd");
+}
+
+size_t conv1d_causal_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t K,
+                                         ssm_dtype_t dtype) {
+  if (B <= 0 || L <= 0 || D <= 0 || K <= 0) return 0;
+  return conv_ws(B, L, D, K, dtype, nullptr, nullptr);
+}
+
+int conv1d_causal_bwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D,
+                      int64_t K, const void* x, const float* W, const void* dout, void* dx,
+                      float* dW, float* db, void* ws, size_t ws_bytes) {
+  if (B <= 0 || L <= 0 || D <= 0 || K <= 0)
+    return fail(SSM_ERR_ARG, "sizes must be positive (B=%lld L=%lld D=%lld K=%lld)",
+                (long long)B, (long long)L, (long long)D, (long long)K);
+  if (dtype != SSM_F32 && dtype != SSM_BF16)
+    return fail(SSM_ERR_UNSUPPORTED, "dtype %d not supported", int(dtype));
+  if (K > 8) return fail(SSM_ERR_UNSUPPORTED, "conv width K=%lld not supported (1..8)", (long long)K);
+  if (B > kMaxElems / L || B * L > kMaxElems / D) return fail(SSM_ERR_ARG, "tensor sizes overflow");
+  int rc = check_ptrs({{x, "x"}, {W, "W"}, {dout, "dout"}, {dx, "dx"}, {dW, "dW"}, {db, "db"}}, {});
+  if (rc) return rc;
+  ssm::ConvPlan p{};
+  const size_t need = conv_ws(B, L, D, K, dtype, &p, nullptr);
+  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  conv_ws(B, L, D, K, dtype, &p, ws);
+  ssm::ConvArgs a{};
+  a.dtype = int(dtype);
+  a.B = B; a.L = L; a.D = D; a.K = K;
+  a.x = x; a.W = W; a.dout = dout; a.dx = dx; a.dW = dW; a.db = db;
+  return hip_status(ssm::launch_conv1d_bwd(a, p, static_cast<hipStream_t>(stream)),
+                    "conv1d_causal_bwd");
+}
+
+size_t rmsnorm_bwd_workspace_bytes(int64_t R, int64_t M, ssm_dtype_t dtype) {
+  if (R <= 0 || M <= 0) return 0;
+  return rms_ws(R, M, dtype, nullptr, nullptr);
+}
+
+int rmsnorm_bwd(void* stream, ssm_dtype_t dtype, int64_t R, int64_t M, const void* dy,
+                const void* x, const float* scale, const float* rms, void* dx, float* dscale,
+                void* ws, size_t ws_bytes) {
+  if (R <= 0 || M <= 0)
+    return fail(SSM_ERR_ARG, "sizes must be positive (R=%lld M=%lld)", (long long)R, (long long)M);
+  if (dtype != SSM_F32 && dtype != SSM_BF16)
+    return fail(SSM_ERR_UNSUPPORTED, "dtype %d not supported", int(dtype));
+  if (R > kMaxElems / M) return fail(SSM_ERR_ARG, "tensor sizes overflow");
+  ssm::RmsPlan p{};
+  if (!rms_plan(R, M, dtype, &p))
+    return fail(SSM_ERR_UNSUPPORTED, "row length M=%lld not supported for this dtype", (long long)M);
+  int rc = check_ptrs({{dy, "dy"}, {x, "x"}, {scale, "scale"}, {rms, "rms"}, {dx, "dx"},
+                       {dscale, "dscale"}}, {});
+  if (rc) return rc;
+  const size_t need = rms_ws(R, M, dtype, &p, nullptr);
+  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  rms_ws(R, M, dtype, &p, ws);
+  ssm::RmsArgs a{};
+  a.dtype = int(dtype);
+  a.R = R; a.M = M;
+  a.dy = dy; a.x = x; a.scale = scale; a.rms = rms; a.dx = dx; a.dscale = dscale;
+  return hip_status(ssm::launch_rmsnorm_bwd(a, p, static_cast<hipStream_t>(stream)), "rmsnorm_bwd");
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Internal interface between the C ABI (api.cpp) and the kernel translation units.
+// Arguments arrive here already validated; plans carry workspace pointers carved
+// out of the caller's workspace.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+// Checkpoint interval of the forward scan: the state before every kTc-th step is
+// saved for the backward.
+constexpr int kTc = 16;
+
+struct ScanArgs {
+  int dtype;  // 0 f32, 1 bf16
+  int64_t B, L, D, N;
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dv;
+  const float* h0;  // nullable [B][D][N]
+  void* y;          // fwd output
+  float* h_last;    // nullable
+  // backward
+  const void* dy;
+  void* dx;
+  void* ddelta;
+  float* dA;
+  float* dB;
+  float* dC;
+  float* dD;
+  float* dh0;  // nullable
+};
+
+// Coarse chunking of the sequence (shared rule for forward and backward).
+struct Chunking {
+  int nc;       // number of coarse chunks
+  int64_t Lc;   // chunk length, a multiple of kTc
+  int64_t nf;   // number of checkpoints, ceil(L / kTc)
+};
+
+struct FwdPlan {
+  int nc;
+  int64_t Lc, nf;
+  float* S;     // [B][nc][D][N]   (nc > 1)
+  float* SD;    // [B][nc][D]      (nc > 1)
+  float* hin;   // [B][nc][D][N]   (nc > 1)
+  float* ckpt;  // [B][nf][D][N]   nullable
+};
+
+struct BwdPlan {
+  int nc;
+  int64_t Lc, nf, ng;
+  const float* ckpt;  // [B][nf][D][N]
+  float* GS;          // [B][nc][D][N]  (nc > 1)
+  float* SD;          // [B][nc][D]     (nc > 1)
+  float* gin;         // [B][nc][D][N]  (nc > 1)
+  float* dBp;         // [ng][B][L][N]
+  float* dCp;         // [ng][B][L][N]
+  float* dAp;         // [B*nc][D][N]
+  float* dDp;         // [B*nc][D]
+};
+
+struct ConvArgs {
+  int dtype;
+  int64_t B, L, D, K;
+  const void* x;
+  const float* W;
+  const void* dout;
+  void* dx;
+  float* dW;
+  float* db;
+};
+
+struct ConvPlan {
+  int64_t Tb, nTb, vec;
+  float* dWp;  // [B*nTb][D][K]
+  float* dbp;  // [B*nTb][D]
+};
+
+struct RmsArgs {
+  int dtype;
+  int64_t R, M;
+  const void* dy;
+  const void* x;
+  const float* scale;
+  const float* rms;
+  void* dx;
+  float* dscale;
+};
+
+struct RmsPlan {
+  int64_t vec, passes, rows_per_block, nblk;
+  float* dsp;  // [nblk][M]
+};
+
+hipError_t launch_scan_fwd(const ScanArgs& a, const FwdPlan& p, hipStream_t st);
+hipError_t launch_scan_bwd(const ScanArgs& a, const BwdPlan& p, hipStream_t st);
+hipError_t launch_conv1d_bwd(const ConvArgs& a, const ConvPlan& p, hipStream_t st);
+hipError_t launch_rmsnorm_bwd(const RmsArgs& a, const RmsPlan& p, hipStream_t st);
+// out[j] (+)= sum_{p < P} part[p*J + j], summed in order p = 0, 1, ..., P-1.
+hipError_t launch_reduce(const float* part, int64_t P, int64_t J, float* out, bool accumulate,
+                         hipStream_t st);
+
+}  // namespace ssm

@@ -1,0 +1,272 @@
+// Selective-scan backward (backpropagation through time across the SSM state) for
+// gfx950.
+//
+// With upstream gradient dy, the state adjoint obeys the reverse recurrence
+//   g_t[n] = dy_t C_t[n] + a_{t+1}[n] g_{t+1}[n],      g_L = 0,
+// and the gradients are
+//   dx_t     = Dv dy_t + delta_t sum_n g_t[n] B_t[n]
+//   ddelta_t = sum_n g_t[n] (A[n] a_t[n] h_{t-1}[n] + B_t[n] x_t)
+//   dA[n]   += sum_{b,t} g_t[n] delta_t a_t[n] h_{t-1}[n]
+//   dB_t[n]  = sum_d g_t[n] delta_t x_t          dC_t[n] = sum_d dy_t h_t[n]
+//   dDv     += sum_{b,t} dy_t x_t                dh0[n]  = a_0[n] g_0[n]
+// The forward states are recomputed from the forward's checkpoints (the forward
+// recompute shared by the CPU and GPU backward in the rustytorch backward_cuda
+// commit); every contribution to a cross-channel or cross-time sum is kept and
+// summed in a fixed order, with no atomics (foxhunt ml-alpha backward-scratch commit:
+// per-channel slots followed by a reduction, nothing dropped).
+//
+// Parallel form (coarse chunks as in the forward).  Running the adjoint through a
+// chunk is linear: the adjoint pushed out of the chunk's first step is
+//   gp_start = G + P (.) gp_end,  P[n] = prod_t a_t[n],
+// with G the pushed adjoint of the chunk alone (gp_end = 0).  Launches:
+//   1. k_bwd_summary: G and sum(delta) of chunks 1..nc-1 (skipped when nc == 1);
+//   2. k_bwd_carry:   adjoint arriving at the end of every chunk;
+//   3. k_bwd_main:    per chunk, walk the kTc-step checkpoint intervals backwards:
+//                     recompute a_t and h_t of the interval from its checkpoint into
+//                     registers, then run the reverse step; dx and ddelta are
+//                     written, dB/dC are summed over the workgroup's 64 channels
+//                     (butterfly + LDS) into per-group partials, dA/dDv into
+//                     per-(batch, chunk) partials;
+//   4. k_reduce (reduce.hip): fixed-order sums of the partials.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ssm {
+
+template <typename T, int N>
+__global__ __launch_bounds__(256) void k_bwd_summary(
+    int64_t L, int64_t D, int64_t Lc, int nc, const T* __restrict__ delta,
+    const float* __restrict__ A, const T* __restrict__ Cm, const T* __restrict__ dy,
+    float* __restrict__ GS, float* __restrict__ SD) {
+  constexpr int NS = N / 4;
+  const int c = blockIdx.z + 1, b = blockIdx.y, tid = threadIdx.x, q = tid & 3;
+  const int64_t d = int64_t(blockIdx.x) * 64 + (tid >> 2);
+  if (d >= D) return;
+  float A2[NS], gp[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    A2[j] = A[d * N + q * NS + j] * kLog2e;
+    gp[j] = 0.f;
+  }
+  float sd = 0.f;
+  const int64_t t0 = int64_t(c) * Lc, t1 = (t0 + Lc < L) ? t0 + Lc : L;
+#pragma unroll 4
+  for (int64_t t = t1 - 1; t >= t0; --t) {
+    const int64_t i = (int64_t(b) * L + t) * D + d;
+    const float dl = ld(delta, i), dyv = ld(dy, i);
+    float Cv[NS];
+    load_vec<T, NS>(Cm + (int64_t(b) * L + t) * N + q * NS, Cv);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const float g = __builtin_fmaf(dyv, Cv[j], gp[j]);
+      gp[j] = __builtin_amdgcn_exp2f(dl * A2[j]) * g;
+    }
+    sd += dl;
+  }
+  const int64_t o = (int64_t(b) * nc + c) * D + d;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) GS[o * N + q * NS + j] = gp[j];
+  if (q == 0) SD[o] = sd;
+}
+
+template <int N>
+__global__ __launch_bounds__(256) void k_bwd_carry(
+    int64_t B, int64_t D, int nc, const float* __restrict__ A, const float* __restrict__ GS,
+    const float* __restrict__ SD, float* __restrict__ gin) {
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= B * D * N) return;
+  const int64_t n = idx % N, bd = idx / N, d = bd % D, b = bd / D;
+  const float A2 = A[d * N + n] * kLog2e;
+  float gp = 0.f;
+  for (int c = nc - 1; c >= 0; --c) {
+    const int64_t o = (b * nc + c) * D + d;
+    gin[o * N + n] = gp;
+    if (c > 0) {
+      const float P = __builtin_amdgcn_exp2f(A2 * SD[o]);
+      gp = __builtin_fmaf(P, gp, GS[o * N + n]);
+    }
+  }
+}
+
+template <typename T, int N>
+__global__ __launch_bounds__(256) void k_bwd_main(
+    int64_t B, int64_t L, int64_t D, int64_t Lc, int nc, int64_t nf,
+    const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
+    const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dv,
+    const T* __restrict__ dy, const float* __restrict__ ckpt, const float* __restrict__ gin,
+    T* __restrict__ dx, T* __restrict__ ddelta, float* __restrict__ dBp,
+    float* __restrict__ dCp, float* __restrict__ dAp, float* __restrict__ dDp,
+    float* __restrict__ dh0) {
+  constexpr int NS = N / 4;
+  constexpr int V = 2 * NS;  // per-lane values summed over channels: dB (NS), dC (NS)
+  __shared__ float red[4][kTc][2 * N];
+
+  const int c = blockIdx.z, b = blockIdx.y, grp = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = tid & 3;
+  const int64_t d = int64_t(grp) * 64 + (tid >> 2);
+  const bool act = d < D;
+
+  float A2[NS], gp[NS], dA_acc[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    A2[j] = act ? A[d * N + q * NS + j] * kLog2e : 0.f;
+    gp[j] = (act && gin) ? gin[((int64_t(b) * nc + c) * D + d) * N + q * NS + j] : 0.f;
+    dA_acc[j] = 0.f;
+  }
+  const float Dd = act ? Dv[d] : 0.f;
+  float dD_acc = 0.f;
+
+  const int64_t t0 = int64_t(c) * Lc, t1 = (t0 + Lc < L) ? t0 + Lc : L;
+  const int64_t nfine = (t1 - t0 + kTc - 1) / kTc;
+  const int writer = chan_reduce_writer<V>(lane);
+  const int vidx = chan_reduce_index<V>(lane);
+  const int ridx = (vidx < NS) ? (q * NS + vidx) : (N + q * NS + (vidx - NS));
+
+  for (int64_t fi = nfine - 1; fi >= 0; --fi) {
+    const int64_t tf = t0 + fi * kTc;
+    float as[kTc][NS], hs[kTc][NS];
+    {
+      float h[NS];
+#pragma unroll
+      for (int j = 0; j < NS; ++j)
+        h[j] = act ? ckpt[((int64_t(b) * nf + tf / kTc) * D + d) * N + q * NS + j] : 0.f;
+#pragma unroll
+      for (int s = 0; s < kTc; ++s) {
+        const int64_t t = tf + s;
+        const bool v = act && t < L;
+        const int64_t i = (int64_t(b) * L + t) * D + d;
+        const float dl = v ? ld(delta, i) : 0.f;
+        const float xv = v ? ld(x, i) : 0.f;
+        float Bv[NS];
+        if (t < L) load_vec<T, NS>(Bm + (int64_t(b) * L + t) * N + q * NS, Bv);
+        else zero(Bv);
+        const float u = dl * xv;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          const float a = __builtin_amdgcn_exp2f(dl * A2[j]);
+          h[j] = __builtin_fmaf(a, h[j], u * Bv[j]);
+          as[s][j] = a;
+          hs[s][j] = h[j];
+        }
+      }
+    }
+#pragma unroll
+    for (int s = kTc - 1; s >= 0; --s) {
+      const int64_t t = tf + s;
+      const bool tv = t < L;
+      const bool v = act && tv;
+      const int64_t i = (int64_t(b) * L + t) * D + d;
+      const float dl = v ? ld(delta, i) : 0.f;
+      const float xv = v ? ld(x, i) : 0.f;
+      const float dyv = v ? ld(dy, i) : 0.f;
+      float Bv[NS], Cv[NS];
+      if (tv) {
+        load_vec<T, NS>(Bm + (int64_t(b) * L + t) * N + q * NS, Bv);
+        load_vec<T, NS>(Cm + (int64_t(b) * L + t) * N + q * NS, Cv);
+      } else {
+        zero(Bv);
+        zero(Cv);
+      }
+      const float u = dl * xv;
+      float sB = 0.f, sAq = 0.f;
+      float vals[V];
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const float g = __builtin_fmaf(dyv, Cv[j], gp[j]);
+        const float qq = __builtin_fmaf(-u, Bv[j], hs[s][j]);  // a_t h_{t-1}
+        const float gq = g * qq;
+        dA_acc[j] = __builtin_fmaf(gq, dl, dA_acc[j]);
+        sAq = __builtin_fmaf(gq, A2[j], sAq);
+        sB = __builtin_fmaf(g, Bv[j], sB);
+        vals[j] = g * u;
+        vals[NS + j] = dyv * hs[s][j];
+        gp[j] = as[s][j] * g;
+      }
+      sB = quad_sum(sB);
+      sAq = quad_sum(sAq);
+      if (v && q == 0) {
+        st(dx, i, __builtin_fmaf(Dd, dyv, dl * sB));
+        st(ddelta, i, __builtin_fmaf(kLn2, sAq, xv * sB));
+      }
+      dD_acc = __builtin_fmaf(dyv, xv, dD_acc);
+      chan_reduce<V>(vals, lane);
+      if (writer) red[wave][s][ridx] = vals[0];
+    }
+    __syncthreads();
+    // sum the four wavefronts' channel sums and write this group's partial
+    for (int k = tid; k < kTc * 2 * N; k += 256) {
+      const int s = k / (2 * N), r = k % (2 * N);
+      const int64_t t = tf + s;
+      if (t < L) {
+        const float sum = (red[0][s][r] + red[1][s][r]) + (red[2][s][r] + red[3][s][r]);
+        const int64_t o = ((int64_t(grp) * B + b) * L + t) * N;
+        if (r < N) dBp[o + r] = sum;
+        else dCp[o + r - N] = sum;
+      }
+    }
+    __syncthreads();
+  }
+
+  if (act) {
+    const int64_t o = (int64_t(b) * nc + c) * D + d;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) dAp[o * N + q * NS + j] = dA_acc[j];
+    if (q == 0) dDp[o] = dD_acc;
+    if (dh0 && c == 0) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) dh0[(int64_t(b) * D + d) * N + q * NS + j] = gp[j];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// host launcher
+// ---------------------------------------------------------------------------------
+template <typename T, int N>
+static hipError_t bwd_impl(const ScanArgs& a, const BwdPlan& p, hipStream_t st) {
+  const T* x = static_cast<const T*>(a.x);
+  const T* delta = static_cast<const T*>(a.delta);
+  const T* Bm = static_cast<const T*>(a.Bm);
+  const T* Cm = static_cast<const T*>(a.Cm);
+  const T* dy = static_cast<const T*>(a.dy);
+  const dim3 block(256);
+  const float* gin = nullptr;
+  if (p.nc > 1) {
+    hipLaunchKernelGGL((k_bwd_summary<T, N>), dim3(p.ng, a.B, p.nc - 1), block, 0, st, a.L,
+                       a.D, p.Lc, p.nc, delta, a.A, Cm, dy, p.GS, p.SD);
+    const int64_t tot = a.B * a.D * N;
+    hipLaunchKernelGGL((k_bwd_carry<N>), dim3((tot + 255) / 256), block, 0, st, a.B, a.D,
+                       p.nc, a.A, p.GS, p.SD, p.gin);
+    gin = p.gin;
+  }
+  hipLaunchKernelGGL((k_bwd_main<T, N>), dim3(p.ng, a.B, p.nc), block, 0, st, a.B, a.L, a.D,
+                     p.Lc, p.nc, p.nf, x, delta, a.A, Bm, Cm, a.Dv, dy, p.ckpt, gin,
+                     static_cast<T*>(a.dx), static_cast<T*>(a.ddelta), p.dBp, p.dCp, p.dAp,
+                     p.dDp, a.dh0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t BLN = a.B * a.L * N;
+  if ((e = launch_reduce(p.dBp, p.ng, BLN, a.dB, false, st)) != hipSuccess) return e;
+  if ((e = launch_reduce(p.dCp, p.ng, BLN, a.dC, false, st)) != hipSuccess) return e;
+  if ((e = launch_reduce(p.dAp, a.B * p.nc, a.D * N, a.dA, true, st)) != hipSuccess) return e;
+  return launch_reduce(p.dDp, a.B * p.nc, a.D, a.dD, true, st);
+}
+
+hipError_t launch_scan_bwd(const ScanArgs& a, const BwdPlan& p, hipStream_t st) {
+  if (a.dtype == 0) {
+    switch (a.N) {
+      case 4: return bwd_impl<float, 4>(a, p, st);
+      case 8: return bwd_impl<float, 8>(a, p, st);
+      case 16: return bwd_impl<float, 16>(a, p, st);
+    }
+  } else {
+    switch (a.N) {
+      case 4: return bwd_impl<bf16_t, 4>(a, p, st);
+      case 8: return bwd_impl<bf16_t, 8>(a, p, st);
+      case 16: return bwd_impl<bf16_t, 16>(a, p, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ssm

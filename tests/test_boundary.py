@@ -1,0 +1,231 @@
+"""C-ABI boundary tests that need no GPU.
+
+The library must load, export every function ``include/ssm_scan.h`` declares, and reject
+bad arguments on the host before any HIP call: null required pointers, non-positive or
+overflowing sizes, unsupported N / K / dtype / M, misaligned pointers and too-small
+workspaces each return their documented code with a message.  Fake (never dereferenced)
+device addresses are passed; every call here is rejected by validation, so no kernel is
+launched and no device memory is touched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_state_space_02_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
+
+FAKE = 0x7F0000000000          # 16-byte aligned, never dereferenced
+MIS = FAKE + 4                 # misaligned
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b([a-z_0-9]+)\s*\(", src)
+    skip = {"if", "for", "while", "sizeof", "return"}
+    return sorted({n for n in names if n not in skip})
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("ssm_scan_fwd", "ssm_scan_bwd", "conv1d_causal_bwd", "rmsnorm_bwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = b.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"symbol {name} declared in ssm_scan.h is not exported"
+    assert set(b.EXPORTS) == set(declared_functions())
+
+
+def test_version_and_empty_error():
+    assert b.version().startswith("ssmscan-gfx950")
+
+
+def _fwd(lib, B=2, L=64, D=32, N=16, dtype=0, x=FAKE, delta=FAKE, A=FAKE, Bm=FAKE, Cm=FAKE,
+         Dv=FAKE, h0=None, y=FAKE, ckpt=None, h_last=None, ws=None, ws_bytes=0):
+    return lib.ssm_scan_fwd(None, dtype, B, L, D, N, x, delta, A, Bm, Cm, Dv, h0, y, ckpt,
+                            h_last, ws, ws_bytes)
+
+
+def _bwd(lib, B=2, L=64, D=32, N=16, dtype=0, ckpt=FAKE, ws=None, ws_bytes=0, **kw):
+    p = dict(x=FAKE, delta=FAKE, A=FAKE, Bm=FAKE, Cm=FAKE, Dv=FAKE, h0=None, dy=FAKE,
+             dx=FAKE, ddelta=FAKE, dA=FAKE, dB=FAKE, dC=FAKE, dD=FAKE, dh0=None)
+    p.update(kw)
+    return lib.ssm_scan_bwd(None, dtype, B, L, D, N, p["x"], p["delta"], p["A"], p["Bm"],
+                            p["Cm"], p["Dv"], p["h0"], p["dy"], ckpt, p["dx"], p["ddelta"],
+                            p["dA"], p["dB"], p["dC"], p["dD"], p["dh0"], ws, ws_bytes)
+
+
+@pytest.mark.parametrize("dims", [(0, 8, 8, 16), (2, 0, 8, 16), (2, 8, 0, 16), (2, 8, 8, 0),
+                                  (-1, 8, 8, 16)])
+def test_scan_rejects_nonpositive_sizes(dims):
+    lib = b.load()
+    B, L, D, N = dims
+    assert _fwd(lib, B, L, D, N) == b.SSM_ERR_ARG
+    assert "positive" in b.last_error()
+    assert _bwd(lib, B, L, D, N) == b.SSM_ERR_ARG
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 12, 32, 64])
+def test_scan_rejects_unsupported_state_size(N):
+    lib = b.load()
+    assert _fwd(lib, N=N) == b.SSM_ERR_UNSUPPORTED
+    assert "state size" in b.last_error()
+    assert _bwd(lib, N=N) == b.SSM_ERR_UNSUPPORTED
+
+
+def test_scan_rejects_unsupported_dtype_and_batch():
+    lib = b.load()
+    assert _fwd(lib, dtype=2) == b.SSM_ERR_UNSUPPORTED
+    assert _fwd(lib, B=70000) == b.SSM_ERR_UNSUPPORTED
+
+
+def test_scan_rejects_overflowing_sizes():
+    lib = b.load()
+    assert _fwd(lib, B=60000, L=1 << 30, D=1 << 20) == b.SSM_ERR_ARG
+    assert "overflow" in b.last_error()
+
+
+@pytest.mark.parametrize("missing", ["x", "delta", "A", "Bm", "Cm", "Dv", "y"])
+def test_fwd_rejects_null_required_pointer(missing):
+    lib = b.load()
+    assert _fwd(lib, **{missing: None}) == b.SSM_ERR_ARG
+    assert missing in b.last_error()
+
+
+@pytest.mark.parametrize("missing", ["x", "delta", "A", "Bm", "Cm", "Dv", "dy", "dx", "ddelta",
+                                     "dA", "dB", "dC", "dD"])
+def test_bwd_rejects_null_required_pointer(missing):
+    lib = b.load()
+    assert _bwd(lib, **{missing: None}) == b.SSM_ERR_ARG
+    assert missing in b.last_error()
+
+
+@pytest.mark.parametrize("bad", ["x", "Bm", "y", "h0", "ckpt", "h_last"])
+def test_fwd_rejects_misaligned_pointer(bad):
+    lib = b.load()
+    assert _fwd(lib, **{bad: MIS}) == b.SSM_ERR_ALIGN
+    assert bad in b.last_error()
+
+
+def test_bwd_rejects_misaligned_pointer():
+    lib = b.load()
+    assert _bwd(lib, dh0=MIS) == b.SSM_ERR_ALIGN
+    assert _bwd(lib, dB=MIS) == b.SSM_ERR_ALIGN
+    assert _bwd(lib, ckpt=MIS) == b.SSM_ERR_ALIGN
+
+
+def test_scan_rejects_small_workspace():
+    lib = b.load()
+    # a workload with several coarse chunks needs a forward workspace
+    B, L, D, N = 2, 4096, 64, 16
+    need = b.ssm_scan_fwd_workspace_bytes(B, L, D, N, 0)
+    assert need > 0
+    assert _fwd(lib, B, L, D, N, ws=FAKE, ws_bytes=need - 1) == b.SSM_ERR_WORKSPACE
+    assert "workspace" in b.last_error()
+    assert _fwd(lib, B, L, D, N, ws=None, ws_bytes=need) == b.SSM_ERR_WORKSPACE
+    assert _fwd(lib, B, L, D, N, ws=MIS, ws_bytes=need) == b.SSM_ERR_ALIGN
+    needb = b.ssm_scan_bwd_workspace_bytes(B, L, D, N, 0, 1)
+    assert _bwd(lib, B, L, D, N, ws=FAKE, ws_bytes=needb - 1) == b.SSM_ERR_WORKSPACE
+
+
+def test_workspace_queries_are_consistent():
+    for (B, L, D, N) in [(1, 1, 1, 4), (2, 8, 8, 4), (256, 32, 64, 16), (8, 2048, 1536, 16),
+                         (2, 16384, 5120, 16), (3, 333, 80, 8)]:
+        assert b.ssm_scan_ckpt_bytes(B, L, D, N) == B * ((L + 15) // 16) * D * N * 4
+        with_ck = b.ssm_scan_bwd_workspace_bytes(B, L, D, N, 1, 1)
+        without = b.ssm_scan_bwd_workspace_bytes(B, L, D, N, 1, 0)
+        # recomputing the forward needs room for the checkpoints
+        assert without >= with_ck + b.ssm_scan_ckpt_bytes(B, L, D, N)
+        assert with_ck >= 2 * B * L * N * 4      # the dB and dC partials
+    assert b.ssm_scan_ckpt_bytes(0, 1, 1, 4) == 0
+    assert b.ssm_scan_fwd_workspace_bytes(1, 1, 1, 4, 0) == 0
+
+
+def _conv(lib, B=2, L=64, D=32, K=4, dtype=0, x=FAKE, W=FAKE, dout=FAKE, dx=FAKE, dW=FAKE,
+          db=FAKE, ws=None, ws_bytes=0):
+    return lib.conv1d_causal_bwd(None, dtype, B, L, D, K, x, W, dout, dx, dW, db, ws, ws_bytes)
+
+
+def test_conv_validation():
+    lib = b.load()
+    assert _conv(lib, K=0) == b.SSM_ERR_ARG
+    assert _conv(lib, K=9) == b.SSM_ERR_UNSUPPORTED
+    assert _conv(lib, L=0) == b.SSM_ERR_ARG
+    assert _conv(lib, dtype=5) == b.SSM_ERR_UNSUPPORTED
+    for name in ("x", "W", "dout", "dx", "dW", "db"):
+        assert _conv(lib, **{name: None}) == b.SSM_ERR_ARG
+        assert name in b.last_error()
+        assert _conv(lib, **{name: MIS}) == b.SSM_ERR_ALIGN
+    need = b.conv1d_causal_bwd_workspace_bytes(2, 64, 32, 4, 0)
+    assert need > 0
+    assert _conv(lib, ws=FAKE, ws_bytes=need - 1) == b.SSM_ERR_WORKSPACE
+
+
+def _rms(lib, R=64, M=128, dtype=0, dy=FAKE, x=FAKE, scale=FAKE, rms=FAKE, dx=FAKE,
+         dscale=FAKE, ws=None, ws_bytes=0):
+    return lib.rmsnorm_bwd(None, dtype, R, M, dy, x, scale, rms, dx, dscale, ws, ws_bytes)
+
+
+def test_rms_validation():
+    lib = b.load()
+    assert _rms(lib, R=0) == b.SSM_ERR_ARG
+    assert _rms(lib, M=-3) == b.SSM_ERR_ARG
+    assert _rms(lib, dtype=7) == b.SSM_ERR_UNSUPPORTED
+    assert _rms(lib, M=8192 + 8, dtype=1) == b.SSM_ERR_UNSUPPORTED
+    assert _rms(lib, M=4096 + 4, dtype=0) == b.SSM_ERR_UNSUPPORTED
+    assert _rms(lib, M=1025, dtype=0) == b.SSM_ERR_UNSUPPORTED       # not a multiple of 4
+    for name in ("dy", "x", "scale", "rms", "dx", "dscale"):
+        assert _rms(lib, **{name: None}) == b.SSM_ERR_ARG
+        assert _rms(lib, **{name: MIS}) == b.SSM_ERR_ALIGN
+    need = b.rmsnorm_bwd_workspace_bytes(64, 128, 0)
+    assert need > 0
+    assert _rms(lib, ws=FAKE, ws_bytes=need - 1) == b.SSM_ERR_WORKSPACE
+    assert b.rmsnorm_bwd_workspace_bytes(10, 8192, 1) > 0
+    assert b.rmsnorm_bwd_workspace_bytes(10, 8193, 1) == 0
+
+
+def test_error_message_is_per_call():
+    lib = b.load()
+    assert _fwd(lib, N=3) == b.SSM_ERR_UNSUPPORTED
+    msg1 = b.last_error()
+    assert _conv(lib, K=9) == b.SSM_ERR_UNSUPPORTED
+    assert b.last_error() != msg1
+
+
+def test_binding_rejects_cpu_and_strided_tensors():
+    import torch
+    x = torch.zeros(2, 8, 8)
+    with pytest.raises(ValueError, match="GPU"):
+        b._ptr(x, "x")
+    # strided views never reach the library
+    class FakeCuda:
+        pass
+    with pytest.raises(TypeError):
+        b._ptr(FakeCuda(), "x")
+
+
+def test_product_path_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(b, "_lib", None)
+    monkeypatch.setattr(b, "LIB_PATH", "/nonexistent/libssmscan.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        b.load()
+
+
+def test_no_oracle_in_product_sources():
+    # the product (library sources and binding) never references the oracle
+    pkg = os.path.join(ROOT, "selective_state_space_02_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in src and "from oracle" not in src, f
+                assert "liboracle" not in src, f
+    csrc = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
+    assert "ssm_scan.h" not in csrc and "common.hpp" not in csrc
