@@ -1,0 +1,312 @@
+"""Benchmark of the selective-scan hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of seeded synthetic input already
+resident in HBM: ssm_scan_fwd (with checkpoints), ssm_scan_bwd, conv1d_causal_bwd and
+rmsnorm_bwd, each through the C ABI.  Default workload: the Mamba-2.8B-shaped layer
+(B=2, L=16384, d_inner=5120, d_state=16, d_conv=4, bf16 activations, f32 state and
+arithmetic; RMSNorm backward over [32768, 2560]).
+
+Prints one JSON line: tokens*channels per second of the step (B*L*D / step time), the
+step's algorithmic HBM bytes per second, a roofline entry for the dominant kernel
+(measured live with HIP events recorded around that kernel on its own stream), and the
+f64 CPU oracle timed on a bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py --gpus N        (N > 1 exits: this build runs on one GPU)
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "scan fwd+bwd tokens·channels/sec and achieved HBM GB/s (% of peak), 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+
+# Algorithmic floating-point work per state update (b, t, d, n) of the backward main
+# kernel (recompute of a_t and h_t from the checkpoint, the adjoint step and every
+# gradient contribution); FMA counts 2, exp 1.  Derivation in the design doc.
+BWD_MAIN_FLOPS_PER_UPDATE = 20
+
+
+class HipEvents:
+    """Raw hipEvent_t pairs (the library's timing hook records them itself, so they are
+    created and read through the HIP runtime directly)."""
+
+    def __init__(self):
+        import ctypes
+        self.c = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventQuery.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def pair(self):
+        a, b = self.c.c_void_p(), self.c.c_void_p()
+        assert self.hip.hipEventCreate(self.c.byref(a)) == 0
+        assert self.hip.hipEventCreate(self.c.byref(b)) == 0
+        self.made += [a.value, b.value]
+        return a.value, b.value
+
+    def record(self, ev, stream_handle):
+        assert self.hip.hipEventRecord(self.c.c_void_p(ev), self.c.c_void_p(stream_handle)) == 0
+
+    def elapsed_ms(self, start, stop):
+        """None if the pair was never recorded (a kernel the workload did not launch)."""
+        ms = self.c.c_float()
+        rc = self.hip.hipEventElapsedTime(self.c.byref(ms), self.c.c_void_p(start), self.c.c_void_p(stop))
+        return ms.value if rc == 0 else None
+
+    def destroy(self):
+        for e in self.made:
+            self.hip.hipEventDestroy(self.c.c_void_p(e))
+        self.made = []
+
+
+def algorithmic_bytes(w):
+    """Bytes the method must move per step (HBM), by operation."""
+    s = 2 if w.dtype == "bf16" else 4
+    E = w.B * w.L * w.D
+    P = w.B * w.L * w.N
+    DN = w.D * w.N
+    fwd = 3 * E * s + 2 * P * s + (DN + w.D) * 4
+    bwd = 5 * E * s + 2 * P * s + 2 * P * 4 + 3 * (DN + w.D) * 4
+    conv = 3 * E * s + w.D * w.K * 4 * 3 + w.D * 4 * 2
+    RM = w.rms_rows * w.rms_dim
+    rms = 3 * RM * s + w.rms_dim * 4 * 3 + w.rms_rows * 4
+    return dict(scan_fwd=fwd, scan_bwd=bwd, conv_bwd=conv, rms_bwd=rms)
+
+
+def bwd_main_bytes(w):
+    """Algorithmic HBM bytes of the backward main kernel alone: x, delta, dy, B, C read;
+    dx, ddelta written (the dB/dC/dA/dD sums leave through the reduction kernels)."""
+    s = 2 if w.dtype == "bf16" else 4
+    E = w.B * w.L * w.D
+    P = w.B * w.L * w.N
+    return 5 * E * s + 2 * P * s
+
+
+def cpu_baseline(w, cpu_inputs, sample_channels, budget_note):
+    """The f64 oracle on a bounded sample: the scan forward+backward and the conv1d
+    backward on `sample_channels` channels (all batch rows, full length), and the
+    RMSNorm backward on the same fraction of its rows.  Scaled to tokens*channels/s of
+    the sample."""
+    import oracle
+    from selective_state_space_02_amd import synth
+
+    frac = sample_channels / w.D
+    p, c, r = cpu_inputs
+    q = {}
+    for k in ("x", "delta", "dy"):
+        q[k] = synth.as_f64(p[k][:, :, :sample_channels].contiguous())
+    q["A"] = synth.as_f64(p["A"][:sample_channels].contiguous())
+    q["Dv"] = synth.as_f64(p["Dv"][:sample_channels].contiguous())
+    q["Bm"] = synth.as_f64(p["Bm"])
+    q["Cm"] = synth.as_f64(p["Cm"])
+    cq = {k: synth.as_f64(v[..., :sample_channels].contiguous() if v.dim() == 3 else
+                          v[:sample_channels].contiguous()) for k, v in c.items()}
+    nrows = max(1, int(round(w.rms_rows * frac)))
+    rq = {"x": synth.as_f64(r["x"][:nrows]), "dy": synth.as_f64(r["dy"][:nrows]),
+          "scale": synth.as_f64(r["scale"]), "rms": synth.as_f64(r["rms"][:nrows])}
+    t0 = time.perf_counter()
+    oracle.scan_fwd(q["x"], q["delta"], q["A"], q["Bm"], q["Cm"], q["Dv"])
+    oracle.scan_bwd(q["x"], q["delta"], q["A"], q["Bm"], q["Cm"], q["Dv"], q["dy"])
+    t1 = time.perf_counter()
+    oracle.conv1d_bwd(cq["x"], cq["W"], cq["dout"])
+    t2 = time.perf_counter()
+    oracle.rmsnorm_bwd(rq["dy"], rq["x"], rq["scale"], rq["rms"])
+    t3 = time.perf_counter()
+    tokch = w.B * w.L * sample_channels
+    return {
+        "value": tokch / (t3 - t0),
+        "unit": "tokens*channels/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"{sample_channels} of {w.D} channels (all {w.B} batch rows x {w.L} steps) "
+                   f"for the scan fwd+bwd and conv1d bwd, {nrows} of {w.rms_rows} rows for the "
+                   f"RMSNorm bwd; f64; {budget_note}"),
+        "seconds": {"scan_fwd_bwd": t1 - t0, "conv_bwd": t2 - t1, "rms_bwd": t3 - t2},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mamba-2.8b")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-channels", type=int, default=0,
+                    help="channels in the oracle's sample (default: about 10-30 s of CPU work)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this build runs on one GPU: every figure is one GPU's "
+                          "throughput; --gpus must be 1"}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from selective_state_space_02_amd import binding as ssm
+    from selective_state_space_02_amd import synth
+    from selective_state_space_02_amd.workloads import BY_NAME
+
+    w = BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ssm.load()
+    print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
+
+    cpu_inputs = (synth.scan_inputs(w, args.seed), synth.conv_inputs(w, args.seed),
+                  synth.rms_inputs(w, args.seed))
+    p, c, r = ({k: v.to(dev) for k, v in d.items()} for d in cpu_inputs)
+    f32 = torch.float32
+    code = ssm.SSM_BF16 if w.dtype == "bf16" else ssm.SSM_F32
+    B, L, D, N, K = w.B, w.L, w.D, w.N, w.K
+    # every buffer allocated once, outside the timed region
+    y = torch.empty_like(p["x"])
+    ckpt = ssm.new_ckpt(B, L, D, N, dev)
+    ws_f = torch.empty(max(1, ssm.ssm_scan_fwd_workspace_bytes(B, L, D, N, code)), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(1, ssm.ssm_scan_bwd_workspace_bytes(B, L, D, N, code, True)), dtype=torch.uint8, device=dev)
+    dx = torch.empty_like(p["x"])
+    ddelta = torch.empty_like(p["x"])
+    dA = torch.zeros((D, N), dtype=f32, device=dev)
+    dB = torch.empty((B, L, N), dtype=f32, device=dev)
+    dC = torch.empty((B, L, N), dtype=f32, device=dev)
+    dD = torch.zeros((D,), dtype=f32, device=dev)
+    cdx = torch.empty_like(c["x"])
+    dW = torch.zeros((D, K), dtype=f32, device=dev)
+    db = torch.zeros((D,), dtype=f32, device=dev)
+    ws_c = torch.empty(max(1, ssm.conv1d_causal_bwd_workspace_bytes(B, L, D, K, code)), dtype=torch.uint8, device=dev)
+    rdx = torch.empty_like(r["x"])
+    dscale = torch.zeros((w.rms_dim,), dtype=f32, device=dev)
+    ws_r = torch.empty(max(1, ssm.rmsnorm_bwd_workspace_bytes(w.rms_rows, w.rms_dim, code)), dtype=torch.uint8, device=dev)
+
+    def call_fwd():
+        ssm.ssm_scan_fwd(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], p["Dv"], y=y, ckpt=ckpt, ws=ws_f)
+
+    def call_bwd():
+        ssm.ssm_scan_bwd(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], p["Dv"], p["dy"], ckpt=ckpt,
+                         dx=dx, ddelta=ddelta, dA=dA, dB=dB, dC=dC, dD=dD, ws=ws_b)
+
+    def call_conv():
+        ssm.conv1d_causal_bwd(c["x"], c["W"], c["dout"], dx=cdx, dW=dW, db=db, ws=ws_c)
+
+    def call_rms():
+        ssm.rmsnorm_bwd(r["dy"], r["x"], r["scale"], r["rms"], dx=rdx, dscale=dscale, ws=ws_r)
+
+    calls = [("scan_fwd", call_fwd), ("scan_bwd", call_bwd), ("conv_bwd", call_conv), ("rms_bwd", call_rms)]
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        for _, f in calls:
+            f()
+    torch.cuda.synchronize()
+
+    # events: per call (on torch's current stream, the stream every call is launched on)
+    # and around the backward main kernel through the library's timing hook
+    K_ = args.steps
+    he = HipEvents()
+    ev = {name: [he.pair() for _ in range(K_)] for name, _ in calls}
+    kernels = ["bwd_main", "fwd_output", "fwd_summary", "bwd_summary", "conv_bwd", "rms_bwd"]
+    kev = {k: [he.pair() for _ in range(K_)] for k in kernels}
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    print(f"[bench] timing {K_} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K_):
+        for k in kernels:
+            ssm.ssm_set_kernel_timer(k, *kev[k][i])
+        for name, f in calls:
+            he.record(ev[name][i][0], stream)
+            f()
+            he.record(ev[name][i][1], stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for k in kernels:
+        ssm.ssm_set_kernel_timer(k, None, None)
+
+    ms_per_step = (t1 - t0) * 1e3 / K_
+    call_ms = {name: sum(he.elapsed_ms(*pr) for pr in ev[name]) / K_ for name, _ in calls}
+
+    def kernel_ms(k):
+        vals = [he.elapsed_ms(*pr) for pr in kev[k]]
+        if any(v is None for v in vals):
+            return None        # a kernel this workload does not launch
+        return sum(vals) / K_
+    kern_ms = {k: kernel_ms(k) for k in kernels}
+    he.destroy()
+
+    tokch = B * L * D
+    value = tokch / (ms_per_step * 1e-3)
+    ab = algorithmic_bytes(w)
+    step_bytes = sum(ab.values())
+    scan_ms = call_ms["scan_fwd"] + call_ms["scan_bwd"]
+    main_ms = kern_ms["bwd_main"]
+    main_flops = BWD_MAIN_FLOPS_PER_UPDATE * B * L * D * N
+    achieved_tflops = main_flops / (main_ms * 1e-3) / 1e12
+    main_gbps = bwd_main_bytes(w) / (main_ms * 1e-3) / 1e9
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=f32, device=dev)
+        b2 = torch.empty_like(a)
+        b2.copy_(a)
+        torch.cuda.synchronize()
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens*channels/s",
+        "n_gpus": 1,
+        "steps": K_,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "L": L, "D": D, "N": N, "K": K,
+                   "io_dtype": w.dtype, "rms_rows": w.rms_rows, "rms_dim": w.rms_dim,
+                   "step": "ssm_scan_fwd + ssm_scan_bwd + conv1d_causal_bwd + rmsnorm_bwd"},
+        "hbm": {"algorithmic_bytes_per_step": step_bytes,
+                "GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+                "frac_of_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                "scan_fwd_bwd_GBps": (ab["scan_fwd"] + ab["scan_bwd"]) / (scan_ms * 1e-3) / 1e9},
+        "scan_fwd_bwd_tokens_channels_per_s": tokch / (scan_ms * 1e-3),
+        "call_ms": call_ms,
+        "kernel_ms": kern_ms,
+        "roofline": {
+            "kernel": "k_bwd_main (scan backward main)",
+            "bound": "alu",
+            "achieved": achieved_tflops,
+            "peak": FP32_VECTOR_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved_tflops / FP32_VECTOR_PEAK_TFLOPS,
+            "traffic": None,
+            "avg_launch_ms": main_ms,
+            "algorithmic_flops_per_launch": main_flops,
+            "algorithmic_bytes_per_launch": bwd_main_bytes(w),
+            "hbm_GBps_algorithmic": main_gbps,
+        },
+    }
+    if not args.no_cpu_baseline:
+        sample = args.cpu_sample_channels or max(16, min(w.D, 2048))
+        print(f"[bench] cpu baseline: oracle on {sample} channels", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, cpu_inputs, sample, "timed on this host's cores")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -23,7 +23,8 @@
  * - Streams.  `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *   Calls only enqueue work: they return before the GPU finishes and never
  *   synchronize.  Buffers must stay alive until the stream work completes.  Calls
- *   are re-entrant; the library keeps no state except a per-thread error message.
+ *   are re-entrant; the library keeps no state except a per-thread error message
+ *   and the per-thread timing hook below.
  * - Workspace.  Scratch (partial sums, chunk carries) lives in a caller buffer `ws`
  *   of at least the size the matching *_workspace_bytes() query returns for the
  *   same arguments; ws may be NULL when that size is 0.  Its content on entry is
@@ -64,6 +65,17 @@ const char *ssm_last_error(void);
 
 /* Library version string. */
 const char *ssm_version(void);
+
+/* Timing hook (measurement only; for benchmarks and profilers).  Arms, for the calling
+ * thread, a pair of caller-owned hipEvent_t (passed as void*) around one kernel: every
+ * later launch of that kernel by this thread records `start` on the call's stream just
+ * before the launch and `stop` just after it (the pair is re-recorded at each launch,
+ * so read it before the next call).  start = stop = NULL disarms.  The kernels:
+ *   1 scan-forward chunk summary    2 scan-forward carry    3 scan-forward output
+ *   4 scan-backward chunk summary   5 scan-backward carry   6 scan-backward main
+ *   7 conv1d backward               8 RMSNorm backward
+ * Returns SSM_ERR_ARG for an unknown id or a half-set pair.  Has no effect on results. */
+int ssm_set_kernel_timer(int kernel, void *start, void *stop);
 
 /* ---------------------------------------------------------------------------------
  * Selective scan (Mamba S6).  The pages name this scan and its reverse pass -- the

@@ -20,7 +20,7 @@ SSM_F32, SSM_BF16 = 0, 1
 SSM_OK, SSM_ERR_ARG, SSM_ERR_UNSUPPORTED, SSM_ERR_WORKSPACE, SSM_ERR_ALIGN, SSM_ERR_HIP = (
     0, -1, -2, -3, -4, -5)
 
-EXPORTS = ("ssm_last_error", "ssm_version", "ssm_scan_ckpt_bytes",
+EXPORTS = ("ssm_last_error", "ssm_version", "ssm_set_kernel_timer", "ssm_scan_ckpt_bytes",
            "ssm_scan_fwd_workspace_bytes", "ssm_scan_bwd_workspace_bytes", "ssm_scan_fwd",
            "ssm_scan_bwd", "conv1d_causal_bwd_workspace_bytes", "conv1d_causal_bwd",
            "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd")
@@ -56,6 +56,8 @@ def load():
     lib.ssm_last_error.argtypes = []
     lib.ssm_version.restype = ctypes.c_char_p
     lib.ssm_version.argtypes = []
+    lib.ssm_set_kernel_timer.restype = _E
+    lib.ssm_set_kernel_timer.argtypes = [_E, _P, _P]
     lib.ssm_scan_ckpt_bytes.restype = _S
     lib.ssm_scan_ckpt_bytes.argtypes = [_I] * 4
     lib.ssm_scan_fwd_workspace_bytes.restype = _S
@@ -84,6 +86,19 @@ def last_error() -> str:
 
 def version() -> str:
     return load().ssm_version().decode()
+
+
+KERNEL_IDS = {"fwd_summary": 1, "fwd_carry": 2, "fwd_output": 3, "bwd_summary": 4,
+              "bwd_carry": 5, "bwd_main": 6, "conv_bwd": 7, "rms_bwd": 8}
+
+
+def ssm_set_kernel_timer(kernel, start=None, stop=None):
+    """Arm (a pair of raw hipEvent_t handles, as ints) or disarm (None, None) the timing
+    hook around one kernel, named as in KERNEL_IDS or by its id."""
+    kid = KERNEL_IDS.get(kernel, kernel)
+    sp = ctypes.c_void_p(start) if start is not None else None
+    ep = ctypes.c_void_p(stop) if stop is not None else None
+    _check(load().ssm_set_kernel_timer(int(kid), sp, ep))
 
 
 def _check(rc):

@@ -15,6 +15,12 @@ namespace {
 
 thread_local std::string g_err;
 
+// Timing hook: per-thread caller events recorded around one kernel's launch.
+struct TimerSlot {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+thread_local TimerSlot g_timer[ssm::kKNumIds];
+
 int fail(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -218,7 +224,24 @@ size_t rms_ws(int64_t R, int64_t M, ssm_dtype_t dt, ssm::RmsPlan* plan, void* ws
 
 }  // namespace
 
+void ssm::timer_mark(int id, bool stop, hipStream_t st) {
+  if (id <= 0 || id >= kKNumIds) return;
+  hipEvent_t e = stop ? g_timer[id].stop : g_timer[id].start;
+  if (e) (void)hipEventRecord(e, st);
+}
+
 extern "C" {
+
+int ssm_set_kernel_timer(int kernel, void* start, void* stop) {
+  if (kernel <= 0 || kernel >= ssm::kKNumIds)
+    return fail(SSM_ERR_ARG, "unknown kernel id %d", kernel);
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(SSM_ERR_ARG, "start and stop events must both be set or both be NULL");
+  g_timer[kernel].start = static_cast<hipEvent_t>(start);
+  g_timer[kernel].stop = static_cast<hipEvent_t>(stop);
+  return ok();
+}
+
 
 const char* ssm_last_error(void) { return g_err.c_str(); }
 

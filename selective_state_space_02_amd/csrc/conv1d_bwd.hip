@@ -103,12 +103,14 @@ static hipError_t conv_k(const ConvArgs& a, const ConvPlan& p, hipStream_t st) {
   T* dx = static_cast<T*>(a.dx);
   const int64_t colblocks = (a.D / p.vec + 255) / 256;
   const dim3 grid(colblocks * a.B * p.nTb);
+  timer_mark(kKConvBwd, false, st);
   if (p.vec == 4)
     hipLaunchKernelGGL((k_conv_bwd<T, K, 4>), grid, dim3(256), 0, st, a.L, a.D, p.Tb, p.nTb,
                        colblocks, x, a.W, g, dx, p.dWp, p.dbp);
   else
     hipLaunchKernelGGL((k_conv_bwd<T, K, 1>), grid, dim3(256), 0, st, a.L, a.D, p.Tb, p.nTb,
                        colblocks, x, a.W, g, dx, p.dWp, p.dbp);
+  timer_mark(kKConvBwd, true, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t P = a.B * p.nTb;

@@ -96,6 +96,24 @@ struct RmsPlan {
   float* dsp;  // [nblk][M]
 };
 
+// Kernel identifiers of the timing hook (values are part of the C ABI, see
+// ssm_set_kernel_timer in ssm_scan.h).
+enum KernelId {
+  kKFwdSummary = 1,
+  kKFwdCarry = 2,
+  kKFwdOutput = 3,
+  kKBwdSummary = 4,
+  kKBwdCarry = 5,
+  kKBwdMain = 6,
+  kKConvBwd = 7,
+  kKRmsBwd = 8,
+  kKNumIds = 9
+};
+
+// Records the caller's event for kernel `id` on stream st (stop = false: before the
+// launch, true: after it), if the calling thread armed one; otherwise does nothing.
+void timer_mark(int id, bool stop, hipStream_t st);
+
 hipError_t launch_scan_fwd(const ScanArgs& a, const FwdPlan& p, hipStream_t st);
 hipError_t launch_scan_bwd(const ScanArgs& a, const BwdPlan& p, hipStream_t st);
 hipError_t launch_conv1d_bwd(const ConvArgs& a, const ConvPlan& p, hipStream_t st);

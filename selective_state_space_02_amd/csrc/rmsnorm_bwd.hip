@@ -93,9 +93,11 @@ __global__ __launch_bounds__(256) void k_rms_bwd(
 
 template <typename T, int VEC, int PASSES>
 static void rms_launch(const RmsArgs& a, const RmsPlan& p, hipStream_t st) {
+  timer_mark(kKRmsBwd, false, st);
   hipLaunchKernelGGL((k_rms_bwd<T, VEC, PASSES>), dim3(p.nblk), dim3(256), 0, st, a.R, a.M,
                      p.rows_per_block, static_cast<const T*>(a.dy), static_cast<const T*>(a.x),
                      a.scale, a.rms, static_cast<T*>(a.dx), p.dsp);
+  timer_mark(kKRmsBwd, true, st);
 }
 
 template <typename T, int VEC>

@@ -232,17 +232,23 @@ static hipError_t bwd_impl(const ScanArgs& a, const BwdPlan& p, hipStream_t st) 
   const dim3 block(256);
   const float* gin = nullptr;
   if (p.nc > 1) {
+    timer_mark(kKBwdSummary, false, st);
     hipLaunchKernelGGL((k_bwd_summary<T, N>), dim3(p.ng, a.B, p.nc - 1), block, 0, st, a.L,
                        a.D, p.Lc, p.nc, delta, a.A, Cm, dy, p.GS, p.SD);
+    timer_mark(kKBwdSummary, true, st);
     const int64_t tot = a.B * a.D * N;
+    timer_mark(kKBwdCarry, false, st);
     hipLaunchKernelGGL((k_bwd_carry<N>), dim3((tot + 255) / 256), block, 0, st, a.B, a.D,
                        p.nc, a.A, p.GS, p.SD, p.gin);
+    timer_mark(kKBwdCarry, true, st);
     gin = p.gin;
   }
+  timer_mark(kKBwdMain, false, st);
   hipLaunchKernelGGL((k_bwd_main<T, N>), dim3(p.ng, a.B, p.nc), block, 0, st, a.B, a.L, a.D,
                      p.Lc, p.nc, p.nf, x, delta, a.A, Bm, Cm, a.Dv, dy, p.ckpt, gin,
                      static_cast<T*>(a.dx), static_cast<T*>(a.ddelta), p.dBp, p.dCp, p.dAp,
                      p.dDp, a.dh0);
+  timer_mark(kKBwdMain, true, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t BLN = a.B * a.L * N;

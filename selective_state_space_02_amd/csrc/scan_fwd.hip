@@ -151,16 +151,22 @@ static hipError_t fwd_impl(const ScanArgs& a, const FwdPlan& p, hipStream_t st) 
   const int64_t groups = (a.D + 63) / 64;
   const float* hin = a.h0;  // [B][1][D][N] == [B][D][N] when nc == 1
   if (p.nc > 1) {
+    timer_mark(kKFwdSummary, false, st);
     hipLaunchKernelGGL((k_fwd_summary<T, N>), dim3(groups, a.B, p.nc - 1), block, 0, st, a.L,
                        a.D, p.Lc, p.nc, x, delta, a.A, Bm, p.S, p.SD);
+    timer_mark(kKFwdSummary, true, st);
     const int64_t tot = a.B * a.D * N;
+    timer_mark(kKFwdCarry, false, st);
     hipLaunchKernelGGL((k_fwd_carry<N>), dim3((tot + 255) / 256), block, 0, st, a.B, a.D,
                        p.nc, a.A, a.h0, p.S, p.SD, p.hin);
+    timer_mark(kKFwdCarry, true, st);
     hin = p.hin;
   }
+  timer_mark(kKFwdOutput, false, st);
   hipLaunchKernelGGL((k_fwd_output<T, N>), dim3(groups, a.B, p.nc), block, 0, st, a.L, a.D,
                      p.Lc, p.nc, p.nf, x, delta, a.A, Bm, Cm, a.Dv, hin,
                      static_cast<T*>(a.y), p.ckpt, a.h_last);
+  timer_mark(kKFwdOutput, true, st);
   return hipGetLastError();
 }
 
