@@ -136,6 +136,8 @@ int check_scan_dims(ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D, int64_t 
   if (N != 4 && N != 8 && N != 16)
     return fail(SSM_ERR_UNSUPPORTED, "state size N=%lld not supported (4, 8 or 16)", (long long)N);
   if (B > 65535) return fail(SSM_ERR_UNSUPPORTED, "batch B=%lld exceeds 65535", (long long)B);
+  if (D > (int64_t(1) << 26))
+    return fail(SSM_ERR_UNSUPPORTED, "channels D=%lld exceed 2^26", (long long)D);
   if (B > kMaxElems / L || B * L > kMaxElems / D || B * L * D > kMaxElems / N)
     return fail(SSM_ERR_ARG, "tensor sizes overflow");
   return SSM_OK;

@@ -145,28 +145,72 @@ __device__ __forceinline__ float xor_lane(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
-// Sum V values per lane over the 16 lanes that share (lane & 3), i.e. over the 16
-// channels of a wavefront.  Butterfly reduce-scatter: at each of log2(V) steps a
-// lane keeps half of its values and adds the partner's copy of that half.  Steps
-// use lane bits 5, 4, ...; the lane bits left over after the halving are summed
-// directly.  On return lane l holds in v[0] the total of value index
-// chan_reduce_index<V>(l), duplicated over the lanes that differ only in the
-// leftover bits (chan_reduce_writer<V>(l) picks one of them).
+// DPP move within rows of 16 lanes, writing only the banks (groups of 4 lanes) set in
+// BANK; other lanes return `old`.  row_ror:n (CTRL 0x120 + n) reads lane (i - n) mod 16.
+template <int CTRL, int BANK>
+__device__ __forceinline__ float dpp_masked(float old, float src) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, 0xF, BANK, false));
+}
+
+// gfx950 lane swaps: after swap32(a, b), lanes 0-31 hold (a, a of lane+32) and lanes
+// 32-63 hold (b of lane-32, b); swap16 does the same between rows 0/1 and 2/3.
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+// Sum V (2, 4 or 8) values per lane over the 16 lanes that share (lane & 3), i.e. over
+// the 16 channels of a wavefront.  Butterfly reduce-scatter over lane bits 5, 4, 3: at
+// each halving step a lane keeps half of its values (the lower half if its bit is 0)
+// and adds the partner's copy of that half -- a lane swap does the exchange for bits
+// 5 and 4, bank-masked DPP rotations for bit 3.  Lane bits left over once one value
+// remains are summed pairwise.  On return lane l holds in v[0] the total of value
+// index chan_reduce_index<V>(l); every lane holds a total (duplicated over the
+// leftover bits; chan_reduce_writer<V>(l) picks one lane per value).
 template <int V>
 __device__ __forceinline__ void chan_reduce(float (&v)[V], int lane) {
-  int bit = 5;
+  static_assert(V == 2 || V == 4 || V == 8, "V must be 2, 4 or 8");
+  // bit 5 (lane distance 32)
 #pragma unroll
-  for (int half = V / 2; half >= 1; half /= 2, --bit) {
-    const bool upper = (lane >> bit) & 1;
-#pragma unroll
-    for (int k = 0; k < half; ++k) {
-      const float keep = upper ? v[k + half] : v[k];
-      const float send = upper ? v[k] : v[k + half];
-      v[k] = keep + xor_lane(send, 1 << bit);
-    }
+  for (int k = 0; k < V / 2; ++k) {
+    float a = v[k], b = v[k + V / 2];
+    swap32(a, b);
+    v[k] = a + b;
   }
+  // bit 4 (distance 16)
+  if constexpr (V >= 4) {
 #pragma unroll
-  for (; bit >= 2; --bit) v[0] += xor_lane(v[0], 1 << bit);
+    for (int k = 0; k < V / 4; ++k) {
+      float a = v[k], b = v[k + V / 4];
+      swap16(a, b);
+      v[k] = a + b;
+    }
+  } else {
+    float a = v[0], b = v[0];
+    swap16(a, b);
+    v[0] = a + b;
+  }
+  // bit 3 (distance 8, inside a row: row_ror:8 pairs lane i with i^8)
+  if constexpr (V >= 8) {
+    const float lo = v[0], hi = v[1];
+    const float t = dpp_masked<0x128, 0xC>(0.f, hi);  // lanes 8-15: hi of lane i-8
+    const float r = dpp_masked<0x128, 0x3>(t, lo);    // lanes 0-7: lo of lane i+8
+    v[0] = ((lane & 8) ? hi : lo) + r;
+  } else {
+    v[0] += dpp_masked<0x128, 0xF>(0.f, v[0]);
+  }
+  // bit 2 (distance 4): banks 0,2 read lane i+4 (row_ror:12), banks 1,3 lane i-4 (row_ror:4)
+  {
+    const float t = dpp_masked<0x124, 0xA>(0.f, v[0]);
+    v[0] += dpp_masked<0x12C, 0x5>(t, v[0]);
+  }
 }
 
 template <int V>

@@ -30,43 +30,81 @@
 //   4. k_reduce (reduce.hip): fixed-order sums of the partials.
 #include "common.hpp"
 #include "launch.hpp"
+#include "tile.hpp"
 
 namespace ssm {
 
 template <typename T, int N>
-__global__ __launch_bounds__(256) void k_bwd_summary(
+__global__ __launch_bounds__(256, 2) void k_bwd_summary(
     int64_t L, int64_t D, int64_t Lc, int nc, const T* __restrict__ delta,
     const float* __restrict__ A, const T* __restrict__ Cm, const T* __restrict__ dy,
     float* __restrict__ GS, float* __restrict__ SD) {
   constexpr int NS = N / 4;
-  const int c = blockIdx.z + 1, b = blockIdx.y, tid = threadIdx.x, q = tid & 3;
-  const int64_t d = int64_t(blockIdx.x) * 64 + (tid >> 2);
-  if (d >= D) return;
+  __shared__ float sd[2][kTc][kTileCh], sdy[2][kTc][kTileCh], sC[2][kTc][N];
+  const int c = blockIdx.z + 1, b = blockIdx.y, tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
+  const int64_t d0 = int64_t(blockIdx.x) * kTileCh, d = d0 + cl;
+  const bool act = d < D;
+  const int D32 = int(D);
+  const int dvalid = (D - d0 < kTileCh) ? int(D - d0) : kTileCh;
+  const T* db = delta + int64_t(b) * L * D + d0;
+  const T* dyb = dy + int64_t(b) * L * D + d0;
+  const T* Cb = Cm + int64_t(b) * L * N;
   float A2[NS], gp[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
-    A2[j] = A[d * N + q * NS + j] * kLog2e;
+    A2[j] = act ? A[d * N + q * NS + j] * kLog2e : 0.f;
     gp[j] = 0.f;
   }
-  float sd = 0.f;
+  float sdl = 0.f;
   const int64_t t0 = int64_t(c) * Lc, t1 = (t0 + Lc < L) ? t0 + Lc : L;
-#pragma unroll 4
-  for (int64_t t = t1 - 1; t >= t0; --t) {
-    const int64_t i = (int64_t(b) * L + t) * D + d;
-    const float dl = ld(delta, i), dyv = ld(dy, i);
-    float Cv[NS];
-    load_vec<T, NS>(Cm + (int64_t(b) * L + t) * N + q * NS, Cv);
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const float g = __builtin_fmaf(dyv, Cv[j], gp[j]);
-      gp[j] = __builtin_amdgcn_exp2f(dl * A2[j]) * g;
+  const int ntile = int((t1 - t0 + kTc - 1) / kTc);
+  // tiles are walked from the last one backwards
+  ChFetch<T> fd, fy;
+  VecFetch<T, N> fC;
+  int64_t tf = t0 + int64_t(ntile - 1) * kTc;
+  int tv = clamp_valid(L - tf);
+  fd.fetch(db + tf * D, D32, tv, dvalid, tid);
+  fy.fetch(dyb + tf * D, D32, tv, dvalid, tid);
+  fC.fetch(Cb + tf * N, tv, tid);
+  fd.commit(sd[0], tv, dvalid, tid);
+  fy.commit(sdy[0], tv, dvalid, tid);
+  fC.commit(sC[0], tv, tid);
+  __syncthreads();
+  for (int it = 0; it < ntile; ++it, tf -= kTc) {
+    const int buf = it & 1;
+    const bool more = it + 1 < ntile;
+    if (more) {
+      const int64_t tn = tf - kTc;
+      tv = kTc;  // every tile but the last one is full
+      fd.fetch(db + tn * D, D32, tv, dvalid, tid);
+      fy.fetch(dyb + tn * D, D32, tv, dvalid, tid);
+      fC.fetch(Cb + tn * N, tv, tid);
     }
-    sd += dl;
-  }
-  const int64_t o = (int64_t(b) * nc + c) * D + d;
 #pragma unroll
-  for (int j = 0; j < NS; ++j) GS[o * N + q * NS + j] = gp[j];
-  if (q == 0) SD[o] = sd;
+    for (int s = kTc - 1; s >= 0; --s) {
+      const float dl = sd[buf][s][cl], dyv = sdy[buf][s][cl];
+      float Cv[NS];
+      tile_read_vec<N, NS>(sC[buf], s, q, Cv);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const float g = __builtin_fmaf(dyv, Cv[j], gp[j]);
+        gp[j] = __builtin_amdgcn_exp2f(dl * A2[j]) * g;
+      }
+      sdl += dl;
+    }
+    if (more) {
+      fd.commit(sd[buf ^ 1], tv, dvalid, tid);
+      fy.commit(sdy[buf ^ 1], tv, dvalid, tid);
+      fC.commit(sC[buf ^ 1], tv, tid);
+    }
+    __syncthreads();
+  }
+  if (act) {
+    const int64_t o = (int64_t(b) * nc + c) * D + d;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) GS[o * N + q * NS + j] = gp[j];
+    if (q == 0) SD[o] = sdl;
+  }
 }
 
 template <int N>
@@ -89,7 +127,7 @@ __global__ __launch_bounds__(256) void k_bwd_carry(
 }
 
 template <typename T, int N>
-__global__ __launch_bounds__(256) void k_bwd_main(
+__global__ __launch_bounds__(256, 2) void k_bwd_main(
     int64_t B, int64_t L, int64_t D, int64_t Lc, int nc, int64_t nf,
     const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dv,
@@ -99,12 +137,26 @@ __global__ __launch_bounds__(256) void k_bwd_main(
     float* __restrict__ dh0) {
   constexpr int NS = N / 4;
   constexpr int V = 2 * NS;  // per-lane values summed over channels: dB (NS), dC (NS)
-  __shared__ float red[4][kTc][2 * N];
+  __shared__ float sx[2][kTc][kTileCh], sd[2][kTc][kTileCh], sdy[2][kTc][kTileCh];
+  __shared__ float sB[2][kTc][N], sC[2][kTc][N];
+  __shared__ float red[2][4][kTc][2 * N];
 
   const int c = blockIdx.z, b = blockIdx.y, grp = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = tid & 3;
-  const int64_t d = int64_t(grp) * 64 + (tid >> 2);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = tid & 3, cl = tid >> 2;
+  const int64_t d0 = int64_t(grp) * kTileCh, d = d0 + cl;
   const bool act = d < D;
+  const int D32 = int(D);
+  const int dvalid = (D - d0 < kTileCh) ? int(D - d0) : kTileCh;
+  const T* xb = x + int64_t(b) * L * D + d0;
+  const T* db = delta + int64_t(b) * L * D + d0;
+  const T* dyb = dy + int64_t(b) * L * D + d0;
+  const T* Bb = Bm + int64_t(b) * L * N;
+  const T* Cb = Cm + int64_t(b) * L * N;
+  T* dxb = dx + int64_t(b) * L * D + d;
+  T* ddb = ddelta + int64_t(b) * L * D + d;
+  const float* ckb = ckpt + (int64_t(b) * nf * D + d) * N + q * NS;  // + f*D*N
+  float* pB = dBp + (int64_t(grp) * B + b) * L * N;
+  float* pC = dCp + (int64_t(grp) * B + b) * L * N;
 
   float A2[NS], gp[NS], dA_acc[NS];
 #pragma unroll
@@ -117,58 +169,74 @@ __global__ __launch_bounds__(256) void k_bwd_main(
   float dD_acc = 0.f;
 
   const int64_t t0 = int64_t(c) * Lc, t1 = (t0 + Lc < L) ? t0 + Lc : L;
-  const int64_t nfine = (t1 - t0 + kTc - 1) / kTc;
-  const int writer = chan_reduce_writer<V>(lane);
+  const int ntile = int((t1 - t0 + kTc - 1) / kTc);
+  const bool writer = chan_reduce_writer<V>(lane);
   const int vidx = chan_reduce_index<V>(lane);
   const int ridx = (vidx < NS) ? (q * NS + vidx) : (N + q * NS + (vidx - NS));
 
-  for (int64_t fi = nfine - 1; fi >= 0; --fi) {
-    const int64_t tf = t0 + fi * kTc;
+  // tiles are walked from the last one backwards; the checkpoint of the next tile is
+  // fetched together with its inputs
+  ChFetch<T> fx, fd, fy;
+  VecFetch<T, N> fB, fC;
+  float hck[NS];
+  int64_t tf = t0 + int64_t(ntile - 1) * kTc;
+  int tv = clamp_valid(L - tf);
+  fx.fetch(xb + tf * D, D32, tv, dvalid, tid);
+  fd.fetch(db + tf * D, D32, tv, dvalid, tid);
+  fy.fetch(dyb + tf * D, D32, tv, dvalid, tid);
+  fB.fetch(Bb + tf * N, tv, tid);
+  fC.fetch(Cb + tf * N, tv, tid);
+#pragma unroll
+  for (int j = 0; j < NS; ++j) hck[j] = act ? ckb[(tf / kTc) * D * N + j] : 0.f;
+  fx.commit(sx[0], tv, dvalid, tid);
+  fd.commit(sd[0], tv, dvalid, tid);
+  fy.commit(sdy[0], tv, dvalid, tid);
+  fB.commit(sB[0], tv, tid);
+  fC.commit(sC[0], tv, tid);
+  __syncthreads();
+
+  for (int it = 0; it < ntile; ++it, tf -= kTc) {
+    const int buf = it & 1;
+    const bool more = it + 1 < ntile;
+    float h[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) h[j] = hck[j];
+    if (more) {
+      const int64_t tn = tf - kTc;
+      tv = kTc;  // every tile but the last one is full
+      fx.fetch(xb + tn * D, D32, tv, dvalid, tid);
+      fd.fetch(db + tn * D, D32, tv, dvalid, tid);
+      fy.fetch(dyb + tn * D, D32, tv, dvalid, tid);
+      fB.fetch(Bb + tn * N, tv, tid);
+      fC.fetch(Cb + tn * N, tv, tid);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) hck[j] = act ? ckb[(tn / kTc) * D * N + j] : 0.f;
+    }
+    // recompute a_t and h_t of this tile from its checkpoint
     float as[kTc][NS], hs[kTc][NS];
-    {
-      float h[NS];
 #pragma unroll
-      for (int j = 0; j < NS; ++j)
-        h[j] = act ? ckpt[((int64_t(b) * nf + tf / kTc) * D + d) * N + q * NS + j] : 0.f;
+    for (int s = 0; s < kTc; ++s) {
+      const float dl = sd[buf][s][cl], u = dl * sx[buf][s][cl];
+      float Bv[NS];
+      tile_read_vec<N, NS>(sB[buf], s, q, Bv);
 #pragma unroll
-      for (int s = 0; s < kTc; ++s) {
-        const int64_t t = tf + s;
-        const bool v = act && t < L;
-        const int64_t i = (int64_t(b) * L + t) * D + d;
-        const float dl = v ? ld(delta, i) : 0.f;
-        const float xv = v ? ld(x, i) : 0.f;
-        float Bv[NS];
-        if (t < L) load_vec<T, NS>(Bm + (int64_t(b) * L + t) * N + q * NS, Bv);
-        else zero(Bv);
-        const float u = dl * xv;
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-          const float a = __builtin_amdgcn_exp2f(dl * A2[j]);
-          h[j] = __builtin_fmaf(a, h[j], u * Bv[j]);
-          as[s][j] = a;
-          hs[s][j] = h[j];
-        }
+      for (int j = 0; j < NS; ++j) {
+        const float a = __builtin_amdgcn_exp2f(dl * A2[j]);
+        h[j] = __builtin_fmaf(a, h[j], u * Bv[j]);
+        as[s][j] = a;
+        hs[s][j] = h[j];
       }
     }
+    // reverse step
+    const int smax = (t1 - tf < kTc) ? int(t1 - tf) : kTc;
 #pragma unroll
     for (int s = kTc - 1; s >= 0; --s) {
-      const int64_t t = tf + s;
-      const bool tv = t < L;
-      const bool v = act && tv;
-      const int64_t i = (int64_t(b) * L + t) * D + d;
-      const float dl = v ? ld(delta, i) : 0.f;
-      const float xv = v ? ld(x, i) : 0.f;
-      const float dyv = v ? ld(dy, i) : 0.f;
+      const float dl = sd[buf][s][cl], xv = sx[buf][s][cl], dyv = sdy[buf][s][cl];
       float Bv[NS], Cv[NS];
-      if (tv) {
-        load_vec<T, NS>(Bm + (int64_t(b) * L + t) * N + q * NS, Bv);
-        load_vec<T, NS>(Cm + (int64_t(b) * L + t) * N + q * NS, Cv);
-      } else {
-        zero(Bv);
-        zero(Cv);
-      }
+      tile_read_vec<N, NS>(sB[buf], s, q, Bv);
+      tile_read_vec<N, NS>(sC[buf], s, q, Cv);
       const float u = dl * xv;
-      float sB = 0.f, sAq = 0.f;
+      float sBg = 0.f, sAq = 0.f;
       float vals[V];
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
@@ -177,34 +245,40 @@ __global__ __launch_bounds__(256) void k_bwd_main(
         const float gq = g * qq;
         dA_acc[j] = __builtin_fmaf(gq, dl, dA_acc[j]);
         sAq = __builtin_fmaf(gq, A2[j], sAq);
-        sB = __builtin_fmaf(g, Bv[j], sB);
+        sBg = __builtin_fmaf(g, Bv[j], sBg);
         vals[j] = g * u;
         vals[NS + j] = dyv * hs[s][j];
         gp[j] = as[s][j] * g;
       }
-      sB = quad_sum(sB);
+      sBg = quad_sum(sBg);
       sAq = quad_sum(sAq);
-      if (v && q == 0) {
-        st(dx, i, __builtin_fmaf(Dd, dyv, dl * sB));
-        st(ddelta, i, __builtin_fmaf(kLn2, sAq, xv * sB));
+      if (act && q == 0 && s < smax) {
+        const int64_t i = (tf + s) * D;
+        st(dxb, i, __builtin_fmaf(Dd, dyv, dl * sBg));
+        st(ddb, i, __builtin_fmaf(kLn2, sAq, xv * sBg));
       }
       dD_acc = __builtin_fmaf(dyv, xv, dD_acc);
       chan_reduce<V>(vals, lane);
-      if (writer) red[wave][s][ridx] = vals[0];
+      if (writer) red[buf][wave][s][ridx] = vals[0];
+    }
+    if (more) {
+      fx.commit(sx[buf ^ 1], tv, dvalid, tid);
+      fd.commit(sd[buf ^ 1], tv, dvalid, tid);
+      fy.commit(sdy[buf ^ 1], tv, dvalid, tid);
+      fB.commit(sB[buf ^ 1], tv, tid);
+      fC.commit(sC[buf ^ 1], tv, tid);
     }
     __syncthreads();
-    // sum the four wavefronts' channel sums and write this group's partial
+    // the four wavefronts' channel sums of this tile -> this group's partial
     for (int k = tid; k < kTc * 2 * N; k += 256) {
       const int s = k / (2 * N), r = k % (2 * N);
-      const int64_t t = tf + s;
-      if (t < L) {
-        const float sum = (red[0][s][r] + red[1][s][r]) + (red[2][s][r] + red[3][s][r]);
-        const int64_t o = ((int64_t(grp) * B + b) * L + t) * N;
-        if (r < N) dBp[o + r] = sum;
-        else dCp[o + r - N] = sum;
+      if (s < smax) {
+        const float sum = (red[buf][0][s][r] + red[buf][1][s][r]) + (red[buf][2][s][r] + red[buf][3][s][r]);
+        const int64_t o = (tf + s) * N;
+        if (r < N) pB[o + r] = sum;
+        else pC[o + r - N] = sum;
       }
     }
-    __syncthreads();
   }
 
   if (act) {

@@ -16,48 +16,81 @@
 //   3. k_fwd_output:  every chunk re-runs its steps from the true start state,
 //                     writes y, the state before every kTc-th step (checkpoints for
 //                     the backward) and the final state.
-// Lane layout: quad = channel, NS = N/4 states per lane (see common.hpp).
+// Lane layout: quad = channel, NS = N/4 states per lane (see common.hpp).  Inputs
+// are staged through LDS one kTc-step tile at a time, the next tile's global loads in
+// flight while the current one is computed (tile.hpp).
 #include "common.hpp"
 #include "launch.hpp"
+#include "tile.hpp"
 
 namespace ssm {
 
 template <typename T, int N>
-__global__ __launch_bounds__(256) void k_fwd_summary(
+__global__ __launch_bounds__(256, 2) void k_fwd_summary(
     int64_t L, int64_t D, int64_t Lc, int nc, const T* __restrict__ x,
     const T* __restrict__ delta, const float* __restrict__ A, const T* __restrict__ Bm,
     float* __restrict__ S, float* __restrict__ SD) {
   constexpr int NS = N / 4;
-  const int c = blockIdx.z, b = blockIdx.y, tid = threadIdx.x, q = tid & 3;
-  const int64_t d = int64_t(blockIdx.x) * 64 + (tid >> 2);
+  __shared__ float sx[2][kTc][kTileCh], sd[2][kTc][kTileCh], sB[2][kTc][N];
+  const int c = blockIdx.z, b = blockIdx.y, tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
+  const int64_t d0 = int64_t(blockIdx.x) * kTileCh, d = d0 + cl;
   const bool act = d < D;
+  const int D32 = int(D);
+  const int dvalid = (D - d0 < kTileCh) ? int(D - d0) : kTileCh;
+  const T* xb = x + int64_t(b) * L * D + d0;
+  const T* db = delta + int64_t(b) * L * D + d0;
+  const T* Bb = Bm + int64_t(b) * L * N;
   float A2[NS], h[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     A2[j] = act ? A[d * N + q * NS + j] * kLog2e : 0.f;
     h[j] = 0.f;
   }
-  float sd = 0.f;
-  const int64_t t0 = int64_t(c) * Lc, t1 = t0 + Lc;  // chunks 0..nc-2 are full
-  if (act) {
-#pragma unroll 4
-    for (int64_t t = t0; t < t1; ++t) {
-      const int64_t i = (int64_t(b) * L + t) * D + d;
-      const float dl = ld(delta, i), xv = ld(x, i);
+  float sdl = 0.f;
+  const int64_t t0 = int64_t(c) * Lc;  // chunks 0..nc-2 are full
+  const int ntile = int(Lc / kTc);
+  ChFetch<T> fx, fd;
+  VecFetch<T, N> fB;
+  fx.fetch(xb + t0 * D, D32, kTc, dvalid, tid);
+  fd.fetch(db + t0 * D, D32, kTc, dvalid, tid);
+  fB.fetch(Bb + t0 * N, kTc, tid);
+  fx.commit(sx[0], kTc, dvalid, tid);
+  fd.commit(sd[0], kTc, dvalid, tid);
+  fB.commit(sB[0], kTc, tid);
+  __syncthreads();
+  for (int it = 0; it < ntile; ++it) {
+    const int buf = it & 1;
+    const bool more = it + 1 < ntile;
+    if (more) {
+      const int64_t tn = t0 + int64_t(it + 1) * kTc;
+      fx.fetch(xb + tn * D, D32, kTc, dvalid, tid);
+      fd.fetch(db + tn * D, D32, kTc, dvalid, tid);
+      fB.fetch(Bb + tn * N, kTc, tid);
+    }
+#pragma unroll
+    for (int s = 0; s < kTc; ++s) {
+      const float dl = sd[buf][s][cl], u = dl * sx[buf][s][cl];
       float Bv[NS];
-      load_vec<T, NS>(Bm + (int64_t(b) * L + t) * N + q * NS, Bv);
-      const float u = dl * xv;
+      tile_read_vec<N, NS>(sB[buf], s, q, Bv);
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         const float a = __builtin_amdgcn_exp2f(dl * A2[j]);
         h[j] = __builtin_fmaf(a, h[j], u * Bv[j]);
       }
-      sd += dl;
+      sdl += dl;
     }
+    if (more) {
+      fx.commit(sx[buf ^ 1], kTc, dvalid, tid);
+      fd.commit(sd[buf ^ 1], kTc, dvalid, tid);
+      fB.commit(sB[buf ^ 1], kTc, tid);
+    }
+    __syncthreads();
+  }
+  if (act) {
     const int64_t o = (int64_t(b) * nc + c) * D + d;
 #pragma unroll
     for (int j = 0; j < NS; ++j) S[o * N + q * NS + j] = h[j];
-    if (q == 0) SD[o] = sd;
+    if (q == 0) SD[o] = sdl;
   }
 }
 
@@ -84,43 +117,73 @@ __global__ __launch_bounds__(256) void k_fwd_carry(
 // y (nullable: only the checkpoints are wanted); ckpt (nullable): [B][nf][D][N],
 // the state before step f*kTc.
 template <typename T, int N>
-__global__ __launch_bounds__(256) void k_fwd_output(
+__global__ __launch_bounds__(256, 2) void k_fwd_output(
     int64_t L, int64_t D, int64_t Lc, int nc, int64_t nf, const T* __restrict__ x,
     const T* __restrict__ delta, const float* __restrict__ A, const T* __restrict__ Bm,
     const T* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ hin,
     T* __restrict__ y, float* __restrict__ ckpt, float* __restrict__ h_last) {
   constexpr int NS = N / 4;
-  const int c = blockIdx.z, b = blockIdx.y, tid = threadIdx.x, q = tid & 3;
-  const int64_t d = int64_t(blockIdx.x) * 64 + (tid >> 2);
+  __shared__ float sx[2][kTc][kTileCh], sd[2][kTc][kTileCh], sB[2][kTc][N], sC[2][kTc][N];
+  const int c = blockIdx.z, b = blockIdx.y, tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
+  const int64_t d0 = int64_t(blockIdx.x) * kTileCh, d = d0 + cl;
   const bool act = d < D;
-  if (!act) return;  // no cross-channel work in this kernel
+  const int D32 = int(D);
+  const int dvalid = (D - d0 < kTileCh) ? int(D - d0) : kTileCh;
+  const T* xb = x + int64_t(b) * L * D + d0;
+  const T* db = delta + int64_t(b) * L * D + d0;
+  const T* Bb = Bm + int64_t(b) * L * N;
+  const T* Cb = Cm + int64_t(b) * L * N;
+  T* yb = y ? y + int64_t(b) * L * D + d : nullptr;
+  float* ckb = ckpt ? ckpt + (int64_t(b) * nf * D + d) * N + q * NS : nullptr;  // + f*D*N
   float A2[NS], h[NS];
 #pragma unroll
-  for (int j = 0; j < NS; ++j) A2[j] = A[d * N + q * NS + j] * kLog2e;
-  const float Dd = Dv[d];
-  if (hin) {
+  for (int j = 0; j < NS; ++j) A2[j] = act ? A[d * N + q * NS + j] * kLog2e : 0.f;
+  const float Dd = act ? Dv[d] : 0.f;
+  if (hin && act) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) h[j] = hin[((int64_t(b) * nc + c) * D + d) * N + q * NS + j];
   } else {
     zero(h);
   }
   const int64_t t0 = int64_t(c) * Lc, t1 = (t0 + Lc < L) ? t0 + Lc : L;
-  for (int64_t tf = t0; tf < t1; tf += kTc) {
-    if (ckpt) {
-      const int64_t o = ((int64_t(b) * nf + tf / kTc) * D + d) * N + q * NS;
-#pragma unroll
-      for (int j = 0; j < NS; ++j) ckpt[o + j] = h[j];
+  const int ntile = int((t1 - t0 + kTc - 1) / kTc);
+  ChFetch<T> fx, fd;
+  VecFetch<T, N> fB, fC;
+  int tv = clamp_valid(L - t0);
+  fx.fetch(xb + t0 * D, D32, tv, dvalid, tid);
+  fd.fetch(db + t0 * D, D32, tv, dvalid, tid);
+  fB.fetch(Bb + t0 * N, tv, tid);
+  fC.fetch(Cb + t0 * N, tv, tid);
+  fx.commit(sx[0], tv, dvalid, tid);
+  fd.commit(sd[0], tv, dvalid, tid);
+  fB.commit(sB[0], tv, tid);
+  fC.commit(sC[0], tv, tid);
+  __syncthreads();
+  for (int it = 0; it < ntile; ++it) {
+    const int buf = it & 1;
+    const int64_t tf = t0 + int64_t(it) * kTc;
+    const bool more = it + 1 < ntile;
+    if (more) {
+      const int64_t tn = tf + kTc;
+      tv = clamp_valid(L - tn);
+      fx.fetch(xb + tn * D, D32, tv, dvalid, tid);
+      fd.fetch(db + tn * D, D32, tv, dvalid, tid);
+      fB.fetch(Bb + tn * N, tv, tid);
+      fC.fetch(Cb + tn * N, tv, tid);
     }
-#pragma unroll 4
+    if (ckb && act) {
+      float* o = ckb + (tf / kTc) * D * N;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) o[j] = h[j];
+    }
+    const int smax = (t1 - tf < kTc) ? int(t1 - tf) : kTc;
+#pragma unroll
     for (int s = 0; s < kTc; ++s) {
-      const int64_t t = tf + s;
-      if (t >= t1) break;
-      const int64_t i = (int64_t(b) * L + t) * D + d;
-      const float dl = ld(delta, i), xv = ld(x, i);
-      float Bv[NS], Cv[NS];
-      load_vec<T, NS>(Bm + (int64_t(b) * L + t) * N + q * NS, Bv);
-      load_vec<T, NS>(Cm + (int64_t(b) * L + t) * N + q * NS, Cv);
+      const float dl = sd[buf][s][cl], xv = sx[buf][s][cl];
       const float u = dl * xv;
+      float Bv[NS], Cv[NS];
+      tile_read_vec<N, NS>(sB[buf], s, q, Bv);
+      tile_read_vec<N, NS>(sC[buf], s, q, Cv);
       float yp = 0.f;
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
@@ -129,10 +192,17 @@ __global__ __launch_bounds__(256) void k_fwd_output(
         yp = __builtin_fmaf(Cv[j], h[j], yp);
       }
       yp = quad_sum(yp);
-      if (y && q == 0) st(y, i, __builtin_fmaf(Dd, xv, yp));
+      if (yb && act && q == 0 && s < smax) st(yb, (tf + s) * D, __builtin_fmaf(Dd, xv, yp));
     }
+    if (more) {
+      fx.commit(sx[buf ^ 1], tv, dvalid, tid);
+      fd.commit(sd[buf ^ 1], tv, dvalid, tid);
+      fB.commit(sB[buf ^ 1], tv, tid);
+      fC.commit(sC[buf ^ 1], tv, tid);
+    }
+    __syncthreads();
   }
-  if (h_last && c == nc - 1) {
+  if (h_last && act && c == nc - 1) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) h_last[(int64_t(b) * D + d) * N + q * NS + j] = h[j];
   }
@@ -148,7 +218,7 @@ static hipError_t fwd_impl(const ScanArgs& a, const FwdPlan& p, hipStream_t st) 
   const T* Bm = static_cast<const T*>(a.Bm);
   const T* Cm = static_cast<const T*>(a.Cm);
   const dim3 block(256);
-  const int64_t groups = (a.D + 63) / 64;
+  const int64_t groups = (a.D + kTileCh - 1) / kTileCh;
   const float* hin = a.h0;  // [B][1][D][N] == [B][D][N] when nc == 1
   if (p.nc > 1) {
     timer_mark(kKFwdSummary, false, st);
