@@ -60,26 +60,44 @@ struct Carver {
 // ---------------------------------------------------------------------------------
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Coarse chunking: enough chunks that B * ceil(D/16) * nc wavefronts fill the GPU,
-// chunk lengths a multiple of the checkpoint interval.
-ssm::Chunking choose_chunks(int64_t B, int64_t L, int64_t D, int64_t target_waves) {
+// MI355X: 256 compute units.  Resident workgroups per CU of the kernel that dominates
+// each pass (set by its registers and LDS): the forward output kernel fits 5, the
+// backward main kernel 2.
+constexpr int64_t kCUs = 256;
+constexpr int64_t kFwdSlots = kCUs * 5;
+constexpr int64_t kBwdSlots = kCUs * 2;
+// Per-step cost of the chunk-summary pass relative to the main pass.
+constexpr double kFwdSummaryCost = 0.7;
+constexpr double kBwdSummaryCost = 0.2;
+
+// Coarse chunking of the sequence: the chunk length is a multiple of the checkpoint
+// interval; the count minimises (rounds of resident workgroups) x (chunk length) x
+// (1 + summary cost x (nc-1)/nc), so a launch neither leaves the GPU idle nor ends
+// with a nearly empty last round of workgroups.
+ssm::Chunking choose_chunks(int64_t B, int64_t L, int64_t D, int64_t slots, double alpha) {
   ssm::Chunking c;
   c.nf = cdiv(L, ssm::kTc);
-  const int64_t chan_waves = B * cdiv(D, 16);
-  int64_t nc = cdiv(target_waves, chan_waves);
-  if (nc < 1) nc = 1;
-  if (nc > c.nf) nc = c.nf;
-  if (nc > 65535) nc = 65535;
-  c.Lc = cdiv(c.nf, nc) * ssm::kTc;
-  c.nc = int(cdiv(L, c.Lc));
+  const int64_t W = B * cdiv(D, 64);  // workgroups per chunk
+  const int64_t ncmax = c.nf < 256 ? c.nf : 256;
+  double best = 0.0;
+  c.nc = 1;
+  c.Lc = c.nf * ssm::kTc;
+  for (int64_t nc = 1; nc <= ncmax; ++nc) {
+    const int64_t tiles = cdiv(c.nf, nc);
+    if (cdiv(c.nf, tiles) != nc) continue;  // the same chunking as a smaller count
+    const double cost = double(cdiv(W * nc, slots)) * double(tiles) *
+                        (1.0 + alpha * double(nc - 1) / double(nc));
+    if (nc == 1 || cost < best * (1.0 - 1e-9)) {
+      best = cost;
+      c.nc = int(nc);
+      c.Lc = tiles * ssm::kTc;
+    }
+  }
   return c;
 }
 
-constexpr int64_t kFwdTargetWaves = 4096;
-constexpr int64_t kBwdTargetWaves = 2048;
-
 size_t fwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, ssm::FwdPlan* plan, void* ws) {
-  const ssm::Chunking c = choose_chunks(B, L, D, kFwdTargetWaves);
+  const ssm::Chunking c = choose_chunks(B, L, D, kFwdSlots, kFwdSummaryCost);
   Carver cv(ws);
   ssm::FwdPlan p{};
   p.nc = c.nc;
@@ -100,7 +118,7 @@ size_t ckpt_floats(int64_t B, int64_t L, int64_t D, int64_t N) {
 
 size_t bwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, bool with_ckpt, ssm::BwdPlan* plan,
               float** ckpt_out, ssm::FwdPlan* fplan, void* ws) {
-  const ssm::Chunking c = choose_chunks(B, L, D, kBwdTargetWaves);
+  const ssm::Chunking c = choose_chunks(B, L, D, kBwdSlots, kBwdSummaryCost);
   Carver cv(ws);
   ssm::BwdPlan p{};
   p.nc = c.nc;
@@ -116,6 +134,11 @@ size_t bwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, bool with_ckpt, ssm::B
   p.dCp = cv.take(size_t(p.ng) * B * L * N);
   p.dAp = cv.take(size_t(B) * c.nc * D * N);
   p.dDp = cv.take(size_t(B) * c.nc * D);
+  {
+    const int64_t t1 = ssm::reduce_tmp_floats(p.ng, B * L * N);
+    const int64_t t2 = ssm::reduce_tmp_floats(B * c.nc, D * N);
+    p.rtmp = cv.take(size_t(t1 > t2 ? t1 : t2));
+  }
   if (!with_ckpt) {
     float* ck = cv.take(ckpt_floats(B, L, D, N));
     if (ckpt_out) *ckpt_out = ck;
@@ -193,6 +216,7 @@ size_t conv_ws(int64_t B, int64_t L, int64_t D, int64_t K, ssm_dtype_t dt, ssm::
   Carver cv(ws);
   p.dWp = cv.take(size_t(B) * p.nTb * D * K);
   p.dbp = cv.take(size_t(B) * p.nTb * D);
+  p.rtmp = cv.take(size_t(ssm::reduce_tmp_floats(B * p.nTb, D * K)));
   if (plan) *plan = p;
   return cv.off;
 }
@@ -220,6 +244,7 @@ size_t rms_ws(int64_t R, int64_t M, ssm_dtype_t dt, ssm::RmsPlan* plan, void* ws
   if (!rms_plan(R, M, dt, &p)) return 0;
   Carver cv(ws);
   p.dsp = cv.take(size_t(p.nblk) * M);
+  p.rtmp = cv.take(size_t(ssm::reduce_tmp_floats(p.nblk, M)));
   if (plan) *plan = p;
   return cv.off;
 }

@@ -114,8 +114,8 @@ static hipError_t conv_k(const ConvArgs& a, const ConvPlan& p, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t P = a.B * p.nTb;
-  if ((e = launch_reduce(p.dWp, P, a.D * a.K, a.dW, true, st)) != hipSuccess) return e;
-  return launch_reduce(p.dbp, P, a.D, a.db, true, st);
+  if ((e = launch_reduce(p.dWp, P, a.D * a.K, a.dW, true, p.rtmp, st)) != hipSuccess) return e;
+  return launch_reduce(p.dbp, P, a.D, a.db, true, p.rtmp, st);
 }
 
 template <typename T>

@@ -61,6 +61,7 @@ struct BwdPlan {
   float* dCp;         // [ng][B][L][N]
   float* dAp;         // [B*nc][D][N]
   float* dDp;         // [B*nc][D]
+  float* rtmp;        // reduction scratch
 };
 
 struct ConvArgs {
@@ -78,6 +79,7 @@ struct ConvPlan {
   int64_t Tb, nTb, vec;
   float* dWp;  // [B*nTb][D][K]
   float* dbp;  // [B*nTb][D]
+  float* rtmp; // reduction scratch
 };
 
 struct RmsArgs {
@@ -94,6 +96,7 @@ struct RmsArgs {
 struct RmsPlan {
   int64_t vec, passes, rows_per_block, nblk;
   float* dsp;  // [nblk][M]
+  float* rtmp; // reduction scratch
 };
 
 // Kernel identifiers of the timing hook (values are part of the C ABI, see
@@ -118,8 +121,10 @@ hipError_t launch_scan_fwd(const ScanArgs& a, const FwdPlan& p, hipStream_t st);
 hipError_t launch_scan_bwd(const ScanArgs& a, const BwdPlan& p, hipStream_t st);
 hipError_t launch_conv1d_bwd(const ConvArgs& a, const ConvPlan& p, hipStream_t st);
 hipError_t launch_rmsnorm_bwd(const RmsArgs& a, const RmsPlan& p, hipStream_t st);
-// out[j] (+)= sum_{p < P} part[p*J + j], summed in order p = 0, 1, ..., P-1.
+// out[j] (+)= sum_{p < P} part[p*J + j] in a fixed order; tmp holds
+// reduce_tmp_floats(P, J) floats (may be null when that is 0).
 hipError_t launch_reduce(const float* part, int64_t P, int64_t J, float* out, bool accumulate,
-                         hipStream_t st);
+                         float* tmp, hipStream_t st);
+int64_t reduce_tmp_floats(int64_t P, int64_t J);
 
 }  // namespace ssm

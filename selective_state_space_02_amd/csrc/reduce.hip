@@ -1,28 +1,62 @@
-// Fixed-order sum of partial buffers: out[j] (+)= part[0][j] + part[1][j] + ... in
-// index order, one thread per output.  No atomics, so results are bit-identical from
-// run to run (the atomicAdd-free scratch-plus-reduce pattern of the foxhunt ml-alpha
-// backward-scratch commit, with the partials pre-reduced in registers/LDS first).
+// Fixed-order sum of partial buffers, out[j] (+)= sum_p part[p][j].  No atomics: the
+// order of every addition is fixed by the code, so results are bit-identical from run
+// to run (the atomicAdd-free scratch-plus-reduce pattern of the foxhunt ml-alpha
+// backward-scratch commit, applied after the partials were pre-reduced in registers
+// and LDS).
+//
+// One thread per output j sums a segment of at most kSeg partials with kAcc
+// independent accumulators (partial p goes to accumulator p mod kAcc; the accumulators
+// are then added in index order), so kAcc loads are in flight per thread.  When P
+// exceeds kSeg, a first launch writes one sum per segment to a temporary buffer and the
+// segments are summed the same way (reduce_tmp_floats() floats of temporary space).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace ssm {
 
-__global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ part, int64_t P,
-                                                int64_t J, float* __restrict__ out,
-                                                int accumulate) {
+constexpr int kSeg = 64;
+constexpr int kAcc = 4;
+
+__global__ __launch_bounds__(256) void k_reduce_seg(const float* __restrict__ part, int64_t P,
+                                                    int64_t J, float* __restrict__ out,
+                                                    int accumulate) {
   const int64_t j = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (j >= J) return;
-  float s = 0.f;
-  for (int64_t p = 0; p < P; ++p) s += part[p * J + j];
-  out[j] = accumulate ? out[j] + s : s;
+  const int64_t p0 = int64_t(blockIdx.y) * kSeg;
+  const int64_t p1 = (p0 + kSeg < P) ? p0 + kSeg : P;
+  float acc[kAcc] = {0.f, 0.f, 0.f, 0.f};
+  int64_t p = p0;
+  for (; p + kAcc <= p1; p += kAcc) {
+#pragma unroll
+    for (int k = 0; k < kAcc; ++k) acc[k] += part[(p + k) * J + j];
+  }
+  for (int k = 0; p < p1; ++p, ++k) acc[k] += part[p * J + j];
+  const float s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  float* o = out + int64_t(blockIdx.y) * J;  // one row per segment (a single row if P <= kSeg)
+  o[j] = accumulate ? o[j] + s : s;
+}
+
+int64_t reduce_tmp_floats(int64_t P, int64_t J) {
+  if (P <= kSeg) return 0;
+  const int64_t S = (P + kSeg - 1) / kSeg;
+  return S * J + reduce_tmp_floats(S, J);
 }
 
 hipError_t launch_reduce(const float* part, int64_t P, int64_t J, float* out, bool accumulate,
-                         hipStream_t st) {
+                         float* tmp, hipStream_t st) {
   if (J <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_reduce, dim3((J + 255) / 256), dim3(256), 0, st, part, P, J, out,
-                     accumulate ? 1 : 0);
-  return hipGetLastError();
+  const dim3 block(256);
+  const int64_t gx = (J + 255) / 256;
+  if (P <= kSeg) {
+    hipLaunchKernelGGL(k_reduce_seg, dim3(gx, 1), block, 0, st, part, P, J, out,
+                       accumulate ? 1 : 0);
+    return hipGetLastError();
+  }
+  const int64_t S = (P + kSeg - 1) / kSeg;
+  hipLaunchKernelGGL(k_reduce_seg, dim3(gx, S), block, 0, st, part, P, J, tmp, 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_reduce(tmp, S, J, out, accumulate, tmp + S * J, st);
 }
 
 }  // namespace ssm

@@ -120,7 +120,7 @@ hipError_t launch_rmsnorm_bwd(const RmsArgs& a, const RmsPlan& p, hipStream_t st
   else
     e = (p.vec == 8) ? rms_v<bf16_t, 8>(a, p, st) : rms_v<bf16_t, 1>(a, p, st);
   if (e != hipSuccess) return e;
-  return launch_reduce(p.dsp, p.nblk, a.M, a.dscale, true, st);
+  return launch_reduce(p.dsp, p.nblk, a.M, a.dscale, true, p.rtmp, st);
 }
 
 }  // namespace ssm

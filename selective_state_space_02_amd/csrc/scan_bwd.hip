@@ -35,7 +35,7 @@
 namespace ssm {
 
 template <typename T, int N>
-__global__ __launch_bounds__(256, 2) void k_bwd_summary(
+__global__ __launch_bounds__(256, 4) void k_bwd_summary(
     int64_t L, int64_t D, int64_t Lc, int nc, const T* __restrict__ delta,
     const float* __restrict__ A, const T* __restrict__ Cm, const T* __restrict__ dy,
     float* __restrict__ GS, float* __restrict__ SD) {
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_summary(
       fy.fetch(dyb + tn * D, D32, tv, dvalid, tid);
       fC.fetch(Cb + tn * N, tv, tid);
     }
-#pragma unroll
+#pragma unroll 4
     for (int s = kTc - 1; s >= 0; --s) {
       const float dl = sd[buf][s][cl], dyv = sdy[buf][s][cl];
       float Cv[NS];
@@ -326,10 +326,11 @@ static hipError_t bwd_impl(const ScanArgs& a, const BwdPlan& p, hipStream_t st) 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t BLN = a.B * a.L * N;
-  if ((e = launch_reduce(p.dBp, p.ng, BLN, a.dB, false, st)) != hipSuccess) return e;
-  if ((e = launch_reduce(p.dCp, p.ng, BLN, a.dC, false, st)) != hipSuccess) return e;
-  if ((e = launch_reduce(p.dAp, a.B * p.nc, a.D * N, a.dA, true, st)) != hipSuccess) return e;
-  return launch_reduce(p.dDp, a.B * p.nc, a.D, a.dD, true, st);
+  if ((e = launch_reduce(p.dBp, p.ng, BLN, a.dB, false, p.rtmp, st)) != hipSuccess) return e;
+  if ((e = launch_reduce(p.dCp, p.ng, BLN, a.dC, false, p.rtmp, st)) != hipSuccess) return e;
+  if ((e = launch_reduce(p.dAp, a.B * p.nc, a.D * N, a.dA, true, p.rtmp, st)) != hipSuccess)
+    return e;
+  return launch_reduce(p.dDp, a.B * p.nc, a.D, a.dD, true, p.rtmp, st);
 }
 
 hipError_t launch_scan_bwd(const ScanArgs& a, const BwdPlan& p, hipStream_t st) {

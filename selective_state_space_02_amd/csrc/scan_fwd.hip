@@ -26,7 +26,7 @@
 namespace ssm {
 
 template <typename T, int N>
-__global__ __launch_bounds__(256, 2) void k_fwd_summary(
+__global__ __launch_bounds__(256, 4) void k_fwd_summary(
     int64_t L, int64_t D, int64_t Lc, int nc, const T* __restrict__ x,
     const T* __restrict__ delta, const float* __restrict__ A, const T* __restrict__ Bm,
     float* __restrict__ S, float* __restrict__ SD) {
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_summary(
       fd.fetch(db + tn * D, D32, kTc, dvalid, tid);
       fB.fetch(Bb + tn * N, kTc, tid);
     }
-#pragma unroll
+#pragma unroll 4
     for (int s = 0; s < kTc; ++s) {
       const float dl = sd[buf][s][cl], u = dl * sx[buf][s][cl];
       float Bv[NS];
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void k_fwd_carry(
 // y (nullable: only the checkpoints are wanted); ckpt (nullable): [B][nf][D][N],
 // the state before step f*kTc.
 template <typename T, int N>
-__global__ __launch_bounds__(256, 2) void k_fwd_output(
+__global__ __launch_bounds__(256, 4) void k_fwd_output(
     int64_t L, int64_t D, int64_t Lc, int nc, int64_t nf, const T* __restrict__ x,
     const T* __restrict__ delta, const float* __restrict__ A, const T* __restrict__ Bm,
     const T* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ hin,
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_output(
       for (int j = 0; j < NS; ++j) o[j] = h[j];
     }
     const int smax = (t1 - tf < kTc) ? int(t1 - tf) : kTc;
-#pragma unroll
+#pragma unroll 4
     for (int s = 0; s < kTc; ++s) {
       const float dl = sd[buf][s][cl], xv = sx[buf][s][cl];
       const float u = dl * xv;
