@@ -72,6 +72,34 @@ class HipEvents:
         self.made = []
 
 
+BWD_MAIN_SOURCES = ("scan_bwd.hip", "common.hpp", "tile.hpp", "launch.hpp")
+COUNTERS_MD = os.path.join(ROOT, "profiles", "k_bwd_main_mamba-2.8b_counters.md")
+
+
+def bwd_main_source_hash():
+    """sha256 over the sources that define the backward main kernel."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in BWD_MAIN_SOURCES:
+        h.update(open(os.path.join(ROOT, "selective_state_space_02_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def counter_traffic(workload_name):
+    """HBM bytes per launch of the backward main kernel from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary (copy-calibrated), or None when there is none for this
+    workload or the kernel's sources changed since the counters were taken."""
+    if workload_name != "mamba-2.8b" or not os.path.exists(COUNTERS_MD):
+        return None
+    text = open(COUNTERS_MD).read()
+    if "```json" not in text:
+        return None
+    rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    if rec.get("source_sha256") != bwd_main_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 def algorithmic_bytes(w):
     """Bytes the method must move per step (HBM), by operation."""
     s = 2 if w.dtype == "bf16" else 4
@@ -294,7 +322,7 @@ def main():
             "peak": FP32_VECTOR_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved_tflops / FP32_VECTOR_PEAK_TFLOPS,
-            "traffic": None,
+            "traffic": counter_traffic(w.name),
             "avg_launch_ms": main_ms,
             "algorithmic_flops_per_launch": main_flops,
             "algorithmic_bytes_per_launch": bwd_main_bytes(w),
