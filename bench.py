@@ -30,7 +30,11 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3
 
 # Algorithmic floating-point work per state update (b, t, d, n) of the backward main
 # kernel (recompute of a_t and h_t from the checkpoint, the adjoint step and every
-# gradient contribution); FMA counts 2, exp 1.  Derivation in the design doc.
+# gradient contribution); FMA counts 2, exp 1.  Recompute: exp(delta*A) 2, h = a*h + u
+# 2, the d-loop's a and h stores 1 -> 5.  Reverse: g = dy*C + a*g' 2, dC term dy*h 1
+# (plus its reduction into the lane's partial 1), dB term g*u 1 (+1), dx/ddelta terms
+# g*B and g*h_prev*a 4, dA term 2, the a*g carry product 1, reductions over the
+# quarter's states 2 -> 15.
 BWD_MAIN_FLOPS_PER_UPDATE = 20
 
 

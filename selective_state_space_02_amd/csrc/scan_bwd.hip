@@ -140,6 +140,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(
   __shared__ float sx[2][kTc][kTileCh], sd[2][kTc][kTileCh], sdy[2][kTc][kTileCh];
   __shared__ float sB[2][kTc][N], sC[2][kTc][N];
   __shared__ float red[2][4][kTc][2 * N];
+  __shared__ float sdx[2][kTc][kTileCh], sdd[2][kTc][kTileCh];
 
   const int c = blockIdx.z, b = blockIdx.y, grp = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = tid & 3, cl = tid >> 2;
@@ -152,8 +153,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(
   const T* dyb = dy + int64_t(b) * L * D + d0;
   const T* Bb = Bm + int64_t(b) * L * N;
   const T* Cb = Cm + int64_t(b) * L * N;
-  T* dxb = dx + int64_t(b) * L * D + d;
-  T* ddb = ddelta + int64_t(b) * L * D + d;
+  T* dxb = dx + int64_t(b) * L * D + d0;
+  T* ddb = ddelta + int64_t(b) * L * D + d0;
   const float* ckb = ckpt + (int64_t(b) * nf * D + d) * N + q * NS;  // + f*D*N
   float* pB = dBp + (int64_t(grp) * B + b) * L * N;
   float* pC = dCp + (int64_t(grp) * B + b) * L * N;
@@ -227,8 +228,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(
         hs[s][j] = h[j];
       }
     }
-    // reverse step
+    // reverse step; the channel sums of step s+1 are formed while step s computes
     const int smax = (t1 - tf < kTc) ? int(t1 - tf) : kTc;
+    float pv[V];
 #pragma unroll
     for (int s = kTc - 1; s >= 0; --s) {
       const float dl = sd[buf][s][cl], xv = sx[buf][s][cl], dyv = sdy[buf][s][cl];
@@ -252,15 +254,20 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(
       }
       sBg = quad_sum(sBg);
       sAq = quad_sum(sAq);
-      if (act && q == 0 && s < smax) {
-        const int64_t i = (tf + s) * D;
-        st(dxb, i, __builtin_fmaf(Dd, dyv, dl * sBg));
-        st(ddb, i, __builtin_fmaf(kLn2, sAq, xv * sBg));
+      if (q == 0) {
+        sdx[buf][s][cl] = __builtin_fmaf(Dd, dyv, dl * sBg);
+        sdd[buf][s][cl] = __builtin_fmaf(kLn2, sAq, xv * sBg);
       }
       dD_acc = __builtin_fmaf(dyv, xv, dD_acc);
-      chan_reduce<V>(vals, lane);
-      if (writer) red[buf][wave][s][ridx] = vals[0];
+      if (s < kTc - 1) {
+        chan_reduce<V>(pv, lane);
+        if (writer) red[buf][wave][s + 1][ridx] = pv[0];
+      }
+#pragma unroll
+      for (int k = 0; k < V; ++k) pv[k] = vals[k];
     }
+    chan_reduce<V>(pv, lane);
+    if (writer) red[buf][wave][0][ridx] = pv[0];
     if (more) {
       fx.commit(sx[buf ^ 1], tv, dvalid, tid);
       fd.commit(sd[buf ^ 1], tv, dvalid, tid);
@@ -269,7 +276,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(
       fC.commit(sC[buf ^ 1], tv, tid);
     }
     __syncthreads();
-    // the four wavefronts' channel sums of this tile -> this group's partial
+    // this tile's dx and ddelta, and the four wavefronts' channel sums -> this group's partial
+    tile_store_ch(dxb + tf * D, sdx[buf], D32, smax, dvalid, tid);
+    tile_store_ch(ddb + tf * D, sdd[buf], D32, smax, dvalid, tid);
     for (int k = tid; k < kTc * 2 * N; k += 256) {
       const int s = k / (2 * N), r = k % (2 * N);
       if (s < smax) {

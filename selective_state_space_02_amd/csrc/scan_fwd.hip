@@ -124,6 +124,7 @@ __global__ __launch_bounds__(256, 4) void k_fwd_output(
     T* __restrict__ y, float* __restrict__ ckpt, float* __restrict__ h_last) {
   constexpr int NS = N / 4;
   __shared__ float sx[2][kTc][kTileCh], sd[2][kTc][kTileCh], sB[2][kTc][N], sC[2][kTc][N];
+  __shared__ float sy[2][kTc][kTileCh];
   const int c = blockIdx.z, b = blockIdx.y, tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
   const int64_t d0 = int64_t(blockIdx.x) * kTileCh, d = d0 + cl;
   const bool act = d < D;
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(256, 4) void k_fwd_output(
   const T* db = delta + int64_t(b) * L * D + d0;
   const T* Bb = Bm + int64_t(b) * L * N;
   const T* Cb = Cm + int64_t(b) * L * N;
-  T* yb = y ? y + int64_t(b) * L * D + d : nullptr;
+  T* yb = y ? y + int64_t(b) * L * D + d0 : nullptr;
   float* ckb = ckpt ? ckpt + (int64_t(b) * nf * D + d) * N + q * NS : nullptr;  // + f*D*N
   float A2[NS], h[NS];
 #pragma unroll
@@ -163,6 +164,10 @@ __global__ __launch_bounds__(256, 4) void k_fwd_output(
     const int buf = it & 1;
     const int64_t tf = t0 + int64_t(it) * kTc;
     const bool more = it + 1 < ntile;
+    if (yb && it > 0) {  // y of the previous tile, staged in LDS before the last barrier
+      const int64_t tp = tf - kTc;
+      tile_store_ch(yb + tp * D, sy[buf ^ 1], D32, kTc, dvalid, tid);
+    }
     if (more) {
       const int64_t tn = tf + kTc;
       tv = clamp_valid(L - tn);
@@ -176,7 +181,6 @@ __global__ __launch_bounds__(256, 4) void k_fwd_output(
 #pragma unroll
       for (int j = 0; j < NS; ++j) o[j] = h[j];
     }
-    const int smax = (t1 - tf < kTc) ? int(t1 - tf) : kTc;
 #pragma unroll 4
     for (int s = 0; s < kTc; ++s) {
       const float dl = sd[buf][s][cl], xv = sx[buf][s][cl];
@@ -192,7 +196,7 @@ __global__ __launch_bounds__(256, 4) void k_fwd_output(
         yp = __builtin_fmaf(Cv[j], h[j], yp);
       }
       yp = quad_sum(yp);
-      if (yb && act && q == 0 && s < smax) st(yb, (tf + s) * D, __builtin_fmaf(Dd, xv, yp));
+      if (q == 0) sy[buf][s][cl] = __builtin_fmaf(Dd, xv, yp);
     }
     if (more) {
       fx.commit(sx[buf ^ 1], tv, dvalid, tid);
@@ -201,6 +205,10 @@ __global__ __launch_bounds__(256, 4) void k_fwd_output(
       fC.commit(sC[buf ^ 1], tv, tid);
     }
     __syncthreads();
+  }
+  if (yb) {  // y of the last tile
+    const int64_t tl = t0 + int64_t(ntile - 1) * kTc;
+    tile_store_ch(yb + tl * D, sy[(ntile - 1) & 1], D32, clamp_valid(t1 - tl), dvalid, tid);
   }
   if (h_last && act && c == nc - 1) {
 #pragma unroll

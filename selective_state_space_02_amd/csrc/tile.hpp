@@ -61,6 +61,19 @@ struct VecFetch {
   }
 };
 
+// Writes an LDS tile of per-channel outputs back to a [.,L,D] tensor with the same
+// coalesced mapping as the fetch (a wavefront stores 64 consecutive channels of one
+// step); tile = base + tf*D + d0; only steps < tvalid and channels < dvalid are written.
+template <typename T>
+__device__ __forceinline__ void tile_store_ch(T* __restrict__ tile, const float (*sm)[kTileCh],
+                                              int D32, int tvalid, int dvalid, int tid) {
+#pragma unroll
+  for (int k = 0; k < kChPerThread; ++k) {
+    const int e = tid + kTileThreads * k, s = e >> 6, c = e & 63;
+    if (s < tvalid && c < dvalid) tile[s * D32 + c] = from_f32<T>(sm[s][c]);
+  }
+}
+
 // The NS state values of lane quarter q at step s of an LDS vector tile.
 template <int N, int NS>
 __device__ __forceinline__ void tile_read_vec(const float (*sm)[N], int s, int q, float (&o)[NS]) {
