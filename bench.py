@@ -29,12 +29,11 @@ HBM_PEAK_GBPS = 8000.0
 FP32_VECTOR_PEAK_TFLOPS = 157.3
 
 # Algorithmic floating-point work per state update (b, t, d, n) of the backward main
-# kernel (recompute of a_t and h_t from the checkpoint, the adjoint step and every
-# gradient contribution); FMA counts 2, exp 1.  Recompute: exp(delta*A) 2, h = a*h + u
-# 2, the d-loop's a and h stores 1 -> 5.  Reverse: g = dy*C + a*g' 2, dC term dy*h 1
-# (plus its reduction into the lane's partial 1), dB term g*u 1 (+1), dx/ddelta terms
-# g*B and g*h_prev*a 4, dA term 2, the a*g carry product 1, reductions over the
-# quarter's states 2 -> 15.
+# kernel, counting FMA 2, mul/add 1, exp 1.  Recompute of a_t and h_t from the
+# checkpoint: delta*A 1, exp 1, delta*x*B 1, state FMA 2 -> 5.  Reverse: g = dy*C + g' 2,
+# a*h_{t-1} 1, dA term g*q*delta accumulated 3, ddelta term sum g*A*q 2, the shared
+# dx/ddelta term sum g*B 2, dB term g*delta*x and its channel sum 2, dC term dy*h and its
+# channel sum 2, carry a*g 1 -> 15.
 BWD_MAIN_FLOPS_PER_UPDATE = 20
 
 
