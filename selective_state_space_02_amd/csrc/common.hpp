@@ -147,12 +147,6 @@ __device__ __forceinline__ float xor_lane(float v, int mask) {
 
 // DPP move within rows of 16 lanes, writing only the banks (groups of 4 lanes) set in
 // BANK; other lanes return `old`.  row_ror:n (CTRL 0x120 + n) reads lane (i - n) mod 16.
-template <int CTRL, int BANK>
-__device__ __forceinline__ float dpp_masked(float old, float src) {
-  return __int_as_float(
-      __builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, 0xF, BANK, false));
-}
-
 // gfx950 lane swaps: after swap32(a, b), lanes 0-31 hold (a, a of lane+32) and lanes
 // 32-63 hold (b of lane-32, b); swap16 does the same between rows 0/1 and 2/3.
 __device__ __forceinline__ void swap32(float& a, float& b) {
@@ -166,16 +160,17 @@ __device__ __forceinline__ void swap16(float& a, float& b) {
   b = __uint_as_float(r[1]);
 }
 
-// Sum V (2, 4 or 8) values per lane over the 16 lanes that share (lane & 3), i.e. over
-// the 16 channels of a wavefront.  Butterfly reduce-scatter over lane bits 5, 4, 3: at
-// each halving step a lane keeps half of its values (the lower half if its bit is 0)
-// and adds the partner's copy of that half -- a lane swap does the exchange for bits
-// 5 and 4, bank-masked DPP rotations for bit 3.  Lane bits left over once one value
-// remains are summed pairwise.  On return lane l holds in v[0] the total of value
-// index chan_reduce_index<V>(l); every lane holds a total (duplicated over the
-// leftover bits; chan_reduce_writer<V>(l) picks one lane per value).
+// Reduce-scatter of V (2, 4 or 8) values per lane over the 16 lanes that share
+// (lane & 3), i.e. over the 16 channels of a wavefront: the halving steps of a
+// butterfly over lane bits 5, 4 (V >= 4) and 3 (V == 8).  At each step a lane keeps
+// half of its values (the lower half if its bit is 0) and adds the partner's copy of
+// that half; a lane swap does the exchange for bits 5 and 4, a row_ror:8 DPP (lane i
+// reads lane i^8 inside a row of 16) for bit 3.  On return v[0] of lane l holds value
+// index k = l / (64/V), summed over the V channels that agree with l in the remaining
+// channel bits: the 16/V partial sums of (k, l & 3) sit in lanes
+// chan_partial_lane<V>(k, p, l & 3), p < 16/V, and are added by the caller.
 template <int V>
-__device__ __forceinline__ void chan_reduce(float (&v)[V], int lane) {
+__device__ __forceinline__ void chan_reduce_scatter(float (&v)[V], int lane) {
   static_assert(V == 2 || V == 4 || V == 8, "V must be 2, 4 or 8");
   // bit 5 (lane distance 32)
 #pragma unroll
@@ -192,41 +187,20 @@ __device__ __forceinline__ void chan_reduce(float (&v)[V], int lane) {
       swap16(a, b);
       v[k] = a + b;
     }
-  } else {
-    float a = v[0], b = v[0];
-    swap16(a, b);
-    v[0] = a + b;
   }
-  // bit 3 (distance 8, inside a row: row_ror:8 pairs lane i with i^8)
+  // bit 3 (distance 8): a lane sends the half its partner keeps
   if constexpr (V >= 8) {
-    const float lo = v[0], hi = v[1];
-    const float t = dpp_masked<0x128, 0xC>(0.f, hi);  // lanes 8-15: hi of lane i-8
-    const float r = dpp_masked<0x128, 0x3>(t, lo);    // lanes 0-7: lo of lane i+8
-    v[0] = ((lane & 8) ? hi : lo) + r;
-  } else {
-    v[0] += dpp_masked<0x128, 0xF>(0.f, v[0]);
-  }
-  // bit 2 (distance 4): banks 0,2 read lane i+4 (row_ror:12), banks 1,3 lane i-4 (row_ror:4)
-  {
-    const float t = dpp_masked<0x124, 0xA>(0.f, v[0]);
-    v[0] += dpp_masked<0x12C, 0x5>(t, v[0]);
+    const bool up = (lane & 8) != 0;
+    const float keep = up ? v[1] : v[0], send = up ? v[0] : v[1];
+    v[0] = keep + dpp<0x128>(send);
   }
 }
 
+// Lane that holds partial p (p < 16/V) of value index k for state quarter q after
+// chan_reduce_scatter<V>.
 template <int V>
-__device__ __forceinline__ int chan_reduce_index(int lane) {
-  int idx = 0, bit = 5;
-#pragma unroll
-  for (int half = V / 2; half >= 1; half /= 2, --bit)
-    if ((lane >> bit) & 1) idx += half;
-  return idx;
-}
-
-template <int V>
-__device__ __forceinline__ bool chan_reduce_writer(int lane) {
-  constexpr int H = (V >= 8) ? 3 : (V >= 4) ? 2 : (V >= 2) ? 1 : 0;  // log2(V)
-  constexpr int R = 4 - H;                                           // leftover bits
-  return ((lane >> 2) & ((1 << R) - 1)) == 0;
+__device__ __forceinline__ constexpr int chan_partial_lane(int k, int p, int q) {
+  return k * (64 / V) + p * 4 + q;
 }
 
 }  // namespace ssm

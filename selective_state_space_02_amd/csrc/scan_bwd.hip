@@ -137,9 +137,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(
     float* __restrict__ dh0) {
   constexpr int NS = N / 4;
   constexpr int V = 2 * NS;  // per-lane values summed over channels: dB (NS), dC (NS)
+  constexpr int NP = 16 / V;  // partial sums per value left by chan_reduce_scatter
   __shared__ float sx[2][kTc][kTileCh], sd[2][kTc][kTileCh], sdy[2][kTc][kTileCh];
   __shared__ float sB[2][kTc][N], sC[2][kTc][N];
-  __shared__ float red[2][4][kTc][2 * N];
+  __shared__ float red[2][4][kTc][64];  // [buffer][wavefront][step][lane]
   __shared__ float sdx[2][kTc][kTileCh], sdd[2][kTc][kTileCh];
 
   const int c = blockIdx.z, b = blockIdx.y, grp = blockIdx.x;
@@ -171,9 +172,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(
 
   const int64_t t0 = int64_t(c) * Lc, t1 = (t0 + Lc < L) ? t0 + Lc : L;
   const int ntile = int((t1 - t0 + kTc - 1) / kTc);
-  const bool writer = chan_reduce_writer<V>(lane);
-  const int vidx = chan_reduce_index<V>(lane);
-  const int ridx = (vidx < NS) ? (q * NS + vidx) : (N + q * NS + (vidx - NS));
 
   // tiles are walked from the last one backwards; the checkpoint of the next tile is
   // fetched together with its inputs
@@ -238,7 +236,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(
       tile_read_vec<N, NS>(sB[buf], s, q, Bv);
       tile_read_vec<N, NS>(sC[buf], s, q, Cv);
       const float u = dl * xv;
-      float sBg = 0.f, sAq = 0.f;
+      float sBg, sAq;
       float vals[V];
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
@@ -246,28 +244,30 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(
         const float qq = __builtin_fmaf(-u, Bv[j], hs[s][j]);  // a_t h_{t-1}
         const float gq = g * qq;
         dA_acc[j] = __builtin_fmaf(gq, dl, dA_acc[j]);
-        sAq = __builtin_fmaf(gq, A2[j], sAq);
-        sBg = __builtin_fmaf(g, Bv[j], sBg);
+        sAq = j ? __builtin_fmaf(gq, A2[j], sAq) : gq * A2[j];
+        sBg = j ? __builtin_fmaf(g, Bv[j], sBg) : g * Bv[j];
         vals[j] = g * u;
         vals[NS + j] = dyv * hs[s][j];
         gp[j] = as[s][j] * g;
       }
+      // the four lanes of a channel hold identical sums and write the same values, so
+      // the step has no branch and its work can interleave with its neighbours'
       sBg = quad_sum(sBg);
       sAq = quad_sum(sAq);
-      if (q == 0) {
-        sdx[buf][s][cl] = __builtin_fmaf(Dd, dyv, dl * sBg);
-        sdd[buf][s][cl] = __builtin_fmaf(kLn2, sAq, xv * sBg);
-      }
+      sdx[buf][s][cl] = __builtin_fmaf(Dd, dyv, dl * sBg);
+      sdd[buf][s][cl] = __builtin_fmaf(kLn2, sAq, xv * sBg);
       dD_acc = __builtin_fmaf(dyv, xv, dD_acc);
       if (s < kTc - 1) {
-        chan_reduce<V>(pv, lane);
-        if (writer) red[buf][wave][s + 1][ridx] = pv[0];
+        chan_reduce_scatter<V>(pv, lane);
+        red[buf][wave][s + 1][lane] = pv[0];
       }
 #pragma unroll
       for (int k = 0; k < V; ++k) pv[k] = vals[k];
+      // keep each step's work together: hoisting across steps runs out of registers
+      __builtin_amdgcn_sched_barrier(0);
     }
-    chan_reduce<V>(pv, lane);
-    if (writer) red[buf][wave][0][ridx] = pv[0];
+    chan_reduce_scatter<V>(pv, lane);
+    red[buf][wave][0][lane] = pv[0];
     if (more) {
       fx.commit(sx[buf ^ 1], tv, dvalid, tid);
       fd.commit(sd[buf ^ 1], tv, dvalid, tid);
@@ -282,7 +282,16 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(
     for (int k = tid; k < kTc * 2 * N; k += 256) {
       const int s = k / (2 * N), r = k % (2 * N);
       if (s < smax) {
-        const float sum = (red[buf][0][s][r] + red[buf][1][s][r]) + (red[buf][2][s][r] + red[buf][3][s][r]);
+        // value index and state quarter of output r (dB_n for r < N, dC_n above)
+        const int n = r % N, vi = (r / N) * NS + n % NS, qr = n / NS;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          float part = red[buf][w][s][chan_partial_lane<V>(vi, 0, qr)];
+#pragma unroll
+          for (int pi = 1; pi < NP; ++pi) part += red[buf][w][s][chan_partial_lane<V>(vi, pi, qr)];
+          sum = w ? sum + part : part;
+        }
         const int64_t o = (tf + s) * N;
         if (r < N) pB[o + r] = sum;
         else pC[o + r - N] = sum;
