@@ -92,8 +92,8 @@ int ssm_set_kernel_timer(int kernel, void *start, void *stop);
  *
  * Shapes: x, delta, y, dy, dx, ddelta [B,L,D]; Bm, Cm [B,L,N] (shared by all
  * channels); A, dA [D,N]; Dv, dD [D]; h0, h_last, dh0 [B,D,N]; dB, dC [B,L,N] f32.
- * Supported: N in {4, 8, 16}; B <= 65535; L, D >= 1 (tails handled, no multiple
- * required).
+ * Supported: N in {4, 8, 16}; B <= 65535; 1 <= D <= 2^24; L >= 1 (tails
+ * handled, no multiple required; D a multiple of 4 takes the vectorised path).
  *
  * Checkpoints.  The forward can save the state before every 16th step into `ckpt`
  * (ssm_scan_ckpt_bytes() bytes; layout private to this library version) for the

@@ -150,8 +150,9 @@ int check_scan_dims(ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D, int64_t 
   if (N != 4 && N != 8 && N != 16)
     return fail(SSM_ERR_UNSUPPORTED, "state size N=%lld not supported (4, 8 or 16)", (long long)N);
   if (B > 65535) return fail(SSM_ERR_UNSUPPORTED, "batch B=%lld exceeds 65535", (long long)B);
-  if (D > (int64_t(1) << 26))
-    return fail(SSM_ERR_UNSUPPORTED, "channels D=%lld exceed 2^26", (long long)D);
+  // a 16-step tile of one channel group spans < 2^31 bytes (32-bit buffer offsets)
+  if (D > (int64_t(1) << 24))
+    return fail(SSM_ERR_UNSUPPORTED, "channels D=%lld exceed 2^24", (long long)D);
   if (B > kMaxElems / L || B * L > kMaxElems / D || B * L * D > kMaxElems / N)
     return fail(SSM_ERR_ARG, "tensor sizes overflow");
   return SSM_OK;
@@ -300,6 +301,7 @@ int ssm_scan_fwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t 
   a.B = B; a.L = L; a.D = D; a.N = N;
   a.x = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dv = Dv; a.h0 = h0;
   a.y = y; a.h_last = h_last;
+  a.vec4 = D % 4 == 0;
   return hip_status(ssm::launch_scan_fwd(a, p, static_cast<hipStream_t>(stream)), "ssm_scan_fwd");
 }
 
@@ -329,6 +331,7 @@ int ssm_scan_bwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t 
   a.x = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dv = Dv; a.h0 = h0;
   a.dy = dy; a.dx = dx; a.ddelta = ddelta; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD;
   a.dh0 = dh0;
+  a.vec4 = D % 4 == 0;
   if (with_ckpt) {
     p.ckpt = ckpt;
   } else {

@@ -31,6 +31,14 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
   return __builtin_bit_cast(bf16_t, (__bf16)v);
 }
 
+// Two floats as packed bf16 (lo in bits 0-15), rounded to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const b2 r = __builtin_convertvector(f2{lo, hi}, b2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 template <typename T>
 __device__ __forceinline__ float ld(const T* p, int64_t i) { return to_f32(p[i]); }
 
@@ -147,6 +155,23 @@ __device__ __forceinline__ float xor_lane(float v, int mask) {
 
 // DPP move within rows of 16 lanes, writing only the banks (groups of 4 lanes) set in
 // BANK; other lanes return `old`.  row_ror:n (CTRL 0x120 + n) reads lane (i - n) mod 16.
+// Ordering fence for unrolled step loops: each value is treated as redefined here and
+// no memory access moves across.  Work of later steps that depends on these values
+// (or on loads issued after the fence) cannot be hoisted above it, so the compiler
+// does not interleave whole steps (which would keep the operands of many steps live
+// at once); independent work inside a step is still scheduled freely.
+__device__ __forceinline__ void step_fence() { asm volatile("" ::: "memory"); }
+template <typename T0, typename... Ts>
+__device__ __forceinline__ void step_fence(T0& v, Ts&... rest) {
+  asm volatile("" : "+v"(v));
+  step_fence(rest...);
+}
+template <int K>
+__device__ __forceinline__ void step_fence_arr(float (&v)[K]) {
+#pragma unroll
+  for (int k = 0; k < K; ++k) asm volatile("" : "+v"(v[k]));
+}
+
 // gfx950 lane swaps: after swap32(a, b), lanes 0-31 hold (a, a of lane+32) and lanes
 // 32-63 hold (b of lane-32, b); swap16 does the same between rows 0/1 and 2/3.
 __device__ __forceinline__ void swap32(float& a, float& b) {

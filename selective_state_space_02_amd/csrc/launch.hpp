@@ -14,6 +14,7 @@ constexpr int kTc = 16;
 struct ScanArgs {
   int dtype;  // 0 f32, 1 bf16
   int64_t B, L, D, N;
+  bool vec4;  // D % 4 == 0: per-channel tiles move 4 channels per thread
   const void* x;
   const void* delta;
   const float* A;

@@ -25,8 +25,8 @@
 //                     recompute a_t and h_t of the interval from its checkpoint into
 //                     registers, then run the reverse step; dx and ddelta are
 //                     written, dB/dC are summed over the workgroup's 64 channels
-//                     (butterfly + LDS) into per-group partials, dA/dDv into
-//                     per-(batch, chunk) partials;
+//                     (reduce-scatter across lanes, then LDS) into per-group
+//                     partials, dA/dDv into per-(batch, chunk) partials;
 //   4. k_reduce (reduce.hip): fixed-order sums of the partials.
 #include "common.hpp"
 #include "launch.hpp"
@@ -34,7 +34,9 @@
 
 namespace ssm {
 
-template <typename T, int N>
+// Chunk summaries of the adjoint: G (pushed adjoint of the chunk alone) and the sum of
+// delta, for chunks 1..nc-1.
+template <typename T, int N, int VEC>
 __global__ __launch_bounds__(256, 4) void k_bwd_summary(
     int64_t L, int64_t D, int64_t Lc, int nc, const T* __restrict__ delta,
     const float* __restrict__ A, const T* __restrict__ Cm, const T* __restrict__ dy,
@@ -59,26 +61,27 @@ __global__ __launch_bounds__(256, 4) void k_bwd_summary(
   const int64_t t0 = int64_t(c) * Lc, t1 = (t0 + Lc < L) ? t0 + Lc : L;
   const int ntile = int((t1 - t0 + kTc - 1) / kTc);
   // tiles are walked from the last one backwards
-  ChFetch<T> fd, fy;
+  const ChTile<T, VEC> gt(D32, dvalid, tid);
+  const uint32_t voff = VecFetch<T, N>::offset(tid);
+  ChFetch<T, VEC> fd, fy;
   VecFetch<T, N> fC;
   int64_t tf = t0 + int64_t(ntile - 1) * kTc;
-  int tv = clamp_valid(L - tf);
-  fd.fetch(db + tf * D, D32, tv, dvalid, tid);
-  fy.fetch(dyb + tf * D, D32, tv, dvalid, tid);
-  fC.fetch(Cb + tf * N, tv, tid);
-  fd.commit(sd[0], tv, dvalid, tid);
-  fy.commit(sdy[0], tv, dvalid, tid);
-  fC.commit(sC[0], tv, tid);
+  const int tv = clamp_valid(L - tf);
+  fd.fetch(gt, db + tf * D, D32, tv, dvalid);
+  fy.fetch(gt, dyb + tf * D, D32, tv, dvalid);
+  fC.fetch(Cb + tf * N, tv, voff);
+  fd.commit(gt, sd[0]);
+  fy.commit(gt, sdy[0]);
+  fC.commit(sC[0], tid);
   __syncthreads();
   for (int it = 0; it < ntile; ++it, tf -= kTc) {
     const int buf = it & 1;
     const bool more = it + 1 < ntile;
-    if (more) {
+    if (more) {  // every tile but the last one is full
       const int64_t tn = tf - kTc;
-      tv = kTc;  // every tile but the last one is full
-      fd.fetch(db + tn * D, D32, tv, dvalid, tid);
-      fy.fetch(dyb + tn * D, D32, tv, dvalid, tid);
-      fC.fetch(Cb + tn * N, tv, tid);
+      fd.fetch(gt, db + tn * D, D32, kTc, dvalid);
+      fy.fetch(gt, dyb + tn * D, D32, kTc, dvalid);
+      fC.fetch(Cb + tn * N, kTc, voff);
     }
 #pragma unroll 4
     for (int s = kTc - 1; s >= 0; --s) {
@@ -93,9 +96,9 @@ __global__ __launch_bounds__(256, 4) void k_bwd_summary(
       sdl += dl;
     }
     if (more) {
-      fd.commit(sd[buf ^ 1], tv, dvalid, tid);
-      fy.commit(sdy[buf ^ 1], tv, dvalid, tid);
-      fC.commit(sC[buf ^ 1], tv, tid);
+      fd.commit(gt, sd[buf ^ 1]);
+      fy.commit(gt, sdy[buf ^ 1]);
+      fC.commit(sC[buf ^ 1], tid);
     }
     __syncthreads();
   }
@@ -126,8 +129,18 @@ __global__ __launch_bounds__(256) void k_bwd_carry(
   }
 }
 
-template <typename T, int N>
-__global__ __launch_bounds__(256, 2) void k_bwd_main(
+// Main backward pass: one chunk of one batch row for 64 channels.  Checkpoint intervals
+// (tiles of kTc steps) are walked from the last one backwards.  Per tile the states are
+// recomputed from the interval's checkpoint into a register stash of kTc/SPLIT steps
+// (with SPLIT = 2 the first half of the interval is recomputed twice so that only half
+// is held at a time), then the reverse step runs over the stashed steps.  dx and ddelta
+// of a step overwrite the step's x and delta in LDS (a channel's slots are read and
+// written only by the channel's four lanes, reads first) and are stored after the tile
+// with coalesced writes; the dB/dC partials of each lane go to LDS and are summed there.
+// Two barriers per tile: after the compute (outputs complete) and after the next
+// tile's inputs are committed.
+template <typename T, int N, int VEC, int SPLIT, int WAVES>
+__global__ __launch_bounds__(256, WAVES) void k_bwd_main(
     int64_t B, int64_t L, int64_t D, int64_t Lc, int nc, int64_t nf,
     const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dv,
@@ -135,13 +148,14 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(
     T* __restrict__ dx, T* __restrict__ ddelta, float* __restrict__ dBp,
     float* __restrict__ dCp, float* __restrict__ dAp, float* __restrict__ dDp,
     float* __restrict__ dh0) {
-  constexpr int NS = N / 4;
-  constexpr int V = 2 * NS;  // per-lane values summed over channels: dB (NS), dC (NS)
-  constexpr int NP = 16 / V;  // partial sums per value left by chan_reduce_scatter
+  constexpr int NS = N / 4;       // states per lane
+  constexpr int V = 2 * NS;       // per-lane values summed over channels: dB, dC
+  constexpr int NP = 16 / V;      // partials per value left in LDS by chan_reduce_scatter
+  constexpr int SL = kTc / SPLIT; // stashed steps
+  static_assert(SPLIT == 1 || SPLIT == 2, "unsupported stash split");
   __shared__ float sx[2][kTc][kTileCh], sd[2][kTc][kTileCh], sdy[2][kTc][kTileCh];
   __shared__ float sB[2][kTc][N], sC[2][kTc][N];
-  __shared__ float red[2][4][kTc][64];  // [buffer][wavefront][step][lane]
-  __shared__ float sdx[2][kTc][kTileCh], sdd[2][kTc][kTileCh];
+  __shared__ float red[4][kTc][64];  // [wavefront][step][lane]
 
   const int c = blockIdx.z, b = blockIdx.y, grp = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = tid & 3, cl = tid >> 2;
@@ -156,7 +170,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(
   const T* Cb = Cm + int64_t(b) * L * N;
   T* dxb = dx + int64_t(b) * L * D + d0;
   T* ddb = ddelta + int64_t(b) * L * D + d0;
-  const float* ckb = ckpt + (int64_t(b) * nf * D + d) * N + q * NS;  // + f*D*N
+  // checkpoint f of this group: ckpt + ((b*nf + f)*D + d0)*N, lane at (cl*N + q*NS)
+  const float* ckg = ckpt + (int64_t(b) * nf * D + d0) * N;
+  const uint32_t ckoff = act ? uint32_t(cl * N + q * NS) * 4u : kOffNone;
+  const uint32_t ckbytes = uint32_t(dvalid * N) * 4u;
   float* pB = dBp + (int64_t(grp) * B + b) * L * N;
   float* pC = dCp + (int64_t(grp) * B + b) * L * N;
 
@@ -173,112 +190,141 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(
   const int64_t t0 = int64_t(c) * Lc, t1 = (t0 + Lc < L) ? t0 + Lc : L;
   const int ntile = int((t1 - t0 + kTc - 1) / kTc);
 
-  // tiles are walked from the last one backwards; the checkpoint of the next tile is
-  // fetched together with its inputs
-  ChFetch<T> fx, fd, fy;
+  const ChTile<T, VEC> gt(D32, dvalid, tid);
+  const uint32_t voff = VecFetch<T, N>::offset(tid);
+  ChFetch<T, VEC> fx, fd, fy;
   VecFetch<T, N> fB, fC;
-  float hck[NS];
-  int64_t tf = t0 + int64_t(ntile - 1) * kTc;
-  int tv = clamp_valid(L - tf);
-  fx.fetch(xb + tf * D, D32, tv, dvalid, tid);
-  fd.fetch(db + tf * D, D32, tv, dvalid, tid);
-  fy.fetch(dyb + tf * D, D32, tv, dvalid, tid);
-  fB.fetch(Bb + tf * N, tv, tid);
-  fC.fetch(Cb + tf * N, tv, tid);
-#pragma unroll
-  for (int j = 0; j < NS; ++j) hck[j] = act ? ckb[(tf / kTc) * D * N + j] : 0.f;
-  fx.commit(sx[0], tv, dvalid, tid);
-  fd.commit(sd[0], tv, dvalid, tid);
-  fy.commit(sdy[0], tv, dvalid, tid);
-  fB.commit(sB[0], tv, tid);
-  fC.commit(sC[0], tv, tid);
+  float hcur[NS], hnxt[NS];  // checkpoints of the current and the next tile
+  auto fetch = [&](int64_t tt, int tvalid, float (&hk)[NS]) {
+    fx.fetch(gt, xb + tt * D, D32, tvalid, dvalid);
+    fd.fetch(gt, db + tt * D, D32, tvalid, dvalid);
+    fy.fetch(gt, dyb + tt * D, D32, tvalid, dvalid);
+    fB.fetch(Bb + tt * N, tvalid, voff);
+    fC.fetch(Cb + tt * N, tvalid, voff);
+    buf_load_states<NS>(buf_rsrc(ckg + (tt / kTc) * D * N, ckbytes), ckoff, hk);
+  };
+  auto commit = [&](int bf) {
+    fx.commit(gt, sx[bf]);
+    fd.commit(gt, sd[bf]);
+    fy.commit(gt, sdy[bf]);
+    fB.commit(sB[bf], tid);
+    fC.commit(sC[bf], tid);
+  };
+
+  int64_t tf = t0 + int64_t(ntile - 1) * kTc;  // first step of the current tile
+  fetch(tf, clamp_valid(L - tf), hcur);
+  commit(0);
+  if (ntile > 1) fetch(tf - kTc, kTc, hnxt);  // every tile but the last one is full
   __syncthreads();
 
+  float pv[V];  // channel-sum values of the step above the current one
   for (int it = 0; it < ntile; ++it, tf -= kTc) {
     const int buf = it & 1;
-    const bool more = it + 1 < ntile;
-    float h[NS];
 #pragma unroll
-    for (int j = 0; j < NS; ++j) h[j] = hck[j];
-    if (more) {
-      const int64_t tn = tf - kTc;
-      tv = kTc;  // every tile but the last one is full
-      fx.fetch(xb + tn * D, D32, tv, dvalid, tid);
-      fd.fetch(db + tn * D, D32, tv, dvalid, tid);
-      fy.fetch(dyb + tn * D, D32, tv, dvalid, tid);
-      fB.fetch(Bb + tn * N, tv, tid);
-      fC.fetch(Cb + tn * N, tv, tid);
+    for (int half = SPLIT - 1; half >= 0; --half) {
+      const int s0 = half * SL;
+      // Recompute steps 0 .. s0+SL-1 from the checkpoint, stashing a_t and h_t of the
+      // last SL.  The LDS operands of step s+1 are read during step s.
+      float h[NS];
 #pragma unroll
-      for (int j = 0; j < NS; ++j) hck[j] = act ? ckb[(tn / kTc) * D * N + j] : 0.f;
-    }
-    // recompute a_t and h_t of this tile from its checkpoint
-    float as[kTc][NS], hs[kTc][NS];
+      for (int j = 0; j < NS; ++j) h[j] = hcur[j];
+      float as[SL][NS], hs[SL][NS];
+      float ndl = sd[buf][0][cl], nxv = sx[buf][0][cl], nB[NS];
+      tile_read_vec<N, NS>(sB[buf], 0, q, nB);
 #pragma unroll
-    for (int s = 0; s < kTc; ++s) {
-      const float dl = sd[buf][s][cl], u = dl * sx[buf][s][cl];
-      float Bv[NS];
-      tile_read_vec<N, NS>(sB[buf], s, q, Bv);
+      for (int s = 0; s < s0 + SL; ++s) {
+        const float dl = ndl, u = dl * nxv;
+        float Bv[NS];
 #pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        const float a = __builtin_amdgcn_exp2f(dl * A2[j]);
-        h[j] = __builtin_fmaf(a, h[j], u * Bv[j]);
-        as[s][j] = a;
-        hs[s][j] = h[j];
+        for (int j = 0; j < NS; ++j) Bv[j] = nB[j];
+        if (s + 1 < s0 + SL) {
+          ndl = sd[buf][s + 1][cl];
+          nxv = sx[buf][s + 1][cl];
+          tile_read_vec<N, NS>(sB[buf], s + 1, q, nB);
+        }
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          const float a = __builtin_amdgcn_exp2f(dl * A2[j]);
+          h[j] = __builtin_fmaf(a, h[j], u * Bv[j]);
+          if (s >= s0) {
+            as[s - s0][j] = a;
+            hs[s - s0][j] = h[j];
+          }
+        }
+        step_fence_arr(h);
+        step_fence_arr(nB);
+        step_fence(ndl, nxv);
       }
-    }
-    // reverse step; the channel sums of step s+1 are formed while step s computes
-    const int smax = (t1 - tf < kTc) ? int(t1 - tf) : kTc;
-    float pv[V];
-#pragma unroll
-    for (int s = kTc - 1; s >= 0; --s) {
-      const float dl = sd[buf][s][cl], xv = sx[buf][s][cl], dyv = sdy[buf][s][cl];
-      float Bv[NS], Cv[NS];
-      tile_read_vec<N, NS>(sB[buf], s, q, Bv);
-      tile_read_vec<N, NS>(sC[buf], s, q, Cv);
-      const float u = dl * xv;
-      float sBg, sAq;
-      float vals[V];
-#pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        const float g = __builtin_fmaf(dyv, Cv[j], gp[j]);
-        const float qq = __builtin_fmaf(-u, Bv[j], hs[s][j]);  // a_t h_{t-1}
-        const float gq = g * qq;
-        dA_acc[j] = __builtin_fmaf(gq, dl, dA_acc[j]);
-        sAq = j ? __builtin_fmaf(gq, A2[j], sAq) : gq * A2[j];
-        sBg = j ? __builtin_fmaf(g, Bv[j], sBg) : g * Bv[j];
-        vals[j] = g * u;
-        vals[NS + j] = dyv * hs[s][j];
-        gp[j] = as[s][j] * g;
-      }
-      // the four lanes of a channel hold identical sums and write the same values, so
-      // the step has no branch and its work can interleave with its neighbours'
-      sBg = quad_sum(sBg);
-      sAq = quad_sum(sAq);
-      sdx[buf][s][cl] = __builtin_fmaf(Dd, dyv, dl * sBg);
-      sdd[buf][s][cl] = __builtin_fmaf(kLn2, sAq, xv * sBg);
-      dD_acc = __builtin_fmaf(dyv, xv, dD_acc);
-      if (s < kTc - 1) {
-        chan_reduce_scatter<V>(pv, lane);
-        red[buf][wave][s + 1][lane] = pv[0];
+      // Reverse step over the stash; the channel sums of step s+1 are formed during
+      // step s, and the LDS operands of step s-1 are read during step s.
+      float rdl, rxv, rdy, rB[NS], rC[NS];
+      {
+        const int s = s0 + SL - 1;
+        rdl = sd[buf][s][cl];
+        rxv = sx[buf][s][cl];
+        rdy = sdy[buf][s][cl];
+        tile_read_vec<N, NS>(sB[buf], s, q, rB);
+        tile_read_vec<N, NS>(sC[buf], s, q, rC);
       }
 #pragma unroll
-      for (int k = 0; k < V; ++k) pv[k] = vals[k];
-      // keep each step's work together: hoisting across steps runs out of registers
-      __builtin_amdgcn_sched_barrier(0);
+      for (int i = SL - 1; i >= 0; --i) {
+        const int s = s0 + i;
+        const float dl = rdl, xv = rxv, dyv = rdy;
+        float Bv[NS], Cv[NS];
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          Bv[j] = rB[j];
+          Cv[j] = rC[j];
+        }
+        if (i > 0) {
+          rdl = sd[buf][s - 1][cl];
+          rxv = sx[buf][s - 1][cl];
+          rdy = sdy[buf][s - 1][cl];
+          tile_read_vec<N, NS>(sB[buf], s - 1, q, rB);
+          tile_read_vec<N, NS>(sC[buf], s - 1, q, rC);
+        }
+        const float u = dl * xv;
+        float sBg, sAq;
+        float vals[V];
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          const float g = __builtin_fmaf(dyv, Cv[j], gp[j]);
+          const float qq = __builtin_fmaf(-u, Bv[j], hs[i][j]);  // a_t h_{t-1}
+          const float gq = g * qq;
+          dA_acc[j] = __builtin_fmaf(gq, dl, dA_acc[j]);
+          sAq = j ? __builtin_fmaf(gq, A2[j], sAq) : gq * A2[j];
+          sBg = j ? __builtin_fmaf(g, Bv[j], sBg) : g * Bv[j];
+          vals[j] = g * u;
+          vals[NS + j] = dyv * hs[i][j];
+          gp[j] = as[i][j] * g;
+        }
+        // identical in the channel's four lanes, which all write the same values
+        sBg = quad_sum(sBg);
+        sAq = quad_sum(sAq);
+        sx[buf][s][cl] = __builtin_fmaf(Dd, dyv, dl * sBg);   // dx
+        sd[buf][s][cl] = __builtin_fmaf(kLn2, sAq, xv * sBg);  // ddelta
+        dD_acc = __builtin_fmaf(dyv, xv, dD_acc);
+        if (s < kTc - 1) {
+          chan_reduce_scatter<V>(pv, lane);
+          red[wave][s + 1][lane] = pv[0];
+        }
+#pragma unroll
+        for (int k = 0; k < V; ++k) pv[k] = vals[k];
+        step_fence_arr(gp);
+        step_fence_arr(dA_acc);
+        step_fence_arr(rB);
+        step_fence_arr(rC);
+        step_fence(dD_acc, rdl, rxv, rdy);
+      }
     }
     chan_reduce_scatter<V>(pv, lane);
-    red[buf][wave][0][lane] = pv[0];
-    if (more) {
-      fx.commit(sx[buf ^ 1], tv, dvalid, tid);
-      fd.commit(sd[buf ^ 1], tv, dvalid, tid);
-      fy.commit(sdy[buf ^ 1], tv, dvalid, tid);
-      fB.commit(sB[buf ^ 1], tv, tid);
-      fC.commit(sC[buf ^ 1], tv, tid);
-    }
+    red[wave][0][lane] = pv[0];
     __syncthreads();
-    // this tile's dx and ddelta, and the four wavefronts' channel sums -> this group's partial
-    tile_store_ch(dxb + tf * D, sdx[buf], D32, smax, dvalid, tid);
-    tile_store_ch(ddb + tf * D, sdd[buf], D32, smax, dvalid, tid);
+
+    // this tile's dx and ddelta, and the channel sums -> this group's dB/dC partials
+    const int smax = (t1 - tf < kTc) ? int(t1 - tf) : kTc;
+    tile_store_ch(gt, dxb + tf * D, sx[buf], D32, smax, dvalid);
+    tile_store_ch(gt, ddb + tf * D, sd[buf], D32, smax, dvalid);
     for (int k = tid; k < kTc * 2 * N; k += 256) {
       const int s = k / (2 * N), r = k % (2 * N);
       if (s < smax) {
@@ -287,9 +333,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(
         float sum = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          float part = red[buf][w][s][chan_partial_lane<V>(vi, 0, qr)];
+          float part = red[w][s][chan_partial_lane<V>(vi, 0, qr)];
 #pragma unroll
-          for (int pi = 1; pi < NP; ++pi) part += red[buf][w][s][chan_partial_lane<V>(vi, pi, qr)];
+          for (int pi = 1; pi < NP; ++pi) part += red[w][s][chan_partial_lane<V>(vi, pi, qr)];
           sum = w ? sum + part : part;
         }
         const int64_t o = (tf + s) * N;
@@ -297,6 +343,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(
         else pC[o + r - N] = sum;
       }
     }
+    if (it + 1 < ntile) {
+      commit(buf ^ 1);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) hcur[j] = hnxt[j];
+      if (it + 2 < ntile) fetch(tf - 2 * kTc, kTc, hnxt);
+    }
+    __syncthreads();
   }
 
   if (act) {
@@ -311,10 +364,20 @@ __global__ __launch_bounds__(256, 2) void k_bwd_main(
   }
 }
 
+// Stash split and waves per SIMD of k_bwd_main per state size.  Its LDS (41-45 KB)
+// admits three workgroups per CU; at N = 16 the full stash does not fit the register
+// budget of three waves per SIMD, the split one does (measured 2.05 vs 2.11 ms on the
+// 2 x 16384 x 5120 layer against the full stash at two waves).
+template <int N>
+struct BwdMainCfg {
+  static constexpr int kSplit = (N == 16) ? 2 : 1;
+  static constexpr int kWaves = 3;
+};
+
 // ---------------------------------------------------------------------------------
 // host launcher
 // ---------------------------------------------------------------------------------
-template <typename T, int N>
+template <typename T, int N, int VEC>
 static hipError_t bwd_impl(const ScanArgs& a, const BwdPlan& p, hipStream_t st) {
   const T* x = static_cast<const T*>(a.x);
   const T* delta = static_cast<const T*>(a.delta);
@@ -325,8 +388,8 @@ static hipError_t bwd_impl(const ScanArgs& a, const BwdPlan& p, hipStream_t st) 
   const float* gin = nullptr;
   if (p.nc > 1) {
     timer_mark(kKBwdSummary, false, st);
-    hipLaunchKernelGGL((k_bwd_summary<T, N>), dim3(p.ng, a.B, p.nc - 1), block, 0, st, a.L,
-                       a.D, p.Lc, p.nc, delta, a.A, Cm, dy, p.GS, p.SD);
+    hipLaunchKernelGGL((k_bwd_summary<T, N, VEC>), dim3(p.ng, a.B, p.nc - 1), block, 0, st,
+                       a.L, a.D, p.Lc, p.nc, delta, a.A, Cm, dy, p.GS, p.SD);
     timer_mark(kKBwdSummary, true, st);
     const int64_t tot = a.B * a.D * N;
     timer_mark(kKBwdCarry, false, st);
@@ -336,10 +399,11 @@ static hipError_t bwd_impl(const ScanArgs& a, const BwdPlan& p, hipStream_t st) 
     gin = p.gin;
   }
   timer_mark(kKBwdMain, false, st);
-  hipLaunchKernelGGL((k_bwd_main<T, N>), dim3(p.ng, a.B, p.nc), block, 0, st, a.B, a.L, a.D,
-                     p.Lc, p.nc, p.nf, x, delta, a.A, Bm, Cm, a.Dv, dy, p.ckpt, gin,
-                     static_cast<T*>(a.dx), static_cast<T*>(a.ddelta), p.dBp, p.dCp, p.dAp,
-                     p.dDp, a.dh0);
+  using Cfg = BwdMainCfg<N>;
+  hipLaunchKernelGGL((k_bwd_main<T, N, VEC, Cfg::kSplit, Cfg::kWaves>), dim3(p.ng, a.B, p.nc),
+                     block, 0, st, a.B, a.L, a.D, p.Lc, p.nc, p.nf, x, delta, a.A, Bm, Cm,
+                     a.Dv, dy, p.ckpt, gin, static_cast<T*>(a.dx), static_cast<T*>(a.ddelta),
+                     p.dBp, p.dCp, p.dAp, p.dDp, a.dh0);
   timer_mark(kKBwdMain, true, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -351,18 +415,23 @@ static hipError_t bwd_impl(const ScanArgs& a, const BwdPlan& p, hipStream_t st) 
   return launch_reduce(p.dDp, a.B * p.nc, a.D, a.dD, true, p.rtmp, st);
 }
 
+template <typename T, int N>
+static hipError_t bwd_vec(const ScanArgs& a, const BwdPlan& p, hipStream_t st) {
+  return a.vec4 ? bwd_impl<T, N, 4>(a, p, st) : bwd_impl<T, N, 1>(a, p, st);
+}
+
 hipError_t launch_scan_bwd(const ScanArgs& a, const BwdPlan& p, hipStream_t st) {
   if (a.dtype == 0) {
     switch (a.N) {
-      case 4: return bwd_impl<float, 4>(a, p, st);
-      case 8: return bwd_impl<float, 8>(a, p, st);
-      case 16: return bwd_impl<float, 16>(a, p, st);
+      case 4: return bwd_vec<float, 4>(a, p, st);
+      case 8: return bwd_vec<float, 8>(a, p, st);
+      case 16: return bwd_vec<float, 16>(a, p, st);
     }
   } else {
     switch (a.N) {
-      case 4: return bwd_impl<bf16_t, 4>(a, p, st);
-      case 8: return bwd_impl<bf16_t, 8>(a, p, st);
-      case 16: return bwd_impl<bf16_t, 16>(a, p, st);
+      case 4: return bwd_vec<bf16_t, 4>(a, p, st);
+      case 8: return bwd_vec<bf16_t, 8>(a, p, st);
+      case 16: return bwd_vec<bf16_t, 16>(a, p, st);
     }
   }
   return hipErrorInvalidValue;

@@ -25,7 +25,7 @@
 
 namespace ssm {
 
-template <typename T, int N>
+template <typename T, int N, int VEC>
 __global__ __launch_bounds__(256, 4) void k_fwd_summary(
     int64_t L, int64_t D, int64_t Lc, int nc, const T* __restrict__ x,
     const T* __restrict__ delta, const float* __restrict__ A, const T* __restrict__ Bm,
@@ -49,23 +49,25 @@ __global__ __launch_bounds__(256, 4) void k_fwd_summary(
   float sdl = 0.f;
   const int64_t t0 = int64_t(c) * Lc;  // chunks 0..nc-2 are full
   const int ntile = int(Lc / kTc);
-  ChFetch<T> fx, fd;
+  const ChTile<T, VEC> gt(D32, dvalid, tid);
+  const uint32_t voff = VecFetch<T, N>::offset(tid);
+  ChFetch<T, VEC> fx, fd;
   VecFetch<T, N> fB;
-  fx.fetch(xb + t0 * D, D32, kTc, dvalid, tid);
-  fd.fetch(db + t0 * D, D32, kTc, dvalid, tid);
-  fB.fetch(Bb + t0 * N, kTc, tid);
-  fx.commit(sx[0], kTc, dvalid, tid);
-  fd.commit(sd[0], kTc, dvalid, tid);
-  fB.commit(sB[0], kTc, tid);
+  fx.fetch(gt, xb + t0 * D, D32, kTc, dvalid);
+  fd.fetch(gt, db + t0 * D, D32, kTc, dvalid);
+  fB.fetch(Bb + t0 * N, kTc, voff);
+  fx.commit(gt, sx[0]);
+  fd.commit(gt, sd[0]);
+  fB.commit(sB[0], tid);
   __syncthreads();
   for (int it = 0; it < ntile; ++it) {
     const int buf = it & 1;
     const bool more = it + 1 < ntile;
     if (more) {
       const int64_t tn = t0 + int64_t(it + 1) * kTc;
-      fx.fetch(xb + tn * D, D32, kTc, dvalid, tid);
-      fd.fetch(db + tn * D, D32, kTc, dvalid, tid);
-      fB.fetch(Bb + tn * N, kTc, tid);
+      fx.fetch(gt, xb + tn * D, D32, kTc, dvalid);
+      fd.fetch(gt, db + tn * D, D32, kTc, dvalid);
+      fB.fetch(Bb + tn * N, kTc, voff);
     }
 #pragma unroll 4
     for (int s = 0; s < kTc; ++s) {
@@ -80,9 +82,9 @@ __global__ __launch_bounds__(256, 4) void k_fwd_summary(
       sdl += dl;
     }
     if (more) {
-      fx.commit(sx[buf ^ 1], kTc, dvalid, tid);
-      fd.commit(sd[buf ^ 1], kTc, dvalid, tid);
-      fB.commit(sB[buf ^ 1], kTc, tid);
+      fx.commit(gt, sx[buf ^ 1]);
+      fd.commit(gt, sd[buf ^ 1]);
+      fB.commit(sB[buf ^ 1], tid);
     }
     __syncthreads();
   }
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(256) void k_fwd_carry(
 // hin: start state of each chunk, [B][nc][D][N]; may be null (zero start).
 // y (nullable: only the checkpoints are wanted); ckpt (nullable): [B][nf][D][N],
 // the state before step f*kTc.
-template <typename T, int N>
+template <typename T, int N, int VEC>
 __global__ __launch_bounds__(256, 4) void k_fwd_output(
     int64_t L, int64_t D, int64_t Lc, int nc, int64_t nf, const T* __restrict__ x,
     const T* __restrict__ delta, const float* __restrict__ A, const T* __restrict__ Bm,
@@ -135,7 +137,10 @@ __global__ __launch_bounds__(256, 4) void k_fwd_output(
   const T* Bb = Bm + int64_t(b) * L * N;
   const T* Cb = Cm + int64_t(b) * L * N;
   T* yb = y ? y + int64_t(b) * L * D + d0 : nullptr;
-  float* ckb = ckpt ? ckpt + (int64_t(b) * nf * D + d) * N + q * NS : nullptr;  // + f*D*N
+  // checkpoint f of this group: ckpt + ((b*nf + f)*D + d0)*N, lane at (cl*N + q*NS)
+  float* ckg = ckpt ? ckpt + (int64_t(b) * nf * D + d0) * N : nullptr;
+  const uint32_t ckoff = act ? uint32_t(cl * N + q * NS) * 4u : kOffNone;
+  const uint32_t ckbytes = uint32_t(dvalid * N) * 4u;
   float A2[NS], h[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) A2[j] = act ? A[d * N + q * NS + j] * kLog2e : 0.f;
@@ -148,39 +153,35 @@ __global__ __launch_bounds__(256, 4) void k_fwd_output(
   }
   const int64_t t0 = int64_t(c) * Lc, t1 = (t0 + Lc < L) ? t0 + Lc : L;
   const int ntile = int((t1 - t0 + kTc - 1) / kTc);
-  ChFetch<T> fx, fd;
+  const ChTile<T, VEC> gt(D32, dvalid, tid);
+  const uint32_t voff = VecFetch<T, N>::offset(tid);
+  ChFetch<T, VEC> fx, fd;
   VecFetch<T, N> fB, fC;
   int tv = clamp_valid(L - t0);
-  fx.fetch(xb + t0 * D, D32, tv, dvalid, tid);
-  fd.fetch(db + t0 * D, D32, tv, dvalid, tid);
-  fB.fetch(Bb + t0 * N, tv, tid);
-  fC.fetch(Cb + t0 * N, tv, tid);
-  fx.commit(sx[0], tv, dvalid, tid);
-  fd.commit(sd[0], tv, dvalid, tid);
-  fB.commit(sB[0], tv, tid);
-  fC.commit(sC[0], tv, tid);
+  fx.fetch(gt, xb + t0 * D, D32, tv, dvalid);
+  fd.fetch(gt, db + t0 * D, D32, tv, dvalid);
+  fB.fetch(Bb + t0 * N, tv, voff);
+  fC.fetch(Cb + t0 * N, tv, voff);
+  fx.commit(gt, sx[0]);
+  fd.commit(gt, sd[0]);
+  fB.commit(sB[0], tid);
+  fC.commit(sC[0], tid);
   __syncthreads();
   for (int it = 0; it < ntile; ++it) {
     const int buf = it & 1;
     const int64_t tf = t0 + int64_t(it) * kTc;
     const bool more = it + 1 < ntile;
-    if (yb && it > 0) {  // y of the previous tile, staged in LDS before the last barrier
-      const int64_t tp = tf - kTc;
-      tile_store_ch(yb + tp * D, sy[buf ^ 1], D32, kTc, dvalid, tid);
-    }
+    if (yb && it > 0)  // y of the previous tile, staged in LDS before the last barrier
+      tile_store_ch(gt, yb + (tf - kTc) * D, sy[buf ^ 1], D32, kTc, dvalid);
     if (more) {
       const int64_t tn = tf + kTc;
       tv = clamp_valid(L - tn);
-      fx.fetch(xb + tn * D, D32, tv, dvalid, tid);
-      fd.fetch(db + tn * D, D32, tv, dvalid, tid);
-      fB.fetch(Bb + tn * N, tv, tid);
-      fC.fetch(Cb + tn * N, tv, tid);
+      fx.fetch(gt, xb + tn * D, D32, tv, dvalid);
+      fd.fetch(gt, db + tn * D, D32, tv, dvalid);
+      fB.fetch(Bb + tn * N, tv, voff);
+      fC.fetch(Cb + tn * N, tv, voff);
     }
-    if (ckb && act) {
-      float* o = ckb + (tf / kTc) * D * N;
-#pragma unroll
-      for (int j = 0; j < NS; ++j) o[j] = h[j];
-    }
+    if (ckg) buf_store_states<NS>(h, buf_rsrc(ckg + (tf / kTc) * D * N, ckbytes), ckoff);
 #pragma unroll 4
     for (int s = 0; s < kTc; ++s) {
       const float dl = sd[buf][s][cl], xv = sx[buf][s][cl];
@@ -195,20 +196,20 @@ __global__ __launch_bounds__(256, 4) void k_fwd_output(
         h[j] = __builtin_fmaf(a, h[j], u * Bv[j]);
         yp = __builtin_fmaf(Cv[j], h[j], yp);
       }
-      yp = quad_sum(yp);
-      if (q == 0) sy[buf][s][cl] = __builtin_fmaf(Dd, xv, yp);
+      yp = quad_sum(yp);  // identical in the channel's four lanes, which all write it
+      sy[buf][s][cl] = __builtin_fmaf(Dd, xv, yp);
     }
     if (more) {
-      fx.commit(sx[buf ^ 1], tv, dvalid, tid);
-      fd.commit(sd[buf ^ 1], tv, dvalid, tid);
-      fB.commit(sB[buf ^ 1], tv, tid);
-      fC.commit(sC[buf ^ 1], tv, tid);
+      fx.commit(gt, sx[buf ^ 1]);
+      fd.commit(gt, sd[buf ^ 1]);
+      fB.commit(sB[buf ^ 1], tid);
+      fC.commit(sC[buf ^ 1], tid);
     }
     __syncthreads();
   }
   if (yb) {  // y of the last tile
     const int64_t tl = t0 + int64_t(ntile - 1) * kTc;
-    tile_store_ch(yb + tl * D, sy[(ntile - 1) & 1], D32, clamp_valid(t1 - tl), dvalid, tid);
+    tile_store_ch(gt, yb + tl * D, sy[(ntile - 1) & 1], D32, clamp_valid(t1 - tl), dvalid);
   }
   if (h_last && act && c == nc - 1) {
 #pragma unroll
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(256, 4) void k_fwd_output(
 // ---------------------------------------------------------------------------------
 // host launcher
 // ---------------------------------------------------------------------------------
-template <typename T, int N>
+template <typename T, int N, int VEC>
 static hipError_t fwd_impl(const ScanArgs& a, const FwdPlan& p, hipStream_t st) {
   const T* x = static_cast<const T*>(a.x);
   const T* delta = static_cast<const T*>(a.delta);
@@ -230,7 +231,7 @@ static hipError_t fwd_impl(const ScanArgs& a, const FwdPlan& p, hipStream_t st) 
   const float* hin = a.h0;  // [B][1][D][N] == [B][D][N] when nc == 1
   if (p.nc > 1) {
     timer_mark(kKFwdSummary, false, st);
-    hipLaunchKernelGGL((k_fwd_summary<T, N>), dim3(groups, a.B, p.nc - 1), block, 0, st, a.L,
+    hipLaunchKernelGGL((k_fwd_summary<T, N, VEC>), dim3(groups, a.B, p.nc - 1), block, 0, st, a.L,
                        a.D, p.Lc, p.nc, x, delta, a.A, Bm, p.S, p.SD);
     timer_mark(kKFwdSummary, true, st);
     const int64_t tot = a.B * a.D * N;
@@ -241,25 +242,30 @@ static hipError_t fwd_impl(const ScanArgs& a, const FwdPlan& p, hipStream_t st) 
     hin = p.hin;
   }
   timer_mark(kKFwdOutput, false, st);
-  hipLaunchKernelGGL((k_fwd_output<T, N>), dim3(groups, a.B, p.nc), block, 0, st, a.L, a.D,
+  hipLaunchKernelGGL((k_fwd_output<T, N, VEC>), dim3(groups, a.B, p.nc), block, 0, st, a.L, a.D,
                      p.Lc, p.nc, p.nf, x, delta, a.A, Bm, Cm, a.Dv, hin,
                      static_cast<T*>(a.y), p.ckpt, a.h_last);
   timer_mark(kKFwdOutput, true, st);
   return hipGetLastError();
 }
 
+template <typename T, int N>
+static hipError_t fwd_vec(const ScanArgs& a, const FwdPlan& p, hipStream_t st) {
+  return a.vec4 ? fwd_impl<T, N, 4>(a, p, st) : fwd_impl<T, N, 1>(a, p, st);
+}
+
 hipError_t launch_scan_fwd(const ScanArgs& a, const FwdPlan& p, hipStream_t st) {
   if (a.dtype == 0) {
     switch (a.N) {
-      case 4: return fwd_impl<float, 4>(a, p, st);
-      case 8: return fwd_impl<float, 8>(a, p, st);
-      case 16: return fwd_impl<float, 16>(a, p, st);
+      case 4: return fwd_vec<float, 4>(a, p, st);
+      case 8: return fwd_vec<float, 8>(a, p, st);
+      case 16: return fwd_vec<float, 16>(a, p, st);
     }
   } else {
     switch (a.N) {
-      case 4: return fwd_impl<bf16_t, 4>(a, p, st);
-      case 8: return fwd_impl<bf16_t, 8>(a, p, st);
-      case 16: return fwd_impl<bf16_t, 16>(a, p, st);
+      case 4: return fwd_vec<bf16_t, 4>(a, p, st);
+      case 8: return fwd_vec<bf16_t, 8>(a, p, st);
+      case 16: return fwd_vec<bf16_t, 16>(a, p, st);
     }
   }
   return hipErrorInvalidValue;

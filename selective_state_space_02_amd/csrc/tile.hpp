@@ -1,80 +1,203 @@
-// Staging of scan inputs through LDS, one tile at a time.
+// Staging of scan inputs and outputs through LDS, one tile at a time, with buffer
+// (descriptor-based) memory instructions.
 //
 // A tile is kTc consecutive steps of one batch row for the workgroup's 64 channels.
-// Every element of a per-channel tensor ([B,L,D]: x, delta, dy) and of a per-step
-// vector ([B,L,N]: B, C) is fetched once with a coalesced load -- a wavefront reads 64
-// consecutive channels of one step -- and held in a register, raw, while the previous
-// tile is being computed; it is converted to f32 and written to one of two LDS buffers
-// only after that compute ("commit"), so the load latency overlaps the compute.
+// Every element of a per-channel tensor ([B,L,D]: x, delta, dy; outputs y, dx, ddelta)
+// and of a per-step vector ([B,L,N]: B, C) moves once, coalesced: a thread owns VEC
+// consecutive channels of one step (VEC = 4 when D is a multiple of 4, else 1), so a
+// wavefront covers whole rows of 64 channels.  Loads are issued into registers while
+// the previous tile is being computed and written to one of two LDS buffers only after
+// that compute ("commit"), so their latency overlaps the compute.
 //
-// Loads are unconditional: an element outside the tensor (step >= L or channel >= D)
-// is read from the tile's first element instead (always inside) and replaced by zero
-// at commit.  A zero step is an exact identity of the recurrence (a = exp(0) = 1, no
-// input, no output), so the compute loops carry no tail branches.
+// Bounds are handled by the buffer hardware: a descriptor spans only the valid part of
+// the tile (loads beyond it return 0, stores beyond it are dropped), and a thread whose
+// channels lie past D carries an offset beyond every descriptor.  A zero step is an
+// exact identity of the recurrence (a = exp(0) = 1, no input, no output), so the
+// compute loops carry no tail branches.  The per-thread offset does not depend on the
+// tile; only the descriptors (scalar registers) are rebuilt per tile.
 #pragma once
 #include "common.hpp"
 
 namespace ssm {
 
 constexpr int kTileThreads = 256;
-constexpr int kTileCh = 64;                                 // channels per workgroup
-constexpr int kChPerThread = kTc * kTileCh / kTileThreads;  // 4
+constexpr int kTileCh = 64;  // channels per workgroup
 
-// One per-channel tensor's share of a tile: element e = tid + 256 k sits at step e/64,
-// channel e%64 of the tile.
-template <typename T>
+// Descriptor over [base, base + bytes): gfx9-family raw buffer (stride 0), with the
+// default data format word of that family.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+constexpr uint32_t kOffNone = 0x80000000u;  // beyond every descriptor built here
+
+// VEC elements of T moved by one buffer instruction.
+template <typename T, int VEC>
+struct BufVec;
+template <>
+struct BufVec<float, 4> {
+  using raw_t = __attribute__((ext_vector_type(4))) unsigned;
+  __device__ static raw_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  }
+  __device__ static void store(raw_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+  }
+  __device__ static void unpack(raw_t v, float (&o)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = __uint_as_float(v[i]);
+  }
+  __device__ static raw_t pack(const float (&f)[4]) {
+    raw_t v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f[i]);
+    return v;
+  }
+};
+template <>
+struct BufVec<bf16_t, 4> {
+  using raw_t = __attribute__((ext_vector_type(2))) unsigned;
+  __device__ static raw_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  }
+  __device__ static void store(raw_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+  }
+  __device__ static void unpack(raw_t v, float (&o)[4]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      o[2 * i] = __uint_as_float(v[i] << 16);
+      o[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+    }
+  }
+  __device__ static raw_t pack(const float (&f)[4]) {
+    raw_t v;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) v[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    return v;
+  }
+};
+template <>
+struct BufVec<float, 1> {
+  using raw_t = unsigned;
+  __device__ static raw_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+  __device__ static void store(raw_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+  }
+  __device__ static void unpack(raw_t v, float (&o)[1]) { o[0] = __uint_as_float(v); }
+  __device__ static raw_t pack(const float (&f)[1]) { return __float_as_uint(f[0]); }
+};
+template <>
+struct BufVec<bf16_t, 1> {
+  using raw_t = unsigned short;
+  __device__ static raw_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  }
+  __device__ static void store(raw_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
+  }
+  __device__ static void unpack(raw_t v, float (&o)[1]) {
+    o[0] = __uint_as_float(uint32_t(v) << 16);
+  }
+  __device__ static raw_t pack(const float (&f)[1]) { return from_f32<bf16_t>(f[0]); }
+};
+
+// Placement of a thread in a per-channel tile: TPR threads per step row, RPP rows per
+// pass of the 256 threads, kPer passes per tile.  Pass k covers rows s_in + k*RPP.
+template <typename T, int VEC>
+struct ChTile {
+  static constexpr int TPR = kTileCh / VEC;
+  static constexpr int RPP = kTileThreads / TPR;
+  static constexpr int kPer = kTc / RPP;
+  int s_in, c;   // row (in pass 0) and first channel of this thread
+  uint32_t off;  // byte offset of (s_in, c) from the tile start, or kOffNone
+  __device__ __forceinline__ ChTile(int D32, int dvalid, int tid) {
+    s_in = tid / TPR;
+    c = (tid % TPR) * VEC;
+    off = c < dvalid ? uint32_t(s_in * D32 + c) * uint32_t(sizeof(T)) : kOffNone;
+  }
+  // Descriptor of pass k of the tile at `tile` (= base + tf*D + d0) with tvalid valid
+  // rows and dvalid valid channels: rows k*RPP .. tvalid-1, the last one up to dvalid.
+  __device__ __forceinline__ static __amdgpu_buffer_rsrc_t rsrc(const T* tile, int D32,
+                                                                int tvalid, int dvalid, int k) {
+    const int tv = tvalid - k * RPP;
+    const uint32_t bytes = tv > 0 ? uint32_t((tv - 1) * D32 + dvalid) * uint32_t(sizeof(T)) : 0u;
+    return buf_rsrc(tile + int64_t(k) * RPP * D32, bytes);
+  }
+};
+
+// One per-channel input tensor's share of a tile.
+template <typename T, int VEC>
 struct ChFetch {
-  T raw[kChPerThread];
-  // tile = base + tf*D + d0 (the tile's first element); tvalid = L - tf; dvalid = D - d0.
-  __device__ __forceinline__ void fetch(const T* __restrict__ tile, int D32, int tvalid,
-                                        int dvalid, int tid) {
+  using G = ChTile<T, VEC>;
+  using BV = BufVec<T, VEC>;
+  typename BV::raw_t raw[G::kPer];
+  __device__ __forceinline__ void fetch(const G& g, const T* tile, int D32, int tvalid,
+                                        int dvalid) {
 #pragma unroll
-    for (int k = 0; k < kChPerThread; ++k) {
-      const int e = tid + kTileThreads * k, s = e >> 6, c = e & 63;
-      const bool ok = s < tvalid && c < dvalid;
-      raw[k] = tile[ok ? s * D32 + c : 0];
-    }
+    for (int k = 0; k < G::kPer; ++k)
+      raw[k] = BV::load(G::rsrc(tile, D32, tvalid, dvalid, k), g.off);
   }
-  __device__ __forceinline__ void commit(float (*sm)[kTileCh], int tvalid, int dvalid,
-                                         int tid) const {
+  __device__ __forceinline__ void commit(const G& g, float (*sm)[kTileCh]) const {
 #pragma unroll
-    for (int k = 0; k < kChPerThread; ++k) {
-      const int e = tid + kTileThreads * k, s = e >> 6, c = e & 63;
-      const bool ok = s < tvalid && c < dvalid;
-      sm[s][c] = ok ? to_f32(raw[k]) : 0.f;
+    for (int k = 0; k < G::kPer; ++k) {
+      float v[VEC];
+      BV::unpack(raw[k], v);
+      float* dst = &sm[g.s_in + k * G::RPP][g.c];
+      if constexpr (VEC == 4) {
+        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        dst[0] = v[0];
+      }
     }
   }
 };
 
-// One per-step vector's share of a tile: thread tid < kTc*N owns element tid (step
-// tid/N, state tid%N).
-template <typename T, int N>
-struct VecFetch {
-  T raw;
-  __device__ __forceinline__ void fetch(const T* __restrict__ tile /* base + tf*N */,
-                                        int tvalid, int tid) {
-    const bool ok = tid < kTc * N && tid / N < tvalid;
-    raw = tile[ok ? tid : 0];
-  }
-  __device__ __forceinline__ void commit(float (*sm)[N], int tvalid, int tid) const {
-    if (tid < kTc * N) sm[tid / N][tid % N] = (tid / N < tvalid) ? to_f32(raw) : 0.f;
-  }
-};
-
-// Writes an LDS tile of per-channel outputs back to a [.,L,D] tensor with the same
-// coalesced mapping as the fetch (a wavefront stores 64 consecutive channels of one
-// step); tile = base + tf*D + d0; only steps < tvalid and channels < dvalid are written.
-template <typename T>
-__device__ __forceinline__ void tile_store_ch(T* __restrict__ tile, const float (*sm)[kTileCh],
-                                              int D32, int tvalid, int dvalid, int tid) {
+// Writes an LDS tile of per-channel outputs to a [.,L,D] tensor; tile = base + tf*D + d0;
+// rows >= tvalid and channels >= dvalid are not written.
+template <typename T, int VEC>
+__device__ __forceinline__ void tile_store_ch(const ChTile<T, VEC>& g, T* tile,
+                                              const float (*sm)[kTileCh], int D32, int tvalid,
+                                              int dvalid) {
+  using G = ChTile<T, VEC>;
+  using BV = BufVec<T, VEC>;
 #pragma unroll
-  for (int k = 0; k < kChPerThread; ++k) {
-    const int e = tid + kTileThreads * k, s = e >> 6, c = e & 63;
-    if (s < tvalid && c < dvalid) tile[s * D32 + c] = from_f32<T>(sm[s][c]);
+  for (int k = 0; k < G::kPer; ++k) {
+    const float* src = &sm[g.s_in + k * G::RPP][g.c];
+    float v[VEC];
+    if constexpr (VEC == 4) {
+      const float4 f = *reinterpret_cast<const float4*>(src);
+      v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+    } else {
+      v[0] = src[0];
+    }
+    BV::store(BV::pack(v), G::rsrc(tile, D32, tvalid, dvalid, k), g.off);
   }
 }
 
-// The NS state values of lane quarter q at step s of an LDS vector tile.
+// One per-step vector's share of a tile ([kTc][N] contiguous): thread tid < kTc*N owns
+// element tid (step tid/N, state tid%N).
+template <typename T, int N>
+struct VecFetch {
+  using BV = BufVec<T, 1>;
+  typename BV::raw_t raw;
+  __device__ __forceinline__ static uint32_t offset(int tid) {
+    return tid < kTc * N ? uint32_t(tid) * uint32_t(sizeof(T)) : kOffNone;
+  }
+  // tile = base + tf*N
+  __device__ __forceinline__ void fetch(const T* tile, int tvalid, uint32_t off) {
+    raw = BV::load(buf_rsrc(tile, uint32_t(tvalid * N) * uint32_t(sizeof(T))), off);
+  }
+  __device__ __forceinline__ void commit(float (*sm)[N], int tid) const {
+    float v[1];
+    BV::unpack(raw, v);
+    if (tid < kTc * N) sm[tid / N][tid % N] = v[0];
+  }
+};
+
+// The NS state values of state group q (states q*NS .. q*NS+NS-1) at step s of an LDS
+// vector tile.
 template <int N, int NS>
 __device__ __forceinline__ void tile_read_vec(const float (*sm)[N], int s, int q, float (&o)[NS]) {
   if constexpr (NS == 4) {
@@ -85,6 +208,41 @@ __device__ __forceinline__ void tile_read_vec(const float (*sm)[N], int s, int q
     o[0] = v.x; o[1] = v.y;
   } else {
     o[0] = sm[s][q];
+  }
+}
+
+// NS consecutive f32 state values of one lane through a descriptor (loads past it
+// return 0, stores past it are dropped).
+template <int NS>
+__device__ __forceinline__ void buf_load_states(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                float (&o)[NS]) {
+  if constexpr (NS == 4) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = __uint_as_float(v[j]);
+  } else if constexpr (NS == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    o[0] = __uint_as_float(v[0]);
+    o[1] = __uint_as_float(v[1]);
+  } else {
+    o[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  }
+}
+template <int NS>
+__device__ __forceinline__ void buf_store_states(const float (&v)[NS], __amdgpu_buffer_rsrc_t r,
+                                                 uint32_t off) {
+  if constexpr (NS == 4) {
+    __attribute__((ext_vector_type(4))) unsigned u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) u[j] = __float_as_uint(v[j]);
+    __builtin_amdgcn_raw_buffer_store_b128(u, r, off, 0, 0);
+  } else if constexpr (NS == 2) {
+    __attribute__((ext_vector_type(2))) unsigned u;
+    u[0] = __float_as_uint(v[0]);
+    u[1] = __float_as_uint(v[1]);
+    __builtin_amdgcn_raw_buffer_store_b64(u, r, off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), r, off, 0, 0);
   }
 }
 
