@@ -83,17 +83,29 @@ __global__ __launch_bounds__(256, 4) void k_bwd_summary(
       fy.fetch(gt, dyb + tn * D, D32, kTc, dvalid);
       fC.fetch(Cb + tn * N, kTc, voff);
     }
-#pragma unroll 4
+    // the LDS operands of step s-1 are read during step s
+    float ndl = sd[buf][kTc - 1][cl], ndy = sdy[buf][kTc - 1][cl], nC[NS];
+    tile_read_vec<N, NS>(sC[buf], kTc - 1, q, nC);
+#pragma unroll
     for (int s = kTc - 1; s >= 0; --s) {
-      const float dl = sd[buf][s][cl], dyv = sdy[buf][s][cl];
+      const float dl = ndl, dyv = ndy;
       float Cv[NS];
-      tile_read_vec<N, NS>(sC[buf], s, q, Cv);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) Cv[j] = nC[j];
+      if (s > 0) {
+        ndl = sd[buf][s - 1][cl];
+        ndy = sdy[buf][s - 1][cl];
+        tile_read_vec<N, NS>(sC[buf], s - 1, q, nC);
+      }
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         const float g = __builtin_fmaf(dyv, Cv[j], gp[j]);
         gp[j] = __builtin_amdgcn_exp2f(dl * A2[j]) * g;
       }
       sdl += dl;
+      step_fence_arr(gp);
+      step_fence_arr(nC);
+      step_fence(sdl, ndl, ndy);
     }
     if (more) {
       fd.commit(gt, sd[buf ^ 1]);

@@ -25,6 +25,9 @@
 
 namespace ssm {
 
+// Waves per SIMD targeted by k_fwd_output (its LDS, 20 KB, admits eight workgroups).
+constexpr int kFwdOutputWaves = 6;
+
 template <typename T, int N, int VEC>
 __global__ __launch_bounds__(256, 4) void k_fwd_summary(
     int64_t L, int64_t D, int64_t Lc, int nc, const T* __restrict__ x,
@@ -117,16 +120,18 @@ __global__ __launch_bounds__(256) void k_fwd_carry(
 
 // hin: start state of each chunk, [B][nc][D][N]; may be null (zero start).
 // y (nullable: only the checkpoints are wanted); ckpt (nullable): [B][nf][D][N],
-// the state before step f*kTc.
+// the state before step f*kTc.  y of a step overwrites the step's x in LDS (a
+// channel's slots are read and written only by its four lanes, reads first) and is
+// stored after the tile; two barriers per tile: after the compute (y complete) and
+// after the next tile's inputs are committed.
 template <typename T, int N, int VEC>
-__global__ __launch_bounds__(256, 4) void k_fwd_output(
+__global__ __launch_bounds__(256, kFwdOutputWaves) void k_fwd_output(
     int64_t L, int64_t D, int64_t Lc, int nc, int64_t nf, const T* __restrict__ x,
     const T* __restrict__ delta, const float* __restrict__ A, const T* __restrict__ Bm,
     const T* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ hin,
     T* __restrict__ y, float* __restrict__ ckpt, float* __restrict__ h_last) {
   constexpr int NS = N / 4;
   __shared__ float sx[2][kTc][kTileCh], sd[2][kTc][kTileCh], sB[2][kTc][N], sC[2][kTc][N];
-  __shared__ float sy[2][kTc][kTileCh];
   const int c = blockIdx.z, b = blockIdx.y, tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
   const int64_t d0 = int64_t(blockIdx.x) * kTileCh, d = d0 + cl;
   const bool act = d < D;
@@ -157,59 +162,68 @@ __global__ __launch_bounds__(256, 4) void k_fwd_output(
   const uint32_t voff = VecFetch<T, N>::offset(tid);
   ChFetch<T, VEC> fx, fd;
   VecFetch<T, N> fB, fC;
-  int tv = clamp_valid(L - t0);
-  fx.fetch(gt, xb + t0 * D, D32, tv, dvalid);
-  fd.fetch(gt, db + t0 * D, D32, tv, dvalid);
-  fB.fetch(Bb + t0 * N, tv, voff);
-  fC.fetch(Cb + t0 * N, tv, voff);
-  fx.commit(gt, sx[0]);
-  fd.commit(gt, sd[0]);
-  fB.commit(sB[0], tid);
-  fC.commit(sC[0], tid);
+  auto fetch = [&](int64_t tt) {
+    const int tv = clamp_valid(L - tt);
+    fx.fetch(gt, xb + tt * D, D32, tv, dvalid);
+    fd.fetch(gt, db + tt * D, D32, tv, dvalid);
+    fB.fetch(Bb + tt * N, tv, voff);
+    fC.fetch(Cb + tt * N, tv, voff);
+  };
+  auto commit = [&](int bf) {
+    fx.commit(gt, sx[bf]);
+    fd.commit(gt, sd[bf]);
+    fB.commit(sB[bf], tid);
+    fC.commit(sC[bf], tid);
+  };
+  fetch(t0);
+  commit(0);
+  if (ntile > 1) fetch(t0 + kTc);
   __syncthreads();
   for (int it = 0; it < ntile; ++it) {
     const int buf = it & 1;
     const int64_t tf = t0 + int64_t(it) * kTc;
-    const bool more = it + 1 < ntile;
-    if (yb && it > 0)  // y of the previous tile, staged in LDS before the last barrier
-      tile_store_ch(gt, yb + (tf - kTc) * D, sy[buf ^ 1], D32, kTc, dvalid);
-    if (more) {
-      const int64_t tn = tf + kTc;
-      tv = clamp_valid(L - tn);
-      fx.fetch(gt, xb + tn * D, D32, tv, dvalid);
-      fd.fetch(gt, db + tn * D, D32, tv, dvalid);
-      fB.fetch(Bb + tn * N, tv, voff);
-      fC.fetch(Cb + tn * N, tv, voff);
-    }
     if (ckg) buf_store_states<NS>(h, buf_rsrc(ckg + (tf / kTc) * D * N, ckbytes), ckoff);
-#pragma unroll 4
+    // the LDS operands of step s+1 are read during step s
+    float ndl = sd[buf][0][cl], nxv = sx[buf][0][cl], nB[NS], nC[NS];
+    tile_read_vec<N, NS>(sB[buf], 0, q, nB);
+    tile_read_vec<N, NS>(sC[buf], 0, q, nC);
+#pragma unroll
     for (int s = 0; s < kTc; ++s) {
-      const float dl = sd[buf][s][cl], xv = sx[buf][s][cl];
-      const float u = dl * xv;
+      const float dl = ndl, xv = nxv;
       float Bv[NS], Cv[NS];
-      tile_read_vec<N, NS>(sB[buf], s, q, Bv);
-      tile_read_vec<N, NS>(sC[buf], s, q, Cv);
-      float yp = 0.f;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        Bv[j] = nB[j];
+        Cv[j] = nC[j];
+      }
+      if (s + 1 < kTc) {
+        ndl = sd[buf][s + 1][cl];
+        nxv = sx[buf][s + 1][cl];
+        tile_read_vec<N, NS>(sB[buf], s + 1, q, nB);
+        tile_read_vec<N, NS>(sC[buf], s + 1, q, nC);
+      }
+      const float u = dl * xv;
+      float yp;
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         const float a = __builtin_amdgcn_exp2f(dl * A2[j]);
         h[j] = __builtin_fmaf(a, h[j], u * Bv[j]);
-        yp = __builtin_fmaf(Cv[j], h[j], yp);
+        yp = j ? __builtin_fmaf(Cv[j], h[j], yp) : Cv[j] * h[j];
       }
       yp = quad_sum(yp);  // identical in the channel's four lanes, which all write it
-      sy[buf][s][cl] = __builtin_fmaf(Dd, xv, yp);
-    }
-    if (more) {
-      fx.commit(gt, sx[buf ^ 1]);
-      fd.commit(gt, sd[buf ^ 1]);
-      fB.commit(sB[buf ^ 1], tid);
-      fC.commit(sC[buf ^ 1], tid);
+      sx[buf][s][cl] = __builtin_fmaf(Dd, xv, yp);  // y
+      step_fence_arr(h);
+      step_fence_arr(nB);
+      step_fence_arr(nC);
+      step_fence(ndl, nxv);
     }
     __syncthreads();
-  }
-  if (yb) {  // y of the last tile
-    const int64_t tl = t0 + int64_t(ntile - 1) * kTc;
-    tile_store_ch(gt, yb + tl * D, sy[(ntile - 1) & 1], D32, clamp_valid(t1 - tl), dvalid);
+    if (yb) tile_store_ch(gt, yb + tf * D, sx[buf], D32, clamp_valid(t1 - tf), dvalid);
+    if (it + 1 < ntile) {
+      commit(buf ^ 1);
+      if (it + 2 < ntile) fetch(tf + 2 * kTc);
+    }
+    __syncthreads();
   }
   if (h_last && act && c == nc - 1) {
 #pragma unroll
