@@ -189,22 +189,24 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 // conv plan
-void conv_plan(int64_t B, int64_t L, int64_t D, ssm_dtype_t, ssm::ConvPlan* p) {
-  p->vec = (D % 4 == 0) ? 4 : 1;
-  const int64_t colblocks = cdiv(D / p->vec, 256);
-  // about 2048 blocks; time blocks of at least 64 steps
-  int64_t nTb = cdiv(2048, colblocks * B);
-  int64_t maxTb = cdiv(L, 64);
+void conv_plan(int64_t B, int64_t L, int64_t D, int64_t K, ssm::ConvPlan* p) {
+  // about 4096 workgroups; a workgroup spans 64 lanes of 4 channels (2 above width 4;
+  // 1 when D is not a multiple of 4); time blocks are multiples of 64 steps (four
+  // wavefronts x groups of 8 or 16 steps)
+  const int64_t vec = (D % 4 != 0) ? 1 : (K <= 4 ? 4 : 2);
+  const int64_t cgroups = cdiv(D, 64 * vec);
+  int64_t nTb = cdiv(4096, cgroups * B);
+  const int64_t maxTb = cdiv(L, 64);
   if (nTb > maxTb) nTb = maxTb;
   if (nTb < 1) nTb = 1;
-  p->Tb = cdiv(L, nTb);
+  p->Tb = cdiv(cdiv(L, nTb), 64) * 64;
   p->nTb = cdiv(L, p->Tb);
 }
 
 size_t conv_ws(int64_t B, int64_t L, int64_t D, int64_t K, ssm_dtype_t dt, ssm::ConvPlan* plan,
                void* ws) {
   ssm::ConvPlan p{};
-  conv_plan(B, L, D, dt, &p);
+  conv_plan(B, L, D, K, &p);
   Carver cv(ws);
   p.dWp = cv.take(size_t(B) * p.nTb * D * K);
   p.dbp = cv.take(size_t(B) * p.nTb * D);

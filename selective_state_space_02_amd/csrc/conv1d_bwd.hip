@@ -9,107 +9,139 @@
 // The page's step function is one timestep of this (its weight and bias terms, and
 // the newest-tap input term); here the whole sequence is done at once, exactly.
 //
-// Mapping: a thread owns VEC consecutive channels and a block of Tb timesteps.  It
-// walks time forwards keeping the next K upstream values and the last K inputs in
-// ring buffers (register indices fixed by unrolling over K), writes dx, and keeps
-// dW/db partial sums in registers; per-(batch, time block) partials are summed in a
+// Mapping: a lane owns VEC consecutive channels (4, 2 or 1), so every load and store
+// of a wavefront is one contiguous row of 64*VEC channels; a workgroup owns those
+// channels and a block of Tb timesteps, which its four wavefronts take in interleaved
+// groups of R steps.  For a group a thread loads the R + K - 1 rows of g and of x the
+// group touches (the K - 1 halo rows are shared with the neighbouring group, so they
+// come from cache), all at once -- many rows in flight per wavefront keep HBM busy --
+// then computes dx, dW and db of the group from registers.  dW/db partials are summed
+// over the four wavefronts in LDS; per-(batch, time block) partials are summed in a
 // fixed order by k_reduce.  HBM traffic: read g and x once, write dx once.
 #include "common.hpp"
 #include "launch.hpp"
+#include "tile.hpp"
 
 namespace ssm {
 
 template <typename T, int K, int VEC>
 __global__ __launch_bounds__(256) void k_conv_bwd(
-    int64_t L, int64_t D, int64_t Tb, int64_t nTb, int64_t colblocks,
+    int64_t L, int64_t D, int64_t Tb, int64_t nTb, int64_t cgroups,
     const T* __restrict__ x, const float* __restrict__ W, const T* __restrict__ g,
     T* __restrict__ dx, float* __restrict__ dWp, float* __restrict__ dbp) {
+  constexpr int R = (VEC > 1) ? 8 : 16;  // steps per group
+  constexpr int H = R + K - 1;           // rows loaded per group
+  constexpr int CW = 64 * VEC;           // channels per workgroup
+  using BV = BufVec<T, VEC>;
+  __shared__ float red[4][K + 1][CW];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
   const int64_t bid = blockIdx.x;
-  const int64_t cb = bid % colblocks, rest = bid / colblocks;
+  const int64_t cg = bid % cgroups, rest = bid / cgroups;
   const int64_t tb = rest % nTb, b = rest / nTb;
-  const int64_t d0 = (cb * 256 + threadIdx.x) * VEC;
-  if (d0 >= D) return;
+  // D is a multiple of VEC: a lane's channels are all valid or all past D; lanes past
+  // D read the group's last valid vector and store nothing
+  const int64_t c0 = cg * CW;
+  const bool act = c0 + int64_t(lane) * VEC < D;
+  const uint32_t lc = act ? uint32_t(lane) * VEC : uint32_t(D - VEC - c0);
   const int64_t t0 = tb * Tb, t1 = (t0 + Tb < L) ? t0 + Tb : L;
-  const T* xb = x + b * L * D + d0;
-  const T* gb = g + b * L * D + d0;
-  T* dxb = dx + b * L * D + d0;
+  const T* xg = x + b * L * D + c0;
+  const T* gg = g + b * L * D + c0;
+  T* dxg = dx + b * L * D + c0;
 
-  float w[VEC][K];
-#pragma unroll
-  for (int v = 0; v < VEC; ++v)
-#pragma unroll
-    for (int k = 0; k < K; ++k) w[v][k] = W[(d0 + v) * K + k];
-
-  // ring buffers: slot (t - t0) mod K
-  float gr[K][VEC], xr[K][VEC];
-#pragma unroll
-  for (int m = 0; m < K; ++m) {
-    const int64_t t = t0 + m;
-    if (t < L) load_vec<T, VEC>(gb + t * D, gr[m]);
-    else zero(gr[m]);
-  }
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int64_t t = t0 - K + 1 + k;
-    if (t >= 0) load_vec<T, VEC>(xb + t * D, xr[(1 + k) % K]);
-    else zero(xr[(1 + k) % K]);
-  }
-  float dW[VEC][K], db[VEC];
+  float w[VEC][K], dW[VEC][K], db[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) {
     db[v] = 0.f;
 #pragma unroll
-    for (int k = 0; k < K; ++k) dW[v][k] = 0.f;
-  }
-
-  for (int64_t s0 = t0; s0 < t1; s0 += K) {
-#pragma unroll
-    for (int r = 0; r < K; ++r) {
-      const int64_t s = s0 + r;
-      if (s >= t1) break;
-      float o[VEC];
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        float acc = 0.f;
-#pragma unroll
-        for (int k = 0; k < K; ++k) acc = __builtin_fmaf(gr[(r + K - 1 - k) % K][v], w[v][k], acc);
-        o[v] = acc;
-        const float gv = gr[r][v];
-        db[v] += gv;
-#pragma unroll
-        for (int k = 0; k < K; ++k) dW[v][k] = __builtin_fmaf(gv, xr[(r + 1 + k) % K][v], dW[v][k]);
-      }
-      VecStore<T, VEC>::run(dxb + s * D, o);
-      // refill: g[s+K] into the slot of g[s]; x[s+1] into the slot of x[s+1-K]
-      if (s + K < L) load_vec<T, VEC>(gb + (s + K) * D, gr[r]);
-      else zero(gr[r]);
-      if (s + 1 < L) load_vec<T, VEC>(xb + (s + 1) * D, xr[(r + 1) % K]);
-      else zero(xr[(r + 1) % K]);
+    for (int k = 0; k < K; ++k) {
+      w[v][k] = W[(c0 + lc + v) * K + k];
+      dW[v][k] = 0.f;
     }
   }
-  const int64_t p = b * nTb + tb;
+  const uint32_t rowb = uint32_t(D) * uint32_t(sizeof(T));  // bytes per timestep
+  const uint32_t loff = lc * uint32_t(sizeof(T));
+  for (int64_t ts = t0 + int64_t(wave) * R; ts < t1; ts += 4 * R) {
+    // xr[i] = x[ts - K + 1 + i], gr[i] = g[ts + i]; rows outside [0, L) are zero.  One
+    // descriptor per tensor starting at the group's first valid row; rows are scalar
+    // offsets from it, lanes vector offsets.
+    const int64_t x0 = (ts - (K - 1) < 0) ? 0 : ts - (K - 1);
+    const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xg + x0 * D, uint32_t(H) * rowb);
+    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gg + ts * D, uint32_t(H) * rowb);
+    typename BV::raw_t xraw[H], graw[H];
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+      const int64_t tx = ts - (K - 1) + i, tg = ts + i;
+      xraw[i] = (tx >= 0 && tx < L) ? BV::load(rx, loff, uint32_t(tx - x0) * rowb)
+                                    : typename BV::raw_t{};
+      graw[i] = (tg < L) ? BV::load(rg, loff, uint32_t(i) * rowb) : typename BV::raw_t{};
+    }
+    const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dxg + ts * D, uint32_t(R) * rowb);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t t = ts + r;
+      if (t < t1) {
+        float gv[K][VEC], xv[K][VEC], o[VEC];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          BV::unpack(graw[r + K - 1 - k], gv[k]);  // g[t + K-1-k]
+          BV::unpack(xraw[r + k], xv[k]);          // x[t - K+1+k]
+        }
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          float acc = 0.f;
+#pragma unroll
+          for (int k = 0; k < K; ++k) acc = __builtin_fmaf(gv[k][v], w[v][k], acc);
+          o[v] = acc;
+          const float gt = gv[K - 1][v];  // g[t]
+          db[v] += gt;
+#pragma unroll
+          for (int k = 0; k < K; ++k) dW[v][k] = __builtin_fmaf(gt, xv[k][v], dW[v][k]);
+        }
+        if (act) BV::store(BV::pack(o), rd, loff, uint32_t(r) * rowb);
+      }
+    }
+  }
 #pragma unroll
   for (int v = 0; v < VEC; ++v) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) dWp[(p * D + d0 + v) * K + k] = dW[v][k];
-    dbp[p * D + d0 + v] = db[v];
+    for (int k = 0; k < K; ++k) red[wave][k][lane * VEC + v] = dW[v][k];
+    red[wave][K][lane * VEC + v] = db[v];
+  }
+  __syncthreads();
+  if (wave == 0 && act) {
+    const int64_t p = b * nTb + tb;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      const int64_t d = c0 + lc + v;
+      const int j = lane * VEC + v;
+#pragma unroll
+      for (int k = 0; k <= K; ++k) {
+        const float s = (red[0][k][j] + red[1][k][j]) + (red[2][k][j] + red[3][k][j]);
+        if (k < K) dWp[(p * D + d) * K + k] = s;
+        else dbp[p * D + d] = s;
+      }
+    }
   }
 }
 
+// lanes' channel count: 4 (2 for widths above 4, bounding registers) when D allows
 template <typename T, int K>
 static hipError_t conv_k(const ConvArgs& a, const ConvPlan& p, hipStream_t st) {
   const T* x = static_cast<const T*>(a.x);
   const T* g = static_cast<const T*>(a.dout);
   T* dx = static_cast<T*>(a.dx);
-  const int64_t colblocks = (a.D / p.vec + 255) / 256;
-  const dim3 grid(colblocks * a.B * p.nTb);
+  constexpr int VW = (K <= 4) ? 4 : 2;
+  const int vec = (a.D % 4 == 0) ? VW : 1;
+  const int64_t cgroups = (a.D + 64 * vec - 1) / (64 * vec);
+  const dim3 grid(unsigned(cgroups * a.B * p.nTb));
   timer_mark(kKConvBwd, false, st);
-  if (p.vec == 4)
-    hipLaunchKernelGGL((k_conv_bwd<T, K, 4>), grid, dim3(256), 0, st, a.L, a.D, p.Tb, p.nTb,
-                       colblocks, x, a.W, g, dx, p.dWp, p.dbp);
+  if (vec == VW)
+    hipLaunchKernelGGL((k_conv_bwd<T, K, VW>), grid, dim3(256), 0, st, a.L, a.D, p.Tb, p.nTb,
+                       cgroups, x, a.W, g, dx, p.dWp, p.dbp);
   else
     hipLaunchKernelGGL((k_conv_bwd<T, K, 1>), grid, dim3(256), 0, st, a.L, a.D, p.Tb, p.nTb,
-                       colblocks, x, a.W, g, dx, p.dWp, p.dbp);
+                       cgroups, x, a.W, g, dx, p.dWp, p.dbp);
   timer_mark(kKConvBwd, true, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

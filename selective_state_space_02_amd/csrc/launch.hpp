@@ -77,7 +77,7 @@ struct ConvArgs {
 };
 
 struct ConvPlan {
-  int64_t Tb, nTb, vec;
+  int64_t Tb, nTb;  // time block (a multiple of 64 steps) and the number of blocks
   float* dWp;  // [B*nTb][D][K]
   float* dbp;  // [B*nTb][D]
   float* rtmp; // reduction scratch

@@ -30,17 +30,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uin
 }
 constexpr uint32_t kOffNone = 0x80000000u;  // beyond every descriptor built here
 
-// VEC elements of T moved by one buffer instruction.
+// VEC elements of T moved by one buffer instruction (at vector offset off plus scalar
+// offset soff).
 template <typename T, int VEC>
 struct BufVec;
 template <>
 struct BufVec<float, 4> {
   using raw_t = __attribute__((ext_vector_type(4))) unsigned;
-  __device__ static raw_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  __device__ static raw_t load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
   }
-  __device__ static void store(raw_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+  __device__ static void store(raw_t v, __amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, soff, 0);
   }
   __device__ static void unpack(raw_t v, float (&o)[4]) {
 #pragma unroll
@@ -56,11 +57,11 @@ struct BufVec<float, 4> {
 template <>
 struct BufVec<bf16_t, 4> {
   using raw_t = __attribute__((ext_vector_type(2))) unsigned;
-  __device__ static raw_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  __device__ static raw_t load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
   }
-  __device__ static void store(raw_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+  __device__ static void store(raw_t v, __amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, soff, 0);
   }
   __device__ static void unpack(raw_t v, float (&o)[4]) {
 #pragma unroll
@@ -79,11 +80,11 @@ struct BufVec<bf16_t, 4> {
 template <>
 struct BufVec<float, 1> {
   using raw_t = unsigned;
-  __device__ static raw_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  __device__ static raw_t load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
   }
-  __device__ static void store(raw_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+  __device__ static void store(raw_t v, __amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, soff, 0);
   }
   __device__ static void unpack(raw_t v, float (&o)[1]) { o[0] = __uint_as_float(v); }
   __device__ static raw_t pack(const float (&f)[1]) { return __float_as_uint(f[0]); }
@@ -91,16 +92,52 @@ struct BufVec<float, 1> {
 template <>
 struct BufVec<bf16_t, 1> {
   using raw_t = unsigned short;
-  __device__ static raw_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  __device__ static raw_t load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0);
   }
-  __device__ static void store(raw_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-    __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
+  __device__ static void store(raw_t v, __amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, off, soff, 0);
   }
   __device__ static void unpack(raw_t v, float (&o)[1]) {
     o[0] = __uint_as_float(uint32_t(v) << 16);
   }
   __device__ static raw_t pack(const float (&f)[1]) { return from_f32<bf16_t>(f[0]); }
+};
+
+template <>
+struct BufVec<float, 2> {
+  using raw_t = __attribute__((ext_vector_type(2))) unsigned;
+  __device__ static raw_t load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
+  }
+  __device__ static void store(raw_t v, __amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, soff, 0);
+  }
+  __device__ static void unpack(raw_t v, float (&o)[2]) {
+    o[0] = __uint_as_float(v[0]);
+    o[1] = __uint_as_float(v[1]);
+  }
+  __device__ static raw_t pack(const float (&f)[2]) {
+    raw_t v;
+    v[0] = __float_as_uint(f[0]);
+    v[1] = __float_as_uint(f[1]);
+    return v;
+  }
+};
+template <>
+struct BufVec<bf16_t, 2> {
+  using raw_t = unsigned;
+  __device__ static raw_t load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
+  }
+  __device__ static void store(raw_t v, __amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, soff, 0);
+  }
+  __device__ static void unpack(raw_t v, float (&o)[2]) {
+    o[0] = __uint_as_float(v << 16);
+    o[1] = __uint_as_float(v & 0xFFFF0000u);
+  }
+  __device__ static raw_t pack(const float (&f)[2]) { return pack_bf16x2(f[0], f[1]); }
 };
 
 // Placement of a thread in a per-channel tile: TPR threads per step row, RPP rows per

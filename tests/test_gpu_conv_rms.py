@@ -31,7 +31,8 @@ def conv_ref(p):
 
 
 CONV_CASES = [custom(B=3, L=100, D=20, K=4), custom(B=2, L=37, D=21, K=4, dtype="bf16"),
-              custom(B=1, L=5, D=8, K=8), custom(B=2, L=300, D=1028, K=4, dtype="bf16")] + \
+              custom(B=1, L=5, D=8, K=8), custom(B=2, L=300, D=1028, K=4, dtype="bf16"),
+              custom(B=1, L=1000, D=70, K=8, dtype="bf16")] + \
              [custom(B=2, L=70, D=12, K=k) for k in (1, 2, 3, 5, 6, 7)]
 
 
