@@ -221,10 +221,8 @@ bool rms_plan(int64_t R, int64_t M, ssm_dtype_t dt, ssm::RmsPlan* p) {
   p->vec = (M % full == 0) ? full : 1;
   const int64_t per_pass = 64 * p->vec;
   const int64_t need = cdiv(M, per_pass);
-  int64_t passes = 1;
-  while (passes < need) passes *= 2;
-  if (passes > 16) return false;
-  p->passes = passes;
+  if (need > 16) return false;
+  p->passes = need <= 8 ? need : 16;  // rows of up to 8 passes stay in registers
   // about 512 blocks of 4 wavefronts, at least 4 rows per block
   int64_t rpb = cdiv(R, 512);
   if (rpb < 4) rpb = 4;

@@ -5,11 +5,13 @@
 // and the scale gradient dscale[i] += sum_r dy[r,i] x[r,i] inv (accumulated).
 //
 // Mapping: one wavefront per row at a time (4 wavefronts per block walk disjoint
-// rows); a lane owns PASSES groups of VEC consecutive columns.  Pass 1 reads the row
-// and forms the dot product (wavefront DPP/shuffle sum); pass 2 re-reads it (cache
-// hit), writes dx and accumulates the scale-gradient terms in registers.  At the end
-// the four wavefronts' column sums are added through LDS into one partial per block;
-// k_reduce sums the block partials in a fixed order.
+// rows); a lane owns PASSES groups of VEC consecutive columns.  Rows of at most eight
+// groups per lane (k_rms_bwd_res) are read once into registers: the dot product is
+// formed (wavefront DPP/shuffle sum), then dx is written from the same registers and
+// the scale-gradient terms accumulate in registers; scale is staged in LDS.  Longer
+// rows (k_rms_bwd) are read twice, the second time for dx.  At the end the four
+// wavefronts' column sums are added through LDS into one partial per block; k_reduce
+// sums the block partials in a fixed order.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -20,6 +22,133 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 4; m < 64; m <<= 1) v += xor_lane(v, m);
   return v;
+}
+
+// VEC consecutive row values kept raw (as stored) in registers.
+template <typename T, int VEC>
+struct RowVec;
+template <>
+struct RowVec<bf16_t, 8> {
+  using raw_t = uint4;
+  __device__ static raw_t load(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ static void fence(raw_t& v) { step_fence(v.x, v.y, v.z, v.w); }
+  __device__ static void unpack(raw_t v, float (&o)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o[2 * k] = __uint_as_float(w[k] << 16);
+      o[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+  }
+};
+template <>
+struct RowVec<float, 4> {
+  using raw_t = float4;
+  __device__ static raw_t load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ static void fence(raw_t& v) { step_fence(v.x, v.y, v.z, v.w); }
+  __device__ static void unpack(raw_t v, float (&o)[4]) {
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  }
+};
+template <>
+struct RowVec<bf16_t, 1> {
+  using raw_t = uint32_t;
+  __device__ static raw_t load(const bf16_t* p) { return p[0]; }
+  __device__ static void fence(raw_t& v) { step_fence(v); }
+  __device__ static void unpack(raw_t v, float (&o)[1]) { o[0] = __uint_as_float(v << 16); }
+};
+template <>
+struct RowVec<float, 1> {
+  using raw_t = float;
+  __device__ static raw_t load(const float* p) { return p[0]; }
+  __device__ static void fence(raw_t& v) { step_fence(v); }
+  __device__ static void unpack(raw_t v, float (&o)[1]) { o[0] = v; }
+};
+
+template <typename T, int VEC, int PASSES>
+__global__ __launch_bounds__(256) void k_rms_bwd_res(
+    int64_t R, int64_t M, int64_t rows_per_block, const T* __restrict__ dy,
+    const T* __restrict__ x, const float* __restrict__ scale, const float* __restrict__ rms,
+    T* __restrict__ dx, float* __restrict__ dsp) {
+  using RV = RowVec<T, VEC>;
+  constexpr int CP = 64 * VEC;  // columns per pass
+  __shared__ float ssc[PASSES * CP];
+  __shared__ float part[4][CP];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int i = tid; i < PASSES * CP; i += 256) ssc[i] = (i < M) ? scale[i] : 0.f;
+  float acc[PASSES][VEC];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[p][v] = 0.f;
+  __syncthreads();
+  const int64_t r0 = int64_t(blockIdx.x) * rows_per_block;
+  const int64_t r1 = (r0 + rows_per_block < R) ? r0 + rows_per_block : R;
+  const float invM = 1.0f / float(M);
+  for (int64_t r = r0 + wave; r < r1; r += 4) {
+    const T* dyr = dy + r * M;
+    const T* xr = x + r * M;
+    typename RV::raw_t rd[PASSES], rx[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int col = (p * 64 + lane) * VEC;
+      if (col < M) {
+        rd[p] = RV::load(dyr + col);
+        rx[p] = RV::load(xr + col);
+      } else {
+        rd[p] = {};
+        rx[p] = {};
+      }
+    }
+    const float inv = 1.0f / rms[r];
+    float dot = 0.f;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int col = (p * 64 + lane) * VEC;
+      float a[VEC], b[VEC];
+      RV::unpack(rd[p], a);
+      RV::unpack(rx[p], b);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) dot = __builtin_fmaf(a[v] * ssc[col + v], b[v], dot);
+    }
+    // the output pass unpacks the raw row again rather than keeping it unpacked
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      RV::fence(rd[p]);
+      RV::fence(rx[p]);
+    }
+    dot = wave_sum(dot);
+    const float cr = dot * inv * inv * invM;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int col = (p * 64 + lane) * VEC;
+      if (col < M) {
+        float a[VEC], b[VEC], o[VEC];
+        RV::unpack(rd[p], a);
+        RV::unpack(rx[p], b);
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          o[v] = inv * __builtin_fmaf(ssc[col + v], a[v], -b[v] * cr);
+          acc[p][v] = __builtin_fmaf(a[v] * b[v], inv, acc[p][v]);
+        }
+        VecStore<T, VEC>::run(dx + r * M + col, o);
+      }
+    }
+  }
+  // sum the four wavefronts' column partials
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) part[wave][lane * VEC + v] = acc[p][v];
+    __syncthreads();
+    for (int k = tid; k < CP; k += 256) {
+      const int64_t col = int64_t(p) * CP + k;
+      if (col < M)
+        dsp[int64_t(blockIdx.x) * M + col] = (part[0][k] + part[1][k]) + (part[2][k] + part[3][k]);
+    }
+    __syncthreads();
+  }
 }
 
 template <typename T, int VEC, int PASSES>
@@ -93,19 +222,30 @@ __global__ __launch_bounds__(256) void k_rms_bwd(
 
 template <typename T, int VEC, int PASSES>
 static void rms_launch(const RmsArgs& a, const RmsPlan& p, hipStream_t st) {
+  const T* dy = static_cast<const T*>(a.dy);
+  const T* x = static_cast<const T*>(a.x);
+  T* dx = static_cast<T*>(a.dx);
   timer_mark(kKRmsBwd, false, st);
-  hipLaunchKernelGGL((k_rms_bwd<T, VEC, PASSES>), dim3(p.nblk), dim3(256), 0, st, a.R, a.M,
-                     p.rows_per_block, static_cast<const T*>(a.dy), static_cast<const T*>(a.x),
-                     a.scale, a.rms, static_cast<T*>(a.dx), p.dsp);
+  if constexpr (PASSES <= 8)
+    hipLaunchKernelGGL((k_rms_bwd_res<T, VEC, PASSES>), dim3(p.nblk), dim3(256), 0, st, a.R,
+                       a.M, p.rows_per_block, dy, x, a.scale, a.rms, dx, p.dsp);
+  else
+    hipLaunchKernelGGL((k_rms_bwd<T, VEC, PASSES>), dim3(p.nblk), dim3(256), 0, st, a.R, a.M,
+                       p.rows_per_block, dy, x, a.scale, a.rms, dx, p.dsp);
   timer_mark(kKRmsBwd, true, st);
 }
 
+// passes: exact count up to 8 (row resident in registers), else 16
 template <typename T, int VEC>
 static hipError_t rms_v(const RmsArgs& a, const RmsPlan& p, hipStream_t st) {
   switch (p.passes) {
     case 1: rms_launch<T, VEC, 1>(a, p, st); break;
     case 2: rms_launch<T, VEC, 2>(a, p, st); break;
+    case 3: rms_launch<T, VEC, 3>(a, p, st); break;
     case 4: rms_launch<T, VEC, 4>(a, p, st); break;
+    case 5: rms_launch<T, VEC, 5>(a, p, st); break;
+    case 6: rms_launch<T, VEC, 6>(a, p, st); break;
+    case 7: rms_launch<T, VEC, 7>(a, p, st); break;
     case 8: rms_launch<T, VEC, 8>(a, p, st); break;
     case 16: rms_launch<T, VEC, 16>(a, p, st); break;
     default: return hipErrorInvalidValue;
