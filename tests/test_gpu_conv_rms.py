@@ -83,7 +83,8 @@ def rms_ref(p):
 
 RMS_CASES = [custom(B=1, L=7, D=8), custom(B=3, L=11, D=100), custom(B=2, L=9, D=96, dtype="bf16"),
              custom(B=2, L=50, D=1000, dtype="bf16"), custom(B=1, L=33, D=4096),
-             custom(B=1, L=17, D=8192, dtype="bf16"), custom(B=4, L=16, D=2)]
+             custom(B=1, L=17, D=8192, dtype="bf16"), custom(B=4, L=16, D=2),
+             custom(B=2, L=5, D=203), custom(B=1, L=6, D=777, dtype="bf16")]
 
 
 @pytest.mark.parametrize("w", RMS_CASES, ids=lambda w: f"R{w.rms_rows}M{w.rms_dim}{w.dtype}")
