@@ -95,7 +95,8 @@ int ssm_set_kernel_timer(int kernel, void *start, void *stop);
  * Supported: N in {4, 8, 16}; B <= 65535; 1 <= D <= 2^24; L >= 1 (tails
  * handled, no multiple required; D a multiple of 4 takes the vectorised path).
  *
- * Checkpoints.  The forward can save the state before every 16th step into `ckpt`
+ * Checkpoints.  The forward can save the state before every 8th step (N = 16) or
+ * every 16th step (N = 4, 8) into `ckpt`
  * (ssm_scan_ckpt_bytes() bytes; layout private to this library version) for the
  * backward to recompute states from.  The backward given ckpt == NULL recomputes
  * the forward itself into its workspace.

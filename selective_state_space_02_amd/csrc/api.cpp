@@ -87,6 +87,9 @@ ssm::Chunking choose_chunks(int64_t B, int64_t L, int64_t D, int64_t target) {
   return c;
 }
 
+// checkpoints: the state before every (kTc / ckpt_per_tile(N))-th step
+int64_t ckpt_count(int64_t L, int64_t N) { return cdiv(L, ssm::kTc / ssm::ckpt_per_tile(N)); }
+
 size_t fwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, ssm::FwdPlan* plan, void* ws) {
   const ssm::Chunking c = choose_chunks(B, L, D, kFwdTargetWG);
   Carver cv(ws);
@@ -94,6 +97,7 @@ size_t fwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, ssm::FwdPlan* plan, vo
   p.nc = c.nc;
   p.Lc = c.Lc;
   p.nf = c.nf;
+  p.nck = ckpt_count(L, N);
   if (c.nc > 1) {
     p.S = cv.take(size_t(B) * c.nc * D * N);
     p.SD = cv.take(size_t(B) * c.nc * D);
@@ -104,7 +108,7 @@ size_t fwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, ssm::FwdPlan* plan, vo
 }
 
 size_t ckpt_floats(int64_t B, int64_t L, int64_t D, int64_t N) {
-  return size_t(B) * size_t(cdiv(L, ssm::kTc)) * size_t(D) * size_t(N);
+  return size_t(B) * size_t(ckpt_count(L, N)) * size_t(D) * size_t(N);
 }
 
 size_t bwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, bool with_ckpt, ssm::BwdPlan* plan,
@@ -115,6 +119,7 @@ size_t bwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, bool with_ckpt, ssm::B
   p.nc = c.nc;
   p.Lc = c.Lc;
   p.nf = c.nf;
+  p.nck = ckpt_count(L, N);
   p.ng = cdiv(D, 64);
   if (c.nc > 1) {
     p.GS = cv.take(size_t(B) * c.nc * D * N);

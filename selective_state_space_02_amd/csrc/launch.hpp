@@ -7,9 +7,13 @@
 
 namespace ssm {
 
-// Checkpoint interval of the forward scan: the state before every kTc-th step is
-// saved for the backward.
+// Tile length of the scan kernels (steps staged through LDS at a time).
 constexpr int kTc = 16;
+
+// Checkpoints per tile: the forward saves the state before every (kTc / ckpt_per_tile)-th
+// step for the backward.  At N = 16 the backward stashes half a tile at a time (its
+// register budget), so it needs the state at mid-tile too.
+constexpr int ckpt_per_tile(int64_t N) { return N == 16 ? 2 : 1; }
 
 struct ScanArgs {
   int dtype;  // 0 f32, 1 bf16
@@ -39,22 +43,24 @@ struct ScanArgs {
 struct Chunking {
   int nc;       // number of coarse chunks
   int64_t Lc;   // chunk length, a multiple of kTc
-  int64_t nf;   // number of checkpoints, ceil(L / kTc)
+  int64_t nf;   // number of tiles, ceil(L / kTc)
 };
 
 struct FwdPlan {
   int nc;
   int64_t Lc, nf;
+  int64_t nck;  // number of checkpoints, ceil(L / (kTc / ckpt_per_tile(N)))
   float* S;     // [B][nc][D][N]   (nc > 1)
   float* SD;    // [B][nc][D]      (nc > 1)
   float* hin;   // [B][nc][D][N]   (nc > 1)
-  float* ckpt;  // [B][nf][D][N]   nullable
+  float* ckpt;  // [B][nck][D][N]  nullable
 };
 
 struct BwdPlan {
   int nc;
   int64_t Lc, nf, ng;
-  const float* ckpt;  // [B][nf][D][N]
+  int64_t nck;        // number of checkpoints
+  const float* ckpt;  // [B][nck][D][N]
   float* GS;          // [B][nc][D][N]  (nc > 1)
   float* SD;          // [B][nc][D]     (nc > 1)
   float* gin;         // [B][nc][D][N]  (nc > 1)

@@ -141,11 +141,11 @@ __global__ __launch_bounds__(256) void k_bwd_carry(
   }
 }
 
-// Main backward pass: one chunk of one batch row for 64 channels.  Checkpoint intervals
-// (tiles of kTc steps) are walked from the last one backwards.  Per tile the states are
-// recomputed from the interval's checkpoint into a register stash of kTc/SPLIT steps
-// (with SPLIT = 2 the first half of the interval is recomputed twice so that only half
-// is held at a time), then the reverse step runs over the stashed steps.  dx and ddelta
+// Main backward pass: one chunk of one batch row for 64 channels.  Tiles of kTc steps
+// are walked from the last one backwards.  A tile holds SPLIT checkpoint intervals
+// (SPLIT = ckpt_per_tile(N)); from the last interval to the first, the states of the
+// interval are recomputed from its checkpoint into a register stash, then the reverse
+// step runs over the stashed steps.  dx and ddelta
 // of a step overwrite the step's x and delta in LDS (a channel's slots are read and
 // written only by the channel's four lanes, reads first) and are stored after the tile
 // with coalesced writes; the dB/dC partials of each lane go to LDS and are summed there.
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void k_bwd_carry(
 // tile's inputs are committed.
 template <typename T, int N, int VEC, int SPLIT, int WAVES>
 __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
-    int64_t B, int64_t L, int64_t D, int64_t Lc, int nc, int64_t nf,
+    int64_t B, int64_t L, int64_t D, int64_t Lc, int nc, int64_t nck,
     const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dv,
     const T* __restrict__ dy, const float* __restrict__ ckpt, const float* __restrict__ gin,
@@ -163,8 +163,8 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
   constexpr int NS = N / 4;       // states per lane
   constexpr int V = 2 * NS;       // per-lane values summed over channels: dB, dC
   constexpr int NP = 16 / V;      // partials per value left in LDS by chan_reduce_scatter
-  constexpr int SL = kTc / SPLIT; // stashed steps
-  static_assert(SPLIT == 1 || SPLIT == 2, "unsupported stash split");
+  constexpr int SL = kTc / SPLIT; // stashed steps = checkpoint interval
+  static_assert(SPLIT == ckpt_per_tile(N), "stash split must match the checkpoints");
   __shared__ float sx[2][kTc][kTileCh], sd[2][kTc][kTileCh], sdy[2][kTc][kTileCh];
   __shared__ float sB[2][kTc][N], sC[2][kTc][N];
   __shared__ float red[4][kTc][64];  // [wavefront][step][lane]
@@ -182,8 +182,8 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
   const T* Cb = Cm + int64_t(b) * L * N;
   T* dxb = dx + int64_t(b) * L * D + d0;
   T* ddb = ddelta + int64_t(b) * L * D + d0;
-  // checkpoint f of this group: ckpt + ((b*nf + f)*D + d0)*N, lane at (cl*N + q*NS)
-  const float* ckg = ckpt + (int64_t(b) * nf * D + d0) * N;
+  // checkpoint f of this group: ckpt + ((b*nck + f)*D + d0)*N, lane at (cl*N + q*NS)
+  const float* ckg = ckpt + (int64_t(b) * nck * D + d0) * N;
   const uint32_t ckoff = act ? uint32_t(cl * N + q * NS) * 4u : kOffNone;
   const uint32_t ckbytes = uint32_t(dvalid * N) * 4u;
   float* pB = dBp + (int64_t(grp) * B + b) * L * N;
@@ -206,14 +206,22 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
   const uint32_t voff = VecFetch<T, N>::offset(tid);
   ChFetch<T, VEC> fx, fd, fy;
   VecFetch<T, N> fB, fC;
-  float hcur[NS], hnxt[NS];  // checkpoints of the current and the next tile
-  auto fetch = [&](int64_t tt, int tvalid, float (&hk)[NS]) {
+  float hcur[SPLIT][NS], hnxt[SPLIT][NS];  // checkpoints of the current and the next tile
+  auto fetch = [&](int64_t tt, int tvalid, float (&hk)[SPLIT][NS]) {
     fx.fetch(gt, xb + tt * D, D32, tvalid, dvalid);
     fd.fetch(gt, db + tt * D, D32, tvalid, dvalid);
     fy.fetch(gt, dyb + tt * D, D32, tvalid, dvalid);
     fB.fetch(Bb + tt * N, tvalid, voff);
     fC.fetch(Cb + tt * N, tvalid, voff);
-    buf_load_states<NS>(buf_rsrc(ckg + (tt / kTc) * D * N, ckbytes), ckoff, hk);
+#pragma unroll
+    for (int hf = 0; hf < SPLIT; ++hf) {
+      if (hf == 0 || tt + hf * SL < L) {
+        buf_load_states<NS>(buf_rsrc(ckg + (tt / SL + hf) * D * N, ckbytes), ckoff, hk[hf]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) hk[hf][j] = 0.f;  // an interval wholly past L
+      }
+    }
   };
   auto commit = [&](int bf) {
     fx.commit(gt, sx[bf]);
@@ -235,21 +243,22 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
 #pragma unroll
     for (int half = SPLIT - 1; half >= 0; --half) {
       const int s0 = half * SL;
-      // Recompute steps 0 .. s0+SL-1 from the checkpoint, stashing a_t and h_t of the
-      // last SL.  The LDS operands of step s+1 are read during step s.
+      // Recompute the interval's steps s0 .. s0+SL-1 from its checkpoint into the stash.
+      // The LDS operands of step s+1 are read during step s.
       float h[NS];
 #pragma unroll
-      for (int j = 0; j < NS; ++j) h[j] = hcur[j];
+      for (int j = 0; j < NS; ++j) h[j] = hcur[half][j];
       float as[SL][NS], hs[SL][NS];
-      float ndl = sd[buf][0][cl], nxv = sx[buf][0][cl], nB[NS];
-      tile_read_vec<N, NS>(sB[buf], 0, q, nB);
+      float ndl = sd[buf][s0][cl], nxv = sx[buf][s0][cl], nB[NS];
+      tile_read_vec<N, NS>(sB[buf], s0, q, nB);
 #pragma unroll
-      for (int s = 0; s < s0 + SL; ++s) {
+      for (int i = 0; i < SL; ++i) {
+        const int s = s0 + i;
         const float dl = ndl, u = dl * nxv;
         float Bv[NS];
 #pragma unroll
         for (int j = 0; j < NS; ++j) Bv[j] = nB[j];
-        if (s + 1 < s0 + SL) {
+        if (i + 1 < SL) {
           ndl = sd[buf][s + 1][cl];
           nxv = sx[buf][s + 1][cl];
           tile_read_vec<N, NS>(sB[buf], s + 1, q, nB);
@@ -258,10 +267,8 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
         for (int j = 0; j < NS; ++j) {
           const float a = __builtin_amdgcn_exp2f(dl * A2[j]);
           h[j] = __builtin_fmaf(a, h[j], u * Bv[j]);
-          if (s >= s0) {
-            as[s - s0][j] = a;
-            hs[s - s0][j] = h[j];
-          }
+          as[i][j] = a;
+          hs[i][j] = h[j];
         }
         step_fence_arr(h);
         step_fence_arr(nB);
@@ -358,7 +365,9 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
     if (it + 1 < ntile) {
       commit(buf ^ 1);
 #pragma unroll
-      for (int j = 0; j < NS; ++j) hcur[j] = hnxt[j];
+      for (int hf = 0; hf < SPLIT; ++hf)
+#pragma unroll
+        for (int j = 0; j < NS; ++j) hcur[hf][j] = hnxt[hf][j];
       if (it + 2 < ntile) fetch(tf - 2 * kTc, kTc, hnxt);
     }
     __syncthreads();
@@ -376,13 +385,12 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
   }
 }
 
-// Stash split and waves per SIMD of k_bwd_main per state size.  Its LDS (41-45 KB)
-// admits three workgroups per CU; at N = 16 the full stash does not fit the register
-// budget of three waves per SIMD, the split one does (measured 2.05 vs 2.11 ms on the
-// 2 x 16384 x 5120 layer against the full stash at two waves).
+// Waves per SIMD of k_bwd_main.  Its LDS (41-45 KB) admits three workgroups per CU; at
+// N = 16 a full-tile stash does not fit the register budget of three waves per SIMD, a
+// half-tile one does, hence the mid-tile checkpoints at N = 16 (ckpt_per_tile).
 template <int N>
 struct BwdMainCfg {
-  static constexpr int kSplit = (N == 16) ? 2 : 1;
+  static constexpr int kSplit = ckpt_per_tile(N);
   static constexpr int kWaves = 3;
 };
 
@@ -413,7 +421,7 @@ static hipError_t bwd_impl(const ScanArgs& a, const BwdPlan& p, hipStream_t st) 
   timer_mark(kKBwdMain, false, st);
   using Cfg = BwdMainCfg<N>;
   hipLaunchKernelGGL((k_bwd_main<T, N, VEC, Cfg::kSplit, Cfg::kWaves>), dim3(p.ng, a.B, p.nc),
-                     block, 0, st, a.B, a.L, a.D, p.Lc, p.nc, p.nf, x, delta, a.A, Bm, Cm,
+                     block, 0, st, a.B, a.L, a.D, p.Lc, p.nc, p.nck, x, delta, a.A, Bm, Cm,
                      a.Dv, dy, p.ckpt, gin, static_cast<T*>(a.dx), static_cast<T*>(a.ddelta),
                      p.dBp, p.dCp, p.dAp, p.dDp, a.dh0);
   timer_mark(kKBwdMain, true, st);

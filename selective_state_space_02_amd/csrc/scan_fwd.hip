@@ -119,18 +119,19 @@ __global__ __launch_bounds__(256) void k_fwd_carry(
 }
 
 // hin: start state of each chunk, [B][nc][D][N]; may be null (zero start).
-// y (nullable: only the checkpoints are wanted); ckpt (nullable): [B][nf][D][N],
-// the state before step f*kTc.  y of a step overwrites the step's x in LDS (a
+// y (nullable: only the checkpoints are wanted); ckpt (nullable): [B][nck][D][N],
+// the state before step f*CK, CK = kTc / ckpt_per_tile(N).  y of a step overwrites the step's x in LDS (a
 // channel's slots are read and written only by its four lanes, reads first) and is
 // stored after the tile; two barriers per tile: after the compute (y complete) and
 // after the next tile's inputs are committed.
 template <typename T, int N, int VEC>
 __global__ __launch_bounds__(256, kFwdOutputWaves) void k_fwd_output(
-    int64_t L, int64_t D, int64_t Lc, int nc, int64_t nf, const T* __restrict__ x,
+    int64_t L, int64_t D, int64_t Lc, int nc, int64_t nck, const T* __restrict__ x,
     const T* __restrict__ delta, const float* __restrict__ A, const T* __restrict__ Bm,
     const T* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ hin,
     T* __restrict__ y, float* __restrict__ ckpt, float* __restrict__ h_last) {
   constexpr int NS = N / 4;
+  constexpr int CK = kTc / ckpt_per_tile(N);  // checkpoint interval
   __shared__ float sx[2][kTc][kTileCh], sd[2][kTc][kTileCh], sB[2][kTc][N], sC[2][kTc][N];
   const int c = blockIdx.z, b = blockIdx.y, tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
   const int64_t d0 = int64_t(blockIdx.x) * kTileCh, d = d0 + cl;
@@ -142,8 +143,8 @@ __global__ __launch_bounds__(256, kFwdOutputWaves) void k_fwd_output(
   const T* Bb = Bm + int64_t(b) * L * N;
   const T* Cb = Cm + int64_t(b) * L * N;
   T* yb = y ? y + int64_t(b) * L * D + d0 : nullptr;
-  // checkpoint f of this group: ckpt + ((b*nf + f)*D + d0)*N, lane at (cl*N + q*NS)
-  float* ckg = ckpt ? ckpt + (int64_t(b) * nf * D + d0) * N : nullptr;
+  // checkpoint f of this group: ckpt + ((b*nck + f)*D + d0)*N, lane at (cl*N + q*NS)
+  float* ckg = ckpt ? ckpt + (int64_t(b) * nck * D + d0) * N : nullptr;
   const uint32_t ckoff = act ? uint32_t(cl * N + q * NS) * 4u : kOffNone;
   const uint32_t ckbytes = uint32_t(dvalid * N) * 4u;
   float A2[NS], h[NS];
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(256, kFwdOutputWaves) void k_fwd_output(
   for (int it = 0; it < ntile; ++it) {
     const int buf = it & 1;
     const int64_t tf = t0 + int64_t(it) * kTc;
-    if (ckg) buf_store_states<NS>(h, buf_rsrc(ckg + (tf / kTc) * D * N, ckbytes), ckoff);
+    if (ckg) buf_store_states<NS>(h, buf_rsrc(ckg + (tf / CK) * D * N, ckbytes), ckoff);
     // the LDS operands of step s+1 are read during step s
     float ndl = sd[buf][0][cl], nxv = sx[buf][0][cl], nB[NS], nC[NS];
     tile_read_vec<N, NS>(sB[buf], 0, q, nB);
@@ -212,6 +213,8 @@ __global__ __launch_bounds__(256, kFwdOutputWaves) void k_fwd_output(
       }
       yp = quad_sum(yp);  // identical in the channel's four lanes, which all write it
       sx[buf][s][cl] = __builtin_fmaf(Dd, xv, yp);  // y
+      if (CK < kTc && s % CK == CK - 1 && s + 1 < kTc && ckg && tf + s + 1 < L)  // mid-tile
+        buf_store_states<NS>(h, buf_rsrc(ckg + ((tf + s + 1) / CK) * D * N, ckbytes), ckoff);
       step_fence_arr(h);
       step_fence_arr(nB);
       step_fence_arr(nC);
@@ -257,7 +260,7 @@ static hipError_t fwd_impl(const ScanArgs& a, const FwdPlan& p, hipStream_t st) 
   }
   timer_mark(kKFwdOutput, false, st);
   hipLaunchKernelGGL((k_fwd_output<T, N, VEC>), dim3(groups, a.B, p.nc), block, 0, st, a.L, a.D,
-                     p.Lc, p.nc, p.nf, x, delta, a.A, Bm, Cm, a.Dv, hin,
+                     p.Lc, p.nc, p.nck, x, delta, a.A, Bm, Cm, a.Dv, hin,
                      static_cast<T*>(a.y), p.ckpt, a.h_last);
   timer_mark(kKFwdOutput, true, st);
   return hipGetLastError();
