@@ -147,7 +147,8 @@ def cpu_baseline(w, cpu_inputs, sample_channels, budget_note):
                           v[:sample_channels].contiguous()) for k, v in c.items()}
     nrows = max(1, int(round(w.rms_rows * frac)))
     rq = {"x": synth.as_f64(r["x"][:nrows]), "dy": synth.as_f64(r["dy"][:nrows]),
-          "scale": synth.as_f64(r["scale"]), "rms": synth.as_f64(r["rms"][:nrows])}
+          "scale": synth.as_f64(r["scale"])}
+    _, rq["rms"] = oracle.rmsnorm_fwd(rq["x"], rq["scale"], synth.RMS_EPS)  # saved statistic
     t0 = time.perf_counter()
     oracle.scan_fwd(q["x"], q["delta"], q["A"], q["Bm"], q["Cm"], q["Dv"])
     oracle.scan_bwd(q["x"], q["delta"], q["A"], q["Bm"], q["Cm"], q["Dv"], q["dy"])
@@ -167,6 +168,50 @@ def cpu_baseline(w, cpu_inputs, sample_channels, budget_note):
                    f"RMSNorm bwd; f64; {budget_note}"),
         "seconds": {"scan_fwd_bwd": t1 - t0, "conv_bwd": t2 - t1, "rms_bwd": t3 - t2},
     }
+
+
+def measure_layer_forward(w, c, r, seed, steps, dev):
+    """The layer-forward kernels around the scan (conv1d and RMSNorm forward) on the
+    workload's shapes, timed with the library's timing hook over `steps` launches each.
+    Not part of the step and not in `value`; both are HBM-bound, so each reports its
+    algorithmic bytes (read the input once, write the output once) per second."""
+    import torch
+    from selective_state_space_02_amd import binding as ssm
+    from selective_state_space_02_amd import synth
+    f32 = torch.float32
+    s = 2 if w.dtype == "bf16" else 4
+    cout = torch.empty_like(c["x"])
+    cbias = synth.conv_bias(w, seed).to(dev)
+    ry = torch.empty_like(r["x"])
+    rrms = torch.empty((w.rms_rows,), dtype=f32, device=dev)
+
+    def run():
+        ssm.conv1d_causal_fwd(c["x"], c["W"], cbias, out=cout)
+        ssm.rmsnorm_fwd(r["x"], r["scale"], synth.RMS_EPS, y=ry, rms=rrms)
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    he = HipEvents()
+    names = ("conv_fwd", "rms_fwd")
+    kev = {k: [he.pair() for _ in range(steps)] for k in names}
+    for i in range(steps):
+        for k in names:
+            ssm.ssm_set_kernel_timer(k, *kev[k][i])
+        run()
+    torch.cuda.synchronize()
+    for k in names:
+        ssm.ssm_set_kernel_timer(k, None, None)
+    ms = {k: sum(he.elapsed_ms(*pr) for pr in kev[k]) / steps for k in names}
+    he.destroy()
+    E = w.B * w.L * w.D
+    nbytes = {"conv_fwd": 2 * E * s + w.D * (w.K + 1) * 4,
+              "rms_fwd": 2 * w.rms_rows * w.rms_dim * s + (w.rms_dim + w.rms_rows) * 4}
+    out = {}
+    for k in names:
+        gbps = nbytes[k] / (ms[k] * 1e-3) / 1e9
+        out[k] = {"kernel_ms": ms[k], "algorithmic_bytes": nbytes[k], "GBps": gbps,
+                  "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS}
+    return out
 
 
 def main():
@@ -203,6 +248,8 @@ def main():
     cpu_inputs = (synth.scan_inputs(w, args.seed), synth.conv_inputs(w, args.seed),
                   synth.rms_inputs(w, args.seed))
     p, c, r = ({k: v.to(dev) for k, v in d.items()} for d in cpu_inputs)
+    # the statistic the RMSNorm forward saves for its backward (setup, untimed)
+    _, r["rms"] = ssm.rmsnorm_fwd(r["x"], r["scale"], synth.RMS_EPS)
     f32 = torch.float32
     code = ssm.SSM_BF16 if w.dtype == "bf16" else ssm.SSM_F32
     B, L, D, N, K = w.B, w.L, w.D, w.N, w.K
@@ -289,6 +336,8 @@ def main():
     achieved_tflops = main_flops / (main_ms * 1e-3) / 1e12
     main_gbps = bwd_main_bytes(w) / (main_ms * 1e-3) / 1e9
 
+    layer_fwd = measure_layer_forward(w, c, r, args.seed, K_, dev)
+
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=f32, device=dev)
         b2 = torch.empty_like(a)
@@ -332,6 +381,7 @@ def main():
             "hbm_GBps_algorithmic": main_gbps,
         },
     }
+    out["layer_forward"] = layer_fwd
     if not args.no_cpu_baseline:
         sample = args.cpu_sample_channels or max(16, min(w.D, 2048))
         print(f"[bench] cpu baseline: oracle on {sample} channels", file=sys.stderr, flush=True)

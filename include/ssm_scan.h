@@ -1,11 +1,13 @@
 /*
  * ssm_scan.h -- C ABI of libssmscan.so, the MI355X (gfx950) selective-scan hot path.
  *
- * Four operations on already-projected tensors:
+ * Operations on already-projected tensors:
  *   ssm_scan_fwd       selective-SSM scan, forward
  *   ssm_scan_bwd       its backward (backpropagation through time across the state)
  *   conv1d_causal_bwd  depthwise causal conv1d backward
  *   rmsnorm_bwd        batched RMSNorm backward
+ *   conv1d_causal_fwd  depthwise causal conv1d forward
+ *   rmsnorm_fwd        batched RMSNorm forward (also returns the saved rms)
  *
  * Common conventions
  * ------------------
@@ -74,6 +76,7 @@ const char *ssm_version(void);
  *   1 scan-forward chunk summary    2 scan-forward carry    3 scan-forward output
  *   4 scan-backward chunk summary   5 scan-backward carry   6 scan-backward main
  *   7 conv1d backward               8 RMSNorm backward
+ *   9 conv1d forward               10 RMSNorm forward
  * Returns SSM_ERR_ARG for an unknown id or a half-set pair.  Has no effect on results. */
 int ssm_set_kernel_timer(int kernel, void *start, void *stop);
 
@@ -161,6 +164,28 @@ size_t rmsnorm_bwd_workspace_bytes(int64_t R, int64_t M, ssm_dtype_t dtype);
 int rmsnorm_bwd(void *stream, ssm_dtype_t dtype, int64_t R, int64_t M, const void *dy,
                 const void *x, const float *scale, const float *rms, void *dx,
                 float *dscale, void *ws, size_t ws_bytes);
+
+/* ---------------------------------------------------------------------------------
+ * Depthwise causal conv1d forward, the forward of conv1d_causal_bwd above (the window
+ * of the mamba-rs backward_conv1d_step section holds the last K inputs, tap K-1 the
+ * newest; the sequence starts from a zero window):
+ *     out[b,t,d] = bias[d] + sum_{k<K} W[d,k] * x[b, t-K+1+k, d]   (x = 0 for t < 0)
+ * Shapes: x, out [B,L,D] (dtype); W [D,K] f32; bias [D] f32 or NULL (zero).  No
+ * workspace.  Supported: K in [1, 8].
+ * ------------------------------------------------------------------------------- */
+int conv1d_causal_fwd(void *stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D,
+                      int64_t K, const void *x, const float *W, const float *bias, void *out);
+
+/* ---------------------------------------------------------------------------------
+ * Batched RMSNorm forward, the forward of rmsnorm_bwd above; it also writes the
+ * per-row rms that the backward takes as its saved statistic (the mamba-rs
+ * backward_rms_norm section saves rms, not its inverse):
+ *     rms[r] = sqrt(mean_i x[r,i]^2 + eps),   y[r,i] = x[r,i] / rms[r] * scale[i]
+ * Shapes: x, y [R,M] (dtype); scale [M] f32; rms [R] f32 (out).  eps finite, >= 0.
+ * No workspace.  Supported M: as rmsnorm_bwd.
+ * ------------------------------------------------------------------------------- */
+int rmsnorm_fwd(void *stream, ssm_dtype_t dtype, int64_t R, int64_t M, const void *x,
+                const float *scale, float eps, void *y, float *rms);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,7 @@ SSM_OK, SSM_ERR_ARG, SSM_ERR_UNSUPPORTED, SSM_ERR_WORKSPACE, SSM_ERR_ALIGN, SSM_
 EXPORTS = ("ssm_last_error", "ssm_version", "ssm_set_kernel_timer", "ssm_scan_ckpt_bytes",
            "ssm_scan_fwd_workspace_bytes", "ssm_scan_bwd_workspace_bytes", "ssm_scan_fwd",
            "ssm_scan_bwd", "conv1d_causal_bwd_workspace_bytes", "conv1d_causal_bwd",
-           "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd")
+           "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd", "conv1d_causal_fwd", "rmsnorm_fwd")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -76,6 +76,10 @@ def load():
     lib.rmsnorm_bwd_workspace_bytes.argtypes = [_I] * 2 + [_E]
     lib.rmsnorm_bwd.restype = _E
     lib.rmsnorm_bwd.argtypes = [_P, _E] + [_I] * 2 + [_P] * 6 + [_P, _S]
+    lib.conv1d_causal_fwd.restype = _E
+    lib.conv1d_causal_fwd.argtypes = [_P, _E] + [_I] * 4 + [_P] * 4
+    lib.rmsnorm_fwd.restype = _E
+    lib.rmsnorm_fwd.argtypes = [_P, _E] + [_I] * 2 + [_P, _P, ctypes.c_float, _P, _P]
     _lib = lib
     return lib
 
@@ -89,7 +93,8 @@ def version() -> str:
 
 
 KERNEL_IDS = {"fwd_summary": 1, "fwd_carry": 2, "fwd_output": 3, "bwd_summary": 4,
-              "bwd_carry": 5, "bwd_main": 6, "conv_bwd": 7, "rms_bwd": 8}
+              "bwd_carry": 5, "bwd_main": 6, "conv_bwd": 7, "rms_bwd": 8, "conv_fwd": 9,
+              "rms_fwd": 10}
 
 
 def ssm_set_kernel_timer(kernel, start=None, stop=None):
@@ -284,3 +289,36 @@ def rmsnorm_bwd(dy, x, scale, rms, dx=None, dscale=None, ws=None):
     _check(lib.rmsnorm_bwd(_stream(dev), code, R, M, *args,
                            _ptr(ws, "ws") if ws is not None else None, nbytes))
     return dict(dx=dx, dscale=dscale)
+
+
+def conv1d_causal_fwd(x, W, bias=None, out=None):
+    """Returns out [B, L, D] (dtype of x)."""
+    lib = load()
+    Bsz, L, D = x.shape
+    K = W.shape[1]
+    dev = x.device
+    dt = x.dtype
+    code = _dtype_code(x)
+    f32 = torch.float32
+    out = torch.empty_like(x) if out is None else out
+    bp = _ptr(bias, "bias", f32, (D,), dev) if bias is not None else None
+    _check(lib.conv1d_causal_fwd(_stream(dev), code, Bsz, L, D, K,
+                                 _ptr(x, "x", dt, (Bsz, L, D), dev), _ptr(W, "W", f32, (D, K), dev),
+                                 bp, _ptr(out, "out", dt, (Bsz, L, D), dev)))
+    return out
+
+
+def rmsnorm_fwd(x, scale, eps, y=None, rms=None):
+    """Returns (y [R, M] in the dtype of x, rms [R] f32)."""
+    lib = load()
+    R, M = x.shape
+    dev = x.device
+    dt = x.dtype
+    code = _dtype_code(x)
+    f32 = torch.float32
+    y = torch.empty_like(x) if y is None else y
+    rms = torch.empty((R,), dtype=f32, device=dev) if rms is None else rms
+    _check(lib.rmsnorm_fwd(_stream(dev), code, R, M, _ptr(x, "x", dt, (R, M), dev),
+                           _ptr(scale, "scale", f32, (M,), dev), float(eps),
+                           _ptr(y, "y", dt, (R, M), dev), _ptr(rms, "rms", f32, (R,), dev)))
+    return y, rms

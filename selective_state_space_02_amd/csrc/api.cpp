@@ -228,7 +228,8 @@ bool rms_plan(int64_t R, int64_t M, ssm_dtype_t dt, ssm::RmsPlan* p) {
   const int64_t need = cdiv(M, per_pass);
   if (need > 16) return false;
   p->passes = need <= 8 ? need : 16;  // rows of up to 8 passes stay in registers
-  // about 512 blocks of 4 wavefronts, at least 4 rows per block
+  // about 512 blocks of 4 wavefronts (each block leaves one dscale partial row; 2048
+  // blocks measured no faster and cost a 4x larger reduce), at least 4 rows per block
   int64_t rpb = cdiv(R, 512);
   if (rpb < 4) rpb = 4;
   p->rows_per_block = rpb;
@@ -380,6 +381,55 @@ int conv1d_causal_bwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int
   a.x = x; a.W = W; a.dout = dout; a.dx = dx; a.dW = dW; a.db = db;
   return hip_status(ssm::launch_conv1d_bwd(a, p, static_cast<hipStream_t>(stream)),
                     "conv1d_causal_bwd");
+}
+
+int conv1d_causal_fwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D,
+                      int64_t K, const void* x, const float* W, const float* bias, void* out) {
+  if (B <= 0 || L <= 0 || D <= 0 || K <= 0)
+    return fail(SSM_ERR_ARG, "sizes must be positive (B=%lld L=%lld D=%lld K=%lld)",
+                (long long)B, (long long)L, (long long)D, (long long)K);
+  if (dtype != SSM_F32 && dtype != SSM_BF16)
+    return fail(SSM_ERR_UNSUPPORTED, "dtype %d not supported", int(dtype));
+  if (K > 8) return fail(SSM_ERR_UNSUPPORTED, "conv width K=%lld not supported (1..8)", (long long)K);
+  if (B > kMaxElems / L || B * L > kMaxElems / D) return fail(SSM_ERR_ARG, "tensor sizes overflow");
+  int rc = check_ptrs({{x, "x"}, {W, "W"}, {out, "out"}}, {{bias, "bias"}});
+  if (rc) return rc;
+  ssm::ConvPlan p{};
+  conv_plan(B, L, D, K, &p);
+  ssm::ConvFwdArgs a{};
+  a.dtype = int(dtype);
+  a.B = B; a.L = L; a.D = D; a.K = K;
+  a.Tb = p.Tb; a.nTb = p.nTb;
+  a.x = x; a.W = W; a.bias = bias; a.out = out;
+  return hip_status(ssm::launch_conv1d_fwd(a, static_cast<hipStream_t>(stream)),
+                    "conv1d_causal_fwd");
+}
+
+int rmsnorm_fwd(void* stream, ssm_dtype_t dtype, int64_t R, int64_t M, const void* x,
+                const float* scale, float eps, void* y, float* rms) {
+  if (R <= 0 || M <= 0)
+    return fail(SSM_ERR_ARG, "sizes must be positive (R=%lld M=%lld)", (long long)R, (long long)M);
+  if (!(eps >= 0.f) || eps > 3.0e38f)
+    return fail(SSM_ERR_ARG, "eps must be finite and >= 0 (got %g)", double(eps));
+  if (dtype != SSM_F32 && dtype != SSM_BF16)
+    return fail(SSM_ERR_UNSUPPORTED, "dtype %d not supported", int(dtype));
+  if (R > kMaxElems / M) return fail(SSM_ERR_ARG, "tensor sizes overflow");
+  ssm::RmsPlan p{};
+  if (!rms_plan(R, M, dtype, &p))
+    return fail(SSM_ERR_UNSUPPORTED, "row length M=%lld not supported for this dtype", (long long)M);
+  int rc = check_ptrs({{x, "x"}, {scale, "scale"}, {y, "y"}, {rms, "rms"}}, {});
+  if (rc) return rc;
+  ssm::RmsFwdArgs a{};
+  a.dtype = int(dtype);
+  a.R = R; a.M = M;
+  // no per-block partials in the forward: small blocks (two rows per wavefront) give
+  // every SIMD several wavefronts' rows in flight
+  int64_t rpb = 8;
+  while (cdiv(R, rpb) > INT32_MAX) rpb *= 2;
+  a.vec = p.vec; a.passes = p.passes; a.rows_per_block = rpb; a.nblk = cdiv(R, rpb);
+  a.eps = eps;
+  a.x = x; a.scale = scale; a.y = y; a.rms = rms;
+  return hip_status(ssm::launch_rmsnorm_fwd(a, static_cast<hipStream_t>(stream)), "rmsnorm_fwd");
 }
 
 size_t rmsnorm_bwd_workspace_bytes(int64_t R, int64_t M, ssm_dtype_t dtype) {

@@ -117,7 +117,9 @@ enum KernelId {
   kKBwdMain = 6,
   kKConvBwd = 7,
   kKRmsBwd = 8,
-  kKNumIds = 9
+  kKConvFwd = 9,
+  kKRmsFwd = 10,
+  kKNumIds = 11
 };
 
 // Records the caller's event for kernel `id` on stream st (stop = false: before the
@@ -127,6 +129,29 @@ void timer_mark(int id, bool stop, hipStream_t st);
 hipError_t launch_scan_fwd(const ScanArgs& a, const FwdPlan& p, hipStream_t st);
 hipError_t launch_scan_bwd(const ScanArgs& a, const BwdPlan& p, hipStream_t st);
 hipError_t launch_conv1d_bwd(const ConvArgs& a, const ConvPlan& p, hipStream_t st);
+
+struct ConvFwdArgs {
+  int dtype;
+  int64_t B, L, D, K;
+  int64_t Tb, nTb;  // time blocks, as ConvPlan
+  const void* x;
+  const float* W;
+  const float* bias;  // nullable
+  void* out;
+};
+hipError_t launch_conv1d_fwd(const ConvFwdArgs& a, hipStream_t st);
+
+struct RmsFwdArgs {
+  int dtype;
+  int64_t R, M;
+  int64_t vec, passes, rows_per_block, nblk;  // as RmsPlan
+  float eps;
+  const void* x;
+  const float* scale;
+  void* y;
+  float* rms;
+};
+hipError_t launch_rmsnorm_fwd(const RmsFwdArgs& a, hipStream_t st);
 hipError_t launch_rmsnorm_bwd(const RmsArgs& a, const RmsPlan& p, hipStream_t st);
 // out[j] (+)= sum_{p < P} part[p*J + j] in a fixed order; tmp holds
 // reduce_tmp_floats(P, J) floats (may be null when that is 0).

@@ -8,21 +8,21 @@ tensor order, so the same values can be regenerated without a GPU.
 Storage rules:
   * activations (x, delta, B, C, dy, conv x/dout, norm x/dy) are stored in the
     workload's dtype (f32 or bf16, rounded to nearest-even by ``Tensor.to``);
-  * parameters (A, D, conv W, norm scale, saved rms) are f32; for bf16 workloads they
+  * parameters (A, D, conv W and bias, norm scale) are f32; for bf16 workloads they
     hold bf16-rounded values, so "cast to bf16" and "f32 parameter" give one number.
 
-The saved RMSNorm statistic ``rms = sqrt(mean(x^2) + eps)`` is part of the input
-recipe (the backward consumes the value the forward saved); it is computed here in
-f64 from the stored x.
+The RMSNorm backward also takes the statistic its forward saved (rms); that is the
+forward's arithmetic, so it is not drawn here: the tests take it from the oracle's
+forward, the benchmark from the library's.
 """
 import torch
 
 from .workloads import Workload
 
 # tensor ids (fixed order)
-_X, _DELTA, _B, _C, _DV, _DY, _CX, _CW, _CDOUT, _RX, _RDY, _RSCALE, _H0 = range(1, 14)
+_X, _DELTA, _B, _C, _DV, _DY, _CX, _CW, _CDOUT, _RX, _RDY, _RSCALE, _H0, _CBIAS = range(1, 15)
 
-RMS_EPS = 1e-5
+RMS_EPS = 1e-5  # the RMSNorm eps of every workload
 
 
 def _gen(seed: int, tid: int) -> torch.Generator:
@@ -76,17 +76,20 @@ def conv_inputs(w: Workload, seed: int = 0) -> dict:
     return dict(x=x, W=_param(Wc, w), dout=dout)
 
 
+def conv_bias(w: Workload, seed: int = 0) -> torch.Tensor:
+    """Conv bias [D] ~ U(-0.5, 0.5) (for the conv forward)."""
+    bias = torch.rand((w.D,), generator=_gen(seed, _CBIAS), dtype=torch.float32) - 0.5
+    return _param(bias, w)
+
+
 def rms_inputs(w: Workload, seed: int = 0) -> dict:
-    """x, dy [R,M]; scale [M] ~ U(0.5, 1.5); rms [R] saved by the forward."""
+    """x, dy [R,M]; scale [M] ~ U(0.5, 1.5).  (The saved rms comes from a forward.)"""
     sd = _store_dtype(w)
     R, M = w.rms_rows, w.rms_dim
     x = _normal((R, M), seed, _RX).to(sd)
     dy = _normal((R, M), seed, _RDY).to(sd)
     scale = torch.rand((M,), generator=_gen(seed, _RSCALE), dtype=torch.float32) + 0.5
-    xd = x.to(torch.float64)
-    rms = torch.sqrt((xd * xd).mean(dim=1) + RMS_EPS)
-    del xd
-    return dict(x=x, dy=dy, scale=_param(scale, w), rms=_param(rms, w))
+    return dict(x=x, dy=dy, scale=_param(scale, w))
 
 
 def as_f64(t: torch.Tensor):

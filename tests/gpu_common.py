@@ -68,3 +68,10 @@ def compare(got: dict, ref: dict, keys, label=""):
         assert np.isfinite(errs[k]), (label, k)
         assert errs[k] <= tol_for(got[k]), (label, k, errs[k])
     return errs
+
+
+def with_saved_rms(p: dict) -> dict:
+    """RMSNorm inputs plus the statistic the forward saves (from the oracle's forward,
+    in f64, stored as the f32 the ABI takes)."""
+    _, rms = oracle.rmsnorm_fwd(synth.as_f64(p["x"]), synth.as_f64(p["scale"]), synth.RMS_EPS)
+    return dict(p, rms=torch.from_numpy(rms).to(torch.float32))

@@ -30,9 +30,10 @@ def declared_functions():
     return sorted({n for n in names if n not in skip})
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("ssm_scan_fwd", "ssm_scan_bwd", "conv1d_causal_bwd", "rmsnorm_bwd"):
+    for n in ("ssm_scan_fwd", "ssm_scan_bwd", "conv1d_causal_bwd", "rmsnorm_bwd",
+              "conv1d_causal_fwd", "rmsnorm_fwd"):
         assert n in names
 
 
@@ -190,6 +191,42 @@ def test_rms_validation():
     assert _rms(lib, ws=FAKE, ws_bytes=need - 1) == b.SSM_ERR_WORKSPACE
     assert b.rmsnorm_bwd_workspace_bytes(10, 8192, 1) > 0
     assert b.rmsnorm_bwd_workspace_bytes(10, 8193, 1) == 0
+
+
+def _conv_fwd(lib, B=2, L=64, D=32, K=4, dtype=0, x=FAKE, W=FAKE, bias=None, out=FAKE):
+    return lib.conv1d_causal_fwd(None, dtype, B, L, D, K, x, W, bias, out)
+
+
+def test_conv_fwd_validation():
+    lib = b.load()
+    assert _conv_fwd(lib, K=0) == b.SSM_ERR_ARG
+    assert _conv_fwd(lib, K=9) == b.SSM_ERR_UNSUPPORTED
+    assert _conv_fwd(lib, B=0) == b.SSM_ERR_ARG
+    assert _conv_fwd(lib, dtype=2) == b.SSM_ERR_UNSUPPORTED
+    for name in ("x", "W", "out"):
+        assert _conv_fwd(lib, **{name: None}) == b.SSM_ERR_ARG
+        assert name in b.last_error()
+        assert _conv_fwd(lib, **{name: MIS}) == b.SSM_ERR_ALIGN
+    assert _conv_fwd(lib, bias=MIS) == b.SSM_ERR_ALIGN     # optional, but aligned if given
+
+
+def _rms_fwd(lib, R=64, M=128, dtype=0, x=FAKE, scale=FAKE, eps=1e-5, y=FAKE, rms=FAKE):
+    return lib.rmsnorm_fwd(None, dtype, R, M, x, scale, eps, y, rms)
+
+
+def test_rms_fwd_validation():
+    lib = b.load()
+    assert _rms_fwd(lib, R=0) == b.SSM_ERR_ARG
+    assert _rms_fwd(lib, M=0) == b.SSM_ERR_ARG
+    assert _rms_fwd(lib, eps=-1.0) == b.SSM_ERR_ARG
+    assert _rms_fwd(lib, eps=float("nan")) == b.SSM_ERR_ARG
+    assert _rms_fwd(lib, eps=float("inf")) == b.SSM_ERR_ARG
+    assert _rms_fwd(lib, dtype=3) == b.SSM_ERR_UNSUPPORTED
+    assert _rms_fwd(lib, M=8192 + 8, dtype=1) == b.SSM_ERR_UNSUPPORTED
+    assert _rms_fwd(lib, M=1025, dtype=0) == b.SSM_ERR_UNSUPPORTED
+    for name in ("x", "scale", "y", "rms"):
+        assert _rms_fwd(lib, **{name: None}) == b.SSM_ERR_ARG
+        assert _rms_fwd(lib, **{name: MIS}) == b.SSM_ERR_ALIGN
 
 
 def test_error_message_is_per_call():

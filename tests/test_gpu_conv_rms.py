@@ -13,7 +13,7 @@ import oracle
 from selective_state_space_02_amd import binding as ssm
 from selective_state_space_02_amd import synth
 from selective_state_space_02_amd.workloads import BY_NAME, WORKLOADS, custom
-from tests.gpu_common import compare, say
+from tests.gpu_common import compare, say, with_saved_rms
 
 pytestmark = pytest.mark.gpu
 
@@ -90,14 +90,14 @@ RMS_CASES = [custom(B=1, L=7, D=8), custom(B=3, L=11, D=100), custom(B=2, L=9, D
 @pytest.mark.parametrize("w", RMS_CASES, ids=lambda w: f"R{w.rms_rows}M{w.rms_dim}{w.dtype}")
 def test_rms_matches_oracle(w):
     say(f"[rms parity] R={w.rms_rows} M={w.rms_dim} {w.dtype}")
-    p = synth.rms_inputs(w)
+    p = with_saved_rms(synth.rms_inputs(w))
     compare(rms_gpu(p), rms_ref(p), ("dx", "dscale"), label=f"rms M={w.rms_dim}")
 
 
 @pytest.mark.parametrize("w", WORKLOADS, ids=lambda w: w.name)
 def test_rms_workloads(w):
     say(f"[rms workload] {w.name} R={w.rms_rows} M={w.rms_dim}")
-    p = synth.rms_inputs(w)
+    p = with_saved_rms(synth.rms_inputs(w))
     compare(rms_gpu(p), rms_ref(p), ("dx", "dscale"), label=f"rms {w.name}")
 
 
@@ -108,7 +108,7 @@ def test_rms_single_column_within_rounding_bound():
     # result, so the check is elementwise against that rounding bound:
     #   |dx - dx_ref| <= 8 u inv (|s dy| + |x c|),  u = 2^-24.
     w = custom(B=1, L=64, D=1)
-    p = synth.rms_inputs(w)
+    p = with_saved_rms(synth.rms_inputs(w))
     got = rms_gpu(p)
     q = {k: synth.as_f64(v) for k, v in p.items()}
     ref = rms_ref(p)
