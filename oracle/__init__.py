@@ -38,6 +38,7 @@ def _load():
             "oracle_scan_materialized": [_I] * 4 + [_D] * 8,
             "oracle_scan_bwd": [_I] * 4 + [_D] * 15,
             "oracle_conv1d_fwd": [_I] * 4 + [_D] * 4,
+            "oracle_conv1d_step": [_I] * 3 + [_D] * 5,
             "oracle_conv1d_bwd": [_I] * 4 + [_D] * 6,
             "oracle_conv1d_step_bwd": [_I] * 2 + [_D] * 6,
             "oracle_rmsnorm_fwd": [_I] * 2 + [_D, _D, ctypes.c_double, _D, _D],
@@ -125,6 +126,17 @@ def scan_bwd(x, delta, A, Bm, Cm, Dv, dy, h0=None):
 # ----------------------------------------------------------------------------------
 # conv1d
 # ----------------------------------------------------------------------------------
+
+def conv1d_step(state, x_t, W, bias=None):
+    """One token: state [B,K-1,D] (last K-1 inputs, oldest first) -> (state', out_t [B,D])."""
+    state = _f64(state).copy()
+    x_t, W, bias = map(_f64, (x_t, W, bias))
+    Bsz, D = x_t.shape
+    K = W.shape[1]
+    out = np.empty((Bsz, D))
+    _load().oracle_conv1d_step(Bsz, D, K, _p(state), _p(x_t), _p(W), _p(bias), _p(out))
+    return state, out
+
 
 def conv1d_fwd(x, W, bias=None):
     x, W, bias = map(_f64, (x, W, bias))

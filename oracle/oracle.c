@@ -320,6 +320,28 @@ void oracle_conv1d_fwd(int64_t B, int64_t L, int64_t D, int64_t K, const double 
     }
 }
 
+/* One-token step of the same conv (the decode form of the shift-register window of
+ * the mamba-rs backward_conv1d_step section): state [B][K-1][D] holds the last K-1
+ * inputs, oldest first.  out_t[b,d] = bias[d] + sum_{k<K-1} W[d,k] state[b,k,d]
+ * + W[d,K-1] x_t[b,d]; then the window moves one step (the oldest input drops out,
+ * x_t becomes the newest). */
+void oracle_conv1d_step(int64_t B, int64_t D, int64_t K, double *state, const double *x_t,
+                        const double *W, const double *bias, double *out_t)
+{
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t d = 0; d < D; ++d) {
+            double acc = bias ? bias[d] : 0.0;
+            for (int64_t k = 0; k < K - 1; ++k)
+                acc += W[d * K + k] * state[(b * (K - 1) + k) * D + d];
+            acc += W[d * K + K - 1] * x_t[b * D + d];
+            out_t[b * D + d] = acc;
+            for (int64_t k = 0; k + 1 < K - 1; ++k)
+                state[(b * (K - 1) + k) * D + d] = state[(b * (K - 1) + k + 1) * D + d];
+            if (K > 1)
+                state[(b * (K - 1) + K - 2) * D + d] = x_t[b * D + d];
+        }
+}
+
 /* Exact gradient of oracle_conv1d_fwd for upstream gradient dout:
  *   dx[b,s,d]  = sum_k dout[b, s+K-1-k, d] W[d,k]     (terms with s+K-1-k < L)
  *   dW[d,k]   += sum_{b,t} dout[b,t,d] x[b, t-K+1+k, d]

@@ -85,6 +85,22 @@ def test_conv_sequence_grads_equal_summed_page_steps(K):
     assert rel_err(r["db"], db) < 1e-14
 
 
+@pytest.mark.parametrize("K", [1, 2, 4, 8])
+def test_conv_step_sequence_equals_full_conv(K):
+    # the decode step, started from an all-zero window and fed the sequence one token at
+    # a time, gives the full causal conv's output at every step, and ends holding the
+    # last K-1 inputs
+    w = custom(B=2, L=13, D=5, K=K)
+    p = _conv(w)
+    bias = synth.as_f64(synth.conv_bias(w))
+    full = oracle.conv1d_fwd(p["x"], p["W"], bias)
+    state = np.zeros((w.B, K - 1, w.D))
+    for t in range(w.L):
+        state, o = oracle.conv1d_step(state, p["x"][:, t], p["W"], bias)
+        np.testing.assert_allclose(o, full[:, t], rtol=0, atol=1e-13)
+    np.testing.assert_array_equal(state, p["x"][:, w.L - (K - 1):, :])
+
+
 def test_conv_last_step_input_grad_is_newest_tap():
     # at t = L-1 no later output reads x[L-1] through an older tap
     w = custom(B=2, L=9, D=5, K=4)
