@@ -214,6 +214,68 @@ def measure_layer_forward(w, c, r, seed, steps, dev):
     return out
 
 
+# Sequences decoded together: a serving batch whose f32 state (1024 x 5120 x 16 x 4 B =
+# 335 MB on the 2.8B layer) exceeds the 256 MB Infinity Cache, so the scan step's rate
+# is an HBM rate (at 256 sequences the 84 MB state stays cache-resident across tokens).
+DECODE_BATCH = 1024
+
+
+def measure_decode(w, seed, steps, dev):
+    """One-token decode (conv1d_causal_step then ssm_scan_step) for DECODE_BATCH
+    sequences at the workload's D, N, K, timed with the library's timing hook over `steps`
+    tokens.  Not part of the step and not in `value`.  Both kernels are HBM-bound: the
+    scan step reads and writes its f32 state, the conv step its window."""
+    import torch
+    from selective_state_space_02_amd import binding as ssm
+    from selective_state_space_02_amd import synth
+    from selective_state_space_02_amd.workloads import custom
+    wd = custom(B=DECODE_BATCH, L=1, D=w.D, N=w.N, K=w.K, dtype=w.dtype)
+    p = {k: v.to(dev) for k, v in synth.scan_inputs(wd, seed, with_h0=True).items()}
+    c = {k: v.to(dev) for k, v in synth.conv_inputs(wd, seed).items()}
+    bias = synth.conv_bias(wd, seed).to(dev)
+    Bd, D, N, K = DECODE_BATCH, w.D, w.N, w.K
+    h = p["h0"].clone()
+    state = torch.zeros((Bd, K - 1, D), dtype=c["x"].dtype, device=dev)
+    xt, dt = p["x"][:, 0].contiguous(), p["delta"][:, 0].contiguous()
+    bt, ct = p["Bm"][:, 0].contiguous(), p["Cm"][:, 0].contiguous()
+    cx = c["x"][:, 0].contiguous()
+    cout = torch.empty_like(cx)
+    yt = torch.empty_like(xt)
+
+    def token():
+        ssm.conv1d_causal_step(state, cx, c["W"], bias, out_t=cout)
+        ssm.ssm_scan_step(h, xt, dt, p["A"], bt, ct, p["Dv"], y_t=yt)
+    for _ in range(3):
+        token()
+    torch.cuda.synchronize()
+    he = HipEvents()
+    names = ("conv_step", "scan_step")
+    kev = {k: [he.pair() for _ in range(steps)] for k in names}
+    tev = [he.pair() for _ in range(steps)]
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    for i in range(steps):
+        for k in names:
+            ssm.ssm_set_kernel_timer(k, *kev[k][i])
+        he.record(tev[i][0], stream)
+        token()
+        he.record(tev[i][1], stream)
+    torch.cuda.synchronize()
+    for k in names:
+        ssm.ssm_set_kernel_timer(k, None, None)
+    ms = {k: sum(he.elapsed_ms(*pr) for pr in kev[k]) / steps for k in names}
+    tok_ms = sum(he.elapsed_ms(*pr) for pr in tev) / steps
+    he.destroy()
+    s = 2 if w.dtype == "bf16" else 4
+    nbytes = {"scan_step": 2 * Bd * D * N * 4 + 3 * Bd * D * s + 2 * Bd * N * s + D * (N + 1) * 4,
+              "conv_step": 2 * Bd * (K - 1) * D * s + 2 * Bd * D * s + D * (K + 1) * 4}
+    out = {"batch": Bd, "token_ms": tok_ms, "tokens_per_s": Bd / (tok_ms * 1e-3)}
+    for k in names:
+        gbps = nbytes[k] / (ms[k] * 1e-3) / 1e9
+        out[k] = {"kernel_ms": ms[k], "algorithmic_bytes": nbytes[k], "GBps": gbps,
+                  "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -337,6 +399,7 @@ def main():
     main_gbps = bwd_main_bytes(w) / (main_ms * 1e-3) / 1e9
 
     layer_fwd = measure_layer_forward(w, c, r, args.seed, K_, dev)
+    decode = measure_decode(w, args.seed, K_, dev)
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=f32, device=dev)
@@ -382,6 +445,7 @@ def main():
         },
     }
     out["layer_forward"] = layer_fwd
+    out["decode"] = decode
     if not args.no_cpu_baseline:
         sample = args.cpu_sample_channels or max(16, min(w.D, 2048))
         print(f"[bench] cpu baseline: oracle on {sample} channels", file=sys.stderr, flush=True)

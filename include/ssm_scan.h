@@ -8,6 +8,8 @@
  *   rmsnorm_bwd        batched RMSNorm backward
  *   conv1d_causal_fwd  depthwise causal conv1d forward
  *   rmsnorm_fwd        batched RMSNorm forward (also returns the saved rms)
+ *   ssm_scan_step      one-token decode step of the scan (state updated in place)
+ *   conv1d_causal_step one-token decode step of the conv (window updated in place)
  *
  * Common conventions
  * ------------------
@@ -77,6 +79,7 @@ const char *ssm_version(void);
  *   4 scan-backward chunk summary   5 scan-backward carry   6 scan-backward main
  *   7 conv1d backward               8 RMSNorm backward
  *   9 conv1d forward               10 RMSNorm forward
+ *  11 scan decode step             12 conv1d decode step
  * Returns SSM_ERR_ARG for an unknown id or a half-set pair.  Has no effect on results. */
 int ssm_set_kernel_timer(int kernel, void *start, void *stop);
 
@@ -186,6 +189,36 @@ int conv1d_causal_fwd(void *stream, ssm_dtype_t dtype, int64_t B, int64_t L, int
  * ------------------------------------------------------------------------------- */
 int rmsnorm_fwd(void *stream, ssm_dtype_t dtype, int64_t R, int64_t M, const void *x,
                 const float *scale, float eps, void *y, float *rms);
+
+/* ---------------------------------------------------------------------------------
+ * One-token decode step of the selective scan: the single-step updater the rustytorch
+ * backward_cuda commit describes for inference.  For every batch row b, channel d,
+ * state n:
+ *     h[b,d,n] <- exp(delta_t[b,d] * A[d,n]) * h[b,d,n] + delta_t[b,d] * B_t[b,n] * x_t[b,d]
+ *     y_t[b,d]  = sum_n C_t[b,n] * h[b,d,n] + Dv[d] * x_t[b,d]
+ * i.e. one timestep of ssm_scan_fwd; a sequence decoded token by token from h = h0 gives
+ * the scan's outputs.  Each (b, d) is computed independently, in a fixed order, so the
+ * results do not depend on which other rows share the batch.
+ * Shapes: h [B,D,N] f32 (in/out, updated in place); x_t, delta_t, y_t [B,D] (dtype);
+ * B_t, C_t [B,N] (dtype); A [D,N] f32; Dv [D] f32.  No workspace.  Supported sizes as
+ * ssm_scan_fwd.
+ * ------------------------------------------------------------------------------- */
+int ssm_scan_step(void *stream, ssm_dtype_t dtype, int64_t B, int64_t D, int64_t N, float *h,
+                  const void *x_t, const void *delta_t, const float *A, const void *B_t,
+                  const void *C_t, const float *Dv, void *y_t);
+
+/* ---------------------------------------------------------------------------------
+ * One-token decode step of the depthwise causal conv1d.  state [B,K-1,D] (dtype) holds
+ * the last K-1 inputs, oldest first (all zero at the start of a sequence):
+ *     out_t[b,d] = bias[d] + sum_{k<K-1} W[d,k] * state[b,k,d] + W[d,K-1] * x_t[b,d]
+ * then the window moves one step in place (the oldest input drops out, x_t becomes the
+ * newest).  A sequence stepped token by token gives conv1d_causal_fwd's outputs.
+ * Shapes: x_t, out_t [B,D] (dtype); W [D,K] f32; bias [D] f32 or NULL (zero); state may
+ * be NULL when K = 1.  No workspace.  Supported: K in [1, 8].
+ * ------------------------------------------------------------------------------- */
+int conv1d_causal_step(void *stream, ssm_dtype_t dtype, int64_t B, int64_t D, int64_t K,
+                       void *state, const void *x_t, const float *W, const float *bias,
+                       void *out_t);
 
 #ifdef __cplusplus
 }

@@ -6,5 +6,6 @@ The product is ``libssmscan.so`` (HIP kernels behind a C ABI, declared in
 the package does not load the library; the first binding call does, and raises if it
 is missing.
 """
-from .binding import (SsmError, conv1d_causal_bwd, conv1d_causal_fwd, load,  # noqa: F401
-                      new_ckpt, rmsnorm_bwd, rmsnorm_fwd, ssm_scan_bwd, ssm_scan_fwd, version)
+from .binding import (SsmError, conv1d_causal_bwd, conv1d_causal_fwd,  # noqa: F401
+                      conv1d_causal_step, load, new_ckpt, rmsnorm_bwd, rmsnorm_fwd, ssm_scan_bwd,
+                      ssm_scan_fwd, ssm_scan_step, version)

@@ -23,7 +23,8 @@ SSM_OK, SSM_ERR_ARG, SSM_ERR_UNSUPPORTED, SSM_ERR_WORKSPACE, SSM_ERR_ALIGN, SSM_
 EXPORTS = ("ssm_last_error", "ssm_version", "ssm_set_kernel_timer", "ssm_scan_ckpt_bytes",
            "ssm_scan_fwd_workspace_bytes", "ssm_scan_bwd_workspace_bytes", "ssm_scan_fwd",
            "ssm_scan_bwd", "conv1d_causal_bwd_workspace_bytes", "conv1d_causal_bwd",
-           "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd", "conv1d_causal_fwd", "rmsnorm_fwd")
+           "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd", "conv1d_causal_fwd", "rmsnorm_fwd",
+           "ssm_scan_step", "conv1d_causal_step")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -80,6 +81,10 @@ def load():
     lib.conv1d_causal_fwd.argtypes = [_P, _E] + [_I] * 4 + [_P] * 4
     lib.rmsnorm_fwd.restype = _E
     lib.rmsnorm_fwd.argtypes = [_P, _E] + [_I] * 2 + [_P, _P, ctypes.c_float, _P, _P]
+    lib.ssm_scan_step.restype = _E
+    lib.ssm_scan_step.argtypes = [_P, _E] + [_I] * 3 + [_P] * 8
+    lib.conv1d_causal_step.restype = _E
+    lib.conv1d_causal_step.argtypes = [_P, _E] + [_I] * 3 + [_P] * 5
     _lib = lib
     return lib
 
@@ -94,7 +99,7 @@ def version() -> str:
 
 KERNEL_IDS = {"fwd_summary": 1, "fwd_carry": 2, "fwd_output": 3, "bwd_summary": 4,
               "bwd_carry": 5, "bwd_main": 6, "conv_bwd": 7, "rms_bwd": 8, "conv_fwd": 9,
-              "rms_fwd": 10}
+              "rms_fwd": 10, "scan_step": 11, "conv_step": 12}
 
 
 def ssm_set_kernel_timer(kernel, start=None, stop=None):
@@ -322,3 +327,40 @@ def rmsnorm_fwd(x, scale, eps, y=None, rms=None):
                            _ptr(scale, "scale", f32, (M,), dev), float(eps),
                            _ptr(y, "y", dt, (R, M), dev), _ptr(rms, "rms", f32, (R,), dev)))
     return y, rms
+
+
+def ssm_scan_step(h, x_t, delta_t, A, B_t, C_t, Dv, y_t=None):
+    """One token: advances h [B, D, N] (f32) in place; returns y_t [B, D]."""
+    lib = load()
+    Bsz, D, N = h.shape
+    dev = x_t.device
+    dt = x_t.dtype
+    code = _dtype_code(x_t)
+    f32 = torch.float32
+    y_t = torch.empty_like(x_t) if y_t is None else y_t
+    _check(lib.ssm_scan_step(_stream(dev), code, Bsz, D, N, _ptr(h, "h", f32, (Bsz, D, N), dev),
+                             _ptr(x_t, "x_t", dt, (Bsz, D), dev),
+                             _ptr(delta_t, "delta_t", dt, (Bsz, D), dev),
+                             _ptr(A, "A", f32, (D, N), dev), _ptr(B_t, "B_t", dt, (Bsz, N), dev),
+                             _ptr(C_t, "C_t", dt, (Bsz, N), dev), _ptr(Dv, "Dv", f32, (D,), dev),
+                             _ptr(y_t, "y_t", dt, (Bsz, D), dev)))
+    return y_t
+
+
+def conv1d_causal_step(state, x_t, W, bias=None, out_t=None):
+    """One token: moves the window state [B, K-1, D] in place; returns out_t [B, D]."""
+    lib = load()
+    Bsz, D = x_t.shape
+    K = W.shape[1]
+    dev = x_t.device
+    dt = x_t.dtype
+    code = _dtype_code(x_t)
+    f32 = torch.float32
+    out_t = torch.empty_like(x_t) if out_t is None else out_t
+    sp = _ptr(state, "state", dt, (Bsz, K - 1, D), dev) if K > 1 else None
+    bp = _ptr(bias, "bias", f32, (D,), dev) if bias is not None else None
+    _check(lib.conv1d_causal_step(_stream(dev), code, Bsz, D, K, sp,
+                                  _ptr(x_t, "x_t", dt, (Bsz, D), dev),
+                                  _ptr(W, "W", f32, (D, K), dev), bp,
+                                  _ptr(out_t, "out_t", dt, (Bsz, D), dev)))
+    return out_t

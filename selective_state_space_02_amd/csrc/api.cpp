@@ -432,6 +432,46 @@ int rmsnorm_fwd(void* stream, ssm_dtype_t dtype, int64_t R, int64_t M, const voi
   return hip_status(ssm::launch_rmsnorm_fwd(a, static_cast<hipStream_t>(stream)), "rmsnorm_fwd");
 }
 
+int ssm_scan_step(void* stream, ssm_dtype_t dtype, int64_t B, int64_t D, int64_t N, float* h,
+                  const void* x_t, const void* delta_t, const float* A, const void* B_t,
+                  const void* C_t, const float* Dv, void* y_t) {
+  int rc = check_scan_dims(dtype, B, 1, D, N);
+  if (rc) return rc;
+  rc = check_ptrs({{h, "h"}, {x_t, "x_t"}, {delta_t, "delta_t"}, {A, "A"}, {B_t, "B_t"},
+                   {C_t, "C_t"}, {Dv, "Dv"}, {y_t, "y_t"}}, {});
+  if (rc) return rc;
+  ssm::ScanStepArgs a{};
+  a.dtype = int(dtype);
+  a.B = B; a.D = D; a.N = N;
+  a.h = h; a.x_t = x_t; a.delta_t = delta_t; a.A = A; a.B_t = B_t; a.C_t = C_t; a.Dv = Dv;
+  a.y_t = y_t;
+  return hip_status(ssm::launch_scan_step(a, static_cast<hipStream_t>(stream)), "ssm_scan_step");
+}
+
+int conv1d_causal_step(void* stream, ssm_dtype_t dtype, int64_t B, int64_t D, int64_t K,
+                       void* state, const void* x_t, const float* W, const float* bias,
+                       void* out_t) {
+  if (B <= 0 || D <= 0 || K <= 0)
+    return fail(SSM_ERR_ARG, "sizes must be positive (B=%lld D=%lld K=%lld)", (long long)B,
+                (long long)D, (long long)K);
+  if (dtype != SSM_F32 && dtype != SSM_BF16)
+    return fail(SSM_ERR_UNSUPPORTED, "dtype %d not supported", int(dtype));
+  if (K > 8) return fail(SSM_ERR_UNSUPPORTED, "conv width K=%lld not supported (1..8)", (long long)K);
+  if (B > kMaxElems / D || B * D > (int64_t(1) << 40))
+    return fail(SSM_ERR_ARG, "tensor sizes overflow");
+  int rc = K > 1 ? check_ptrs({{state, "state"}, {x_t, "x_t"}, {W, "W"}, {out_t, "out_t"}},
+                              {{bias, "bias"}})
+                 : check_ptrs({{x_t, "x_t"}, {W, "W"}, {out_t, "out_t"}},
+                              {{state, "state"}, {bias, "bias"}});
+  if (rc) return rc;
+  ssm::ConvStepArgs a{};
+  a.dtype = int(dtype);
+  a.B = B; a.D = D; a.K = K;
+  a.state = state; a.x_t = x_t; a.W = W; a.bias = bias; a.out_t = out_t;
+  return hip_status(ssm::launch_conv1d_step(a, static_cast<hipStream_t>(stream)),
+                    "conv1d_causal_step");
+}
+
 size_t rmsnorm_bwd_workspace_bytes(int64_t R, int64_t M, ssm_dtype_t dtype) {
   if (R <= 0 || M <= 0) return 0;
   return rms_ws(R, M, dtype, nullptr, nullptr);

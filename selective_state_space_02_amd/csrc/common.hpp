@@ -99,6 +99,11 @@ template <> struct VecStore<float, 4> {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
   }
 };
+template <> struct VecStore<float, 2> {
+  static __device__ __forceinline__ void run(float* p, const float (&v)[2]) {
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  }
+};
 template <> struct VecStore<float, 1> {
   static __device__ __forceinline__ void run(float* p, const float (&v)[1]) { p[0] = v[0]; }
 };

@@ -119,7 +119,9 @@ enum KernelId {
   kKRmsBwd = 8,
   kKConvFwd = 9,
   kKRmsFwd = 10,
-  kKNumIds = 11
+  kKScanStep = 11,
+  kKConvStep = 12,
+  kKNumIds = 13
 };
 
 // Records the caller's event for kernel `id` on stream st (stop = false: before the
@@ -152,6 +154,31 @@ struct RmsFwdArgs {
   float* rms;
 };
 hipError_t launch_rmsnorm_fwd(const RmsFwdArgs& a, hipStream_t st);
+
+struct ScanStepArgs {
+  int dtype;
+  int64_t B, D, N;
+  float* h;  // [B][D][N], in place
+  const void* x_t;
+  const void* delta_t;
+  const float* A;
+  const void* B_t;
+  const void* C_t;
+  const float* Dv;
+  void* y_t;
+};
+hipError_t launch_scan_step(const ScanStepArgs& a, hipStream_t st);
+
+struct ConvStepArgs {
+  int dtype;
+  int64_t B, D, K;
+  void* state;  // [B][K-1][D], in place (unused when K == 1)
+  const void* x_t;
+  const float* W;
+  const float* bias;  // nullable
+  void* out_t;
+};
+hipError_t launch_conv1d_step(const ConvStepArgs& a, hipStream_t st);
 hipError_t launch_rmsnorm_bwd(const RmsArgs& a, const RmsPlan& p, hipStream_t st);
 // out[j] (+)= sum_{p < P} part[p*J + j] in a fixed order; tmp holds
 // reduce_tmp_floats(P, J) floats (may be null when that is 0).

@@ -229,6 +229,44 @@ def test_rms_fwd_validation():
         assert _rms_fwd(lib, **{name: MIS}) == b.SSM_ERR_ALIGN
 
 
+def _step(lib, B=2, D=32, N=16, dtype=0, **kw):
+    p = dict(h=FAKE, x_t=FAKE, delta_t=FAKE, A=FAKE, B_t=FAKE, C_t=FAKE, Dv=FAKE, y_t=FAKE)
+    p.update(kw)
+    return lib.ssm_scan_step(None, dtype, B, D, N, p["h"], p["x_t"], p["delta_t"], p["A"],
+                             p["B_t"], p["C_t"], p["Dv"], p["y_t"])
+
+
+def test_scan_step_validation():
+    lib = b.load()
+    assert _step(lib, N=3) == b.SSM_ERR_UNSUPPORTED
+    assert _step(lib, B=0) == b.SSM_ERR_ARG
+    assert _step(lib, D=-1) == b.SSM_ERR_ARG
+    assert _step(lib, B=65536) == b.SSM_ERR_UNSUPPORTED
+    assert _step(lib, dtype=9) == b.SSM_ERR_UNSUPPORTED
+    for name in ("h", "x_t", "delta_t", "A", "B_t", "C_t", "Dv", "y_t"):
+        assert _step(lib, **{name: None}) == b.SSM_ERR_ARG
+        assert name in b.last_error()
+        assert _step(lib, **{name: MIS}) == b.SSM_ERR_ALIGN
+
+
+def _cstep(lib, B=2, D=32, K=4, dtype=0, state=FAKE, x_t=FAKE, W=FAKE, bias=None, out_t=FAKE):
+    return lib.conv1d_causal_step(None, dtype, B, D, K, state, x_t, W, bias, out_t)
+
+
+def test_conv_step_validation():
+    lib = b.load()
+    assert _cstep(lib, K=0) == b.SSM_ERR_ARG
+    assert _cstep(lib, K=9) == b.SSM_ERR_UNSUPPORTED
+    assert _cstep(lib, D=0) == b.SSM_ERR_ARG
+    assert _cstep(lib, dtype=4) == b.SSM_ERR_UNSUPPORTED
+    for name in ("state", "x_t", "W", "out_t"):
+        assert _cstep(lib, **{name: None}) == b.SSM_ERR_ARG
+        assert _cstep(lib, **{name: MIS}) == b.SSM_ERR_ALIGN
+    assert _cstep(lib, bias=MIS) == b.SSM_ERR_ALIGN
+    # a width-1 conv has no window: state may be NULL (still checked for alignment if given)
+    assert _cstep(lib, K=1, state=MIS) == b.SSM_ERR_ALIGN
+
+
 def test_error_message_is_per_call():
     lib = b.load()
     assert _fwd(lib, N=3) == b.SSM_ERR_UNSUPPORTED

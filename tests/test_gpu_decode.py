@@ -1,0 +1,141 @@
+"""GPU parity of the one-token decode steps (ssm_scan_step, conv1d_causal_step).
+
+- One step from a random state against the oracle's step.
+- A whole sequence decoded token by token against the oracle's full scan / conv (the
+  decode form must reproduce the sequence form).
+- Batch invariance: a row's results do not depend on which other rows share the batch
+  (bit-identical when the row is decoded alone).
+- Consistency with the library's own sequence kernels: the decode steps use the same
+  per-step arithmetic as the single-chunk scan and the conv forward, so the outputs are
+  bit-identical to them.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from selective_state_space_02_amd import binding as ssm
+from selective_state_space_02_amd import synth
+from selective_state_space_02_amd.workloads import custom
+from tests.gpu_common import TOL_F32, compare, f64, say
+from tests.helpers import rel_err
+
+pytestmark = pytest.mark.gpu
+
+STEP_CASES = [custom(B=3, L=4, D=20, N=16), custom(B=2, L=4, D=70, N=8, dtype="bf16"),
+              custom(B=5, L=4, D=64, N=4), custom(B=1, L=4, D=5120, N=16, dtype="bf16")]
+
+
+def _cuda(d):
+    return {k: v.cuda() for k, v in d.items()}
+
+
+@pytest.mark.parametrize("w", STEP_CASES, ids=lambda w: f"B{w.B}D{w.D}N{w.N}{w.dtype}")
+def test_scan_step_matches_oracle(w):
+    say(f"[scan step parity] B={w.B} D={w.D} N={w.N} {w.dtype}")
+    p = synth.scan_inputs(w, with_h0=True)
+    t = 2
+    g = _cuda(p)
+    h = g["h0"].clone()
+    y = ssm.ssm_scan_step(h, g["x"][:, t].contiguous(), g["delta"][:, t].contiguous(), g["A"],
+                          g["Bm"][:, t].contiguous(), g["Cm"][:, t].contiguous(), g["Dv"])
+    torch.cuda.synchronize()
+    q = {k: synth.as_f64(v) for k, v in p.items()}
+    hr, yr = oracle.scan_step(q["h0"], q["x"][:, t], q["delta"][:, t], q["A"], q["Bm"][:, t],
+                              q["Cm"][:, t], q["Dv"])
+    compare({"y": y}, {"y": yr}, ("y",), label="scan step")
+    e = rel_err(f64(h), hr)
+    say("scan step h", f"{e:.2e}")
+    assert e <= TOL_F32
+
+
+@pytest.mark.parametrize("w", [custom(B=2, L=200, D=40, N=16), custom(B=3, L=97, D=64, N=8, dtype="bf16")],
+                         ids=lambda w: f"B{w.B}L{w.L}D{w.D}N{w.N}{w.dtype}")
+def test_scan_decode_sequence_matches_oracle_scan(w):
+    say(f"[scan decode sequence] B={w.B} L={w.L} D={w.D} N={w.N} {w.dtype}")
+    p = synth.scan_inputs(w, with_h0=True)
+    g = _cuda(p)
+    h = g["h0"].clone()
+    ys = []
+    for t in range(w.L):
+        ys.append(ssm.ssm_scan_step(h, g["x"][:, t].contiguous(), g["delta"][:, t].contiguous(),
+                                    g["A"], g["Bm"][:, t].contiguous(), g["Cm"][:, t].contiguous(),
+                                    g["Dv"]))
+    y = torch.stack(ys, dim=1)
+    torch.cuda.synchronize()
+    q = {k: synth.as_f64(v) for k, v in p.items()}
+    yr, hl = oracle.scan_fwd(q["x"], q["delta"], q["A"], q["Bm"], q["Cm"], q["Dv"], q["h0"])
+    compare({"y": y}, {"y": yr}, ("y",), label="decoded sequence")
+    assert rel_err(f64(h), hl) <= TOL_F32
+
+
+def test_scan_step_is_batch_invariant():
+    w = custom(B=8, L=4, D=96, N=16)
+    p = _cuda(synth.scan_inputs(w, with_h0=True))
+    sl = lambda k, t: p[k][:, t].contiguous()  # noqa: E731
+    h_all = p["h0"].clone()
+    y_all = ssm.ssm_scan_step(h_all, sl("x", 1), sl("delta", 1), p["A"], sl("Bm", 1), sl("Cm", 1), p["Dv"])
+    r = 5
+    h_one = p["h0"][r:r + 1].clone()
+    y_one = ssm.ssm_scan_step(h_one, p["x"][r:r + 1, 1].contiguous(), p["delta"][r:r + 1, 1].contiguous(),
+                              p["A"], p["Bm"][r:r + 1, 1].contiguous(), p["Cm"][r:r + 1, 1].contiguous(),
+                              p["Dv"])
+    torch.cuda.synchronize()
+    assert torch.equal(y_all[r:r + 1], y_one)
+    assert torch.equal(h_all[r:r + 1], h_one)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scan_decode_is_bit_identical_to_single_chunk_scan(dtype):
+    # 32 steps (two tiles) are one chunk, so the scan runs exactly the decode arithmetic
+    w = custom(B=2, L=32, D=64, N=16, dtype=dtype)
+    p = _cuda(synth.scan_inputs(w, with_h0=True))
+    h_seq = torch.empty_like(p["h0"])
+    y_seq = ssm.ssm_scan_fwd(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], p["Dv"], h0=p["h0"],
+                             h_last=h_seq)
+    h = p["h0"].clone()
+    ys = [ssm.ssm_scan_step(h, p["x"][:, t].contiguous(), p["delta"][:, t].contiguous(), p["A"],
+                            p["Bm"][:, t].contiguous(), p["Cm"][:, t].contiguous(), p["Dv"])
+          for t in range(w.L)]
+    torch.cuda.synchronize()
+    assert torch.equal(torch.stack(ys, dim=1), y_seq)
+    assert torch.equal(h, h_seq)
+
+
+CONV_STEP_CASES = [custom(B=3, L=5, D=20, K=4), custom(B=2, L=9, D=70, K=8, dtype="bf16"),
+                   custom(B=4, L=2, D=33, K=1), custom(B=2, L=5, D=5120, K=4, dtype="bf16")]
+
+
+@pytest.mark.parametrize("w", CONV_STEP_CASES, ids=lambda w: f"B{w.B}D{w.D}K{w.K}{w.dtype}")
+def test_conv_step_matches_oracle(w):
+    say(f"[conv step parity] B={w.B} D={w.D} K={w.K} {w.dtype}")
+    c = synth.conv_inputs(w)
+    bias = synth.conv_bias(w)
+    # a nonzero window: the first K-1 inputs of the sequence (L = K + 1 or more)
+    state = c["x"][:, :w.K - 1].contiguous()
+    xt = c["x"][:, w.K - 1].contiguous()
+    st = state.cuda()
+    out = ssm.conv1d_causal_step(st, xt.cuda(), c["W"].cuda(), bias.cuda())
+    torch.cuda.synchronize()
+    sr, orf = oracle.conv1d_step(synth.as_f64(state), synth.as_f64(xt), synth.as_f64(c["W"]),
+                                 synth.as_f64(bias))
+    compare({"out": out}, {"out": orf}, ("out",), label="conv step")
+    assert np.array_equal(f64(st), sr)   # the window only moves values
+
+
+@pytest.mark.parametrize("w", [custom(B=2, L=50, D=40, K=4), custom(B=1, L=30, D=96, K=7, dtype="bf16")],
+                         ids=lambda w: f"B{w.B}L{w.L}D{w.D}K{w.K}{w.dtype}")
+def test_conv_decode_sequence_matches_oracle_and_forward(w):
+    say(f"[conv decode sequence] B={w.B} L={w.L} D={w.D} K={w.K} {w.dtype}")
+    c = synth.conv_inputs(w)
+    bias = synth.conv_bias(w)
+    g = _cuda(c)
+    bg = bias.cuda()
+    state = torch.zeros((w.B, w.K - 1, w.D), dtype=g["x"].dtype, device="cuda")
+    outs = [ssm.conv1d_causal_step(state, g["x"][:, t].contiguous(), g["W"], bg) for t in range(w.L)]
+    out = torch.stack(outs, dim=1)
+    full = ssm.conv1d_causal_fwd(g["x"], g["W"], bg)
+    torch.cuda.synchronize()
+    ref = oracle.conv1d_fwd(synth.as_f64(c["x"]), synth.as_f64(c["W"]), synth.as_f64(bias))
+    compare({"out": out}, {"out": ref}, ("out",), label="conv decoded sequence")
+    assert torch.equal(out, full)   # same multiply-add order as the forward kernel
