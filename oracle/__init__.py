@@ -43,6 +43,10 @@ def _load():
             "oracle_conv1d_step_bwd": [_I] * 2 + [_D] * 6,
             "oracle_rmsnorm_fwd": [_I] * 2 + [_D, _D, ctypes.c_double, _D, _D],
             "oracle_rmsnorm_bwd": [_I] * 2 + [_D] * 6,
+            "oracle_sigmoid": [_I] + [_D] * 2,
+            "oracle_silu": [_I] + [_D] * 2,
+            "oracle_silu_grad": [_I] + [_D] * 3,
+            "oracle_softplus": [_I] + [_D] * 2,
         }
         for name, args in sigs.items():
             fn = getattr(lib, name)
@@ -190,3 +194,31 @@ def rmsnorm_bwd(dy, x, scale, rms):
     _load().oracle_rmsnorm_bwd(R, M, _p(dy), _p(x), _p(scale), _p(rms), _p(out["dx"]),
                                _p(out["dscale"]))
     return out
+
+
+# ----------------------------------------------------------------------------------
+# elementwise neighbours of the scan
+# ----------------------------------------------------------------------------------
+
+def _elementwise(name, *arrays):
+    arrays = [np.ascontiguousarray(_f64(a)) for a in arrays]
+    out = np.empty_like(arrays[0])
+    getattr(_load(), name)(arrays[0].size, *[_p(a) for a in arrays], _p(out))
+    return out
+
+
+def sigmoid(p):
+    return _elementwise("oracle_sigmoid", p)
+
+
+def silu(p):
+    return _elementwise("oracle_silu", p)
+
+
+def silu_grad(p, dout):
+    """dout * silu'(p)."""
+    return _elementwise("oracle_silu_grad", p, dout)
+
+
+def softplus(z):
+    return _elementwise("oracle_softplus", z)

@@ -298,6 +298,45 @@ void oracle_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, const double *x
 }
 
 /* ------------------------------------------------------------------------------ */
+/* Elementwise neighbours of the scan (plain definitions).  The mamba-rs            */
+/* backward_conv1d_step section takes the conv's upstream gradient after the SiLU   */
+/* backward, i.e. SiLU follows the conv; Mamba's time step is a softplus of its     */
+/* projection plus a bias, and its output gate multiplies by SiLU of z.             */
+/*   silu(p) = p * sigmoid(p),  sigmoid(p) = 1 / (1 + exp(-p))                      */
+/*   silu'(p) = sigmoid(p) * (1 + p * (1 - sigmoid(p)))                              */
+/*   softplus(z) = log(1 + exp(z)) = max(z, 0) + log1p(exp(-|z|)),  softplus' = sigmoid */
+/* ------------------------------------------------------------------------------ */
+
+static double sigmoid(double p) { return 1.0 / (1.0 + exp(-p)); }
+
+void oracle_sigmoid(int64_t n, const double *p, double *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = sigmoid(p[i]);
+}
+
+void oracle_silu(int64_t n, const double *p, double *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = p[i] * sigmoid(p[i]);
+}
+
+/* out = dout * silu'(p): the gradient with respect to p of silu(p) given dout */
+void oracle_silu_grad(int64_t n, const double *p, const double *dout, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        const double sg = sigmoid(p[i]);
+        out[i] = dout[i] * sg * (1.0 + p[i] * (1.0 - sg));
+    }
+}
+
+void oracle_softplus(int64_t n, const double *z, double *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = fmax(z[i], 0.0) + log1p(exp(-fabs(z[i])));
+}
+
+/* ------------------------------------------------------------------------------ */
 /* Depthwise causal conv1d.                                                        */
 /*   out[b,t,d] = bias[d] + sum_k W[d,k] x[b, t-K+1+k, d]   (x = 0 before t = 0)   */
 /* ------------------------------------------------------------------------------ */
