@@ -214,6 +214,60 @@ def measure_layer_forward(w, c, r, seed, steps, dev):
     return out
 
 
+def measure_conv_silu(w, c, seed, steps, dev):
+    """The conv with its SiLU fused (act="silu"), forward and backward, on the workload's
+    shapes, timed with the library's timing hook over `steps` launches each (the backward
+    figure is its main kernel; the dW/db partial reduction is as in the plain backward).
+    Not part of the step and not in `value`.  The fused kernels move the same algorithmic
+    bytes as the plain ones; an unfused chain would add a SiLU pass (read, write) after
+    the forward and a SiLU-backward pass (read du and the conv output, write g) before
+    the backward, counted in `unfused_extra_bytes`."""
+    import torch
+    from selective_state_space_02_amd import binding as ssm
+    from selective_state_space_02_amd import synth
+    f32 = torch.float32
+    s = 2 if w.dtype == "bf16" else 4
+    D, K = w.D, w.K
+    bias = synth.conv_bias(w, seed).to(dev)
+    out = torch.empty_like(c["x"])
+    dx = torch.empty_like(c["x"])
+    dW = torch.zeros((D, K), dtype=f32, device=dev)
+    db = torch.zeros((D,), dtype=f32, device=dev)
+    code = 1 if w.dtype == "bf16" else 0
+    ws = torch.empty(max(1, ssm.conv1d_causal_bwd_workspace_bytes(w.B, w.L, D, K, code)),
+                     dtype=torch.uint8, device=dev)
+
+    def run():
+        ssm.conv1d_causal_fwd(c["x"], c["W"], bias, act="silu", out=out)
+        ssm.conv1d_causal_bwd(c["x"], c["W"], c["dout"], bias=bias, act="silu", dx=dx, dW=dW,
+                              db=db, ws=ws)
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    he = HipEvents()
+    names = ("conv_fwd", "conv_bwd")
+    kev = {k: [he.pair() for _ in range(steps)] for k in names}
+    for i in range(steps):
+        for k in names:
+            ssm.ssm_set_kernel_timer(k, *kev[k][i])
+        run()
+    torch.cuda.synchronize()
+    for k in names:
+        ssm.ssm_set_kernel_timer(k, None, None)
+    ms = {k: sum(he.elapsed_ms(*pr) for pr in kev[k]) / steps for k in names}
+    he.destroy()
+    E = w.B * w.L * D
+    nbytes = {"conv_fwd": 2 * E * s + D * (K + 1) * 4, "conv_bwd": 3 * E * s + D * (K + 1) * 4}
+    extra = {"conv_fwd": 2 * E * s, "conv_bwd": 3 * E * s}
+    res = {}
+    for k in names:
+        gbps = nbytes[k] / (ms[k] * 1e-3) / 1e9
+        res[k + "_silu"] = {"kernel_ms": ms[k], "algorithmic_bytes": nbytes[k], "GBps": gbps,
+                            "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS,
+                            "unfused_extra_bytes": extra[k]}
+    return res
+
+
 # Sequences decoded together: a serving batch whose f32 state (1024 x 5120 x 16 x 4 B =
 # 335 MB on the 2.8B layer) exceeds the 256 MB Infinity Cache, so the scan step's rate
 # is an HBM rate (at 256 sequences the 84 MB state stays cache-resident across tokens).
@@ -400,6 +454,7 @@ def main():
 
     layer_fwd = measure_layer_forward(w, c, r, args.seed, K_, dev)
     decode = measure_decode(w, args.seed, K_, dev)
+    conv_silu = measure_conv_silu(w, c, args.seed, K_, dev)
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=f32, device=dev)
@@ -445,6 +500,7 @@ def main():
         },
     }
     out["layer_forward"] = layer_fwd
+    out["conv_silu"] = conv_silu
     out["decode"] = decode
     if not args.no_cpu_baseline:
         sample = args.cpu_sample_channels or max(16, min(w.D, 2048))

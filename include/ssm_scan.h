@@ -4,9 +4,9 @@
  * Operations on already-projected tensors:
  *   ssm_scan_fwd       selective-SSM scan, forward
  *   ssm_scan_bwd       its backward (backpropagation through time across the state)
- *   conv1d_causal_bwd  depthwise causal conv1d backward
+ *   conv1d_causal_bwd  depthwise causal conv1d backward (optionally through a SiLU)
  *   rmsnorm_bwd        batched RMSNorm backward
- *   conv1d_causal_fwd  depthwise causal conv1d forward
+ *   conv1d_causal_fwd  depthwise causal conv1d forward (optionally followed by SiLU)
  *   rmsnorm_fwd        batched RMSNorm forward (also returns the saved rms)
  *   ssm_scan_step      one-token decode step of the scan (state updated in place)
  *   conv1d_causal_step one-token decode step of the conv (window updated in place)
@@ -55,10 +55,15 @@ extern "C" {
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
 
+/* Activation applied to the conv output: none, or SiLU, silu(p) = p * sigmoid(p) (the
+ * activation the Mamba block puts between its conv and the scan; the mamba-rs
+ * backward_conv1d_step section takes its gradient after the SiLU backward). */
+typedef enum { SSM_ACT_NONE = 0, SSM_ACT_SILU = 1 } ssm_act_t;
+
 enum {
     SSM_OK = 0,
     SSM_ERR_ARG = -1,          /* null required pointer, size <= 0, size overflow */
-    SSM_ERR_UNSUPPORTED = -2,  /* N not in {4,8,16}, K not in [1,8], dtype, M too large */
+    SSM_ERR_UNSUPPORTED = -2,  /* N not in {4,8,16}, K not in [1,8], dtype, act, M too large */
     SSM_ERR_WORKSPACE = -3,    /* ws_bytes smaller than the query's answer */
     SSM_ERR_ALIGN = -4,        /* a tensor pointer is not 16-byte aligned */
     SSM_ERR_HIP = -5           /* the HIP runtime rejected a launch */
@@ -142,15 +147,19 @@ int ssm_scan_bwd(void *stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t 
  *     dx[b,s,d] = sum_k dout[b, s+K-1-k, d] * W[d,k]     (terms with s+K-1-k < L)
  *     dW[d,k]  += sum_{b,t} dout[b,t,d] * x[b, t-K+1+k, d]
  *     db[d]    += sum_{b,t} dout[b,t,d]
- * dout is the gradient of the conv output (taken after any activation backward).
+ With act = SSM_ACT_NONE, dout is the gradient of the conv output itself and bias is
+ * not read.  With act = SSM_ACT_SILU, dout is the gradient of u = silu(out), and the
+ * SiLU backward is fused: the kernel recomputes out (which is why bias is an input) and
+ * uses g = dout * sigmoid(out) * (1 + out * (1 - sigmoid(out))) in place of dout above.
  * Shapes: x, dout, dx [B,L,D] (dtype); W, dW [D,K] f32 (tap K-1 = newest input);
- * db [D] f32.  Supported: K in [1, 8].
+ * bias, db [D] f32; bias may be NULL (zero).  Supported: K in [1, 8].
  * ------------------------------------------------------------------------------- */
 size_t conv1d_causal_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t K,
                                          ssm_dtype_t dtype);
 int conv1d_causal_bwd(void *stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D,
-                      int64_t K, const void *x, const float *W, const void *dout, void *dx,
-                      float *dW, float *db, void *ws, size_t ws_bytes);
+                      int64_t K, const void *x, const float *W, const float *bias,
+                      ssm_act_t act, const void *dout, void *dx, float *dW, float *db,
+                      void *ws, size_t ws_bytes);
 
 /* ---------------------------------------------------------------------------------
  * Batched RMSNorm backward given the saved per-row rms (not its inverse), as the
@@ -173,11 +182,13 @@ int rmsnorm_bwd(void *stream, ssm_dtype_t dtype, int64_t R, int64_t M, const voi
  * of the mamba-rs backward_conv1d_step section holds the last K inputs, tap K-1 the
  * newest; the sequence starts from a zero window):
  *     out[b,t,d] = bias[d] + sum_{k<K} W[d,k] * x[b, t-K+1+k, d]   (x = 0 for t < 0)
+ * With act = SSM_ACT_SILU the stored value is silu(out[b,t,d]) instead.
  * Shapes: x, out [B,L,D] (dtype); W [D,K] f32; bias [D] f32 or NULL (zero).  No
  * workspace.  Supported: K in [1, 8].
  * ------------------------------------------------------------------------------- */
 int conv1d_causal_fwd(void *stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D,
-                      int64_t K, const void *x, const float *W, const float *bias, void *out);
+                      int64_t K, const void *x, const float *W, const float *bias,
+                      ssm_act_t act, void *out);
 
 /* ---------------------------------------------------------------------------------
  * Batched RMSNorm forward, the forward of rmsnorm_bwd above; it also writes the

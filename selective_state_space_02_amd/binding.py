@@ -72,13 +72,13 @@ def load():
     lib.conv1d_causal_bwd_workspace_bytes.restype = _S
     lib.conv1d_causal_bwd_workspace_bytes.argtypes = [_I] * 4 + [_E]
     lib.conv1d_causal_bwd.restype = _E
-    lib.conv1d_causal_bwd.argtypes = [_P, _E] + [_I] * 4 + [_P] * 6 + [_P, _S]
+    lib.conv1d_causal_bwd.argtypes = [_P, _E] + [_I] * 4 + [_P] * 3 + [_E] + [_P] * 4 + [_P, _S]
     lib.rmsnorm_bwd_workspace_bytes.restype = _S
     lib.rmsnorm_bwd_workspace_bytes.argtypes = [_I] * 2 + [_E]
     lib.rmsnorm_bwd.restype = _E
     lib.rmsnorm_bwd.argtypes = [_P, _E] + [_I] * 2 + [_P] * 6 + [_P, _S]
     lib.conv1d_causal_fwd.restype = _E
-    lib.conv1d_causal_fwd.argtypes = [_P, _E] + [_I] * 4 + [_P] * 4
+    lib.conv1d_causal_fwd.argtypes = [_P, _E] + [_I] * 4 + [_P] * 3 + [_E, _P]
     lib.rmsnorm_fwd.restype = _E
     lib.rmsnorm_fwd.argtypes = [_P, _E] + [_I] * 2 + [_P, _P, ctypes.c_float, _P, _P]
     lib.ssm_scan_step.restype = _E
@@ -250,9 +250,23 @@ def conv1d_causal_bwd_workspace_bytes(B, L, D, K, dtype_code) -> int:
     return int(load().conv1d_causal_bwd_workspace_bytes(B, L, D, K, dtype_code))
 
 
-def conv1d_causal_bwd(x, W, dout, dx=None, dW=None, db=None, ws=None):
-    """Returns dict dx (overwritten), dW, db (accumulated; zeros if not given)."""
+# activation after the conv (the C enum ssm_act_t)
+ACTS = {"none": 0, "silu": 1}
+
+
+def _act_code(act) -> int:
+    if act not in ACTS:
+        raise ValueError(f"activation {act!r} not supported (one of {sorted(ACTS)})")
+    return ACTS[act]
+
+
+def conv1d_causal_bwd(x, W, dout, bias=None, act="none", dx=None, dW=None, db=None, ws=None):
+    """Returns dict dx (overwritten), dW, db (accumulated; zeros if not given).
+
+    act="silu": dout is the gradient of silu(conv(x)); the SiLU backward runs in the
+    kernel, which recomputes the conv output from x, W and bias."""
     lib = load()
+    ac = _act_code(act)
     Bsz, L, D = x.shape
     K = W.shape[1]
     dev = x.device
@@ -262,7 +276,8 @@ def conv1d_causal_bwd(x, W, dout, dx=None, dW=None, db=None, ws=None):
     dx = torch.empty_like(x) if dx is None else dx
     dW = torch.zeros((D, K), dtype=f32, device=dev) if dW is None else dW
     db = torch.zeros((D,), dtype=f32, device=dev) if db is None else db
-    args = [_ptr(x, "x", dt, (Bsz, L, D), dev), _ptr(W, "W", f32, (D, K), dev),
+    bp = _ptr(bias, "bias", f32, (D,), dev) if bias is not None else None
+    args = [_ptr(x, "x", dt, (Bsz, L, D), dev), _ptr(W, "W", f32, (D, K), dev), bp, ac,
             _ptr(dout, "dout", dt, (Bsz, L, D), dev), _ptr(dx, "dx", dt, (Bsz, L, D), dev),
             _ptr(dW, "dW", f32, (D, K), dev), _ptr(db, "db", f32, (D,), dev)]
     need = conv1d_causal_bwd_workspace_bytes(Bsz, L, D, K, code)
@@ -296,9 +311,10 @@ def rmsnorm_bwd(dy, x, scale, rms, dx=None, dscale=None, ws=None):
     return dict(dx=dx, dscale=dscale)
 
 
-def conv1d_causal_fwd(x, W, bias=None, out=None):
-    """Returns out [B, L, D] (dtype of x)."""
+def conv1d_causal_fwd(x, W, bias=None, act="none", out=None):
+    """Returns out [B, L, D] (dtype of x); silu of the conv output when act="silu"."""
     lib = load()
+    ac = _act_code(act)
     Bsz, L, D = x.shape
     K = W.shape[1]
     dev = x.device
@@ -309,7 +325,7 @@ def conv1d_causal_fwd(x, W, bias=None, out=None):
     bp = _ptr(bias, "bias", f32, (D,), dev) if bias is not None else None
     _check(lib.conv1d_causal_fwd(_stream(dev), code, Bsz, L, D, K,
                                  _ptr(x, "x", dt, (Bsz, L, D), dev), _ptr(W, "W", f32, (D, K), dev),
-                                 bp, _ptr(out, "out", dt, (Bsz, L, D), dev)))
+                                 bp, ac, _ptr(out, "out", dt, (Bsz, L, D), dev)))
     return out
 
 

@@ -353,6 +353,20 @@ int ssm_scan_bwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t 
   return hip_status(ssm::launch_scan_bwd(a, p, st), "ssm_scan_bwd");
 }
 
+static int check_conv_dims(ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D, int64_t K,
+                           ssm_act_t act) {
+  if (B <= 0 || L <= 0 || D <= 0 || K <= 0)
+    return fail(SSM_ERR_ARG, "sizes must be positive (B=%lld L=%lld D=%lld K=%lld)",
+                (long long)B, (long long)L, (long long)D, (long long)K);
+  if (dtype != SSM_F32 && dtype != SSM_BF16)
+    return fail(SSM_ERR_UNSUPPORTED, "dtype %d not supported", int(dtype));
+  if (act != SSM_ACT_NONE && act != SSM_ACT_SILU)
+    return fail(SSM_ERR_UNSUPPORTED, "activation %d not supported (0 none, 1 SiLU)", int(act));
+  if (K > 8) return fail(SSM_ERR_UNSUPPORTED, "conv width K=%lld not supported (1..8)", (long long)K);
+  if (B > kMaxElems / L || B * L > kMaxElems / D) return fail(SSM_ERR_ARG, "tensor sizes overflow");
+  return SSM_OK;
+}
+
 size_t conv1d_causal_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t K,
                                          ssm_dtype_t dtype) {
   if (B <= 0 || L <= 0 || D <= 0 || K <= 0) return 0;
@@ -360,16 +374,13 @@ size_t conv1d_causal_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_
 }
 
 int conv1d_causal_bwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D,
-                      int64_t K, const void* x, const float* W, const void* dout, void* dx,
-                      float* dW, float* db, void* ws, size_t ws_bytes) {
-  if (B <= 0 || L <= 0 || D <= 0 || K <= 0)
-    return fail(SSM_ERR_ARG, "sizes must be positive (B=%lld L=%lld D=%lld K=%lld)",
-                (long long)B, (long long)L, (long long)D, (long long)K);
-  if (dtype != SSM_F32 && dtype != SSM_BF16)
-    return fail(SSM_ERR_UNSUPPORTED, "dtype %d not supported", int(dtype));
-  if (K > 8) return fail(SSM_ERR_UNSUPPORTED, "conv width K=%lld not supported (1..8)", (long long)K);
-  if (B > kMaxElems / L || B * L > kMaxElems / D) return fail(SSM_ERR_ARG, "tensor sizes overflow");
-  int rc = check_ptrs({{x, "x"}, {W, "W"}, {dout, "dout"}, {dx, "dx"}, {dW, "dW"}, {db, "db"}}, {});
+                      int64_t K, const void* x, const float* W, const float* bias,
+                      ssm_act_t act, const void* dout, void* dx, float* dW, float* db,
+                      void* ws, size_t ws_bytes) {
+  int rc = check_conv_dims(dtype, B, L, D, K, act);
+  if (rc) return rc;
+  rc = check_ptrs({{x, "x"}, {W, "W"}, {dout, "dout"}, {dx, "dx"}, {dW, "dW"}, {db, "db"}},
+                  {{bias, "bias"}});
   if (rc) return rc;
   ssm::ConvPlan p{};
   const size_t need = conv_ws(B, L, D, K, dtype, &p, nullptr);
@@ -378,21 +389,19 @@ int conv1d_causal_bwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int
   ssm::ConvArgs a{};
   a.dtype = int(dtype);
   a.B = B; a.L = L; a.D = D; a.K = K;
-  a.x = x; a.W = W; a.dout = dout; a.dx = dx; a.dW = dW; a.db = db;
+  a.act = int(act);
+  a.x = x; a.W = W; a.bias = act == SSM_ACT_SILU ? bias : nullptr;
+  a.dout = dout; a.dx = dx; a.dW = dW; a.db = db;
   return hip_status(ssm::launch_conv1d_bwd(a, p, static_cast<hipStream_t>(stream)),
                     "conv1d_causal_bwd");
 }
 
 int conv1d_causal_fwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D,
-                      int64_t K, const void* x, const float* W, const float* bias, void* out) {
-  if (B <= 0 || L <= 0 || D <= 0 || K <= 0)
-    return fail(SSM_ERR_ARG, "sizes must be positive (B=%lld L=%lld D=%lld K=%lld)",
-                (long long)B, (long long)L, (long long)D, (long long)K);
-  if (dtype != SSM_F32 && dtype != SSM_BF16)
-    return fail(SSM_ERR_UNSUPPORTED, "dtype %d not supported", int(dtype));
-  if (K > 8) return fail(SSM_ERR_UNSUPPORTED, "conv width K=%lld not supported (1..8)", (long long)K);
-  if (B > kMaxElems / L || B * L > kMaxElems / D) return fail(SSM_ERR_ARG, "tensor sizes overflow");
-  int rc = check_ptrs({{x, "x"}, {W, "W"}, {out, "out"}}, {{bias, "bias"}});
+                      int64_t K, const void* x, const float* W, const float* bias,
+                      ssm_act_t act, void* out) {
+  int rc = check_conv_dims(dtype, B, L, D, K, act);
+  if (rc) return rc;
+  rc = check_ptrs({{x, "x"}, {W, "W"}, {out, "out"}}, {{bias, "bias"}});
   if (rc) return rc;
   ssm::ConvPlan p{};
   conv_plan(B, L, D, K, &p);
@@ -400,6 +409,7 @@ int conv1d_causal_fwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int
   a.dtype = int(dtype);
   a.B = B; a.L = L; a.D = D; a.K = K;
   a.Tb = p.Tb; a.nTb = p.nTb;
+  a.act = int(act);
   a.x = x; a.W = W; a.bias = bias; a.out = out;
   return hip_status(ssm::launch_conv1d_fwd(a, static_cast<hipStream_t>(stream)),
                     "conv1d_causal_fwd");

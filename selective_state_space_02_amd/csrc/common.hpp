@@ -31,6 +31,14 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
   return __builtin_bit_cast(bf16_t, (__bf16)v);
 }
 
+// sigmoid(p) = 1 / (1 + exp(-p)) from the hardware exp2 and reciprocal (about one ulp
+// each); saturates to 0 and 1 in the tails.
+__device__ __forceinline__ float sigmoid_f(float p) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-p * kLog2e));
+}
+// Activation after the conv: 0 none, 1 SiLU (p * sigmoid(p)).
+constexpr int kActNone = 0, kActSilu = 1;
+
 // Two floats as packed bf16 (lo in bits 0-15), rounded to nearest even.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef float f2 __attribute__((ext_vector_type(2)));

@@ -1,8 +1,10 @@
 // Depthwise causal conv1d backward for gfx950.
 //
 // Forward (zero left padding):  out[b,t,d] = bias[d] + sum_k W[d,k] x[b, t-K+1+k, d].
-// Backward for upstream gradient g = dout (taken after the SiLU backward, as in the
-// mamba-rs backward_conv1d_step section):
+// Backward for upstream gradient g = dout of the conv output (the mamba-rs
+// backward_conv1d_step section takes it after the SiLU backward); with the SiLU fused
+// (act = SiLU), dout is the gradient of silu(out) and g = dout * silu'(out) is formed
+// here from the recomputed pre-activation:
 //   dx[b,s,d]  = sum_k g[b, s+K-1-k, d] W[d,k]          (terms with s+K-1-k < L)
 //   dW[d,k]   += sum_{b,t} g[b,t,d] x[b, t-K+1+k, d]
 //   db[d]     += sum_{b,t} g[b,t,d]
@@ -24,13 +26,17 @@
 
 namespace ssm {
 
-template <typename T, int K, int VEC>
+template <typename T, int K, int VEC, int ACT>
 __global__ __launch_bounds__(256) void k_conv_bwd(
     int64_t L, int64_t D, int64_t Tb, int64_t nTb, int64_t cgroups,
-    const T* __restrict__ x, const float* __restrict__ W, const T* __restrict__ g,
-    T* __restrict__ dx, float* __restrict__ dWp, float* __restrict__ dbp) {
+    const T* __restrict__ x, const float* __restrict__ W, const float* __restrict__ bias,
+    const T* __restrict__ g, T* __restrict__ dx, float* __restrict__ dWp,
+    float* __restrict__ dbp) {
   constexpr int R = (VEC > 1) ? 8 : 16;  // steps per group
-  constexpr int H = R + K - 1;           // rows loaded per group
+  constexpr int H = R + K - 1;           // upstream-gradient rows per group
+  // input rows per group: with the SiLU backward fused, the pre-activation of every
+  // gradient row is recomputed, which reaches K - 1 rows further
+  constexpr int HX = (ACT == kActSilu) ? H + K - 1 : H;
   constexpr int CW = 64 * VEC;           // channels per workgroup
   using BV = BufVec<T, VEC>;
   __shared__ float red[4][K + 1][CW];
@@ -49,10 +55,11 @@ __global__ __launch_bounds__(256) void k_conv_bwd(
   const T* gg = g + b * L * D + c0;
   T* dxg = dx + b * L * D + c0;
 
-  float w[VEC][K], dW[VEC][K], db[VEC];
+  float w[VEC][K], bs[VEC], dW[VEC][K], db[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) {
     db[v] = 0.f;
+    bs[v] = bias ? bias[c0 + lc + v] : 0.f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       w[v][k] = W[(c0 + lc + v) * K + k];
@@ -66,34 +73,53 @@ __global__ __launch_bounds__(256) void k_conv_bwd(
     // descriptor per tensor starting at the group's first valid row; rows are scalar
     // offsets from it, lanes vector offsets.
     const int64_t x0 = (ts - (K - 1) < 0) ? 0 : ts - (K - 1);
-    const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xg + x0 * D, uint32_t(H) * rowb);
+    const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xg + x0 * D, uint32_t(HX) * rowb);
     const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gg + ts * D, uint32_t(H) * rowb);
-    typename BV::raw_t xraw[H], graw[H];
+    typename BV::raw_t xraw[HX], graw[H];
 #pragma unroll
-    for (int i = 0; i < H; ++i) {
-      const int64_t tx = ts - (K - 1) + i, tg = ts + i;
+    for (int i = 0; i < HX; ++i) {
+      const int64_t tx = ts - (K - 1) + i;
       xraw[i] = (tx >= 0 && tx < L) ? BV::load(rx, loff, uint32_t(tx - x0) * rowb)
                                     : typename BV::raw_t{};
-      graw[i] = (tg < L) ? BV::load(rg, loff, uint32_t(i) * rowb) : typename BV::raw_t{};
+    }
+#pragma unroll
+    for (int i = 0; i < H; ++i)
+      graw[i] = (ts + i < L) ? BV::load(rg, loff, uint32_t(i) * rowb) : typename BV::raw_t{};
+    // the conv output's gradient of every row the group touches; with SiLU fused, the
+    // upstream value times silu'(pre), pre = bias + sum_k W x recomputed from the inputs
+    float gf[H][VEC];
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+      BV::unpack(graw[i], gf[i]);
+      if constexpr (ACT == kActSilu) {
+        float xw[K][VEC];
+#pragma unroll
+        for (int k = 0; k < K; ++k) BV::unpack(xraw[i + k], xw[k]);  // x[ts + i - K+1+k]
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          float pre = bs[v];
+#pragma unroll
+          for (int k = 0; k < K; ++k) pre = __builtin_fmaf(w[v][k], xw[k][v], pre);
+          const float sg = sigmoid_f(pre);
+          gf[i][v] *= sg * __builtin_fmaf(pre, 1.f - sg, 1.f);
+        }
+      }
     }
     const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dxg + ts * D, uint32_t(R) * rowb);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t t = ts + r;
       if (t < t1) {
-        float gv[K][VEC], xv[K][VEC], o[VEC];
+        float xv[K][VEC], o[VEC];
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-          BV::unpack(graw[r + K - 1 - k], gv[k]);  // g[t + K-1-k]
-          BV::unpack(xraw[r + k], xv[k]);          // x[t - K+1+k]
-        }
+        for (int k = 0; k < K; ++k) BV::unpack(xraw[r + k], xv[k]);  // x[t - K+1+k]
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
           float acc = 0.f;
 #pragma unroll
-          for (int k = 0; k < K; ++k) acc = __builtin_fmaf(gv[k][v], w[v][k], acc);
+          for (int k = 0; k < K; ++k) acc = __builtin_fmaf(gf[r + K - 1 - k][v], w[v][k], acc);
           o[v] = acc;
-          const float gt = gv[K - 1][v];  // g[t]
+          const float gt = gf[r][v];  // g[t]
           db[v] += gt;
 #pragma unroll
           for (int k = 0; k < K; ++k) dW[v][k] = __builtin_fmaf(gt, xv[k][v], dW[v][k]);
@@ -126,8 +152,8 @@ __global__ __launch_bounds__(256) void k_conv_bwd(
 }
 
 // lanes' channel count: 4 (2 for widths above 4, bounding registers) when D allows
-template <typename T, int K>
-static hipError_t conv_k(const ConvArgs& a, const ConvPlan& p, hipStream_t st) {
+template <typename T, int K, int ACT>
+static hipError_t conv_ka(const ConvArgs& a, const ConvPlan& p, hipStream_t st) {
   const T* x = static_cast<const T*>(a.x);
   const T* g = static_cast<const T*>(a.dout);
   T* dx = static_cast<T*>(a.dx);
@@ -137,17 +163,22 @@ static hipError_t conv_k(const ConvArgs& a, const ConvPlan& p, hipStream_t st) {
   const dim3 grid(unsigned(cgroups * a.B * p.nTb));
   timer_mark(kKConvBwd, false, st);
   if (vec == VW)
-    hipLaunchKernelGGL((k_conv_bwd<T, K, VW>), grid, dim3(256), 0, st, a.L, a.D, p.Tb, p.nTb,
-                       cgroups, x, a.W, g, dx, p.dWp, p.dbp);
+    hipLaunchKernelGGL((k_conv_bwd<T, K, VW, ACT>), grid, dim3(256), 0, st, a.L, a.D, p.Tb,
+                       p.nTb, cgroups, x, a.W, a.bias, g, dx, p.dWp, p.dbp);
   else
-    hipLaunchKernelGGL((k_conv_bwd<T, K, 1>), grid, dim3(256), 0, st, a.L, a.D, p.Tb, p.nTb,
-                       cgroups, x, a.W, g, dx, p.dWp, p.dbp);
+    hipLaunchKernelGGL((k_conv_bwd<T, K, 1, ACT>), grid, dim3(256), 0, st, a.L, a.D, p.Tb,
+                       p.nTb, cgroups, x, a.W, a.bias, g, dx, p.dWp, p.dbp);
   timer_mark(kKConvBwd, true, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t P = a.B * p.nTb;
   if ((e = launch_reduce(p.dWp, P, a.D * a.K, a.dW, true, p.rtmp, st)) != hipSuccess) return e;
   return launch_reduce(p.dbp, P, a.D, a.db, true, p.rtmp, st);
+}
+
+template <typename T, int K>
+static hipError_t conv_k(const ConvArgs& a, const ConvPlan& p, hipStream_t st) {
+  return a.act == kActSilu ? conv_ka<T, K, kActSilu>(a, p, st) : conv_ka<T, K, kActNone>(a, p, st);
 }
 
 template <typename T>

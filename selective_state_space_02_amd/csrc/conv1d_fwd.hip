@@ -1,7 +1,9 @@
 // Depthwise causal conv1d forward for gfx950 (zero left padding):
 //   out[b,t,d] = bias[d] + sum_k W[d,k] x[b, t-K+1+k, d]
 // the forward whose per-timestep backward the mamba-rs backward_conv1d_step section
-// gives (its window holds the last K inputs, tap K-1 the newest).
+// gives (its window holds the last K inputs, tap K-1 the newest).  With act = SiLU the
+// kernel stores silu(out) = out * sigmoid(out), the activation the Mamba block applies
+// to the conv output before the scan.
 //
 // Mapping as in the backward (conv1d_bwd.hip): a lane owns VEC consecutive channels, a
 // workgroup 64*VEC channels and a block of Tb steps taken by its four wavefronts in
@@ -14,7 +16,7 @@
 
 namespace ssm {
 
-template <typename T, int K, int VEC>
+template <typename T, int K, int VEC, int ACT>
 __global__ __launch_bounds__(256) void k_conv_fwd(int64_t L, int64_t D, int64_t Tb, int64_t nTb,
                                                   int64_t cgroups, const T* __restrict__ x,
                                                   const float* __restrict__ W,
@@ -70,6 +72,7 @@ __global__ __launch_bounds__(256) void k_conv_fwd(int64_t L, int64_t D, int64_t 
           float acc = bs[v];
 #pragma unroll
           for (int k = 0; k < K; ++k) acc = __builtin_fmaf(w[v][k], xv[k][v], acc);
+          if constexpr (ACT == kActSilu) acc *= sigmoid_f(acc);
           o[v] = acc;
         }
         if (act) BV::store(BV::pack(o), ro, loff, uint32_t(r) * rowb);
@@ -78,8 +81,8 @@ __global__ __launch_bounds__(256) void k_conv_fwd(int64_t L, int64_t D, int64_t 
   }
 }
 
-template <typename T, int K>
-static hipError_t conv_fwd_k(const ConvFwdArgs& a, hipStream_t st) {
+template <typename T, int K, int ACT>
+static hipError_t conv_fwd_ka(const ConvFwdArgs& a, hipStream_t st) {
   constexpr int VW = (K <= 4) ? 4 : 2;
   const int vec = (a.D % 4 == 0) ? VW : 1;
   const int64_t cgroups = (a.D + 64 * vec - 1) / (64 * vec);
@@ -88,13 +91,19 @@ static hipError_t conv_fwd_k(const ConvFwdArgs& a, hipStream_t st) {
   T* out = static_cast<T*>(a.out);
   timer_mark(kKConvFwd, false, st);
   if (vec == VW)
-    hipLaunchKernelGGL((k_conv_fwd<T, K, VW>), grid, dim3(256), 0, st, a.L, a.D, a.Tb, a.nTb,
-                       cgroups, x, a.W, a.bias, out);
+    hipLaunchKernelGGL((k_conv_fwd<T, K, VW, ACT>), grid, dim3(256), 0, st, a.L, a.D, a.Tb,
+                       a.nTb, cgroups, x, a.W, a.bias, out);
   else
-    hipLaunchKernelGGL((k_conv_fwd<T, K, 1>), grid, dim3(256), 0, st, a.L, a.D, a.Tb, a.nTb,
-                       cgroups, x, a.W, a.bias, out);
+    hipLaunchKernelGGL((k_conv_fwd<T, K, 1, ACT>), grid, dim3(256), 0, st, a.L, a.D, a.Tb,
+                       a.nTb, cgroups, x, a.W, a.bias, out);
   timer_mark(kKConvFwd, true, st);
   return hipGetLastError();
+}
+
+template <typename T, int K>
+static hipError_t conv_fwd_k(const ConvFwdArgs& a, hipStream_t st) {
+  return a.act == kActSilu ? conv_fwd_ka<T, K, kActSilu>(a, st)
+                           : conv_fwd_ka<T, K, kActNone>(a, st);
 }
 
 template <typename T>

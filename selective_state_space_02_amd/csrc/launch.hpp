@@ -74,8 +74,10 @@ struct BwdPlan {
 struct ConvArgs {
   int dtype;
   int64_t B, L, D, K;
+  int act;             // kActNone or kActSilu (dout is then the gradient of silu(conv))
   const void* x;
   const float* W;
+  const float* bias;   // nullable; read only with act = kActSilu
   const void* dout;
   void* dx;
   float* dW;
@@ -136,6 +138,7 @@ struct ConvFwdArgs {
   int dtype;
   int64_t B, L, D, K;
   int64_t Tb, nTb;  // time blocks, as ConvPlan
+  int act;          // kActNone or kActSilu (out = silu(conv))
   const void* x;
   const float* W;
   const float* bias;  // nullable

@@ -150,9 +150,10 @@ def test_workspace_queries_are_consistent():
     assert b.ssm_scan_fwd_workspace_bytes(1, 1, 1, 4, 0) == 0
 
 
-def _conv(lib, B=2, L=64, D=32, K=4, dtype=0, x=FAKE, W=FAKE, dout=FAKE, dx=FAKE, dW=FAKE,
-          db=FAKE, ws=None, ws_bytes=0):
-    return lib.conv1d_causal_bwd(None, dtype, B, L, D, K, x, W, dout, dx, dW, db, ws, ws_bytes)
+def _conv(lib, B=2, L=64, D=32, K=4, dtype=0, x=FAKE, W=FAKE, bias=None, act=0, dout=FAKE,
+          dx=FAKE, dW=FAKE, db=FAKE, ws=None, ws_bytes=0):
+    return lib.conv1d_causal_bwd(None, dtype, B, L, D, K, x, W, bias, act, dout, dx, dW, db,
+                                 ws, ws_bytes)
 
 
 def test_conv_validation():
@@ -161,6 +162,10 @@ def test_conv_validation():
     assert _conv(lib, K=9) == b.SSM_ERR_UNSUPPORTED
     assert _conv(lib, L=0) == b.SSM_ERR_ARG
     assert _conv(lib, dtype=5) == b.SSM_ERR_UNSUPPORTED
+    assert _conv(lib, act=2) == b.SSM_ERR_UNSUPPORTED
+    assert "activation" in b.last_error()
+    assert _conv(lib, act=-1) == b.SSM_ERR_UNSUPPORTED
+    assert _conv(lib, act=1, bias=MIS) == b.SSM_ERR_ALIGN    # optional, but aligned if given
     for name in ("x", "W", "dout", "dx", "dW", "db"):
         assert _conv(lib, **{name: None}) == b.SSM_ERR_ARG
         assert name in b.last_error()
@@ -193,8 +198,8 @@ def test_rms_validation():
     assert b.rmsnorm_bwd_workspace_bytes(10, 8193, 1) == 0
 
 
-def _conv_fwd(lib, B=2, L=64, D=32, K=4, dtype=0, x=FAKE, W=FAKE, bias=None, out=FAKE):
-    return lib.conv1d_causal_fwd(None, dtype, B, L, D, K, x, W, bias, out)
+def _conv_fwd(lib, B=2, L=64, D=32, K=4, dtype=0, x=FAKE, W=FAKE, bias=None, act=0, out=FAKE):
+    return lib.conv1d_causal_fwd(None, dtype, B, L, D, K, x, W, bias, act, out)
 
 
 def test_conv_fwd_validation():
@@ -203,6 +208,7 @@ def test_conv_fwd_validation():
     assert _conv_fwd(lib, K=9) == b.SSM_ERR_UNSUPPORTED
     assert _conv_fwd(lib, B=0) == b.SSM_ERR_ARG
     assert _conv_fwd(lib, dtype=2) == b.SSM_ERR_UNSUPPORTED
+    assert _conv_fwd(lib, act=3) == b.SSM_ERR_UNSUPPORTED
     for name in ("x", "W", "out"):
         assert _conv_fwd(lib, **{name: None}) == b.SSM_ERR_ARG
         assert name in b.last_error()
@@ -285,6 +291,10 @@ def test_binding_rejects_cpu_and_strided_tensors():
         pass
     with pytest.raises(TypeError):
         b._ptr(FakeCuda(), "x")
+    # activations are named; an unknown one is rejected before any pointer is formed
+    assert b._act_code("none") == 0 and b._act_code("silu") == 1
+    with pytest.raises(ValueError, match="activation"):
+        b._act_code("gelu")
 
 
 def test_product_path_fails_loudly_without_library(monkeypatch):
