@@ -222,3 +222,57 @@ def silu_grad(p, dout):
 
 def softplus(z):
     return _elementwise("oracle_softplus", z)
+
+
+# ----------------------------------------------------------------------------------
+# the scan with its neighbours (Mamba block): time-step activation and output gate
+# ----------------------------------------------------------------------------------
+
+def _pre_delta(delta_raw, delta_bias):
+    pre = _f64(delta_raw)
+    if delta_bias is not None:
+        pre = pre + _f64(delta_bias)[None, None, :]
+    return pre
+
+
+def scan_fused_fwd(x, delta_raw, A, Bm, Cm, Dv, h0=None, delta_bias=None,
+                   delta_softplus=False, z=None):
+    """The scan between its neighbours in the Mamba block, step by step:
+      1. time step: pre = delta_raw + delta_bias[d];  delta = softplus(pre) when
+         delta_softplus, else pre (dt_proj's output and bias, made positive);
+      2. the selective scan with that delta (scan_fwd);
+      3. output gate: out = y * silu(z) when z is given, else out = y.
+    Returns dict out, y (before the gate), h_last, delta (the scan's time step)."""
+    pre = _pre_delta(delta_raw, delta_bias)
+    delta = softplus(pre) if delta_softplus else pre
+    y, h_last = scan_fwd(x, delta, A, Bm, Cm, Dv, h0)
+    out = y * silu(z) if z is not None else y
+    return dict(out=out, y=y, h_last=h_last, delta=delta)
+
+
+def scan_fused_bwd(x, delta_raw, A, Bm, Cm, Dv, dout, h0=None, delta_bias=None,
+                   delta_softplus=False, z=None):
+    """Gradients of scan_fused_fwd's out for upstream dout, by the chain rule through its
+    three steps in reverse:
+      3. gate:  dy = dout * silu(z),  dz = (dout * y) * silu'(z)   (y recomputed);
+      2. scan:  scan_bwd with dy, giving the gradient d(delta) of the scan's time step;
+      1. time step: ddelta = d(delta) * sigmoid(pre) when delta_softplus (softplus' is
+         the sigmoid), else d(delta); d(delta_bias)[d] = sum over batch and time of it.
+    Returns dict dx, ddelta (with respect to delta_raw), dA, dB, dC, dD, dh0, dz (None
+    without z), ddelta_bias."""
+    pre = _pre_delta(delta_raw, delta_bias)
+    delta = softplus(pre) if delta_softplus else pre
+    dout = _f64(dout)
+    dz = None
+    if z is not None:
+        y, _ = scan_fwd(x, delta, A, Bm, Cm, Dv, h0)
+        dy = dout * silu(z)
+        dz = silu_grad(z, dout * y)
+    else:
+        dy = dout
+    r = scan_bwd(x, delta, A, Bm, Cm, Dv, dy, h0)
+    if delta_softplus:
+        r["ddelta"] = r["ddelta"] * sigmoid(pre)
+    r["ddelta_bias"] = r["ddelta"].sum(axis=(0, 1))
+    r["dz"] = dz
+    return r

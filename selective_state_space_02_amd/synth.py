@@ -20,7 +20,8 @@ import torch
 from .workloads import Workload
 
 # tensor ids (fixed order)
-_X, _DELTA, _B, _C, _DV, _DY, _CX, _CW, _CDOUT, _RX, _RDY, _RSCALE, _H0, _CBIAS = range(1, 15)
+(_X, _DELTA, _B, _C, _DV, _DY, _CX, _CW, _CDOUT, _RX, _RDY, _RSCALE, _H0, _CBIAS, _DRAW, _DBIAS,
+ _Z) = range(1, 18)
 
 RMS_EPS = 1e-5  # the RMSNorm eps of every workload
 
@@ -64,6 +65,22 @@ def scan_inputs(w: Workload, seed: int = 0, with_h0: bool = False) -> dict:
     out = dict(x=x, delta=delta, A=_param(A, w), Bm=Bm, Cm=Cm, Dv=Dv, dy=dy)
     if with_h0:
         out["h0"] = _normal((B, D, N), seed, _H0).contiguous()
+    return out
+
+
+def scan_fused_inputs(w: Workload, seed: int = 0, with_h0: bool = False) -> dict:
+    """scan_inputs without delta, plus the inputs of the scan's neighbours in the Mamba
+    block: delta_raw [B,L,D] ~ N(0, 1) (the time-step projection's output), delta_bias
+    [D] ~ U(-6.9, -2.25) (the bias range that a time step of 1e-3 .. 1e-1 through a
+    softplus gives), and the gate input z [B,L,D] ~ N(0, 1).  dy is the upstream gradient
+    of the gated output."""
+    sd = _store_dtype(w)
+    out = scan_inputs(w, seed, with_h0)
+    del out["delta"]
+    out["delta_raw"] = _normal((w.B, w.L, w.D), seed, _DRAW).to(sd)
+    bias = torch.rand((w.D,), generator=_gen(seed, _DBIAS), dtype=torch.float32)
+    out["delta_bias"] = _param(bias * (6.9 - 2.25) - 6.9, w)
+    out["z"] = _normal((w.B, w.L, w.D), seed, _Z).to(sd)
     return out
 
 

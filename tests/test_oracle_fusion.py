@@ -70,3 +70,88 @@ def test_conv_silu_composition_matches_central_differences(K):
     assert rel_err(r["dx"], fx) < 1e-7
     assert rel_err(r["dW"], fW) < 1e-7
     assert rel_err(r["db"], fb) < 1e-7
+
+
+# ----------------------------------------------------------------------------------
+# the scan between its neighbours: time-step activation and output gate
+# ----------------------------------------------------------------------------------
+
+FUSED_CONFIGS = [dict(delta_softplus=True, bias=True, z=True),
+                 dict(delta_softplus=True, bias=False, z=True),
+                 dict(delta_softplus=False, bias=True, z=False),
+                 dict(delta_softplus=True, bias=True, z=False)]
+
+
+def _fused_inputs(cfg, seed=3):
+    w = custom(B=2, L=6, D=3, N=4)
+    p = {k: synth.as_f64(v) for k, v in synth.scan_fused_inputs(w, seed, with_h0=True).items()}
+    if not cfg["delta_softplus"]:   # keep the time step positive without the softplus
+        p["delta_raw"] = 0.5 * np.abs(p["delta_raw"])
+        p["delta_bias"] = 0.05 * np.abs(p["delta_bias"])
+    if not cfg["bias"]:
+        p["delta_bias"] = None
+    if not cfg["z"]:
+        p["z"] = None
+    return p
+
+
+def _fused_kw(p, cfg):
+    return dict(h0=p["h0"], delta_bias=p["delta_bias"], delta_softplus=cfg["delta_softplus"],
+                z=p["z"])
+
+
+@pytest.mark.parametrize("cfg", FUSED_CONFIGS, ids=lambda c: "-".join(k for k, v in c.items() if v) or "none")
+def test_scan_fused_gradients_match_central_differences(cfg):
+    p = _fused_inputs(cfg)
+    names = ["x", "delta_raw", "A", "Bm", "Cm", "Dv"]
+    dout = p["dy"]
+    r = oracle.scan_fused_bwd(*[p[k] for k in names], dout, **_fused_kw(p, cfg))
+
+    def loss_of(key):
+        def f(t):
+            q = dict(p)
+            q[key] = t
+            o = oracle.scan_fused_fwd(*[q[k] for k in names], **_fused_kw(q, cfg))["out"]
+            return float(np.sum(dout * o))
+        return f
+
+    grads = {"x": "dx", "delta_raw": "ddelta", "A": "dA", "Bm": "dB", "Cm": "dC", "Dv": "dD",
+             "h0": "dh0"}
+    if cfg["z"]:
+        grads["z"] = "dz"
+    if cfg["bias"]:
+        grads["delta_bias"] = "ddelta_bias"
+    for key, gk in grads.items():
+        fd = fd_grad(loss_of(key), p[key])
+        e = rel_err(r[gk], fd)
+        assert e < 1e-7, (key, e)
+    if not cfg["z"]:
+        assert r["dz"] is None
+
+
+def test_scan_fused_without_neighbours_is_the_plain_scan():
+    w = custom(B=2, L=9, D=4, N=8)
+    p = {k: synth.as_f64(v) for k, v in synth.scan_inputs(w, 1, with_h0=True).items()}
+    args = [p[k] for k in ("x", "delta", "A", "Bm", "Cm", "Dv")]
+    f = oracle.scan_fused_fwd(*args, h0=p["h0"])
+    y, hl = oracle.scan_fwd(*args, h0=p["h0"])
+    assert np.array_equal(f["out"], y) and np.array_equal(f["y"], y)
+    assert np.array_equal(f["h_last"], hl)
+    rf = oracle.scan_fused_bwd(*args, p["dy"], h0=p["h0"])
+    rp = oracle.scan_bwd(*args, p["dy"], h0=p["h0"])
+    for k in rp:
+        assert np.array_equal(rf[k], rp[k]), k
+    assert np.array_equal(rf["ddelta_bias"], rp["ddelta"].sum(axis=(0, 1)))
+
+
+def test_scan_fused_time_step_is_positive_and_gate_vanishes_at_zero():
+    cfg = FUSED_CONFIGS[0]
+    p = _fused_inputs(cfg)
+    f = oracle.scan_fused_fwd(p["x"], p["delta_raw"], p["A"], p["Bm"], p["Cm"], p["Dv"],
+                              **_fused_kw(p, cfg))
+    assert np.all(f["delta"] > 0)
+    # silu(0) = 0 closes the gate; z large opens it (silu(z) -> z)
+    zero = oracle.scan_fused_fwd(p["x"], p["delta_raw"], p["A"], p["Bm"], p["Cm"], p["Dv"],
+                                 h0=p["h0"], delta_bias=p["delta_bias"], delta_softplus=True,
+                                 z=np.zeros_like(p["z"]))
+    assert np.all(zero["out"] == 0.0)
