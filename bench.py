@@ -268,6 +268,77 @@ def measure_conv_silu(w, c, seed, steps, dev):
     return res
 
 
+def measure_scan_fused(w, seed, steps, dev):
+    """The scan with its Mamba-block neighbours fused in (ssm_scan_fused_fwd/bwd: time
+    step softplus(delta + bias), output gate y * silu(z)) on the workload's shapes, each
+    call timed with events on the stream it is launched on, over `steps` calls.  Not part
+    of the step and not in `value`.  The fused calls move the plain scan's bytes plus the
+    gate's (z read by the forward, the backward's summary and main passes; y before the
+    gate written and read back; dz written).  Separate elementwise passes around the plain
+    scan would instead move `unfused_extra_bytes` (forward: softplus read+write, gate two
+    reads + write; backward: gate backward three reads + two writes, softplus backward two
+    reads + write, bias sum one read), whose time at the HBM peak is a lower bound on what
+    they would cost."""
+    import torch
+    from selective_state_space_02_amd import binding as ssm
+    from selective_state_space_02_amd import synth
+    f32 = torch.float32
+    code = ssm.SSM_BF16 if w.dtype == "bf16" else ssm.SSM_F32
+    B, L, D, N = w.B, w.L, w.D, w.N
+    g = {k: v.to(dev) for k, v in synth.scan_fused_inputs(w, seed).items()}
+    out = torch.empty_like(g["x"])
+    ysave = torch.empty_like(g["x"])
+    ckpt = ssm.new_ckpt(B, L, D, N, dev)
+    ws_f = torch.empty(max(1, ssm.ssm_scan_fwd_workspace_bytes(B, L, D, N, code)), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(1, ssm.ssm_scan_bwd_workspace_bytes(B, L, D, N, code, True)), dtype=torch.uint8, device=dev)
+    grads = dict(dx=torch.empty_like(g["x"]), ddelta=torch.empty_like(g["x"]),
+                 dA=torch.zeros((D, N), dtype=f32, device=dev),
+                 dB=torch.empty((B, L, N), dtype=f32, device=dev),
+                 dC=torch.empty((B, L, N), dtype=f32, device=dev),
+                 dD=torch.zeros((D,), dtype=f32, device=dev), dz=torch.empty_like(g["x"]),
+                 ddelta_bias=torch.zeros((D,), dtype=f32, device=dev))
+    kw = dict(delta_bias=g["delta_bias"], delta_softplus=True, z=g["z"])
+    args = (g["x"], g["delta_raw"], g["A"], g["Bm"], g["Cm"], g["Dv"])
+
+    def fwd():
+        ssm.ssm_scan_fused_fwd(*args, out=out, y_save=ysave, ckpt=ckpt, ws=ws_f, **kw)
+
+    def bwd():
+        ssm.ssm_scan_fused_bwd(*args, g["dy"], ckpt=ckpt, y_save=ysave, ws=ws_b, **kw, **grads)
+    for _ in range(2):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    he = HipEvents()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ev = {k: [he.pair() for _ in range(steps)] for k in ("fused_fwd", "fused_bwd")}
+    knames = ("fwd_summary", "fwd_output", "bwd_summary", "bwd_main")
+    kev = {k: [he.pair() for _ in range(steps)] for k in knames}
+    for i in range(steps):
+        for k in knames:
+            ssm.ssm_set_kernel_timer(k, *kev[k][i])
+        for k, f in (("fused_fwd", fwd), ("fused_bwd", bwd)):
+            he.record(ev[k][i][0], stream)
+            f()
+            he.record(ev[k][i][1], stream)
+    torch.cuda.synchronize()
+    for k in knames:
+        ssm.ssm_set_kernel_timer(k, None, None)
+    ms = {k: sum(he.elapsed_ms(*pr) for pr in ev[k]) / steps for k in ev}
+    kms = {}
+    for k in knames:
+        vals = [he.elapsed_ms(*pr) for pr in kev[k]]
+        kms[k] = None if any(v is None for v in vals) else sum(vals) / steps
+    he.destroy()
+    s = 2 if w.dtype == "bf16" else 4
+    E = B * L * D * s
+    extra = 2 * E + 3 * E + (5 * E + 3 * E + E)
+    return {"call_ms": ms, "kernel_ms": kms,
+            "tokens_channels_per_s": B * L * D / ((ms["fused_fwd"] + ms["fused_bwd"]) * 1e-3),
+            "fused_extra_bytes": 6 * E, "unfused_extra_bytes": extra,
+            "unfused_extra_ms_at_hbm_peak": extra / (HBM_PEAK_GBPS * 1e9) * 1e3}
+
+
 # Sequences decoded together: a serving batch whose f32 state (1024 x 5120 x 16 x 4 B =
 # 335 MB on the 2.8B layer) exceeds the 256 MB Infinity Cache, so the scan step's rate
 # is an HBM rate (at 256 sequences the 84 MB state stays cache-resident across tokens).
@@ -455,6 +526,9 @@ def main():
     layer_fwd = measure_layer_forward(w, c, r, args.seed, K_, dev)
     decode = measure_decode(w, args.seed, K_, dev)
     conv_silu = measure_conv_silu(w, c, args.seed, K_, dev)
+    scan_fused = measure_scan_fused(w, args.seed, K_, dev)
+    scan_fused["overhead_vs_plain_ms"] = (scan_fused["call_ms"]["fused_fwd"] +
+                                          scan_fused["call_ms"]["fused_bwd"] - scan_ms)
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=f32, device=dev)
@@ -501,6 +575,7 @@ def main():
     }
     out["layer_forward"] = layer_fwd
     out["conv_silu"] = conv_silu
+    out["scan_fused"] = scan_fused
     out["decode"] = decode
     if not args.no_cpu_baseline:
         sample = args.cpu_sample_channels or max(16, min(w.D, 2048))

@@ -4,6 +4,9 @@
  * Operations on already-projected tensors:
  *   ssm_scan_fwd       selective-SSM scan, forward
  *   ssm_scan_bwd       its backward (backpropagation through time across the state)
+ *   ssm_scan_fused_fwd / ssm_scan_fused_bwd
+ *                      the scan with its Mamba-block neighbours fused in: time-step
+ *                      bias and softplus, output gate y * silu(z)
  *   conv1d_causal_bwd  depthwise causal conv1d backward (optionally through a SiLU)
  *   rmsnorm_bwd        batched RMSNorm backward
  *   conv1d_causal_fwd  depthwise causal conv1d forward (optionally followed by SiLU)
@@ -137,6 +140,44 @@ int ssm_scan_bwd(void *stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t 
                  const void *Bm, const void *Cm, const float *Dv, const float *h0,
                  const void *dy, const float *ckpt, void *dx, void *ddelta, float *dA,
                  float *dB, float *dC, float *dD, float *dh0, void *ws, size_t ws_bytes);
+
+/* ---------------------------------------------------------------------------------
+ * The scan between its neighbours in the Mamba block, fused into the scan's kernels.
+ * The pages name the time-step projection's gradient (dt_proj, rustytorch backward_cuda
+ * commit) and the SiLU that precedes the scan's input (mamba-rs backward_conv1d_step
+ * section); the time step's activation and the output gate are not written out there and
+ * are taken as in Mamba: the time step is the projection's output plus a per-channel bias
+ * through a softplus, and the scan output is gated by SiLU of a second branch z.
+ *     pre[b,t,d]   = delta[b,t,d] + delta_bias[d]        (delta_bias NULL: zero)
+ *     dt[b,t,d]    = delta_softplus ? softplus(pre) : pre,  softplus(p) = log(1 + e^p)
+ *     y            = the scan of ssm_scan_fwd with time step dt
+ *     out[b,t,d]   = z ? y[b,t,d] * silu(z[b,t,d]) : y[b,t,d],  silu(p) = p * sigmoid(p)
+ * Forward: y_save (optional, only with z) receives y before the gate, which the backward
+ * with z needs; ckpt and h_last as in ssm_scan_fwd (the state runs on dt).
+ * Backward, for upstream gradient dout of out (chain rule through the three steps):
+ *     dz      = dout * y_save * silu'(z)                    (with z; dz overwritten)
+ *     dy      = z ? dout * silu(z) : dout, the scan's upstream gradient
+ *     ddelta  = d(dt) * (delta_softplus ? sigmoid(pre) : 1), the gradient of delta
+ *     ddelta_bias[d] += sum_{b,t} ddelta[b,t,d]            (optional, accumulated)
+ * and dx, dA, dB, dC, dD, dh0 as ssm_scan_bwd gives them for dt and dy.  With z, y_save
+ * and dz are required; without z they must be NULL.  delta_softplus is 0 or 1.
+ * Shapes and dtypes as the plain scan; z, y_save, out, dz [B,L,D] (dtype); delta_bias,
+ * ddelta_bias [D] f32.  Workspace: ssm_scan_fwd_workspace_bytes /
+ * ssm_scan_bwd_workspace_bytes with the same arguments.  Numerics: softplus and sigmoid
+ * in f32 from the hardware exp2 and log2 (a few ulp); rows past L are zero steps.
+ * ------------------------------------------------------------------------------- */
+int ssm_scan_fused_fwd(void *stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D,
+                       int64_t N, const void *x, const void *delta, const float *A,
+                       const void *Bm, const void *Cm, const float *Dv, const float *h0,
+                       const float *delta_bias, int delta_softplus, const void *z, void *out,
+                       void *y_save, float *ckpt, float *h_last, void *ws, size_t ws_bytes);
+int ssm_scan_fused_bwd(void *stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D,
+                       int64_t N, const void *x, const void *delta, const float *A,
+                       const void *Bm, const void *Cm, const float *Dv, const float *h0,
+                       const float *delta_bias, int delta_softplus, const void *z,
+                       const void *y_save, const void *dout, const float *ckpt, void *dx,
+                       void *ddelta, float *dA, float *dB, float *dC, float *dD, float *dh0,
+                       void *dz, float *ddelta_bias, void *ws, size_t ws_bytes);
 
 /* ---------------------------------------------------------------------------------
  * Depthwise causal conv1d backward.  The mamba-rs 0.5.1 backward_ops.rs section

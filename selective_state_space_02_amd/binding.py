@@ -24,7 +24,7 @@ EXPORTS = ("ssm_last_error", "ssm_version", "ssm_set_kernel_timer", "ssm_scan_ck
            "ssm_scan_fwd_workspace_bytes", "ssm_scan_bwd_workspace_bytes", "ssm_scan_fwd",
            "ssm_scan_bwd", "conv1d_causal_bwd_workspace_bytes", "conv1d_causal_bwd",
            "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd", "conv1d_causal_fwd", "rmsnorm_fwd",
-           "ssm_scan_step", "conv1d_causal_step")
+           "ssm_scan_step", "conv1d_causal_step", "ssm_scan_fused_fwd", "ssm_scan_fused_bwd")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -69,6 +69,10 @@ def load():
     lib.ssm_scan_fwd.argtypes = [_P, _E] + [_I] * 4 + [_P] * 10 + [_P, _S]
     lib.ssm_scan_bwd.restype = _E
     lib.ssm_scan_bwd.argtypes = [_P, _E] + [_I] * 4 + [_P] * 16 + [_P, _S]
+    lib.ssm_scan_fused_fwd.restype = _E
+    lib.ssm_scan_fused_fwd.argtypes = [_P, _E] + [_I] * 4 + [_P] * 8 + [_E] + [_P] * 5 + [_P, _S]
+    lib.ssm_scan_fused_bwd.restype = _E
+    lib.ssm_scan_fused_bwd.argtypes = [_P, _E] + [_I] * 4 + [_P] * 8 + [_E] + [_P] * 13 + [_P, _S]
     lib.conv1d_causal_bwd_workspace_bytes.restype = _S
     lib.conv1d_causal_bwd_workspace_bytes.argtypes = [_I] * 4 + [_E]
     lib.conv1d_causal_bwd.restype = _E
@@ -240,6 +244,86 @@ def ssm_scan_bwd(x, delta, A, Bm, Cm, Dv, dy, ckpt=None, h0=None, dx=None, ddelt
     _check(lib.ssm_scan_bwd(_stream(dev), code, Bsz, L, D, N, *args,
                             _ptr(ws, "ws") if ws is not None else None, nbytes))
     return dict(dx=dx, ddelta=ddelta, dA=dA, dB=dB, dC=dC, dD=dD, dh0=dh0)
+
+
+def ssm_scan_fused_fwd(x, delta, A, Bm, Cm, Dv, h0=None, delta_bias=None, delta_softplus=False,
+                       z=None, out=None, y_save=None, ckpt=None, h_last=None, ws=None):
+    """The scan with its Mamba-block neighbours: time step softplus(delta + delta_bias)
+    (or delta + delta_bias), output y * silu(z) when z is given.  y_save (with z) receives
+    y before the gate, which the backward needs.  Returns out."""
+    lib = load()
+    Bsz, L, D = x.shape
+    N = A.shape[1]
+    dev = x.device
+    dt = x.dtype
+    code = _dtype_code(x)
+    f32 = torch.float32
+    out = torch.empty_like(x) if out is None else out
+    if ckpt is not None and ckpt.numel() * 4 < ssm_scan_ckpt_bytes(Bsz, L, D, N):
+        raise ValueError("ckpt buffer too small (use new_ckpt)")
+    args = [
+        _ptr(x, "x", dt, (Bsz, L, D), dev), _ptr(delta, "delta", dt, (Bsz, L, D), dev),
+        _ptr(A, "A", f32, (D, N), dev), _ptr(Bm, "Bm", dt, (Bsz, L, N), dev),
+        _ptr(Cm, "Cm", dt, (Bsz, L, N), dev), _ptr(Dv, "Dv", f32, (D,), dev),
+        _ptr(h0, "h0", f32, (Bsz, D, N), dev), _ptr(delta_bias, "delta_bias", f32, (D,), dev),
+        1 if delta_softplus else 0, _ptr(z, "z", dt, (Bsz, L, D), dev),
+        _ptr(out, "out", dt, (Bsz, L, D), dev), _ptr(y_save, "y_save", dt, (Bsz, L, D), dev),
+        _ptr(ckpt, "ckpt", f32, None, dev), _ptr(h_last, "h_last", f32, (Bsz, D, N), dev),
+    ]
+    need = ssm_scan_fwd_workspace_bytes(Bsz, L, D, N, code)
+    ws, nbytes = _workspace(need, dev, ws)
+    _check(lib.ssm_scan_fused_fwd(_stream(dev), code, Bsz, L, D, N, *args,
+                                  _ptr(ws, "ws") if ws is not None else None, nbytes))
+    return out
+
+
+def ssm_scan_fused_bwd(x, delta, A, Bm, Cm, Dv, dout, ckpt=None, h0=None, delta_bias=None,
+                       delta_softplus=False, z=None, y_save=None, dx=None, ddelta=None,
+                       dA=None, dB=None, dC=None, dD=None, dh0=None, dz=None,
+                       ddelta_bias=None, ws=None):
+    """Backward of ssm_scan_fused_fwd for upstream dout of its output.  dA, dD and
+    ddelta_bias are accumulated into (zeros allocated if not given; ddelta_bias only when
+    delta_bias is given); every other gradient is overwritten.  With z, y_save is
+    required.  Returns dict dx, ddelta, dA, dB, dC, dD, dh0, dz, ddelta_bias."""
+    lib = load()
+    Bsz, L, D = x.shape
+    N = A.shape[1]
+    dev = x.device
+    dt = x.dtype
+    code = _dtype_code(x)
+    f32 = torch.float32
+    dx = torch.empty_like(x) if dx is None else dx
+    ddelta = torch.empty_like(x) if ddelta is None else ddelta
+    dA = torch.zeros((D, N), dtype=f32, device=dev) if dA is None else dA
+    dB = torch.empty((Bsz, L, N), dtype=f32, device=dev) if dB is None else dB
+    dC = torch.empty((Bsz, L, N), dtype=f32, device=dev) if dC is None else dC
+    dD = torch.zeros((D,), dtype=f32, device=dev) if dD is None else dD
+    if z is not None and dz is None:
+        dz = torch.empty_like(x)
+    if delta_bias is not None and ddelta_bias is None:
+        ddelta_bias = torch.zeros((D,), dtype=f32, device=dev)
+    if ckpt is not None and ckpt.numel() * 4 < ssm_scan_ckpt_bytes(Bsz, L, D, N):
+        raise ValueError("ckpt buffer too small")
+    args = [
+        _ptr(x, "x", dt, (Bsz, L, D), dev), _ptr(delta, "delta", dt, (Bsz, L, D), dev),
+        _ptr(A, "A", f32, (D, N), dev), _ptr(Bm, "Bm", dt, (Bsz, L, N), dev),
+        _ptr(Cm, "Cm", dt, (Bsz, L, N), dev), _ptr(Dv, "Dv", f32, (D,), dev),
+        _ptr(h0, "h0", f32, (Bsz, D, N), dev), _ptr(delta_bias, "delta_bias", f32, (D,), dev),
+        1 if delta_softplus else 0, _ptr(z, "z", dt, (Bsz, L, D), dev),
+        _ptr(y_save, "y_save", dt, (Bsz, L, D), dev), _ptr(dout, "dout", dt, (Bsz, L, D), dev),
+        _ptr(ckpt, "ckpt", f32, None, dev),
+        _ptr(dx, "dx", dt, (Bsz, L, D), dev), _ptr(ddelta, "ddelta", dt, (Bsz, L, D), dev),
+        _ptr(dA, "dA", f32, (D, N), dev), _ptr(dB, "dB", f32, (Bsz, L, N), dev),
+        _ptr(dC, "dC", f32, (Bsz, L, N), dev), _ptr(dD, "dD", f32, (D,), dev),
+        _ptr(dh0, "dh0", f32, (Bsz, D, N), dev), _ptr(dz, "dz", dt, (Bsz, L, D), dev),
+        _ptr(ddelta_bias, "ddelta_bias", f32, (D,), dev),
+    ]
+    need = ssm_scan_bwd_workspace_bytes(Bsz, L, D, N, code, ckpt is not None)
+    ws, nbytes = _workspace(need, dev, ws)
+    _check(lib.ssm_scan_fused_bwd(_stream(dev), code, Bsz, L, D, N, *args,
+                                  _ptr(ws, "ws") if ws is not None else None, nbytes))
+    return dict(dx=dx, ddelta=ddelta, dA=dA, dB=dB, dC=dC, dD=dD, dh0=dh0, dz=dz,
+                ddelta_bias=ddelta_bias)
 
 
 # ----------------------------------------------------------------------------------

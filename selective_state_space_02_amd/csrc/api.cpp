@@ -130,6 +130,7 @@ size_t bwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, bool with_ckpt, ssm::B
   p.dCp = cv.take(size_t(p.ng) * B * L * N);
   p.dAp = cv.take(size_t(B) * c.nc * D * N);
   p.dDp = cv.take(size_t(B) * c.nc * D);
+  p.dbp = cv.take(size_t(B) * c.nc * D);
   {
     const int64_t t1 = ssm::reduce_tmp_floats(p.ng, B * L * N);
     const int64_t t2 = ssm::reduce_tmp_floats(B * c.nc, D * N);
@@ -351,6 +352,95 @@ int ssm_scan_bwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t 
     p.ckpt = own_ckpt;
   }
   return hip_status(ssm::launch_scan_bwd(a, p, st), "ssm_scan_bwd");
+}
+
+int ssm_scan_fused_fwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D,
+                       int64_t N, const void* x, const void* delta, const float* A,
+                       const void* Bm, const void* Cm, const float* Dv, const float* h0,
+                       const float* delta_bias, int delta_softplus, const void* z, void* out,
+                       void* y_save, float* ckpt, float* h_last, void* ws, size_t ws_bytes) {
+  int rc = check_scan_dims(dtype, B, L, D, N);
+  if (rc) return rc;
+  rc = check_ptrs({{x, "x"}, {delta, "delta"}, {A, "A"}, {Bm, "Bm"}, {Cm, "Cm"}, {Dv, "Dv"},
+                   {out, "out"}},
+                  {{h0, "h0"}, {delta_bias, "delta_bias"}, {z, "z"}, {y_save, "y_save"},
+                   {ckpt, "ckpt"}, {h_last, "h_last"}});
+  if (rc) return rc;
+  if (delta_softplus != 0 && delta_softplus != 1)
+    return fail(SSM_ERR_ARG, "delta_softplus must be 0 or 1 (got %d)", delta_softplus);
+  if (y_save && !z) return fail(SSM_ERR_ARG, "y_save is only written with the gate input z");
+  ssm::FwdPlan p{};
+  const size_t need = fwd_ws(B, L, D, N, &p, nullptr);
+  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  fwd_ws(B, L, D, N, &p, ws);
+  p.ckpt = ckpt;
+  ssm::ScanArgs a{};
+  a.dtype = int(dtype);
+  a.B = B; a.L = L; a.D = D; a.N = N;
+  a.x = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dv = Dv; a.h0 = h0;
+  a.y = out; a.h_last = h_last;
+  a.vec4 = D % 4 == 0;
+  a.fused = true;
+  a.dt_bias = delta_bias; a.dt_softplus = delta_softplus != 0;
+  a.z = z; a.ysave = y_save;
+  return hip_status(ssm::launch_scan_fwd(a, p, static_cast<hipStream_t>(stream)),
+                    "ssm_scan_fused_fwd");
+}
+
+int ssm_scan_fused_bwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D,
+                       int64_t N, const void* x, const void* delta, const float* A,
+                       const void* Bm, const void* Cm, const float* Dv, const float* h0,
+                       const float* delta_bias, int delta_softplus, const void* z,
+                       const void* y_save, const void* dout, const float* ckpt, void* dx,
+                       void* ddelta, float* dA, float* dB, float* dC, float* dD, float* dh0,
+                       void* dz, float* ddelta_bias, void* ws, size_t ws_bytes) {
+  int rc = check_scan_dims(dtype, B, L, D, N);
+  if (rc) return rc;
+  rc = check_ptrs({{x, "x"}, {delta, "delta"}, {A, "A"}, {Bm, "Bm"}, {Cm, "Cm"}, {Dv, "Dv"},
+                   {dout, "dout"}, {dx, "dx"}, {ddelta, "ddelta"}, {dA, "dA"}, {dB, "dB"},
+                   {dC, "dC"}, {dD, "dD"}},
+                  {{h0, "h0"}, {delta_bias, "delta_bias"}, {z, "z"}, {y_save, "y_save"},
+                   {ckpt, "ckpt"}, {dh0, "dh0"}, {dz, "dz"}, {ddelta_bias, "ddelta_bias"}});
+  if (rc) return rc;
+  if (delta_softplus != 0 && delta_softplus != 1)
+    return fail(SSM_ERR_ARG, "delta_softplus must be 0 or 1 (got %d)", delta_softplus);
+  if (z && (!y_save || !dz))
+    return fail(SSM_ERR_ARG, "with the gate input z, y_save and dz are required");
+  if (!z && (y_save || dz))
+    return fail(SSM_ERR_ARG, "y_save and dz are only used with the gate input z");
+  const bool with_ckpt = ckpt != nullptr;
+  ssm::BwdPlan p{};
+  ssm::FwdPlan fp{};
+  float* own_ckpt = nullptr;
+  const size_t need = bwd_ws(B, L, D, N, with_ckpt, &p, &own_ckpt, &fp, nullptr);
+  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  bwd_ws(B, L, D, N, with_ckpt, &p, &own_ckpt, &fp, ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  ssm::ScanArgs a{};
+  a.dtype = int(dtype);
+  a.B = B; a.L = L; a.D = D; a.N = N;
+  a.x = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dv = Dv; a.h0 = h0;
+  a.dy = dout; a.dx = dx; a.ddelta = ddelta; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD;
+  a.dh0 = dh0;
+  a.vec4 = D % 4 == 0;
+  a.fused = true;
+  a.dt_bias = delta_bias; a.dt_softplus = delta_softplus != 0;
+  a.z = z; a.ysave = const_cast<void*>(y_save); a.dz = dz; a.ddt_bias = ddelta_bias;
+  if (with_ckpt) {
+    p.ckpt = ckpt;
+  } else {
+    // recompute the forward's checkpoints with the same time step (no output, no gate)
+    fp.ckpt = own_ckpt;
+    ssm::ScanArgs f = a;
+    f.y = nullptr;
+    f.h_last = nullptr;
+    f.z = nullptr;
+    f.ysave = nullptr;
+    hipError_t e = ssm::launch_scan_fwd(f, fp, st);
+    if (e != hipSuccess) return hip_status(e, "ssm_scan_fused_bwd (forward recompute)");
+    p.ckpt = own_ckpt;
+  }
+  return hip_status(ssm::launch_scan_bwd(a, p, st), "ssm_scan_fused_bwd");
 }
 
 static int check_conv_dims(ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D, int64_t K,

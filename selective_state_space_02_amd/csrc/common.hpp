@@ -39,6 +39,27 @@ __device__ __forceinline__ float sigmoid_f(float p) {
 // Activation after the conv: 0 none, 1 SiLU (p * sigmoid(p)).
 constexpr int kActNone = 0, kActSilu = 1;
 
+// log1p(t) for t in [0, 1] from one logarithm: with u = fl(1 + t), the rounding error
+// c = t - (u - 1) is exact (both differences are exact for u in [1, 2]) and at most 2^-24;
+// log1p(t) = log(u) + log(1 + c/u), and log(1 + c/u) = c to within 2^-24 t.  log(u)
+// alone would lose the low bits of t that the rounding of u drops.
+__device__ __forceinline__ float log1p_unit(float t) {
+  const float u = 1.f + t;
+  return __builtin_fmaf(__builtin_amdgcn_logf(u), kLn2, t - (u - 1.f));
+}
+// softplus(v) = log(1 + exp(v)) = max(v, 0) + log1p(exp(-|v|)).
+__device__ __forceinline__ float softplus_f(float v) {
+  return __builtin_fmaxf(v, 0.f) + log1p_unit(__builtin_amdgcn_exp2f(-__builtin_fabsf(v) * kLog2e));
+}
+// softplus(v) and its derivative sigmoid(v) from one exponential: with t = exp(-|v|),
+// sigmoid(v) = 1 / (1 + t) for v >= 0 and t / (1 + t) below.
+__device__ __forceinline__ float softplus_sigmoid(float v, float& sg) {
+  const float t = __builtin_amdgcn_exp2f(-__builtin_fabsf(v) * kLog2e);
+  const float r = __builtin_amdgcn_rcpf(1.f + t);
+  sg = v >= 0.f ? r : t * r;
+  return __builtin_fmaxf(v, 0.f) + log1p_unit(t);
+}
+
 // Two floats as packed bf16 (lo in bits 0-15), rounded to nearest even.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef float f2 __attribute__((ext_vector_type(2)));
@@ -178,6 +199,13 @@ template <typename T0, typename... Ts>
 __device__ __forceinline__ void step_fence(T0& v, Ts&... rest) {
   asm volatile("" : "+v"(v));
   step_fence(rest...);
+}
+// A copy of v the compiler cannot see through: values derived from it are computed
+// where they are used rather than hoisted out of a loop and held in registers.
+template <typename T>
+__device__ __forceinline__ T opaque(T v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 template <int K>
 __device__ __forceinline__ void step_fence_arr(float (&v)[K]) {

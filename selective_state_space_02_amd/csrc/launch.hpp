@@ -37,6 +37,16 @@ struct ScanArgs {
   float* dC;
   float* dD;
   float* dh0;  // nullable
+  // The scan's Mamba-block neighbours (fused entry points only).  The delta input is
+  // then the raw time step: delta_eff = dt_softplus ? softplus(delta + dt_bias[d])
+  // : delta + dt_bias[d]; with z the output is y * silu(z).
+  bool fused;            // selects the kernel variants that apply them
+  const float* dt_bias;  // nullable [D] (zero)
+  bool dt_softplus;
+  const void* z;         // nullable [B,L,D]
+  void* ysave;           // forward: nullable, y before the gate; backward: that input
+  void* dz;              // backward, with z
+  float* ddt_bias;       // backward, nullable, accumulated
 };
 
 // Coarse chunking of the sequence (shared rule for forward and backward).
@@ -68,6 +78,7 @@ struct BwdPlan {
   float* dCp;         // [ng][B][L][N]
   float* dAp;         // [B*nc][D][N]
   float* dDp;         // [B*nc][D]
+  float* dbp;         // [B*nc][D]  time-step bias partials (fused backward)
   float* rtmp;        // reduction scratch
 };
 

@@ -36,13 +36,18 @@ namespace ssm {
 
 // Chunk summaries of the adjoint: G (pushed adjoint of the chunk alone) and the sum of
 // delta, for chunks 1..nc-1.
-template <typename T, int N, int VEC>
+// FZ: delta is the raw time step, mapped at staging (time_step_map); with z (nullable)
+// dy is the gradient of the gated output y * silu(z), and the scan's upstream gradient
+// dy * silu(z) is formed at staging.
+template <typename T, int N, int VEC, bool FZ>
 __global__ __launch_bounds__(256, 4) void k_bwd_summary(
     int64_t L, int64_t D, int64_t Lc, int nc, const T* __restrict__ delta,
     const float* __restrict__ A, const T* __restrict__ Cm, const T* __restrict__ dy,
-    float* __restrict__ GS, float* __restrict__ SD) {
+    const float* __restrict__ dtb, bool sp, const T* __restrict__ z, float* __restrict__ GS,
+    float* __restrict__ SD) {
   constexpr int NS = N / 4;
   __shared__ float sd[2][kTc][kTileCh], sdy[2][kTc][kTileCh], sC[2][kTc][N];
+  __shared__ float sbias[FZ ? kTileCh : 1];
   const int c = blockIdx.z + 1, b = blockIdx.y, tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
   const int64_t d0 = int64_t(blockIdx.x) * kTileCh, d = d0 + cl;
   const bool act = d < D;
@@ -63,26 +68,50 @@ __global__ __launch_bounds__(256, 4) void k_bwd_summary(
   // tiles are walked from the last one backwards
   const ChTile<T, VEC> gt(D32, dvalid, tid);
   const uint32_t voff = VecFetch<T, N>::offset(tid);
-  ChFetch<T, VEC> fd, fy;
+  ChFetch<T, VEC> fd, fy, fz;
   VecFetch<T, N> fC;
+  const T* zb = (FZ && z) ? z + int64_t(b) * L * D + d0 : nullptr;
+  if constexpr (FZ) {
+    if (tid < kTileCh) sbias[tid] = (dtb && tid < dvalid) ? dtb[d0 + tid] : 0.f;
+    __syncthreads();
+  }
+  int pend_tv = 0;  // valid rows of the fetched tile not yet committed
+  auto fetch = [&](int64_t tt, int tvalid) {
+    fd.fetch(gt, db + tt * D, D32, tvalid, dvalid);
+    fy.fetch(gt, dyb + tt * D, D32, tvalid, dvalid);
+    fC.fetch(Cb + tt * N, tvalid, voff);
+    if (zb) fz.fetch(gt, zb + tt * D, D32, tvalid, dvalid);
+    pend_tv = tvalid;
+  };
+  auto commit = [&](int bf) {
+    if constexpr (FZ) {
+      fd.commit_map(gt, sd[bf], [&](int k, float (&v)[VEC]) {
+        const bool ok = gt.s_in + k * ChTile<T, VEC>::RPP < pend_tv && gt.c < dvalid;
+        time_step_map<VEC>(v, &sbias[gt.c], ok, sp, nullptr);
+      });
+      if (zb)
+        fy.commit_map(gt, sdy[bf], [&](int k, float (&v)[VEC]) {
+          float zv[VEC];
+          BufVec<T, VEC>::unpack(fz.raw[k], zv);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) v[i] *= zv[i] * sigmoid_f(zv[i]);
+        });
+      else
+        fy.commit(gt, sdy[bf]);
+    } else {
+      fd.commit(gt, sd[bf]);
+      fy.commit(gt, sdy[bf]);
+    }
+    fC.commit(sC[bf], tid);
+  };
   int64_t tf = t0 + int64_t(ntile - 1) * kTc;
-  const int tv = clamp_valid(L - tf);
-  fd.fetch(gt, db + tf * D, D32, tv, dvalid);
-  fy.fetch(gt, dyb + tf * D, D32, tv, dvalid);
-  fC.fetch(Cb + tf * N, tv, voff);
-  fd.commit(gt, sd[0]);
-  fy.commit(gt, sdy[0]);
-  fC.commit(sC[0], tid);
+  fetch(tf, clamp_valid(L - tf));
+  commit(0);
   __syncthreads();
   for (int it = 0; it < ntile; ++it, tf -= kTc) {
     const int buf = it & 1;
     const bool more = it + 1 < ntile;
-    if (more) {  // every tile but the last one is full
-      const int64_t tn = tf - kTc;
-      fd.fetch(gt, db + tn * D, D32, kTc, dvalid);
-      fy.fetch(gt, dyb + tn * D, D32, kTc, dvalid);
-      fC.fetch(Cb + tn * N, kTc, voff);
-    }
+    if (more) fetch(tf - kTc, kTc);  // every tile but the last one is full
     // the LDS operands of step s-1 are read during step s
     float ndl = sd[buf][kTc - 1][cl], ndy = sdy[buf][kTc - 1][cl], nC[NS];
     tile_read_vec<N, NS>(sC[buf], kTc - 1, q, nC);
@@ -107,11 +136,7 @@ __global__ __launch_bounds__(256, 4) void k_bwd_summary(
       step_fence_arr(nC);
       step_fence(sdl, ndl, ndy);
     }
-    if (more) {
-      fd.commit(gt, sd[buf ^ 1]);
-      fy.commit(gt, sdy[buf ^ 1]);
-      fC.commit(sC[buf ^ 1], tid);
-    }
+    if (more) commit(buf ^ 1);
     __syncthreads();
   }
   if (act) {
@@ -151,14 +176,25 @@ __global__ __launch_bounds__(256) void k_bwd_carry(
 // with coalesced writes; the dB/dC partials of each lane go to LDS and are summed there.
 // Two barriers per tile: after the compute (outputs complete) and after the next
 // tile's inputs are committed.
-template <typename T, int N, int VEC, int SPLIT, int WAVES>
+//
+// FZ: the Mamba-block neighbours.  delta is the raw time step, mapped at staging
+// (time_step_map), whose derivative there (sigmoid, or 1) is kept in LDS for the tile's
+// ddelta store: the stored ddelta is the raw input's gradient, and its per-channel sum
+// over the chunk goes to dbp (time-step bias partials, [B*nc][D]).  With z (nullable),
+// dy is the gradient of the gated output y * silu(z); at staging it becomes the scan's
+// upstream gradient dy * silu(z), and dz = dy * ysave * silu'(z) is stored (ysave: y
+// before the gate, saved by the forward).  The gate's inputs are loaded after the
+// previous tile's compute, so their registers are not held across it.
+template <typename T, int N, int VEC, int SPLIT, int WAVES, bool FZ>
 __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
     int64_t B, int64_t L, int64_t D, int64_t Lc, int nc, int64_t nck,
     const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dv,
     const T* __restrict__ dy, const float* __restrict__ ckpt, const float* __restrict__ gin,
-    T* __restrict__ dx, T* __restrict__ ddelta, float* __restrict__ dBp,
-    float* __restrict__ dCp, float* __restrict__ dAp, float* __restrict__ dDp,
+    const float* __restrict__ dtb, bool sp, const T* __restrict__ z,
+    const T* __restrict__ ysave, T* __restrict__ dx, T* __restrict__ ddelta,
+    T* __restrict__ dz, float* __restrict__ dBp, float* __restrict__ dCp,
+    float* __restrict__ dAp, float* __restrict__ dDp, float* __restrict__ dbp,
     float* __restrict__ dh0) {
   constexpr int NS = N / 4;       // states per lane
   constexpr int V = 2 * NS;       // per-lane values summed over channels: dB, dC
@@ -168,6 +204,10 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
   __shared__ float sx[2][kTc][kTileCh], sd[2][kTc][kTileCh], sdy[2][kTc][kTileCh];
   __shared__ float sB[2][kTc][N], sC[2][kTc][N];
   __shared__ float red[4][kTc][64];  // [wavefront][step][lane]
+  // FZ: time-step bias, the time-step map's derivative for the current tile, and each
+  // thread's running ddelta sums of its VEC channels
+  __shared__ float sbias[FZ ? kTileCh : 1], ssg[FZ ? kTc : 1][kTileCh];
+  __shared__ float sdb[FZ ? kTileThreads * VEC : 1];
 
   const int c = blockIdx.z, b = blockIdx.y, grp = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = tid & 3, cl = tid >> 2;
@@ -203,16 +243,30 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
   const int ntile = int((t1 - t0 + kTc - 1) / kTc);
 
   const ChTile<T, VEC> gt(D32, dvalid, tid);
+  using G = ChTile<T, VEC>;
   const uint32_t voff = VecFetch<T, N>::offset(tid);
   ChFetch<T, VEC> fx, fd, fy;
   VecFetch<T, N> fB, fC;
+  const T* zb = (FZ && z) ? z + int64_t(b) * L * D + d0 : nullptr;
+  const T* ysb = (FZ && z) ? ysave + int64_t(b) * L * D + d0 : nullptr;
+  T* dzb = (FZ && z) ? dz + int64_t(b) * L * D + d0 : nullptr;
+  if constexpr (FZ) {
+    if (tid < kTileCh) sbias[tid] = (dtb && tid < dvalid) ? dtb[d0 + tid] : 0.f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) sdb[tid * VEC + i] = 0.f;
+    __syncthreads();
+  }
   float hcur[SPLIT][NS], hnxt[SPLIT][NS];  // checkpoints of the current and the next tile
+  int pend_tv = 0;                         // valid rows of the fetched, uncommitted tile
+  int64_t pend_tt = 0;                     // and its first step
   auto fetch = [&](int64_t tt, int tvalid, float (&hk)[SPLIT][NS]) {
     fx.fetch(gt, xb + tt * D, D32, tvalid, dvalid);
     fd.fetch(gt, db + tt * D, D32, tvalid, dvalid);
     fy.fetch(gt, dyb + tt * D, D32, tvalid, dvalid);
     fB.fetch(Bb + tt * N, tvalid, voff);
     fC.fetch(Cb + tt * N, tvalid, voff);
+    pend_tv = tvalid;
+    pend_tt = tt;
 #pragma unroll
     for (int hf = 0; hf < SPLIT; ++hf) {
       if (hf == 0 || tt + hf * SL < L) {
@@ -223,16 +277,49 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
       }
     }
   };
+  // the gate's inputs of the pending tile (FZ with z), loaded just before its commit
+  ChFetch<T, VEC> fz, fys;
+  auto fetch_gate = [&]() {
+    if (zb) {
+      fz.fetch(gt, zb + pend_tt * D, D32, pend_tv, dvalid);
+      fys.fetch(gt, ysb + pend_tt * D, D32, pend_tv, dvalid);
+    }
+  };
   auto commit = [&](int bf) {
     fx.commit(gt, sx[bf]);
-    fd.commit(gt, sd[bf]);
-    fy.commit(gt, sdy[bf]);
+    if constexpr (FZ) {
+      // (LDS addresses from opaque copies: rebuilt per tile, not held across the compute)
+      fd.commit_map(gt, sd[bf], [&](int k, float (&v)[VEC]) {
+        const int row = opaque(gt.s_in) + k * G::RPP, cc = opaque(gt.c);
+        time_step_map<VEC>(v, &sbias[cc], row < pend_tv && cc < dvalid, sp, &ssg[row][cc]);
+      });
+      if (zb) {
+        fy.commit_map(gt, sdy[bf], [&](int k, float (&v)[VEC]) {
+          float zv[VEC], yv[VEC], dzv[VEC];
+          BufVec<T, VEC>::unpack(fz.raw[k], zv);
+          BufVec<T, VEC>::unpack(fys.raw[k], yv);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) {
+            const float sg = sigmoid_f(zv[i]);
+            dzv[i] = v[i] * yv[i] * sg * __builtin_fmaf(zv[i], 1.f - sg, 1.f);
+            v[i] *= zv[i] * sg;
+          }
+          tile_store_regs(gt, dzb + pend_tt * D, k, dzv, D32, pend_tv, dvalid);
+        });
+      } else {
+        fy.commit(gt, sdy[bf]);
+      }
+    } else {
+      fd.commit(gt, sd[bf]);
+      fy.commit(gt, sdy[bf]);
+    }
     fB.commit(sB[bf], tid);
     fC.commit(sC[bf], tid);
   };
 
   int64_t tf = t0 + int64_t(ntile - 1) * kTc;  // first step of the current tile
   fetch(tf, clamp_valid(L - tf), hcur);
+  if constexpr (FZ) fetch_gate();
   commit(0);
   if (ntile > 1) fetch(tf - kTc, kTc, hnxt);  // every tile but the last one is full
   __syncthreads();
@@ -339,11 +426,27 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
     chan_reduce_scatter<V>(pv, lane);
     red[wave][0][lane] = pv[0];
     __syncthreads();
+    if constexpr (FZ) {
+      if (it + 1 < ntile) fetch_gate();  // the next tile's, consumed by its commit below
+    }
 
     // this tile's dx and ddelta, and the channel sums -> this group's dB/dC partials
     const int smax = (t1 - tf < kTc) ? int(t1 - tf) : kTc;
     tile_store_ch(gt, dxb + tf * D, sx[buf], D32, smax, dvalid);
-    tile_store_ch(gt, ddb + tf * D, sd[buf], D32, smax, dvalid);
+    if constexpr (FZ) {
+      tile_store_ch_map(gt, ddb + tf * D, sd[buf], D32, smax, dvalid,
+                        [&](int k, float (&v)[VEC]) {
+                          const int row = opaque(gt.s_in) + k * G::RPP, cc = opaque(gt.c);
+                          const int ti = opaque(tid) * VEC;
+#pragma unroll
+                          for (int i = 0; i < VEC; ++i) {
+                            v[i] *= ssg[row][cc + i];
+                            if (row < smax) sdb[ti + i] += v[i];
+                          }
+                        });
+    } else {
+      tile_store_ch(gt, ddb + tf * D, sd[buf], D32, smax, dvalid);
+    }
     for (int k = tid; k < kTc * 2 * N; k += 256) {
       const int s = k / (2 * N), r = k % (2 * N);
       if (s < smax) {
@@ -373,6 +476,16 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
     __syncthreads();
   }
 
+  if constexpr (FZ) {
+    // time-step bias partial of each channel: the sum over the threads that share its
+    // channels (rows of the ChTile placement), in row order
+    if (dbp && tid < kTileCh && tid < dvalid) {
+      const int tc = tid / VEC, ci = tid % VEC;  // thread column and channel within it
+      float sum = 0.f;
+      for (int r = 0; r < G::RPP; ++r) sum += sdb[(r * G::TPR + tc) * VEC + ci];
+      dbp[(int64_t(b) * nc + c) * D + d0 + tid] = sum;
+    }
+  }
   if (act) {
     const int64_t o = (int64_t(b) * nc + c) * D + d;
 #pragma unroll
@@ -397,7 +510,7 @@ struct BwdMainCfg {
 // ---------------------------------------------------------------------------------
 // host launcher
 // ---------------------------------------------------------------------------------
-template <typename T, int N, int VEC>
+template <typename T, int N, int VEC, bool FZ>
 static hipError_t bwd_impl(const ScanArgs& a, const BwdPlan& p, hipStream_t st) {
   const T* x = static_cast<const T*>(a.x);
   const T* delta = static_cast<const T*>(a.delta);
@@ -408,8 +521,9 @@ static hipError_t bwd_impl(const ScanArgs& a, const BwdPlan& p, hipStream_t st) 
   const float* gin = nullptr;
   if (p.nc > 1) {
     timer_mark(kKBwdSummary, false, st);
-    hipLaunchKernelGGL((k_bwd_summary<T, N, VEC>), dim3(p.ng, a.B, p.nc - 1), block, 0, st,
-                       a.L, a.D, p.Lc, p.nc, delta, a.A, Cm, dy, p.GS, p.SD);
+    hipLaunchKernelGGL((k_bwd_summary<T, N, VEC, FZ>), dim3(p.ng, a.B, p.nc - 1), block, 0, st,
+                       a.L, a.D, p.Lc, p.nc, delta, a.A, Cm, dy, a.dt_bias, a.dt_softplus,
+                       static_cast<const T*>(a.z), p.GS, p.SD);
     timer_mark(kKBwdSummary, true, st);
     const int64_t tot = a.B * a.D * N;
     timer_mark(kKBwdCarry, false, st);
@@ -420,10 +534,12 @@ static hipError_t bwd_impl(const ScanArgs& a, const BwdPlan& p, hipStream_t st) 
   }
   timer_mark(kKBwdMain, false, st);
   using Cfg = BwdMainCfg<N>;
-  hipLaunchKernelGGL((k_bwd_main<T, N, VEC, Cfg::kSplit, Cfg::kWaves>), dim3(p.ng, a.B, p.nc),
-                     block, 0, st, a.B, a.L, a.D, p.Lc, p.nc, p.nck, x, delta, a.A, Bm, Cm,
-                     a.Dv, dy, p.ckpt, gin, static_cast<T*>(a.dx), static_cast<T*>(a.ddelta),
-                     p.dBp, p.dCp, p.dAp, p.dDp, a.dh0);
+  hipLaunchKernelGGL((k_bwd_main<T, N, VEC, Cfg::kSplit, Cfg::kWaves, FZ>),
+                     dim3(p.ng, a.B, p.nc), block, 0, st, a.B, a.L, a.D, p.Lc, p.nc, p.nck, x,
+                     delta, a.A, Bm, Cm, a.Dv, dy, p.ckpt, gin, a.dt_bias, a.dt_softplus,
+                     static_cast<const T*>(a.z), static_cast<const T*>(a.ysave),
+                     static_cast<T*>(a.dx), static_cast<T*>(a.ddelta), static_cast<T*>(a.dz),
+                     p.dBp, p.dCp, p.dAp, p.dDp, a.ddt_bias ? p.dbp : nullptr, a.dh0);
   timer_mark(kKBwdMain, true, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -432,12 +548,16 @@ static hipError_t bwd_impl(const ScanArgs& a, const BwdPlan& p, hipStream_t st) 
   if ((e = launch_reduce(p.dCp, p.ng, BLN, a.dC, false, p.rtmp, st)) != hipSuccess) return e;
   if ((e = launch_reduce(p.dAp, a.B * p.nc, a.D * N, a.dA, true, p.rtmp, st)) != hipSuccess)
     return e;
+  if (FZ && a.ddt_bias &&
+      (e = launch_reduce(p.dbp, a.B * p.nc, a.D, a.ddt_bias, true, p.rtmp, st)) != hipSuccess)
+    return e;
   return launch_reduce(p.dDp, a.B * p.nc, a.D, a.dD, true, p.rtmp, st);
 }
 
 template <typename T, int N>
 static hipError_t bwd_vec(const ScanArgs& a, const BwdPlan& p, hipStream_t st) {
-  return a.vec4 ? bwd_impl<T, N, 4>(a, p, st) : bwd_impl<T, N, 1>(a, p, st);
+  if (a.fused) return a.vec4 ? bwd_impl<T, N, 4, true>(a, p, st) : bwd_impl<T, N, 1, true>(a, p, st);
+  return a.vec4 ? bwd_impl<T, N, 4, false>(a, p, st) : bwd_impl<T, N, 1, false>(a, p, st);
 }
 
 hipError_t launch_scan_bwd(const ScanArgs& a, const BwdPlan& p, hipStream_t st) {

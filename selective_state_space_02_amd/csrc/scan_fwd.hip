@@ -28,13 +28,16 @@ namespace ssm {
 // Waves per SIMD targeted by k_fwd_output (its LDS, 20 KB, admits eight workgroups).
 constexpr int kFwdOutputWaves = 6;
 
-template <typename T, int N, int VEC>
+// FZ: delta is the raw time step, mapped at staging (time_step_map, bias dtb, softplus
+// when sp).
+template <typename T, int N, int VEC, bool FZ>
 __global__ __launch_bounds__(256, 4) void k_fwd_summary(
     int64_t L, int64_t D, int64_t Lc, int nc, const T* __restrict__ x,
     const T* __restrict__ delta, const float* __restrict__ A, const T* __restrict__ Bm,
-    float* __restrict__ S, float* __restrict__ SD) {
+    const float* __restrict__ dtb, bool sp, float* __restrict__ S, float* __restrict__ SD) {
   constexpr int NS = N / 4;
   __shared__ float sx[2][kTc][kTileCh], sd[2][kTc][kTileCh], sB[2][kTc][N];
+  __shared__ float sbias[FZ ? kTileCh : 1];
   const int c = blockIdx.z, b = blockIdx.y, tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
   const int64_t d0 = int64_t(blockIdx.x) * kTileCh, d = d0 + cl;
   const bool act = d < D;
@@ -56,11 +59,24 @@ __global__ __launch_bounds__(256, 4) void k_fwd_summary(
   const uint32_t voff = VecFetch<T, N>::offset(tid);
   ChFetch<T, VEC> fx, fd;
   VecFetch<T, N> fB;
+  if constexpr (FZ) {
+    if (tid < kTileCh) sbias[tid] = (dtb && tid < dvalid) ? dtb[d0 + tid] : 0.f;
+    __syncthreads();
+  }
+  // chunks 0..nc-2 are full: every row is valid
+  auto commit_delta = [&](float (*sm)[kTileCh]) {
+    if constexpr (FZ)
+      fd.commit_map(gt, sm, [&](int, float (&v)[VEC]) {
+        time_step_map<VEC>(v, &sbias[gt.c], gt.c < dvalid, sp, nullptr);
+      });
+    else
+      fd.commit(gt, sm);
+  };
   fx.fetch(gt, xb + t0 * D, D32, kTc, dvalid);
   fd.fetch(gt, db + t0 * D, D32, kTc, dvalid);
   fB.fetch(Bb + t0 * N, kTc, voff);
   fx.commit(gt, sx[0]);
-  fd.commit(gt, sd[0]);
+  commit_delta(sd[0]);
   fB.commit(sB[0], tid);
   __syncthreads();
   for (int it = 0; it < ntile; ++it) {
@@ -86,7 +102,7 @@ __global__ __launch_bounds__(256, 4) void k_fwd_summary(
     }
     if (more) {
       fx.commit(gt, sx[buf ^ 1]);
-      fd.commit(gt, sd[buf ^ 1]);
+      commit_delta(sd[buf ^ 1]);
       fB.commit(sB[buf ^ 1], tid);
     }
     __syncthreads();
@@ -124,15 +140,19 @@ __global__ __launch_bounds__(256) void k_fwd_carry(
 // channel's slots are read and written only by its four lanes, reads first) and is
 // stored after the tile; two barriers per tile: after the compute (y complete) and
 // after the next tile's inputs are committed.
-template <typename T, int N, int VEC>
+// FZ: delta is the raw time step, mapped at staging as in k_fwd_summary; with z (nullable)
+// the stored output is y * silu(z), and ysave (nullable) receives y itself.
+template <typename T, int N, int VEC, bool FZ>
 __global__ __launch_bounds__(256, kFwdOutputWaves) void k_fwd_output(
     int64_t L, int64_t D, int64_t Lc, int nc, int64_t nck, const T* __restrict__ x,
     const T* __restrict__ delta, const float* __restrict__ A, const T* __restrict__ Bm,
     const T* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ hin,
-    T* __restrict__ y, float* __restrict__ ckpt, float* __restrict__ h_last) {
+    const float* __restrict__ dtb, bool sp, const T* __restrict__ z, T* __restrict__ y,
+    T* __restrict__ ysave, float* __restrict__ ckpt, float* __restrict__ h_last) {
   constexpr int NS = N / 4;
   constexpr int CK = kTc / ckpt_per_tile(N);  // checkpoint interval
   __shared__ float sx[2][kTc][kTileCh], sd[2][kTc][kTileCh], sB[2][kTc][N], sC[2][kTc][N];
+  __shared__ float sbias[FZ ? kTileCh : 1];
   const int c = blockIdx.z, b = blockIdx.y, tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
   const int64_t d0 = int64_t(blockIdx.x) * kTileCh, d = d0 + cl;
   const bool act = d < D;
@@ -143,6 +163,8 @@ __global__ __launch_bounds__(256, kFwdOutputWaves) void k_fwd_output(
   const T* Bb = Bm + int64_t(b) * L * N;
   const T* Cb = Cm + int64_t(b) * L * N;
   T* yb = y ? y + int64_t(b) * L * D + d0 : nullptr;
+  T* ysb = (FZ && ysave) ? ysave + int64_t(b) * L * D + d0 : nullptr;
+  const T* zb = (FZ && z && y) ? z + int64_t(b) * L * D + d0 : nullptr;
   // checkpoint f of this group: ckpt + ((b*nck + f)*D + d0)*N, lane at (cl*N + q*NS)
   float* ckg = ckpt ? ckpt + (int64_t(b) * nck * D + d0) * N : nullptr;
   const uint32_t ckoff = act ? uint32_t(cl * N + q * NS) * 4u : kOffNone;
@@ -151,31 +173,44 @@ __global__ __launch_bounds__(256, kFwdOutputWaves) void k_fwd_output(
 #pragma unroll
   for (int j = 0; j < NS; ++j) A2[j] = act ? A[d * N + q * NS + j] * kLog2e : 0.f;
   const float Dd = act ? Dv[d] : 0.f;
-  if (hin && act) {
-#pragma unroll
-    for (int j = 0; j < NS; ++j) h[j] = hin[((int64_t(b) * nc + c) * D + d) * N + q * NS + j];
-  } else {
-    zero(h);
-  }
+  // the chunk's start state ([B][nc][D][N], laid out as the checkpoints) under a uniform
+  // branch: a lane-dependent branch here would make the compiler treat the chunk's
+  // (uniform) step offsets as per-lane values and wrap every buffer access below in a
+  // loop over lanes
+  zero(h);
+  if (hin)
+    buf_load_states<NS>(buf_rsrc(hin + ((int64_t(b) * nc + c) * D + d0) * N, ckbytes), ckoff, h);
   const int64_t t0 = int64_t(c) * Lc, t1 = (t0 + Lc < L) ? t0 + Lc : L;
   const int ntile = int((t1 - t0 + kTc - 1) / kTc);
   const ChTile<T, VEC> gt(D32, dvalid, tid);
   const uint32_t voff = VecFetch<T, N>::offset(tid);
-  ChFetch<T, VEC> fx, fd;
+  ChFetch<T, VEC> fx, fd, fz;
   VecFetch<T, N> fB, fC;
+  if constexpr (FZ) {
+    if (tid < kTileCh) sbias[tid] = (dtb && tid < dvalid) ? dtb[d0 + tid] : 0.f;
+  }
+  int pend_tv = 0;  // valid rows of the fetched tile not yet committed
   auto fetch = [&](int64_t tt) {
     const int tv = clamp_valid(L - tt);
     fx.fetch(gt, xb + tt * D, D32, tv, dvalid);
     fd.fetch(gt, db + tt * D, D32, tv, dvalid);
     fB.fetch(Bb + tt * N, tv, voff);
     fC.fetch(Cb + tt * N, tv, voff);
+    pend_tv = tv;
   };
   auto commit = [&](int bf) {
     fx.commit(gt, sx[bf]);
-    fd.commit(gt, sd[bf]);
+    if constexpr (FZ)
+      fd.commit_map(gt, sd[bf], [&](int k, float (&v)[VEC]) {
+        const bool ok = gt.s_in + k * ChTile<T, VEC>::RPP < pend_tv && gt.c < dvalid;
+        time_step_map<VEC>(v, &sbias[gt.c], ok, sp, nullptr);
+      });
+    else
+      fd.commit(gt, sd[bf]);
     fB.commit(sB[bf], tid);
     fC.commit(sC[bf], tid);
   };
+  if constexpr (FZ) __syncthreads();  // sbias
   fetch(t0);
   commit(0);
   if (ntile > 1) fetch(t0 + kTc);
@@ -184,6 +219,8 @@ __global__ __launch_bounds__(256, kFwdOutputWaves) void k_fwd_output(
     const int buf = it & 1;
     const int64_t tf = t0 + int64_t(it) * kTc;
     if (ckg) buf_store_states<NS>(h, buf_rsrc(ckg + (tf / CK) * D * N, ckbytes), ckoff);
+    // the gate input of this tile, used at its store
+    if (FZ && zb) fz.fetch(gt, zb + tf * D, D32, clamp_valid(L - tf), dvalid);
     // the LDS operands of step s+1 are read during step s
     float ndl = sd[buf][0][cl], nxv = sx[buf][0][cl], nB[NS], nC[NS];
     tile_read_vec<N, NS>(sB[buf], 0, q, nB);
@@ -221,7 +258,21 @@ __global__ __launch_bounds__(256, kFwdOutputWaves) void k_fwd_output(
       step_fence(ndl, nxv);
     }
     __syncthreads();
-    if (yb) tile_store_ch(gt, yb + tf * D, sx[buf], D32, clamp_valid(t1 - tf), dvalid);
+    if constexpr (FZ) {
+      if (ysb) tile_store_ch(gt, ysb + tf * D, sx[buf], D32, clamp_valid(t1 - tf), dvalid);
+      if (zb)
+        tile_store_ch_map(gt, yb + tf * D, sx[buf], D32, clamp_valid(t1 - tf), dvalid,
+                          [&](int k, float (&v)[VEC]) {
+                            float zv[VEC];
+                            BufVec<T, VEC>::unpack(fz.raw[k], zv);
+#pragma unroll
+                            for (int i = 0; i < VEC; ++i) v[i] *= zv[i] * sigmoid_f(zv[i]);
+                          });
+      else if (yb)
+        tile_store_ch(gt, yb + tf * D, sx[buf], D32, clamp_valid(t1 - tf), dvalid);
+    } else {
+      if (yb) tile_store_ch(gt, yb + tf * D, sx[buf], D32, clamp_valid(t1 - tf), dvalid);
+    }
     if (it + 1 < ntile) {
       commit(buf ^ 1);
       if (it + 2 < ntile) fetch(tf + 2 * kTc);
@@ -237,7 +288,7 @@ __global__ __launch_bounds__(256, kFwdOutputWaves) void k_fwd_output(
 // ---------------------------------------------------------------------------------
 // host launcher
 // ---------------------------------------------------------------------------------
-template <typename T, int N, int VEC>
+template <typename T, int N, int VEC, bool FZ>
 static hipError_t fwd_impl(const ScanArgs& a, const FwdPlan& p, hipStream_t st) {
   const T* x = static_cast<const T*>(a.x);
   const T* delta = static_cast<const T*>(a.delta);
@@ -248,8 +299,9 @@ static hipError_t fwd_impl(const ScanArgs& a, const FwdPlan& p, hipStream_t st) 
   const float* hin = a.h0;  // [B][1][D][N] == [B][D][N] when nc == 1
   if (p.nc > 1) {
     timer_mark(kKFwdSummary, false, st);
-    hipLaunchKernelGGL((k_fwd_summary<T, N, VEC>), dim3(groups, a.B, p.nc - 1), block, 0, st, a.L,
-                       a.D, p.Lc, p.nc, x, delta, a.A, Bm, p.S, p.SD);
+    hipLaunchKernelGGL((k_fwd_summary<T, N, VEC, FZ>), dim3(groups, a.B, p.nc - 1), block, 0, st,
+                       a.L, a.D, p.Lc, p.nc, x, delta, a.A, Bm, a.dt_bias, a.dt_softplus, p.S,
+                       p.SD);
     timer_mark(kKFwdSummary, true, st);
     const int64_t tot = a.B * a.D * N;
     timer_mark(kKFwdCarry, false, st);
@@ -259,16 +311,18 @@ static hipError_t fwd_impl(const ScanArgs& a, const FwdPlan& p, hipStream_t st) 
     hin = p.hin;
   }
   timer_mark(kKFwdOutput, false, st);
-  hipLaunchKernelGGL((k_fwd_output<T, N, VEC>), dim3(groups, a.B, p.nc), block, 0, st, a.L, a.D,
-                     p.Lc, p.nc, p.nck, x, delta, a.A, Bm, Cm, a.Dv, hin,
-                     static_cast<T*>(a.y), p.ckpt, a.h_last);
+  hipLaunchKernelGGL((k_fwd_output<T, N, VEC, FZ>), dim3(groups, a.B, p.nc), block, 0, st, a.L,
+                     a.D, p.Lc, p.nc, p.nck, x, delta, a.A, Bm, Cm, a.Dv, hin, a.dt_bias,
+                     a.dt_softplus, static_cast<const T*>(a.z), static_cast<T*>(a.y),
+                     static_cast<T*>(a.ysave), p.ckpt, a.h_last);
   timer_mark(kKFwdOutput, true, st);
   return hipGetLastError();
 }
 
 template <typename T, int N>
 static hipError_t fwd_vec(const ScanArgs& a, const FwdPlan& p, hipStream_t st) {
-  return a.vec4 ? fwd_impl<T, N, 4>(a, p, st) : fwd_impl<T, N, 1>(a, p, st);
+  if (a.fused) return a.vec4 ? fwd_impl<T, N, 4, true>(a, p, st) : fwd_impl<T, N, 1, true>(a, p, st);
+  return a.vec4 ? fwd_impl<T, N, 4, false>(a, p, st) : fwd_impl<T, N, 1, false>(a, p, st);
 }
 
 hipError_t launch_scan_fwd(const ScanArgs& a, const FwdPlan& p, hipStream_t st) {

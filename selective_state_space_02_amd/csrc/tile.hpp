@@ -177,10 +177,16 @@ struct ChFetch {
       raw[k] = BV::load(G::rsrc(tile, D32, tvalid, dvalid, k), g.off);
   }
   __device__ __forceinline__ void commit(const G& g, float (*sm)[kTileCh]) const {
+    commit_map(g, sm, [](int, float (&)[VEC]) {});
+  }
+  // As commit, with f(k, v) applied to pass k's values (rows g.s_in + k*RPP) first.
+  template <class F>
+  __device__ __forceinline__ void commit_map(const G& g, float (*sm)[kTileCh], F&& f) const {
 #pragma unroll
     for (int k = 0; k < G::kPer; ++k) {
       float v[VEC];
       BV::unpack(raw[k], v);
+      f(k, v);
       float* dst = &sm[g.s_in + k * G::RPP][g.c];
       if constexpr (VEC == 4) {
         *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
@@ -193,10 +199,12 @@ struct ChFetch {
 
 // Writes an LDS tile of per-channel outputs to a [.,L,D] tensor; tile = base + tf*D + d0;
 // rows >= tvalid and channels >= dvalid are not written.
-template <typename T, int VEC>
-__device__ __forceinline__ void tile_store_ch(const ChTile<T, VEC>& g, T* tile,
-                                              const float (*sm)[kTileCh], int D32, int tvalid,
-                                              int dvalid) {
+// tile_store_ch_map applies f(k, v) to pass k's values (rows g.s_in + k*RPP) before the
+// store.
+template <typename T, int VEC, class F>
+__device__ __forceinline__ void tile_store_ch_map(const ChTile<T, VEC>& g, T* tile,
+                                                  const float (*sm)[kTileCh], int D32,
+                                                  int tvalid, int dvalid, F&& f) {
   using G = ChTile<T, VEC>;
   using BV = BufVec<T, VEC>;
 #pragma unroll
@@ -204,12 +212,45 @@ __device__ __forceinline__ void tile_store_ch(const ChTile<T, VEC>& g, T* tile,
     const float* src = &sm[g.s_in + k * G::RPP][g.c];
     float v[VEC];
     if constexpr (VEC == 4) {
-      const float4 f = *reinterpret_cast<const float4*>(src);
-      v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+      const float4 q = *reinterpret_cast<const float4*>(src);
+      v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
     } else {
       v[0] = src[0];
     }
+    f(k, v);
     BV::store(BV::pack(v), G::rsrc(tile, D32, tvalid, dvalid, k), g.off);
+  }
+}
+template <typename T, int VEC>
+__device__ __forceinline__ void tile_store_ch(const ChTile<T, VEC>& g, T* tile,
+                                              const float (*sm)[kTileCh], int D32, int tvalid,
+                                              int dvalid) {
+  tile_store_ch_map(g, tile, sm, D32, tvalid, dvalid, [](int, float (&)[VEC]) {});
+}
+
+// Pass k of a per-channel output tile straight from registers (the ChTile placement).
+template <typename T, int VEC>
+__device__ __forceinline__ void tile_store_regs(const ChTile<T, VEC>& g, T* tile, int k,
+                                                const float (&v)[VEC], int D32, int tvalid,
+                                                int dvalid) {
+  using BV = BufVec<T, VEC>;
+  BV::store(BV::pack(v), ChTile<T, VEC>::rsrc(tile, D32, tvalid, dvalid, k), g.off);
+}
+
+// The fused scan's time step from its raw input, in place: raw + bias[c] through a
+// softplus when sp (the Mamba time step), zero where !ok (rows past the sequence and
+// channels past D: the identity step).  sg, when given, receives the derivative of that
+// map at the point, sigmoid(raw + bias) or 1.
+template <int VEC>
+__device__ __forceinline__ void time_step_map(float (&v)[VEC], const float* bias, bool ok,
+                                              bool sp, float* sg) {
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) {
+    const float p = v[i] + bias[i];
+    float s = p, d = 1.f;
+    if (sp) s = sg ? softplus_sigmoid(p, d) : softplus_f(p);
+    if (sg) sg[i] = d;
+    v[i] = ok ? s : 0.f;
   }
 }
 

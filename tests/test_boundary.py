@@ -63,6 +63,62 @@ def _bwd(lib, B=2, L=64, D=32, N=16, dtype=0, ckpt=FAKE, ws=None, ws_bytes=0, **
                             p["dA"], p["dB"], p["dC"], p["dD"], p["dh0"], ws, ws_bytes)
 
 
+def _ffwd(lib, B=2, L=64, D=32, N=16, dtype=0, ws=None, ws_bytes=0, **kw):
+    p = dict(x=FAKE, delta=FAKE, A=FAKE, Bm=FAKE, Cm=FAKE, Dv=FAKE, h0=None, delta_bias=None,
+             delta_softplus=1, z=None, out=FAKE, y_save=None, ckpt=None, h_last=None)
+    p.update(kw)
+    return lib.ssm_scan_fused_fwd(None, dtype, B, L, D, N, p["x"], p["delta"], p["A"], p["Bm"],
+                                  p["Cm"], p["Dv"], p["h0"], p["delta_bias"],
+                                  p["delta_softplus"], p["z"], p["out"], p["y_save"], p["ckpt"],
+                                  p["h_last"], ws, ws_bytes)
+
+
+def _fbwd(lib, B=2, L=64, D=32, N=16, dtype=0, ckpt=FAKE, ws=None, ws_bytes=0, **kw):
+    p = dict(x=FAKE, delta=FAKE, A=FAKE, Bm=FAKE, Cm=FAKE, Dv=FAKE, h0=None, delta_bias=None,
+             delta_softplus=1, z=None, y_save=None, dout=FAKE, dx=FAKE, ddelta=FAKE, dA=FAKE,
+             dB=FAKE, dC=FAKE, dD=FAKE, dh0=None, dz=None, ddelta_bias=None)
+    p.update(kw)
+    return lib.ssm_scan_fused_bwd(None, dtype, B, L, D, N, p["x"], p["delta"], p["A"], p["Bm"],
+                                  p["Cm"], p["Dv"], p["h0"], p["delta_bias"],
+                                  p["delta_softplus"], p["z"], p["y_save"], p["dout"], ckpt,
+                                  p["dx"], p["ddelta"], p["dA"], p["dB"], p["dC"], p["dD"],
+                                  p["dh0"], p["dz"], p["ddelta_bias"], ws, ws_bytes)
+
+
+def test_scan_fused_validation():
+    lib = b.load()
+    # sizes and dtypes as the plain scan
+    assert _ffwd(lib, N=3) == b.SSM_ERR_UNSUPPORTED
+    assert _fbwd(lib, L=0) == b.SSM_ERR_ARG
+    assert _ffwd(lib, dtype=4) == b.SSM_ERR_UNSUPPORTED
+    for name in ("x", "delta", "A", "Bm", "Cm", "Dv", "out"):
+        assert _ffwd(lib, **{name: None}) == b.SSM_ERR_ARG
+        assert name in b.last_error()
+    for name in ("dout", "dx", "ddelta", "dA", "dB", "dC", "dD"):
+        assert _fbwd(lib, **{name: None}) == b.SSM_ERR_ARG
+        assert name in b.last_error()
+    # optional pointers are checked for alignment when given
+    for name in ("delta_bias", "z", "y_save", "h_last"):
+        assert _ffwd(lib, **{name: MIS}) == b.SSM_ERR_ALIGN, name
+    for name in ("delta_bias", "z", "y_save", "dz", "ddelta_bias", "dh0"):
+        assert _fbwd(lib, **{name: MIS}) == b.SSM_ERR_ALIGN, name
+    # the softplus switch is 0 or 1
+    assert _ffwd(lib, delta_softplus=2) == b.SSM_ERR_ARG
+    assert "delta_softplus" in b.last_error()
+    assert _fbwd(lib, delta_softplus=-1) == b.SSM_ERR_ARG
+    # the gate's pointers come together
+    assert _ffwd(lib, y_save=FAKE) == b.SSM_ERR_ARG
+    assert "y_save" in b.last_error()
+    assert _fbwd(lib, z=FAKE) == b.SSM_ERR_ARG
+    assert _fbwd(lib, z=FAKE, y_save=FAKE) == b.SSM_ERR_ARG
+    assert _fbwd(lib, z=FAKE, dz=FAKE) == b.SSM_ERR_ARG
+    assert _fbwd(lib, dz=FAKE) == b.SSM_ERR_ARG
+    assert _fbwd(lib, y_save=FAKE) == b.SSM_ERR_ARG
+    # workspaces as the plain scan's
+    need = b.ssm_scan_bwd_workspace_bytes(2, 64, 32, 16, 0, 1)
+    assert _fbwd(lib, ws=FAKE, ws_bytes=need - 1) == b.SSM_ERR_WORKSPACE
+
+
 @pytest.mark.parametrize("dims", [(0, 8, 8, 16), (2, 0, 8, 16), (2, 8, 0, 16), (2, 8, 8, 0),
                                   (-1, 8, 8, 16)])
 def test_scan_rejects_nonpositive_sizes(dims):
