@@ -228,45 +228,64 @@ __device__ __forceinline__ void swap16(float& a, float& b) {
 
 // Reduce-scatter of V (2, 4 or 8) values per lane over the 16 lanes that share
 // (lane & 3), i.e. over the 16 channels of a wavefront: the halving steps of a
-// butterfly over lane bits 5, 4 (V >= 4) and 3 (V == 8).  At each step a lane keeps
-// half of its values (the lower half if its bit is 0) and adds the partner's copy of
-// that half; a lane swap does the exchange for bits 5 and 4, a row_ror:8 DPP (lane i
-// reads lane i^8 inside a row of 16) for bit 3.  On return v[0] of lane l holds value
-// index k = l / (64/V), summed over the V channels that agree with l in the remaining
-// channel bits: the 16/V partial sums of (k, l & 3) sit in lanes
-// chan_partial_lane<V>(k, p, l & 3), p < 16/V, and are added by the caller.
+// butterfly over lane bits 3, 2 (V >= 4) and 4 (V == 8), cheapest first.  At each step
+// a lane keeps half of its values (the lower half if its bit is 0) and adds the
+// partner's copy of that half.  Bits 3 and 2 lie inside a row of 16 lanes, where DPP
+// reads the partner within the add (row_ror:8 reaches lane^8; row_shl:4 and row_shr:4
+// reach lane+4 and lane-4, i.e. lane^4 for lanes with bit 2 clear and set); bit 4 takes
+// a lane swap, which moves a whole pair at once.  On return v[0] of a lane holds the
+// value index whose bits, most significant first, are the lane's bits 3, 2, 4 (as many
+// as log2 V), summed over the channels that agree with the lane in the remaining
+// channel bits: the 16/V partial sums of (k, q) sit in lanes chan_partial_lane<V>(k, p,
+// q), p < 16/V, and are added by the caller.
 template <int V>
 __device__ __forceinline__ void chan_reduce_scatter(float (&v)[V], int lane) {
   static_assert(V == 2 || V == 4 || V == 8, "V must be 2, 4 or 8");
-  // bit 5 (lane distance 32)
+  {  // bit 3 (distance 8): a lane sends the half its partner keeps
+    const bool up = (lane & 8) != 0;
 #pragma unroll
-  for (int k = 0; k < V / 2; ++k) {
-    float a = v[k], b = v[k + V / 2];
-    swap32(a, b);
-    v[k] = a + b;
-  }
-  // bit 4 (distance 16)
-  if constexpr (V >= 4) {
-#pragma unroll
-    for (int k = 0; k < V / 4; ++k) {
-      float a = v[k], b = v[k + V / 4];
-      swap16(a, b);
-      v[k] = a + b;
+    for (int k = 0; k < V / 2; ++k) {
+      const float a = v[k], b = v[k + V / 2];
+      const float keep = up ? b : a, send = up ? a : b;
+      v[k] = keep + dpp<0x128>(send);
     }
   }
-  // bit 3 (distance 8): a lane sends the half its partner keeps
-  if constexpr (V >= 8) {
-    const bool up = (lane & 8) != 0;
-    const float keep = up ? v[1] : v[0], send = up ? v[0] : v[1];
-    v[0] = keep + dpp<0x128>(send);
+  if constexpr (V >= 4) {  // bit 2 (distance 4)
+    const bool up = (lane & 4) != 0;
+#pragma unroll
+    for (int k = 0; k < V / 4; ++k) {
+      const float a = v[k], b = v[k + V / 4];
+      const float lo = a + dpp<0x104>(a);  // bit 2 clear: a of lane+4
+      const float hi = b + dpp<0x114>(b);  // bit 2 set: b of lane-4
+      v[k] = up ? hi : lo;
+    }
+  }
+  if constexpr (V >= 8) {  // bit 4 (distance 16)
+    float a = v[0], b = v[1];
+    swap16(a, b);
+    v[0] = a + b;
   }
 }
 
 // Lane that holds partial p (p < 16/V) of value index k for state quarter q after
-// chan_reduce_scatter<V>.
+// chan_reduce_scatter<V>: k's bits (most significant first) at lane bits 3, 2, 4, p's
+// bits (least significant first) at the channel bits left over.
 template <int V>
 __device__ __forceinline__ constexpr int chan_partial_lane(int k, int p, int q) {
-  return k * (64 / V) + p * 4 + q;
+  constexpr int S = V == 8 ? 3 : (V == 4 ? 2 : 1);
+  constexpr int sb[3] = {3, 2, 4};
+  int l = q;
+  for (int s = 0; s < S; ++s) l |= ((k >> (S - 1 - s)) & 1) << sb[s];
+  int j = 0;
+  for (int bit = 2; bit <= 5; ++bit) {
+    bool used = false;
+    for (int s = 0; s < S; ++s) used = used || sb[s] == bit;
+    if (!used) {
+      l |= ((p >> j) & 1) << bit;
+      ++j;
+    }
+  }
+  return l;
 }
 
 }  // namespace ssm
