@@ -186,6 +186,15 @@ def rmsnorm_fwd(x, scale, eps):
     return y, rms
 
 
+def rmsnorm_residual_fwd(x, residual, scale, eps):
+    """The norm with the residual stream added first (the Mamba block's add-then-norm):
+    h = x + residual, then rmsnorm_fwd(h).  Returns (y, rms, h); h is the residual stream
+    passed on, and the backward of the norm takes it as its input."""
+    h = _f64(x) + _f64(residual)
+    y, rms = rmsnorm_fwd(h, scale, eps)
+    return y, rms, h
+
+
 def rmsnorm_bwd(dy, x, scale, rms):
     """Returns dict dx [R,M], dscale [M] (dscale from zero)."""
     dy, x, scale, rms = map(_f64, (dy, x, scale, rms))

@@ -21,7 +21,7 @@ from .workloads import Workload
 
 # tensor ids (fixed order)
 (_X, _DELTA, _B, _C, _DV, _DY, _CX, _CW, _CDOUT, _RX, _RDY, _RSCALE, _H0, _CBIAS, _DRAW, _DBIAS,
- _Z) = range(1, 18)
+ _Z, _RRES) = range(1, 19)
 
 RMS_EPS = 1e-5  # the RMSNorm eps of every workload
 
@@ -107,6 +107,11 @@ def rms_inputs(w: Workload, seed: int = 0) -> dict:
     dy = _normal((R, M), seed, _RDY).to(sd)
     scale = torch.rand((M,), generator=_gen(seed, _RSCALE), dtype=torch.float32) + 0.5
     return dict(x=x, dy=dy, scale=_param(scale, w))
+
+
+def rms_residual(w: Workload, seed: int = 0) -> torch.Tensor:
+    """The residual stream [R,M] ~ N(0,1) added before the norm (storage dtype)."""
+    return _normal((w.rms_rows, w.rms_dim), seed, _RRES).to(_store_dtype(w))
 
 
 def as_f64(t: torch.Tensor):

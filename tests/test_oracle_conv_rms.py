@@ -206,3 +206,34 @@ def test_rms_invariants():
     assert abs(np.dot(scale, r["dscale"]) - np.sum(dy * y)) < 1e-12 * np.sum(np.abs(dy * y))
 
 
+
+
+# ---------------------------------------------------------------------------------
+# the norm with the residual stream added first
+# ---------------------------------------------------------------------------------
+
+def test_rms_residual_reduces_to_the_plain_norm_and_is_symmetric():
+    w = custom(B=2, L=9, D=40)
+    p = _rms(w)
+    res = synth.as_f64(synth.rms_residual(w))
+    y0, rms0 = oracle.rmsnorm_fwd(p["x"], p["scale"], synth.RMS_EPS)
+    y, rms, h = oracle.rmsnorm_residual_fwd(p["x"], np.zeros_like(res), p["scale"], synth.RMS_EPS)
+    assert np.array_equal(y, y0) and np.array_equal(rms, rms0) and np.array_equal(h, p["x"])
+    a = oracle.rmsnorm_residual_fwd(p["x"], res, p["scale"], synth.RMS_EPS)
+    b = oracle.rmsnorm_residual_fwd(res, p["x"], p["scale"], synth.RMS_EPS)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_rms_residual_gradients_are_the_norm_backward_of_the_sum():
+    # d/dx and d/dresidual of sum(dy * y(x + residual)) are both the norm's dx at the sum
+    w = custom(B=2, L=4, D=6)
+    p = _rms(w)
+    res = synth.as_f64(synth.rms_residual(w))
+    x, dy, scale = p["x"], p["dy"], p["scale"]
+    _, rms, h = oracle.rmsnorm_residual_fwd(x, res, scale, synth.RMS_EPS)
+    dx = oracle.rmsnorm_bwd(dy, h, scale, rms)["dx"]
+    fx = fd_grad(lambda t: float(np.sum(dy * oracle.rmsnorm_residual_fwd(t, res, scale, synth.RMS_EPS)[0])), x)
+    fr = fd_grad(lambda t: float(np.sum(dy * oracle.rmsnorm_residual_fwd(x, t, scale, synth.RMS_EPS)[0])), res)
+    assert rel_err(dx, fx) < 1e-7
+    assert rel_err(dx, fr) < 1e-7
