@@ -171,8 +171,9 @@ def cpu_baseline(w, cpu_inputs, sample_channels, budget_note):
 
 
 def measure_layer_forward(w, c, r, seed, steps, dev):
-    """The layer-forward kernels around the scan (conv1d and RMSNorm forward) on the
-    workload's shapes, timed with the library's timing hook over `steps` launches each.
+    """The layer-forward kernels around the scan (conv1d and RMSNorm forward, the latter
+    also with the residual stream added first) on the workload's shapes, timed with the
+    library's timing hook over `steps` launches each.
     Not part of the step and not in `value`; both are HBM-bound, so each reports its
     algorithmic bytes (read the input once, write the output once) per second."""
     import torch
@@ -202,10 +203,31 @@ def measure_layer_forward(w, c, r, seed, steps, dev):
     for k in names:
         ssm.ssm_set_kernel_timer(k, None, None)
     ms = {k: sum(he.elapsed_ms(*pr) for pr in kev[k]) / steps for k in names}
+    # the norm with the residual stream added first (reads x and residual, writes y and
+    # the summed stream)
+    rres = synth.rms_residual(w, seed).to(dev)
+    rout = torch.empty_like(r["x"])
+
+    def run_res():
+        ssm.rmsnorm_fwd(r["x"], r["scale"], synth.RMS_EPS, y=ry, rms=rrms, residual=rres,
+                        residual_out=rout)
+    for _ in range(2):
+        run_res()
+    torch.cuda.synchronize()
+    rev = [he.pair() for _ in range(steps)]
+    for i in range(steps):
+        ssm.ssm_set_kernel_timer("rms_fwd", *rev[i])
+        run_res()
+    torch.cuda.synchronize()
+    ssm.ssm_set_kernel_timer("rms_fwd", None, None)
+    ms["rms_fwd_residual"] = sum(he.elapsed_ms(*pr) for pr in rev) / steps
+    names = names + ("rms_fwd_residual",)
     he.destroy()
     E = w.B * w.L * w.D
+    RM = w.rms_rows * w.rms_dim
     nbytes = {"conv_fwd": 2 * E * s + w.D * (w.K + 1) * 4,
-              "rms_fwd": 2 * w.rms_rows * w.rms_dim * s + (w.rms_dim + w.rms_rows) * 4}
+              "rms_fwd": 2 * RM * s + (w.rms_dim + w.rms_rows) * 4,
+              "rms_fwd_residual": 4 * RM * s + (w.rms_dim + w.rms_rows) * 4}
     out = {}
     for k in names:
         gbps = nbytes[k] / (ms[k] * 1e-3) / 1e9

@@ -10,7 +10,8 @@
  *   conv1d_causal_bwd  depthwise causal conv1d backward (optionally through a SiLU)
  *   rmsnorm_bwd        batched RMSNorm backward
  *   conv1d_causal_fwd  depthwise causal conv1d forward (optionally followed by SiLU)
- *   rmsnorm_fwd        batched RMSNorm forward (also returns the saved rms)
+ *   rmsnorm_fwd        batched RMSNorm forward (also returns the saved rms), optionally
+ *                      after adding the residual stream
  *   ssm_scan_step      one-token decode step of the scan (state updated in place)
  *   conv1d_causal_step one-token decode step of the conv (window updated in place)
  *
@@ -236,11 +237,16 @@ int conv1d_causal_fwd(void *stream, ssm_dtype_t dtype, int64_t B, int64_t L, int
  * per-row rms that the backward takes as its saved statistic (the mamba-rs
  * backward_rms_norm section saves rms, not its inverse):
  *     rms[r] = sqrt(mean_i x[r,i]^2 + eps),   y[r,i] = x[r,i] / rms[r] * scale[i]
- * Shapes: x, y [R,M] (dtype); scale [M] f32; rms [R] f32 (out).  eps finite, >= 0.
- * No workspace.  Supported M: as rmsnorm_bwd.
+ * With the residual stream (residual and residual_out both given, or both NULL), the
+ * block's add comes first: h = x + residual is computed in f32, rounded to the dtype and
+ * written to residual_out (the stream passed on), and the norm above is applied to that
+ * stored h, so that rmsnorm_bwd with x = residual_out and this rms is exact.
+ * Shapes: x, residual, residual_out, y [R,M] (dtype); scale [M] f32; rms [R] f32 (out).
+ * eps finite, >= 0.  No workspace.  Supported M: as rmsnorm_bwd.
  * ------------------------------------------------------------------------------- */
 int rmsnorm_fwd(void *stream, ssm_dtype_t dtype, int64_t R, int64_t M, const void *x,
-                const float *scale, float eps, void *y, float *rms);
+                const void *residual, const float *scale, float eps, void *y, float *rms,
+                void *residual_out);
 
 /* ---------------------------------------------------------------------------------
  * One-token decode step of the selective scan: the single-step updater the rustytorch

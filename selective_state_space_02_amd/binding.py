@@ -84,7 +84,7 @@ def load():
     lib.conv1d_causal_fwd.restype = _E
     lib.conv1d_causal_fwd.argtypes = [_P, _E] + [_I] * 4 + [_P] * 3 + [_E, _P]
     lib.rmsnorm_fwd.restype = _E
-    lib.rmsnorm_fwd.argtypes = [_P, _E] + [_I] * 2 + [_P, _P, ctypes.c_float, _P, _P]
+    lib.rmsnorm_fwd.argtypes = [_P, _E] + [_I] * 2 + [_P, _P, _P, ctypes.c_float, _P, _P, _P]
     lib.ssm_scan_step.restype = _E
     lib.ssm_scan_step.argtypes = [_P, _E] + [_I] * 3 + [_P] * 8
     lib.conv1d_causal_step.restype = _E
@@ -413,8 +413,11 @@ def conv1d_causal_fwd(x, W, bias=None, act="none", out=None):
     return out
 
 
-def rmsnorm_fwd(x, scale, eps, y=None, rms=None):
-    """Returns (y [R, M] in the dtype of x, rms [R] f32)."""
+def rmsnorm_fwd(x, scale, eps, y=None, rms=None, residual=None, residual_out=None):
+    """Returns (y [R, M] in the dtype of x, rms [R] f32).  With the residual stream
+    (`residual`, same shape and dtype as x) the norm is applied to h = x + residual,
+    which is written to residual_out (allocated if not given) and returned third:
+    (y, rms, residual_out)."""
     lib = load()
     R, M = x.shape
     dev = x.device
@@ -423,10 +426,14 @@ def rmsnorm_fwd(x, scale, eps, y=None, rms=None):
     f32 = torch.float32
     y = torch.empty_like(x) if y is None else y
     rms = torch.empty((R,), dtype=f32, device=dev) if rms is None else rms
+    if residual is not None and residual_out is None:
+        residual_out = torch.empty_like(x)
     _check(lib.rmsnorm_fwd(_stream(dev), code, R, M, _ptr(x, "x", dt, (R, M), dev),
+                           _ptr(residual, "residual", dt, (R, M), dev),
                            _ptr(scale, "scale", f32, (M,), dev), float(eps),
-                           _ptr(y, "y", dt, (R, M), dev), _ptr(rms, "rms", f32, (R,), dev)))
-    return y, rms
+                           _ptr(y, "y", dt, (R, M), dev), _ptr(rms, "rms", f32, (R,), dev),
+                           _ptr(residual_out, "residual_out", dt, (R, M), dev)))
+    return (y, rms) if residual is None else (y, rms, residual_out)
 
 
 def ssm_scan_step(h, x_t, delta_t, A, B_t, C_t, Dv, y_t=None):

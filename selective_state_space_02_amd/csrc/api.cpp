@@ -506,7 +506,8 @@ int conv1d_causal_fwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int
 }
 
 int rmsnorm_fwd(void* stream, ssm_dtype_t dtype, int64_t R, int64_t M, const void* x,
-                const float* scale, float eps, void* y, float* rms) {
+                const void* residual, const float* scale, float eps, void* y, float* rms,
+                void* residual_out) {
   if (R <= 0 || M <= 0)
     return fail(SSM_ERR_ARG, "sizes must be positive (R=%lld M=%lld)", (long long)R, (long long)M);
   if (!(eps >= 0.f) || eps > 3.0e38f)
@@ -517,8 +518,11 @@ int rmsnorm_fwd(void* stream, ssm_dtype_t dtype, int64_t R, int64_t M, const voi
   ssm::RmsPlan p{};
   if (!rms_plan(R, M, dtype, &p))
     return fail(SSM_ERR_UNSUPPORTED, "row length M=%lld not supported for this dtype", (long long)M);
-  int rc = check_ptrs({{x, "x"}, {scale, "scale"}, {y, "y"}, {rms, "rms"}}, {});
+  int rc = check_ptrs({{x, "x"}, {scale, "scale"}, {y, "y"}, {rms, "rms"}},
+                      {{residual, "residual"}, {residual_out, "residual_out"}});
   if (rc) return rc;
+  if ((residual == nullptr) != (residual_out == nullptr))
+    return fail(SSM_ERR_ARG, "residual and residual_out must both be given or both be NULL");
   ssm::RmsFwdArgs a{};
   a.dtype = int(dtype);
   a.R = R; a.M = M;
@@ -528,7 +532,8 @@ int rmsnorm_fwd(void* stream, ssm_dtype_t dtype, int64_t R, int64_t M, const voi
   while (cdiv(R, rpb) > INT32_MAX) rpb *= 2;
   a.vec = p.vec; a.passes = p.passes; a.rows_per_block = rpb; a.nblk = cdiv(R, rpb);
   a.eps = eps;
-  a.x = x; a.scale = scale; a.y = y; a.rms = rms;
+  a.x = x; a.residual = residual; a.scale = scale; a.y = y; a.rms = rms;
+  a.residual_out = residual_out;
   return hip_status(ssm::launch_rmsnorm_fwd(a, static_cast<hipStream_t>(stream)), "rmsnorm_fwd");
 }
 

@@ -163,9 +163,11 @@ struct RmsFwdArgs {
   int64_t vec, passes, rows_per_block, nblk;  // as RmsPlan
   float eps;
   const void* x;
+  const void* residual;  // nullable: added to x first
   const float* scale;
   void* y;
   float* rms;
+  void* residual_out;    // with residual: x + residual, the norm's input
 };
 hipError_t launch_rmsnorm_fwd(const RmsFwdArgs& a, hipStream_t st);
 

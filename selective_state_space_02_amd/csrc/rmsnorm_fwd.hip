@@ -1,6 +1,9 @@
 // Batched RMSNorm forward for gfx950, producing the per-row rms that the mamba-rs
 // backward_rms_norm section takes as its saved statistic:
 //   rms[r] = sqrt(mean_i x[r,i]^2 + eps),   y[r,i] = x[r,i] / rms[r] * scale[i].
+// With a residual stream (RES), the norm's input is h = x + residual, stored (in the
+// activation dtype) as residual_out, and the norm reads the stored h: the pair
+// (residual_out, rms) is then exactly what the backward recomputes from.
 //
 // Mapping: one wavefront per row at a time (4 wavefronts per block walk disjoint rows);
 // a lane owns PASSES groups of VEC consecutive columns.  The row is read once into
@@ -19,11 +22,13 @@ __device__ __forceinline__ float wave_sum_fwd(float v) {
   return v;
 }
 
-template <typename T, int VEC, int PASSES>
+template <typename T, int VEC, int PASSES, bool RES>
 __global__ __launch_bounds__(256) void k_rms_fwd(int64_t R, int64_t M, int64_t rows_per_block,
                                                  float eps, const T* __restrict__ x,
+                                                 const T* __restrict__ res,
                                                  const float* __restrict__ scale,
-                                                 T* __restrict__ y, float* __restrict__ rms) {
+                                                 T* __restrict__ y, float* __restrict__ rms,
+                                                 T* __restrict__ res_out) {
   constexpr int CP = 64 * VEC;  // columns per pass
   __shared__ float ssc[PASSES * CP];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -41,6 +46,13 @@ __global__ __launch_bounds__(256) void k_rms_fwd(int64_t R, int64_t M, int64_t r
       const int col = (p * 64 + lane) * VEC;
       if (col < M) {
         load_vec<T, VEC>(xr + col, v[p]);
+        if constexpr (RES) {
+          float rv[VEC];
+          load_vec<T, VEC>(res + r * M + col, rv);
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) v[p][k] = to_f32(from_f32<T>(v[p][k] + rv[k]));
+          VecStore<T, VEC>::run(res_out + r * M + col, v[p]);
+        }
       } else {
 #pragma unroll
         for (int k = 0; k < VEC; ++k) v[p][k] = 0.f;
@@ -70,10 +82,17 @@ __global__ __launch_bounds__(256) void k_rms_fwd(int64_t R, int64_t M, int64_t r
 
 template <typename T, int VEC, int PASSES>
 static void rms_fwd_launch(const RmsFwdArgs& a, hipStream_t st) {
+  const T* x = static_cast<const T*>(a.x);
+  const T* res = static_cast<const T*>(a.residual);
+  T* y = static_cast<T*>(a.y);
+  T* ro = static_cast<T*>(a.residual_out);
   timer_mark(kKRmsFwd, false, st);
-  hipLaunchKernelGGL((k_rms_fwd<T, VEC, PASSES>), dim3(a.nblk), dim3(256), 0, st, a.R, a.M,
-                     a.rows_per_block, a.eps, static_cast<const T*>(a.x), a.scale,
-                     static_cast<T*>(a.y), a.rms);
+  if (res)
+    hipLaunchKernelGGL((k_rms_fwd<T, VEC, PASSES, true>), dim3(a.nblk), dim3(256), 0, st, a.R,
+                       a.M, a.rows_per_block, a.eps, x, res, a.scale, y, a.rms, ro);
+  else
+    hipLaunchKernelGGL((k_rms_fwd<T, VEC, PASSES, false>), dim3(a.nblk), dim3(256), 0, st, a.R,
+                       a.M, a.rows_per_block, a.eps, x, res, a.scale, y, a.rms, ro);
   timer_mark(kKRmsFwd, true, st);
 }
 

@@ -272,8 +272,9 @@ def test_conv_fwd_validation():
     assert _conv_fwd(lib, bias=MIS) == b.SSM_ERR_ALIGN     # optional, but aligned if given
 
 
-def _rms_fwd(lib, R=64, M=128, dtype=0, x=FAKE, scale=FAKE, eps=1e-5, y=FAKE, rms=FAKE):
-    return lib.rmsnorm_fwd(None, dtype, R, M, x, scale, eps, y, rms)
+def _rms_fwd(lib, R=64, M=128, dtype=0, x=FAKE, residual=None, scale=FAKE, eps=1e-5, y=FAKE,
+             rms=FAKE, residual_out=None):
+    return lib.rmsnorm_fwd(None, dtype, R, M, x, residual, scale, eps, y, rms, residual_out)
 
 
 def test_rms_fwd_validation():
@@ -289,6 +290,12 @@ def test_rms_fwd_validation():
     for name in ("x", "scale", "y", "rms"):
         assert _rms_fwd(lib, **{name: None}) == b.SSM_ERR_ARG
         assert _rms_fwd(lib, **{name: MIS}) == b.SSM_ERR_ALIGN
+    # the residual stream: both pointers or neither, aligned
+    assert _rms_fwd(lib, residual=FAKE) == b.SSM_ERR_ARG
+    assert "residual" in b.last_error()
+    assert _rms_fwd(lib, residual_out=FAKE) == b.SSM_ERR_ARG
+    assert _rms_fwd(lib, residual=MIS, residual_out=FAKE) == b.SSM_ERR_ALIGN
+    assert _rms_fwd(lib, residual=FAKE, residual_out=MIS) == b.SSM_ERR_ALIGN
 
 
 def _step(lib, B=2, D=32, N=16, dtype=0, **kw):

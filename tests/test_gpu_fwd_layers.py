@@ -113,3 +113,42 @@ def test_rms_fwd_rows_have_unit_mean_square_before_scale():
     torch.cuda.synchronize()
     ms = (f64(y) ** 2).mean(axis=1)
     assert np.max(np.abs(ms - 1.0)) < 1e-5
+
+
+RES_CASES = [custom(B=3, L=11, D=100), custom(B=2, L=9, D=96, dtype="bf16"),
+             custom(B=1, L=17, D=8192, dtype="bf16"), custom(B=2, L=5, D=203),
+             custom(B=2, L=9, D=2560, dtype="bf16"), custom(B=1, L=33, D=4096)]
+
+
+@pytest.mark.parametrize("w", RES_CASES + [WORKLOADS[-1]],
+                         ids=lambda w: f"R{w.rms_rows}M{w.rms_dim}{w.dtype}")
+def test_rms_fwd_with_residual_matches_oracle(w):
+    say(f"[rms fwd residual parity] R={w.rms_rows} M={w.rms_dim} {w.dtype}")
+    p = synth.rms_inputs(w)
+    res = synth.rms_residual(w)
+    y, rms, h = ssm.rmsnorm_fwd(p["x"].cuda(), p["scale"].cuda(), synth.RMS_EPS,
+                                residual=res.cuda())
+    torch.cuda.synchronize()
+    yr, rr, hr = oracle.rmsnorm_residual_fwd(synth.as_f64(p["x"]), synth.as_f64(res),
+                                             synth.as_f64(p["scale"]), synth.RMS_EPS)
+    compare({"y": y, "h": h}, {"y": yr, "h": hr}, ("y", "h"), label="rms fwd residual")
+    # the norm reads the stored sum: in bf16 each element of it carries a rounding of at
+    # most 2^-9 relative, which moves the row's rms by at most that much
+    tol = TOL_F32 if w.dtype == "f32" else 2.0 ** -9 + TOL_F32
+    e = rel_err(f64(rms), rr)
+    say("rms fwd residual rms", f"{e:.2e} (bound {tol:.1e})")
+    assert e <= tol
+
+
+def test_rms_fwd_residual_output_feeds_the_backward_exactly():
+    # the stored sum and its rms are what the backward takes: forward on residual_out
+    # alone gives the same y and rms bit for bit
+    w = custom(B=2, L=16, D=2560, dtype="bf16")
+    p = synth.rms_inputs(w)
+    res = synth.rms_residual(w).cuda()
+    x, scale = p["x"].cuda(), p["scale"].cuda()
+    y, rms, h = ssm.rmsnorm_fwd(x, scale, synth.RMS_EPS, residual=res)
+    y2, rms2 = ssm.rmsnorm_fwd(h, scale, synth.RMS_EPS)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(rms, rms2)
+
