@@ -230,35 +230,42 @@ __device__ __forceinline__ void swap16(float& a, float& b) {
 // (lane & 3), i.e. over the 16 channels of a wavefront: the halving steps of a
 // butterfly over lane bits 3, 2 (V >= 4) and 4 (V == 8), cheapest first.  At each step
 // a lane keeps half of its values (the lower half if its bit is 0) and adds the
-// partner's copy of that half.  Bits 3 and 2 lie inside a row of 16 lanes, where DPP
-// reads the partner within the add (row_ror:8 reaches lane^8; row_shl:4 and row_shr:4
-// reach lane+4 and lane-4, i.e. lane^4 for lanes with bit 2 clear and set); bit 4 takes
-// a lane swap, which moves a whole pair at once.  On return v[0] of a lane holds the
+// partner's copy of that half.  Bits 3 and 2 lie inside a row of 16 lanes, where two
+// masked DPP adds per pair do it (dpp_halve); bit 4 takes a lane swap, which moves a
+// whole pair at once.  On return v[0] of a lane holds the
 // value index whose bits, most significant first, are the lane's bits 3, 2, 4 (as many
 // as log2 V), summed over the channels that agree with the lane in the remaining
 // channel bits: the 16/V partial sums of (k, q) sit in lanes chan_partial_lane<V>(k, p,
 // q), p < 16/V, and are added by the caller.
+// One halving step of the reduce-scatter inside a row of 16 lanes, for the value pair
+// (a, b): lanes whose bit (3 or 2) is clear get a + a of the partner, the others
+// b + b of the partner.  DPP's bank mask (bank = lanes 4i .. 4i+3 of a row) writes each
+// half of the lanes with its own add, so no select is needed; the partner is read in the
+// add (row_ror:8 is lane^8; for bit 2, row_shl:4 reads lane+4 in banks 0 and 2 and
+// row_shr:4 lane-4 in banks 1 and 3).  The compiler emits DPP only with full masks,
+// hence the asm; s_nop 1 covers the wait states a DPP read needs after a VALU write.
+template <int BIT>
+__device__ __forceinline__ float dpp_halve(float a, float b) {
+  float r;
+  if constexpr (BIT == 3)
+    asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+        "v_add_f32_dpp %0, %2, %2 row_ror:8 row_mask:0xf bank_mask:0xc"
+        : "=&v"(r) : "v"(a), "v"(b));
+  else
+    asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_shl:4 row_mask:0xf bank_mask:0x5\n\t"
+        "v_add_f32_dpp %0, %2, %2 row_shr:4 row_mask:0xf bank_mask:0xa"
+        : "=&v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 template <int V>
-__device__ __forceinline__ void chan_reduce_scatter(float (&v)[V], int lane) {
+__device__ __forceinline__ void chan_reduce_scatter(float (&v)[V], int) {
   static_assert(V == 2 || V == 4 || V == 8, "V must be 2, 4 or 8");
-  {  // bit 3 (distance 8): a lane sends the half its partner keeps
-    const bool up = (lane & 8) != 0;
 #pragma unroll
-    for (int k = 0; k < V / 2; ++k) {
-      const float a = v[k], b = v[k + V / 2];
-      const float keep = up ? b : a, send = up ? a : b;
-      v[k] = keep + dpp<0x128>(send);
-    }
-  }
-  if constexpr (V >= 4) {  // bit 2 (distance 4)
-    const bool up = (lane & 4) != 0;
+  for (int k = 0; k < V / 2; ++k) v[k] = dpp_halve<3>(v[k], v[k + V / 2]);  // bit 3
+  if constexpr (V >= 4) {
 #pragma unroll
-    for (int k = 0; k < V / 4; ++k) {
-      const float a = v[k], b = v[k + V / 4];
-      const float lo = a + dpp<0x104>(a);  // bit 2 clear: a of lane+4
-      const float hi = b + dpp<0x114>(b);  // bit 2 set: b of lane-4
-      v[k] = up ? hi : lo;
-    }
+    for (int k = 0; k < V / 4; ++k) v[k] = dpp_halve<2>(v[k], v[k + V / 4]);  // bit 2
   }
   if constexpr (V >= 8) {  // bit 4 (distance 16)
     float a = v[0], b = v[1];
