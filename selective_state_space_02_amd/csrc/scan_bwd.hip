@@ -332,9 +332,8 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
       const int s0 = half * SL;
       // Recompute the interval's steps s0 .. s0+SL-1 from its checkpoint into the stash.
       // The LDS operands of step s+1 are read during step s.
-      float h[NS];
-#pragma unroll
-      for (int j = 0; j < NS; ++j) h[j] = hcur[half][j];
+      // each step's state is written straight into its stash slot (and fenced there),
+      // so the stash costs no register copies
       float as[SL][NS], hs[SL][NS];
       float ndl = sd[buf][s0][cl], nxv = sx[buf][s0][cl], nB[NS];
       tile_read_vec<N, NS>(sB[buf], s0, q, nB);
@@ -353,11 +352,10 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
           const float a = __builtin_amdgcn_exp2f(dl * A2[j]);
-          h[j] = __builtin_fmaf(a, h[j], u * Bv[j]);
+          hs[i][j] = __builtin_fmaf(a, i ? hs[i - 1][j] : hcur[half][j], u * Bv[j]);
           as[i][j] = a;
-          hs[i][j] = h[j];
         }
-        step_fence_arr(h);
+        step_fence_arr(hs[i]);
         step_fence_arr(nB);
         step_fence(ndl, nxv);
       }
