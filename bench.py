@@ -126,6 +126,16 @@ def bwd_main_bytes(w):
     return 5 * E * s + 2 * P * s
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, cpu_inputs, sample_channels, budget_note):
     """The f64 oracle on a bounded sample: the scan forward+backward and the conv1d
     backward on `sample_channels` channels (all batch rows, full length), and the
@@ -162,6 +172,7 @@ def cpu_baseline(w, cpu_inputs, sample_channels, budget_note):
         "value": tokch / (t3 - t0),
         "unit": "tokens*channels/s",
         "cores": oracle.num_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"{sample_channels} of {w.D} channels (all {w.B} batch rows x {w.L} steps) "
                    f"for the scan fwd+bwd and conv1d bwd, {nrows} of {w.rms_rows} rows for the "
@@ -361,6 +372,29 @@ def measure_scan_fused(w, seed, steps, dev):
             "unfused_extra_ms_at_hbm_peak": extra / (HBM_PEAK_GBPS * 1e9) * 1e3}
 
 
+def measure_copy_GBps(dev, reps=5):
+    """A plain 1 GiB device-to-device copy (torch's copy on the current stream), timed
+    with events: the practical HBM rate the bandwidth fractions are also quoted against
+    (read + write bytes per second)."""
+    import torch
+    a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    he = HipEvents()
+    st = torch.cuda.current_stream(dev).cuda_stream
+    pairs = [he.pair() for _ in range(reps)]
+    for pr in pairs:
+        he.record(pr[0], st)
+        b.copy_(a)
+        he.record(pr[1], st)
+    torch.cuda.synchronize()
+    ms = sorted(he.elapsed_ms(*pr) for pr in pairs)[reps // 2]
+    he.destroy()
+    del a, b
+    return 2 * (1 << 30) / (ms * 1e-3) / 1e9
+
+
 # Sequences decoded together: a serving batch whose f32 state (1024 x 5120 x 16 x 4 B =
 # 335 MB on the 2.8B layer) exceeds the 256 MB Infinity Cache, so the scan step's rate
 # is an HBM rate (at 256 sequences the 84 MB state stays cache-resident across tokens).
@@ -552,6 +586,8 @@ def main():
     scan_fused["overhead_vs_plain_ms"] = (scan_fused["call_ms"]["fused_fwd"] +
                                           scan_fused["call_ms"]["fused_bwd"] - scan_ms)
 
+    copy_gbps = measure_copy_GBps(dev)
+
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=f32, device=dev)
         b2 = torch.empty_like(a)
@@ -577,7 +613,11 @@ def main():
         "hbm": {"algorithmic_bytes_per_step": step_bytes,
                 "GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
                 "frac_of_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                "scan_fwd_bwd_GBps": (ab["scan_fwd"] + ab["scan_bwd"]) / (scan_ms * 1e-3) / 1e9},
+                "scan_fwd_bwd_GBps": (ab["scan_fwd"] + ab["scan_bwd"]) / (scan_ms * 1e-3) / 1e9,
+                "conv_bwd_GBps": ab["conv_bwd"] / (call_ms["conv_bwd"] * 1e-3) / 1e9,
+                "rms_bwd_GBps": ab["rms_bwd"] / (call_ms["rms_bwd"] * 1e-3) / 1e9,
+                "copy_GBps": copy_gbps,
+                "frac_of_copy": step_bytes / (ms_per_step * 1e-3) / 1e9 / copy_gbps},
         "scan_fwd_bwd_tokens_channels_per_s": tokch / (scan_ms * 1e-3),
         "call_ms": call_ms,
         "kernel_ms": kern_ms,

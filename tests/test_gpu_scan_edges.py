@@ -1,0 +1,58 @@
+"""GPU parity of the scan at the edges of its supported sizes, and on degenerate inputs.
+
+- Sizes: 2^18 channels (4096 channel groups in one launch), the largest batch the grid
+  takes (65535 rows), and a long ragged sequence over one channel group (thousands of
+  coarse chunks and a long carry chain).  Every output is compared with the oracle.
+- Degenerate inputs the method has closed forms for: a zero time step makes every step
+  the identity (the state stays h0, y = C.h0 + Dv.x), and a zero upstream gradient gives
+  exactly zero gradients.
+"""
+import numpy as np
+import pytest
+import torch
+
+from selective_state_space_02_amd import binding as ssm
+from selective_state_space_02_amd import synth
+from selective_state_space_02_amd.workloads import custom
+from tests.gpu_common import compare, f64, say, scan_gpu, scan_oracle
+
+pytestmark = pytest.mark.gpu
+
+ALL = ("y", "h_last", "dx", "ddelta", "dA", "dB", "dC", "dD", "dh0")
+
+EDGES = [
+    ("many-channels-bf16", custom(B=1, L=40, D=1 << 18, N=16, dtype="bf16"), False),
+    ("max-batch-f32", custom(B=65535, L=3, D=8, N=4), True),
+    ("long-ragged-f32", custom(B=1, L=100003, D=8, N=16), True),
+]
+
+
+@pytest.mark.parametrize("name,w,with_h0", EDGES, ids=[e[0] for e in EDGES])
+def test_scan_edge_sizes_match_oracle(name, w, with_h0):
+    say(f"[scan edge] {name} B={w.B} L={w.L} D={w.D} N={w.N} {w.dtype}")
+    p = synth.scan_inputs(w, seed=2, with_h0=with_h0)
+    got = scan_gpu(p, use_ckpt=True)
+    compare(got, scan_oracle(p), ALL, label=name)
+
+
+def test_zero_time_step_is_the_identity():
+    w = custom(B=2, L=70, D=24, N=16)
+    p = synth.scan_inputs(w, seed=3, with_h0=True)
+    p["delta"] = torch.zeros_like(p["delta"])
+    got = scan_gpu(p)
+    h0, x, Cm, Dv = (f64(p[k]) for k in ("h0", "x", "Cm", "Dv"))
+    # every step leaves the state at h0: y = C.h0 + Dv x (f32 arithmetic, exact inputs)
+    y_ref = np.einsum("btn,bdn->btd", Cm, h0) + Dv * x
+    compare({"y": got["y"], "h_last": got["h_last"]}, {"y": y_ref, "h_last": h0},
+            ("y", "h_last"), label="zero time step")
+    # nothing flows to B (its term is scaled by the time step)
+    assert torch.count_nonzero(got["dB"]) == 0
+
+
+def test_zero_upstream_gradient_gives_zero_gradients():
+    w = custom(B=2, L=90, D=40, N=8, dtype="bf16")
+    p = synth.scan_inputs(w, seed=4, with_h0=True)
+    p["dy"] = torch.zeros_like(p["dy"])
+    got = scan_gpu(p)
+    for k in ("dx", "ddelta", "dA", "dB", "dC", "dD", "dh0"):
+        assert torch.count_nonzero(got[k]) == 0, k
