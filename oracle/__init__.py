@@ -285,3 +285,17 @@ def scan_fused_bwd(x, delta_raw, A, Bm, Cm, Dv, dout, h0=None, delta_bias=None,
     r["ddelta_bias"] = r["ddelta"].sum(axis=(0, 1))
     r["dz"] = dz
     return r
+
+
+def scan_fused_step(h, x_t, delta_t, A, B_t, C_t, Dv, delta_bias=None, delta_softplus=False,
+                    z_t=None):
+    """One token of scan_fused_fwd: the time step softplus(delta_t + delta_bias) (or
+    without the softplus), one scan step, then the gate y_t * silu(z_t).  Returns
+    (h', out_t)."""
+    pre = _f64(delta_t)
+    if delta_bias is not None:
+        pre = pre + _f64(delta_bias)[None, :]
+    dt = softplus(pre) if delta_softplus else pre
+    h2, y = scan_step(h, x_t, dt, A, B_t, C_t, Dv)
+    return h2, (y * silu(z_t) if z_t is not None else y)
+

@@ -155,3 +155,32 @@ def test_scan_fused_time_step_is_positive_and_gate_vanishes_at_zero():
                                  h0=p["h0"], delta_bias=p["delta_bias"], delta_softplus=True,
                                  z=np.zeros_like(p["z"]))
     assert np.all(zero["out"] == 0.0)
+
+
+def test_scan_fused_step_decodes_the_fused_sequence():
+    # token by token from h0, the fused step reproduces the pinned fused sequence forward
+    for cfg in FUSED_CONFIGS:
+        p = _fused_inputs(cfg, seed=5)
+        f = oracle.scan_fused_fwd(p["x"], p["delta_raw"], p["A"], p["Bm"], p["Cm"], p["Dv"],
+                                  **_fused_kw(p, cfg))
+        h = p["h0"]
+        for t in range(p["x"].shape[1]):
+            h, o = oracle.scan_fused_step(h, p["x"][:, t], p["delta_raw"][:, t], p["A"],
+                                          p["Bm"][:, t], p["Cm"][:, t], p["Dv"],
+                                          delta_bias=p["delta_bias"],
+                                          delta_softplus=cfg["delta_softplus"],
+                                          z_t=None if p["z"] is None else p["z"][:, t])
+            np.testing.assert_allclose(o, f["out"][:, t], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(h, f["h_last"], rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("K", [1, 4, 7])
+def test_conv_step_with_silu_decodes_the_silu_conv(K):
+    w = custom(B=2, L=9, D=5, K=K)
+    c = {k: synth.as_f64(v) for k, v in synth.conv_inputs(w).items()}
+    bias = synth.as_f64(synth.conv_bias(w))
+    ref = conv_silu_fwd(c["x"], c["W"], bias)
+    state = np.zeros((w.B, K - 1, w.D))
+    for t in range(w.L):
+        state, o = oracle.conv1d_step(state, c["x"][:, t], c["W"], bias)
+        np.testing.assert_allclose(oracle.silu(o), ref[:, t], rtol=1e-13, atol=1e-14)
