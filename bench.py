@@ -454,6 +454,36 @@ def measure_decode(w, seed, steps, dev):
         gbps = nbytes[k] / (ms[k] * 1e-3) / 1e9
         out[k] = {"kernel_ms": ms[k], "algorithmic_bytes": nbytes[k], "GBps": gbps,
                   "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS}
+
+    # the Mamba block's token: conv step with its SiLU, then the fused scan step (time
+    # step softplus(delta + bias), output gate silu(z)), still two launches
+    f = {k: v.to(dev) for k, v in synth.scan_fused_inputs(wd, seed, with_h0=True).items()}
+    hf = f["h0"].clone()
+    ft = {k: f[k][:, 0].contiguous() for k in ("x", "delta_raw", "Bm", "Cm", "z")}
+
+    def fused_token():
+        ssm.conv1d_causal_step(state, cx, c["W"], bias, act="silu", out_t=cout)
+        ssm.ssm_scan_fused_step(hf, ft["x"], ft["delta_raw"], f["A"], ft["Bm"], ft["Cm"], f["Dv"],
+                                delta_bias=f["delta_bias"], delta_softplus=True, z_t=ft["z"],
+                                out_t=yt)
+    for _ in range(3):
+        fused_token()
+    torch.cuda.synchronize()
+    he = HipEvents()
+    fev = [he.pair() for _ in range(steps)]
+    sev = [he.pair() for _ in range(steps)]
+    for i in range(steps):
+        ssm.ssm_set_kernel_timer("scan_step", *sev[i])
+        he.record(fev[i][0], stream)
+        fused_token()
+        he.record(fev[i][1], stream)
+    torch.cuda.synchronize()
+    ssm.ssm_set_kernel_timer("scan_step", None, None)
+    ftok = sum(he.elapsed_ms(*pr) for pr in fev) / steps
+    fscan = sum(he.elapsed_ms(*pr) for pr in sev) / steps
+    he.destroy()
+    out["fused"] = {"token_ms": ftok, "tokens_per_s": Bd / (ftok * 1e-3),
+                    "scan_step_kernel_ms": fscan}
     return out
 
 

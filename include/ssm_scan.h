@@ -14,6 +14,7 @@
  *                      after adding the residual stream
  *   ssm_scan_step      one-token decode step of the scan (state updated in place)
  *   conv1d_causal_step one-token decode step of the conv (window updated in place)
+ *   ssm_scan_fused_step one-token decode step of the fused scan
  *
  * Common conventions
  * ------------------
@@ -270,13 +271,27 @@ int ssm_scan_step(void *stream, ssm_dtype_t dtype, int64_t B, int64_t D, int64_t
  * the last K-1 inputs, oldest first (all zero at the start of a sequence):
  *     out_t[b,d] = bias[d] + sum_{k<K-1} W[d,k] * state[b,k,d] + W[d,K-1] * x_t[b,d]
  * then the window moves one step in place (the oldest input drops out, x_t becomes the
- * newest).  A sequence stepped token by token gives conv1d_causal_fwd's outputs.
+ * newest).  A sequence stepped token by token gives conv1d_causal_fwd's outputs (with
+ * the same act: SSM_ACT_SILU stores silu of the sum).
  * Shapes: x_t, out_t [B,D] (dtype); W [D,K] f32; bias [D] f32 or NULL (zero); state may
- * be NULL when K = 1.  No workspace.  Supported: K in [1, 8].
+ * be NULL when K = 1.  No workspace.  Supported: K in [1, 8], B*D <= 2^38.
  * ------------------------------------------------------------------------------- */
 int conv1d_causal_step(void *stream, ssm_dtype_t dtype, int64_t B, int64_t D, int64_t K,
                        void *state, const void *x_t, const float *W, const float *bias,
-                       void *out_t);
+                       ssm_act_t act, void *out_t);
+
+/* ---------------------------------------------------------------------------------
+ * One token of ssm_scan_fused_fwd: the time step dt = softplus(delta_t + delta_bias)
+ * (delta_softplus = 1) or delta_t + delta_bias (0; delta_bias NULL = zero), one step of
+ * ssm_scan_step with it, and out_t = y_t * silu(z_t) when z_t is given (else y_t).  A
+ * sequence decoded token by token from h = h0 gives ssm_scan_fused_fwd's out and final
+ * state.  Shapes as ssm_scan_step; delta_bias [D] f32; z_t [B,D] (dtype).  No workspace.
+ * ------------------------------------------------------------------------------- */
+int ssm_scan_fused_step(void *stream, ssm_dtype_t dtype, int64_t B, int64_t D, int64_t N,
+                        float *h, const void *x_t, const void *delta_t, const float *A,
+                        const void *B_t, const void *C_t, const float *Dv,
+                        const float *delta_bias, int delta_softplus, const void *z_t,
+                        void *out_t);
 
 #ifdef __cplusplus
 }

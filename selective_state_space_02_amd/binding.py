@@ -24,7 +24,8 @@ EXPORTS = ("ssm_last_error", "ssm_version", "ssm_set_kernel_timer", "ssm_scan_ck
            "ssm_scan_fwd_workspace_bytes", "ssm_scan_bwd_workspace_bytes", "ssm_scan_fwd",
            "ssm_scan_bwd", "conv1d_causal_bwd_workspace_bytes", "conv1d_causal_bwd",
            "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd", "conv1d_causal_fwd", "rmsnorm_fwd",
-           "ssm_scan_step", "conv1d_causal_step", "ssm_scan_fused_fwd", "ssm_scan_fused_bwd")
+           "ssm_scan_step", "conv1d_causal_step", "ssm_scan_fused_fwd", "ssm_scan_fused_bwd",
+           "ssm_scan_fused_step")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -88,7 +89,9 @@ def load():
     lib.ssm_scan_step.restype = _E
     lib.ssm_scan_step.argtypes = [_P, _E] + [_I] * 3 + [_P] * 8
     lib.conv1d_causal_step.restype = _E
-    lib.conv1d_causal_step.argtypes = [_P, _E] + [_I] * 3 + [_P] * 5
+    lib.conv1d_causal_step.argtypes = [_P, _E] + [_I] * 3 + [_P] * 4 + [_E, _P]
+    lib.ssm_scan_fused_step.restype = _E
+    lib.ssm_scan_fused_step.argtypes = [_P, _E] + [_I] * 3 + [_P] * 8 + [_E, _P, _P]
     _lib = lib
     return lib
 
@@ -454,9 +457,38 @@ def ssm_scan_step(h, x_t, delta_t, A, B_t, C_t, Dv, y_t=None):
     return y_t
 
 
-def conv1d_causal_step(state, x_t, W, bias=None, out_t=None):
-    """One token: moves the window state [B, K-1, D] in place; returns out_t [B, D]."""
+def ssm_scan_fused_step(h, x_t, delta_t, A, B_t, C_t, Dv, delta_bias=None,
+                        delta_softplus=False, z_t=None, out_t=None):
+    """One token of the fused scan: advances h [B, D, N] (f32) in place with the time step
+    softplus(delta_t + delta_bias) (or without the softplus); returns out_t [B, D], gated
+    by silu(z_t) when z_t is given."""
     lib = load()
+    Bsz, D, N = h.shape
+    dev = x_t.device
+    dt = x_t.dtype
+    code = _dtype_code(x_t)
+    f32 = torch.float32
+    out_t = torch.empty_like(x_t) if out_t is None else out_t
+    _check(lib.ssm_scan_fused_step(_stream(dev), code, Bsz, D, N,
+                                   _ptr(h, "h", f32, (Bsz, D, N), dev),
+                                   _ptr(x_t, "x_t", dt, (Bsz, D), dev),
+                                   _ptr(delta_t, "delta_t", dt, (Bsz, D), dev),
+                                   _ptr(A, "A", f32, (D, N), dev),
+                                   _ptr(B_t, "B_t", dt, (Bsz, N), dev),
+                                   _ptr(C_t, "C_t", dt, (Bsz, N), dev),
+                                   _ptr(Dv, "Dv", f32, (D,), dev),
+                                   _ptr(delta_bias, "delta_bias", f32, (D,), dev),
+                                   1 if delta_softplus else 0,
+                                   _ptr(z_t, "z_t", dt, (Bsz, D), dev),
+                                   _ptr(out_t, "out_t", dt, (Bsz, D), dev)))
+    return out_t
+
+
+def conv1d_causal_step(state, x_t, W, bias=None, act="none", out_t=None):
+    """One token: moves the window state [B, K-1, D] in place; returns out_t [B, D]
+    (silu of the conv when act="silu")."""
+    lib = load()
+    ac = _act_code(act)
     Bsz, D = x_t.shape
     K = W.shape[1]
     dev = x_t.device
@@ -468,6 +500,6 @@ def conv1d_causal_step(state, x_t, W, bias=None, out_t=None):
     bp = _ptr(bias, "bias", f32, (D,), dev) if bias is not None else None
     _check(lib.conv1d_causal_step(_stream(dev), code, Bsz, D, K, sp,
                                   _ptr(x_t, "x_t", dt, (Bsz, D), dev),
-                                  _ptr(W, "W", f32, (D, K), dev), bp,
+                                  _ptr(W, "W", f32, (D, K), dev), bp, ac,
                                   _ptr(out_t, "out_t", dt, (Bsz, D), dev)))
     return out_t

@@ -553,16 +553,43 @@ int ssm_scan_step(void* stream, ssm_dtype_t dtype, int64_t B, int64_t D, int64_t
   return hip_status(ssm::launch_scan_step(a, static_cast<hipStream_t>(stream)), "ssm_scan_step");
 }
 
+int ssm_scan_fused_step(void* stream, ssm_dtype_t dtype, int64_t B, int64_t D, int64_t N,
+                        float* h, const void* x_t, const void* delta_t, const float* A,
+                        const void* B_t, const void* C_t, const float* Dv,
+                        const float* delta_bias, int delta_softplus, const void* z_t,
+                        void* out_t) {
+  int rc = check_scan_dims(dtype, B, 1, D, N);
+  if (rc) return rc;
+  rc = check_ptrs({{h, "h"}, {x_t, "x_t"}, {delta_t, "delta_t"}, {A, "A"}, {B_t, "B_t"},
+                   {C_t, "C_t"}, {Dv, "Dv"}, {out_t, "out_t"}},
+                  {{delta_bias, "delta_bias"}, {z_t, "z_t"}});
+  if (rc) return rc;
+  if (delta_softplus != 0 && delta_softplus != 1)
+    return fail(SSM_ERR_ARG, "delta_softplus must be 0 or 1 (got %d)", delta_softplus);
+  ssm::ScanStepArgs a{};
+  a.dtype = int(dtype);
+  a.B = B; a.D = D; a.N = N;
+  a.h = h; a.x_t = x_t; a.delta_t = delta_t; a.A = A; a.B_t = B_t; a.C_t = C_t; a.Dv = Dv;
+  a.y_t = out_t;
+  a.fused = true;
+  a.dt_bias = delta_bias; a.dt_softplus = delta_softplus != 0; a.z_t = z_t;
+  return hip_status(ssm::launch_scan_step(a, static_cast<hipStream_t>(stream)),
+                    "ssm_scan_fused_step");
+}
+
 int conv1d_causal_step(void* stream, ssm_dtype_t dtype, int64_t B, int64_t D, int64_t K,
                        void* state, const void* x_t, const float* W, const float* bias,
-                       void* out_t) {
+                       ssm_act_t act, void* out_t) {
   if (B <= 0 || D <= 0 || K <= 0)
     return fail(SSM_ERR_ARG, "sizes must be positive (B=%lld D=%lld K=%lld)", (long long)B,
                 (long long)D, (long long)K);
   if (dtype != SSM_F32 && dtype != SSM_BF16)
     return fail(SSM_ERR_UNSUPPORTED, "dtype %d not supported", int(dtype));
+  if (act != SSM_ACT_NONE && act != SSM_ACT_SILU)
+    return fail(SSM_ERR_UNSUPPORTED, "activation %d not supported (0 none, 1 SiLU)", int(act));
   if (K > 8) return fail(SSM_ERR_UNSUPPORTED, "conv width K=%lld not supported (1..8)", (long long)K);
-  if (B > kMaxElems / D || B * D > (int64_t(1) << 40))
+  // one thread per (b, d): the grid's 2^31 - 1 blocks of 256 bound B*D
+  if (B > kMaxElems / D || B * D > (int64_t(1) << 38))
     return fail(SSM_ERR_ARG, "tensor sizes overflow");
   int rc = K > 1 ? check_ptrs({{state, "state"}, {x_t, "x_t"}, {W, "W"}, {out_t, "out_t"}},
                               {{bias, "bias"}})
@@ -572,6 +599,7 @@ int conv1d_causal_step(void* stream, ssm_dtype_t dtype, int64_t B, int64_t D, in
   ssm::ConvStepArgs a{};
   a.dtype = int(dtype);
   a.B = B; a.D = D; a.K = K;
+  a.act = int(act);
   a.state = state; a.x_t = x_t; a.W = W; a.bias = bias; a.out_t = out_t;
   return hip_status(ssm::launch_conv1d_step(a, static_cast<hipStream_t>(stream)),
                     "conv1d_causal_step");

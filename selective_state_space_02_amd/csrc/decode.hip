@@ -15,6 +15,10 @@
 // over the window (state, x_t), in the conv forward kernel's order; the window then
 // moves one step.
 //
+// Fused forms, as the sequence kernels' (same functions, same order, so decoding stays
+// bit-identical to them): the scan step's time step softplus(delta_t + bias) (FZ) and
+// output gate y * silu(z_t); the conv step's SiLU (ACT).
+//
 // Both are HBM-bound: the scan step reads and writes h (8 bytes per state), the conv
 // step reads and writes the window.
 #include "common.hpp"
@@ -22,7 +26,7 @@
 
 namespace ssm {
 
-template <typename T, int N>
+template <typename T, int N, bool FZ>
 __global__ __launch_bounds__(256) void k_scan_step(int64_t D, float* __restrict__ h,
                                                    const T* __restrict__ x_t,
                                                    const T* __restrict__ delta_t,
@@ -30,13 +34,23 @@ __global__ __launch_bounds__(256) void k_scan_step(int64_t D, float* __restrict_
                                                    const T* __restrict__ B_t,
                                                    const T* __restrict__ C_t,
                                                    const float* __restrict__ Dv,
+                                                   const float* __restrict__ dtb, bool sp,
+                                                   const T* __restrict__ z_t,
                                                    T* __restrict__ y_t) {
   constexpr int NS = N / 4;
   const int tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
   const int64_t b = blockIdx.y, d = int64_t(blockIdx.x) * 64 + cl;
   if (d >= D) return;  // a channel's four lanes leave together; the quad sum stays in-quad
   const int64_t bd = b * D + d;
-  const float xv = to_f32(x_t[bd]), dl = to_f32(delta_t[bd]);
+  const float xv = to_f32(x_t[bd]);
+  float dl = to_f32(delta_t[bd]);
+  float zv = 0.f;  // the gate input, loaded with the other inputs (not at the store)
+  if constexpr (FZ) {
+    const float bias = dtb ? dtb[d] : 0.f;
+    if (z_t) zv = to_f32(z_t[bd]);
+    dl += bias;
+    if (sp) dl = softplus_f(dl);
+  }
   float hv[NS], Av[NS], Bv[NS], Cv[NS];
   VecLoad<float, NS>::run(h + bd * N + q * NS, hv);
   VecLoad<float, NS>::run(A + d * N + q * NS, Av);
@@ -52,10 +66,16 @@ __global__ __launch_bounds__(256) void k_scan_step(int64_t D, float* __restrict_
   }
   yp = quad_sum(yp);
   VecStore<float, NS>::run(h + bd * N + q * NS, hv);
-  if (q == 0) y_t[bd] = from_f32<T>(__builtin_fmaf(Dv[d], xv, yp));
+  if (q == 0) {
+    float yv = __builtin_fmaf(Dv[d], xv, yp);
+    if constexpr (FZ) {
+      if (z_t) yv *= zv * sigmoid_f(zv);
+    }
+    y_t[bd] = from_f32<T>(yv);
+  }
 }
 
-template <typename T, int K>
+template <typename T, int K, int ACT>
 __global__ __launch_bounds__(256) void k_conv_step(int64_t B, int64_t D, T* __restrict__ state,
                                                    const T* __restrict__ x_t,
                                                    const float* __restrict__ W,
@@ -71,19 +91,29 @@ __global__ __launch_bounds__(256) void k_conv_step(int64_t B, int64_t D, T* __re
   float acc = bias ? bias[d] : 0.f;
 #pragma unroll
   for (int k = 0; k < K; ++k) acc = __builtin_fmaf(W[d * K + k], win[k], acc);
+  if constexpr (ACT == kActSilu) acc *= sigmoid_f(acc);
   out_t[i] = from_f32<T>(acc);
   // the values came from T, so storing them back in T is exact
 #pragma unroll
   for (int k = 0; k < K - 1; ++k) state[(b * (K - 1) + k) * D + d] = from_f32<T>(win[k + 1]);
 }
 
+template <typename T, int N, bool FZ>
+static void scan_step_nf(const ScanStepArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((k_scan_step<T, N, FZ>), dim3(unsigned((a.D + 63) / 64), unsigned(a.B)),
+                     dim3(256), 0, st, a.D, a.h, static_cast<const T*>(a.x_t),
+                     static_cast<const T*>(a.delta_t), a.A, static_cast<const T*>(a.B_t),
+                     static_cast<const T*>(a.C_t), a.Dv, a.dt_bias, a.dt_softplus,
+                     static_cast<const T*>(a.z_t), static_cast<T*>(a.y_t));
+}
+
 template <typename T, int N>
 static hipError_t scan_step_n(const ScanStepArgs& a, hipStream_t st) {
   timer_mark(kKScanStep, false, st);
-  hipLaunchKernelGGL((k_scan_step<T, N>), dim3(unsigned((a.D + 63) / 64), unsigned(a.B)),
-                     dim3(256), 0, st, a.D, a.h, static_cast<const T*>(a.x_t),
-                     static_cast<const T*>(a.delta_t), a.A, static_cast<const T*>(a.B_t),
-                     static_cast<const T*>(a.C_t), a.Dv, static_cast<T*>(a.y_t));
+  if (a.fused)
+    scan_step_nf<T, N, true>(a, st);
+  else
+    scan_step_nf<T, N, false>(a, st);
   timer_mark(kKScanStep, true, st);
   return hipGetLastError();
 }
@@ -102,13 +132,21 @@ hipError_t launch_scan_step(const ScanStepArgs& a, hipStream_t st) {
   return a.dtype == 0 ? scan_step_t<float>(a, st) : scan_step_t<bf16_t>(a, st);
 }
 
+template <typename T, int K, int ACT>
+static void conv_step_ka(const ConvStepArgs& a, hipStream_t st) {
+  const int64_t n = a.B * a.D;
+  hipLaunchKernelGGL((k_conv_step<T, K, ACT>), dim3(unsigned((n + 255) / 256)), dim3(256), 0, st,
+                     a.B, a.D, static_cast<T*>(a.state), static_cast<const T*>(a.x_t), a.W,
+                     a.bias, static_cast<T*>(a.out_t));
+}
+
 template <typename T, int K>
 static hipError_t conv_step_k(const ConvStepArgs& a, hipStream_t st) {
-  const int64_t n = a.B * a.D;
   timer_mark(kKConvStep, false, st);
-  hipLaunchKernelGGL((k_conv_step<T, K>), dim3(unsigned((n + 255) / 256)), dim3(256), 0, st, a.B,
-                     a.D, static_cast<T*>(a.state), static_cast<const T*>(a.x_t), a.W, a.bias,
-                     static_cast<T*>(a.out_t));
+  if (a.act == kActSilu)
+    conv_step_ka<T, K, kActSilu>(a, st);
+  else
+    conv_step_ka<T, K, kActNone>(a, st);
   timer_mark(kKConvStep, true, st);
   return hipGetLastError();
 }

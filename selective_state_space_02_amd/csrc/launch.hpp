@@ -182,6 +182,11 @@ struct ScanStepArgs {
   const void* C_t;
   const float* Dv;
   void* y_t;
+  // the fused step (time-step bias and softplus, output gate), as ScanArgs
+  bool fused;
+  const float* dt_bias;  // nullable
+  bool dt_softplus;
+  const void* z_t;       // nullable [B][D]
 };
 hipError_t launch_scan_step(const ScanStepArgs& a, hipStream_t st);
 
@@ -192,6 +197,7 @@ struct ConvStepArgs {
   const void* x_t;
   const float* W;
   const float* bias;  // nullable
+  int act;            // kActNone or kActSilu (out_t = silu(conv))
   void* out_t;
 };
 hipError_t launch_conv1d_step(const ConvStepArgs& a, hipStream_t st);

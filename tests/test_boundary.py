@@ -318,8 +318,30 @@ def test_scan_step_validation():
         assert _step(lib, **{name: MIS}) == b.SSM_ERR_ALIGN
 
 
-def _cstep(lib, B=2, D=32, K=4, dtype=0, state=FAKE, x_t=FAKE, W=FAKE, bias=None, out_t=FAKE):
-    return lib.conv1d_causal_step(None, dtype, B, D, K, state, x_t, W, bias, out_t)
+def _cstep(lib, B=2, D=32, K=4, dtype=0, state=FAKE, x_t=FAKE, W=FAKE, bias=None, act=0,
+           out_t=FAKE):
+    return lib.conv1d_causal_step(None, dtype, B, D, K, state, x_t, W, bias, act, out_t)
+
+
+def _fstep(lib, B=2, D=32, N=16, dtype=0, **kw):
+    p = dict(h=FAKE, x_t=FAKE, delta_t=FAKE, A=FAKE, B_t=FAKE, C_t=FAKE, Dv=FAKE,
+             delta_bias=None, delta_softplus=1, z_t=None, out_t=FAKE)
+    p.update(kw)
+    return lib.ssm_scan_fused_step(None, dtype, B, D, N, p["h"], p["x_t"], p["delta_t"], p["A"],
+                                   p["B_t"], p["C_t"], p["Dv"], p["delta_bias"],
+                                   p["delta_softplus"], p["z_t"], p["out_t"])
+
+
+def test_scan_fused_step_validation():
+    lib = b.load()
+    assert _fstep(lib, N=5) == b.SSM_ERR_UNSUPPORTED
+    assert _fstep(lib, B=0) == b.SSM_ERR_ARG
+    assert _fstep(lib, delta_softplus=2) == b.SSM_ERR_ARG
+    for name in ("h", "x_t", "delta_t", "A", "B_t", "C_t", "Dv", "out_t"):
+        assert _fstep(lib, **{name: None}) == b.SSM_ERR_ARG
+        assert name in b.last_error()
+    for name in ("delta_bias", "z_t"):
+        assert _fstep(lib, **{name: MIS}) == b.SSM_ERR_ALIGN
 
 
 def test_conv_step_validation():
@@ -328,6 +350,8 @@ def test_conv_step_validation():
     assert _cstep(lib, K=9) == b.SSM_ERR_UNSUPPORTED
     assert _cstep(lib, D=0) == b.SSM_ERR_ARG
     assert _cstep(lib, dtype=4) == b.SSM_ERR_UNSUPPORTED
+    assert _cstep(lib, act=5) == b.SSM_ERR_UNSUPPORTED
+    assert _cstep(lib, B=1 << 20, D=1 << 19) == b.SSM_ERR_ARG   # beyond one thread per (b, d)
     for name in ("state", "x_t", "W", "out_t"):
         assert _cstep(lib, **{name: None}) == b.SSM_ERR_ARG
         assert _cstep(lib, **{name: MIS}) == b.SSM_ERR_ALIGN

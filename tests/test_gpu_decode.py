@@ -139,3 +139,74 @@ def test_conv_decode_sequence_matches_oracle_and_forward(w):
     ref = oracle.conv1d_fwd(synth.as_f64(c["x"]), synth.as_f64(c["W"]), synth.as_f64(bias))
     compare({"out": out}, {"out": ref}, ("out",), label="conv decoded sequence")
     assert torch.equal(out, full)   # same multiply-add order as the forward kernel
+
+
+# ---------------------------------------------------------------------------------
+# the fused decode steps (time-step softplus and bias, output gate; conv with SiLU)
+# ---------------------------------------------------------------------------------
+
+FUSED_STEP_CASES = [custom(B=3, L=4, D=20, N=16), custom(B=2, L=4, D=70, N=8, dtype="bf16"),
+                    custom(B=1, L=4, D=5120, N=16, dtype="bf16")]
+
+
+@pytest.mark.parametrize("gate", [True, False], ids=["gate", "nogate"])
+@pytest.mark.parametrize("w", FUSED_STEP_CASES, ids=lambda w: f"B{w.B}D{w.D}N{w.N}{w.dtype}")
+def test_scan_fused_step_matches_oracle(w, gate):
+    say(f"[fused step parity] B={w.B} D={w.D} N={w.N} {w.dtype} gate={gate}")
+    p = synth.scan_fused_inputs(w, with_h0=True)
+    t = 1
+    g = _cuda(p)
+    h = g["h0"].clone()
+    sl = lambda k: g[k][:, t].contiguous()  # noqa: E731
+    out = ssm.ssm_scan_fused_step(h, sl("x"), sl("delta_raw"), g["A"], sl("Bm"), sl("Cm"), g["Dv"],
+                                  delta_bias=g["delta_bias"], delta_softplus=True,
+                                  z_t=sl("z") if gate else None)
+    torch.cuda.synchronize()
+    q = {k: synth.as_f64(v) for k, v in p.items()}
+    hr, orf = oracle.scan_fused_step(q["h0"], q["x"][:, t], q["delta_raw"][:, t], q["A"],
+                                     q["Bm"][:, t], q["Cm"][:, t], q["Dv"],
+                                     delta_bias=q["delta_bias"], delta_softplus=True,
+                                     z_t=q["z"][:, t] if gate else None)
+    compare({"out": out}, {"out": orf}, ("out",), label="fused scan step")
+    assert rel_err(f64(h), hr) <= TOL_F32
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fused_decode_is_bit_identical_to_the_fused_single_chunk_scan(dtype):
+    # 32 steps are one chunk: the fused scan runs exactly the fused step's arithmetic
+    w = custom(B=2, L=32, D=64, N=16, dtype=dtype)
+    p = _cuda(synth.scan_fused_inputs(w, with_h0=True))
+    h_seq = torch.empty_like(p["h0"])
+    out_seq = ssm.ssm_scan_fused_fwd(p["x"], p["delta_raw"], p["A"], p["Bm"], p["Cm"], p["Dv"],
+                                     h0=p["h0"], delta_bias=p["delta_bias"], delta_softplus=True,
+                                     z=p["z"], y_save=torch.empty_like(p["x"]), h_last=h_seq)
+    h = p["h0"].clone()
+    outs = [ssm.ssm_scan_fused_step(h, p["x"][:, t].contiguous(), p["delta_raw"][:, t].contiguous(),
+                                    p["A"], p["Bm"][:, t].contiguous(), p["Cm"][:, t].contiguous(),
+                                    p["Dv"], delta_bias=p["delta_bias"], delta_softplus=True,
+                                    z_t=p["z"][:, t].contiguous())
+            for t in range(w.L)]
+    torch.cuda.synchronize()
+    assert torch.equal(torch.stack(outs, dim=1), out_seq)
+    assert torch.equal(h, h_seq)
+
+
+@pytest.mark.parametrize("w", [custom(B=2, L=30, D=40, K=4), custom(B=1, L=20, D=96, K=7, dtype="bf16")],
+                         ids=lambda w: f"B{w.B}D{w.D}K{w.K}{w.dtype}")
+def test_conv_step_with_silu_decodes_the_silu_conv_forward(w):
+    say(f"[conv step silu] B={w.B} D={w.D} K={w.K} {w.dtype}")
+    c = synth.conv_inputs(w)
+    bias = synth.conv_bias(w)
+    g = _cuda(c)
+    bg = bias.cuda()
+    state = torch.zeros((w.B, w.K - 1, w.D), dtype=g["x"].dtype, device="cuda")
+    outs = [ssm.conv1d_causal_step(state, g["x"][:, t].contiguous(), g["W"], bg, act="silu")
+            for t in range(w.L)]
+    out = torch.stack(outs, dim=1)
+    full = ssm.conv1d_causal_fwd(g["x"], g["W"], bg, act="silu")
+    torch.cuda.synchronize()
+    ref = oracle.silu(oracle.conv1d_fwd(synth.as_f64(c["x"]), synth.as_f64(c["W"]),
+                                        synth.as_f64(bias)))
+    compare({"out": out}, {"out": ref}, ("out",), label="conv step silu")
+    assert torch.equal(out, full)
+
