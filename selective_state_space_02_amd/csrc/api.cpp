@@ -6,7 +6,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <string>
+#include <utility>
 
 #include "../../include/ssm_scan.h"
 #include "launch.hpp"
@@ -90,6 +92,16 @@ ssm::Chunking choose_chunks(int64_t B, int64_t L, int64_t D, int64_t target) {
 // checkpoints: the state before every (kTc / ckpt_per_tile(N))-th step
 int64_t ckpt_count(int64_t L, int64_t N) { return cdiv(L, ssm::kTc / ssm::ckpt_per_tile(N)); }
 
+// Largest reduction scratch (floats) over the (partials, outputs) pairs one call reduces.
+int64_t max_tmp(std::initializer_list<std::pair<int64_t, int64_t>> pj) {
+  int64_t m = 0;
+  for (const auto& q : pj) {
+    const int64_t t = ssm::reduce_tmp_floats(q.first, q.second);
+    if (t > m) m = t;
+  }
+  return m;
+}
+
 size_t fwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, ssm::FwdPlan* plan, void* ws) {
   const ssm::Chunking c = choose_chunks(B, L, D, kFwdTargetWG);
   Carver cv(ws);
@@ -132,9 +144,10 @@ size_t bwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, bool with_ckpt, ssm::B
   p.dDp = cv.take(size_t(B) * c.nc * D);
   p.dbp = cv.take(size_t(B) * c.nc * D);
   {
-    const int64_t t1 = ssm::reduce_tmp_floats(p.ng, B * L * N);
-    const int64_t t2 = ssm::reduce_tmp_floats(B * c.nc, D * N);
-    p.rtmp = cv.take(size_t(t1 > t2 ? t1 : t2));
+    // scratch for every reduction the backward runs (dB/dC, dA, dD and the time-step
+    // bias share it in turn); the need is not monotone in the output count
+    const int64_t t = max_tmp({{p.ng, B * L * N}, {B * c.nc, D * N}, {B * c.nc, D}});
+    p.rtmp = cv.take(size_t(t));
   }
   if (!with_ckpt) {
     float* ck = cv.take(ckpt_floats(B, L, D, N));
@@ -216,7 +229,7 @@ size_t conv_ws(int64_t B, int64_t L, int64_t D, int64_t K, ssm_dtype_t dt, ssm::
   Carver cv(ws);
   p.dWp = cv.take(size_t(B) * p.nTb * D * K);
   p.dbp = cv.take(size_t(B) * p.nTb * D);
-  p.rtmp = cv.take(size_t(ssm::reduce_tmp_floats(B * p.nTb, D * K)));
+  p.rtmp = cv.take(size_t(max_tmp({{B * p.nTb, D * K}, {B * p.nTb, D}})));
   if (plan) *plan = p;
   return cv.off;
 }

@@ -4,11 +4,13 @@
 // backward-scratch commit, applied after the partials were pre-reduced in registers
 // and LDS).
 //
-// One thread per output j sums a segment of at most kSeg partials with kAcc
-// independent accumulators (partial p goes to accumulator p mod kAcc; the accumulators
-// are then added in index order), so kAcc loads are in flight per thread.  When P
-// exceeds kSeg, a first launch writes one sum per segment to a temporary buffer and the
-// segments are summed the same way (reduce_tmp_floats() floats of temporary space).
+// One thread per output j sums a segment of partials with kAcc independent accumulators
+// (partial p goes to accumulator p mod kAcc; the accumulators are then added in index
+// order), so kAcc loads are in flight per thread.  When the outputs alone fill the GPU
+// (at least kWideBlocks blocks of 256) or P <= kSeg, one launch sums all P partials.
+// Otherwise a first launch writes one sum per segment of kSeg partials to a temporary
+// buffer and the segments are summed the same way (reduce_tmp_floats() floats of
+// temporary space), so that narrow outputs still spread over many blocks.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -16,14 +18,15 @@ namespace ssm {
 
 constexpr int kSeg = 64;
 constexpr int kAcc = 4;
+constexpr int64_t kWideBlocks = 1024;
 
 __global__ __launch_bounds__(256) void k_reduce_seg(const float* __restrict__ part, int64_t P,
-                                                    int64_t J, float* __restrict__ out,
-                                                    int accumulate) {
+                                                    int64_t J, int64_t seg,
+                                                    float* __restrict__ out, int accumulate) {
   const int64_t j = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (j >= J) return;
-  const int64_t p0 = int64_t(blockIdx.y) * kSeg;
-  const int64_t p1 = (p0 + kSeg < P) ? p0 + kSeg : P;
+  const int64_t p0 = int64_t(blockIdx.y) * seg;
+  const int64_t p1 = (p0 + seg < P) ? p0 + seg : P;
   float acc[kAcc] = {0.f, 0.f, 0.f, 0.f};
   int64_t p = p0;
   for (; p + kAcc <= p1; p += kAcc) {
@@ -36,8 +39,12 @@ __global__ __launch_bounds__(256) void k_reduce_seg(const float* __restrict__ pa
   o[j] = accumulate ? o[j] + s : s;
 }
 
+static bool single_pass(int64_t P, int64_t J) {
+  return P <= kSeg || (J + 255) / 256 >= kWideBlocks;
+}
+
 int64_t reduce_tmp_floats(int64_t P, int64_t J) {
-  if (P <= kSeg) return 0;
+  if (single_pass(P, J)) return 0;
   const int64_t S = (P + kSeg - 1) / kSeg;
   return S * J + reduce_tmp_floats(S, J);
 }
@@ -47,13 +54,14 @@ hipError_t launch_reduce(const float* part, int64_t P, int64_t J, float* out, bo
   if (J <= 0) return hipSuccess;
   const dim3 block(256);
   const int64_t gx = (J + 255) / 256;
-  if (P <= kSeg) {
-    hipLaunchKernelGGL(k_reduce_seg, dim3(gx, 1), block, 0, st, part, P, J, out,
+  if (single_pass(P, J)) {
+    hipLaunchKernelGGL(k_reduce_seg, dim3(gx, 1), block, 0, st, part, P, J, P, out,
                        accumulate ? 1 : 0);
     return hipGetLastError();
   }
   const int64_t S = (P + kSeg - 1) / kSeg;
-  hipLaunchKernelGGL(k_reduce_seg, dim3(gx, S), block, 0, st, part, P, J, tmp, 0);
+  hipLaunchKernelGGL(k_reduce_seg, dim3(gx, S), block, 0, st, part, P, J, int64_t(kSeg), tmp,
+                     0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_reduce(tmp, S, J, out, accumulate, tmp + S * J, st);
