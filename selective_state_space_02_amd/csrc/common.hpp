@@ -213,13 +213,9 @@ __device__ __forceinline__ void step_fence_arr(float (&v)[K]) {
   for (int k = 0; k < K; ++k) asm volatile("" : "+v"(v[k]));
 }
 
-// gfx950 lane swaps: after swap32(a, b), lanes 0-31 hold (a, a of lane+32) and lanes
-// 32-63 hold (b of lane-32, b); swap16 does the same between rows 0/1 and 2/3.
-__device__ __forceinline__ void swap32(float& a, float& b) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  a = __uint_as_float(r[0]);
-  b = __uint_as_float(r[1]);
-}
+// gfx950 lane swap between rows 0/1 and 2/3 of a wavefront (lane distance 16): after
+// swap16(a, b), lanes with bit 4 clear hold (a, a of lane+16) and the others
+// (b of lane-16, b).
 __device__ __forceinline__ void swap16(float& a, float& b) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
   a = __uint_as_float(r[0]);
