@@ -299,3 +299,13 @@ def scan_fused_step(h, x_t, delta_t, A, B_t, C_t, Dv, delta_bias=None, delta_sof
     h2, y = scan_step(h, x_t, dt, A, B_t, C_t, Dv)
     return h2, (y * silu(z_t) if z_t is not None else y)
 
+
+def decode_step(h, conv_state, x_t, W, conv_bias, delta_t, A, B_t, C_t, Dv, delta_bias=None,
+                delta_softplus=False, z_t=None):
+    """One token of the Mamba block's scan branch: the conv step on x_t, its SiLU, then the
+    fused scan step on that input.  Returns (h', conv_state', out_t)."""
+    state2, c = conv1d_step(conv_state, x_t, W, conv_bias)
+    h2, out = scan_fused_step(h, silu(c), delta_t, A, B_t, C_t, Dv, delta_bias=delta_bias,
+                              delta_softplus=delta_softplus, z_t=z_t)
+    return h2, state2, out
+

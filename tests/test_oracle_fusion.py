@@ -184,3 +184,23 @@ def test_conv_step_with_silu_decodes_the_silu_conv(K):
     for t in range(w.L):
         state, o = oracle.conv1d_step(state, c["x"][:, t], c["W"], bias)
         np.testing.assert_allclose(oracle.silu(o), ref[:, t], rtol=1e-13, atol=1e-14)
+
+
+def test_decode_step_decodes_the_block_branch():
+    # conv -> SiLU -> fused scan over a sequence equals the decode step applied token by
+    # token (every piece of the sequence form is pinned above)
+    w = custom(B=2, L=7, D=3, N=4, K=4)
+    p = {k: synth.as_f64(v) for k, v in synth.scan_fused_inputs(w, seed=9, with_h0=True).items()}
+    c = {k: synth.as_f64(v) for k, v in synth.conv_inputs(w, seed=9).items()}
+    cb = synth.as_f64(synth.conv_bias(w, seed=9))
+    u = oracle.silu(oracle.conv1d_fwd(c["x"], c["W"], cb))
+    f = oracle.scan_fused_fwd(u, p["delta_raw"], p["A"], p["Bm"], p["Cm"], p["Dv"], h0=p["h0"],
+                              delta_bias=p["delta_bias"], delta_softplus=True, z=p["z"])
+    h, state = p["h0"], np.zeros((w.B, w.K - 1, w.D))
+    for t in range(w.L):
+        h, state, o = oracle.decode_step(h, state, c["x"][:, t], c["W"], cb, p["delta_raw"][:, t],
+                                         p["A"], p["Bm"][:, t], p["Cm"][:, t], p["Dv"],
+                                         delta_bias=p["delta_bias"], delta_softplus=True,
+                                         z_t=p["z"][:, t])
+        np.testing.assert_allclose(o, f["out"][:, t], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(h, f["h_last"], rtol=1e-13, atol=1e-14)
