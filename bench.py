@@ -484,6 +484,30 @@ def measure_decode(w, seed, steps, dev):
     he.destroy()
     out["fused"] = {"token_ms": ftok, "tokens_per_s": Bd / (ftok * 1e-3),
                     "scan_step_kernel_ms": fscan}
+
+    # the same token in one launch (ssm_decode_step)
+    def one_launch():
+        ssm.ssm_decode_step(hf, state, cx, c["W"], bias, ft["delta_raw"], f["A"], ft["Bm"],
+                            ft["Cm"], f["Dv"], delta_bias=f["delta_bias"], delta_softplus=True,
+                            z_t=ft["z"], out_t=yt)
+    for _ in range(3):
+        one_launch()
+    torch.cuda.synchronize()
+    he = HipEvents()
+    oev = [he.pair() for _ in range(steps)]
+    kev1 = [he.pair() for _ in range(steps)]
+    for i in range(steps):
+        ssm.ssm_set_kernel_timer("decode_step", *kev1[i])
+        he.record(oev[i][0], stream)
+        one_launch()
+        he.record(oev[i][1], stream)
+    torch.cuda.synchronize()
+    ssm.ssm_set_kernel_timer("decode_step", None, None)
+    otok = sum(he.elapsed_ms(*pr) for pr in oev) / steps
+    okern = sum(he.elapsed_ms(*pr) for pr in kev1) / steps
+    he.destroy()
+    out["fused_one_launch"] = {"token_ms": otok, "tokens_per_s": Bd / (otok * 1e-3),
+                               "kernel_ms": okern}
     return out
 
 

@@ -15,6 +15,8 @@
  *   ssm_scan_step      one-token decode step of the scan (state updated in place)
  *   conv1d_causal_step one-token decode step of the conv (window updated in place)
  *   ssm_scan_fused_step one-token decode step of the fused scan
+ *   ssm_decode_step    one decode token of the block's scan branch (conv step, SiLU,
+ *                      fused scan step) in one launch
  *
  * Common conventions
  * ------------------
@@ -90,6 +92,7 @@ const char *ssm_version(void);
  *   7 conv1d backward               8 RMSNorm backward
  *   9 conv1d forward               10 RMSNorm forward
  *  11 scan decode step             12 conv1d decode step
+ *  13 decode token (conv step + SiLU + fused scan step)
  * Returns SSM_ERR_ARG for an unknown id or a half-set pair.  Has no effect on results. */
 int ssm_set_kernel_timer(int kernel, void *start, void *stop);
 
@@ -292,6 +295,22 @@ int ssm_scan_fused_step(void *stream, ssm_dtype_t dtype, int64_t B, int64_t D, i
                         const void *B_t, const void *C_t, const float *Dv,
                         const float *delta_bias, int delta_softplus, const void *z_t,
                         void *out_t);
+
+/* ---------------------------------------------------------------------------------
+ * One decode token of the Mamba block's scan branch in one launch: the conv step on x_t
+ * (conv1d_causal_step with act = SSM_ACT_SILU; its output rounded to the dtype, as that
+ * call stores it), then ssm_scan_fused_step on that input.  Same results, bit for bit, as
+ * those two calls in sequence; conv_state and h are updated in place.
+ * Shapes: h [B,D,N] f32; conv_state [B,K-1,D] (dtype; may be NULL when K = 1); x_t,
+ * delta_t, z_t, out_t [B,D] (dtype); W [D,K] f32; conv_bias, delta_bias [D] f32 or NULL;
+ * A [D,N] f32; B_t, C_t [B,N] (dtype); Dv [D] f32.  No workspace.  Supported: as
+ * ssm_scan_step, K in [1, 8].
+ * ------------------------------------------------------------------------------- */
+int ssm_decode_step(void *stream, ssm_dtype_t dtype, int64_t B, int64_t D, int64_t N,
+                    int64_t K, float *h, void *conv_state, const void *x_t, const float *W,
+                    const float *conv_bias, const void *delta_t, const float *A,
+                    const void *B_t, const void *C_t, const float *Dv, const float *delta_bias,
+                    int delta_softplus, const void *z_t, void *out_t);
 
 #ifdef __cplusplus
 }

@@ -8,6 +8,7 @@ is missing.
 """
 from .binding import (SsmError, conv1d_causal_bwd, conv1d_causal_fwd,  # noqa: F401
                       conv1d_causal_step, load, new_ckpt, rmsnorm_bwd, rmsnorm_fwd, ssm_scan_bwd,
-                      ssm_scan_fused_bwd, ssm_scan_fused_fwd, ssm_scan_fused_step, ssm_scan_fwd,
+                      ssm_decode_step, ssm_scan_fused_bwd, ssm_scan_fused_fwd, ssm_scan_fused_step,
+                      ssm_scan_fwd,
                       ssm_scan_step,
                       version)

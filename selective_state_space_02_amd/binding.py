@@ -25,7 +25,7 @@ EXPORTS = ("ssm_last_error", "ssm_version", "ssm_set_kernel_timer", "ssm_scan_ck
            "ssm_scan_bwd", "conv1d_causal_bwd_workspace_bytes", "conv1d_causal_bwd",
            "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd", "conv1d_causal_fwd", "rmsnorm_fwd",
            "ssm_scan_step", "conv1d_causal_step", "ssm_scan_fused_fwd", "ssm_scan_fused_bwd",
-           "ssm_scan_fused_step")
+           "ssm_scan_fused_step", "ssm_decode_step")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -91,6 +91,8 @@ def load():
     lib.conv1d_causal_step.restype = _E
     lib.conv1d_causal_step.argtypes = [_P, _E] + [_I] * 3 + [_P] * 4 + [_E, _P]
     lib.ssm_scan_fused_step.restype = _E
+    lib.ssm_decode_step.restype = _E
+    lib.ssm_decode_step.argtypes = [_P, _E] + [_I] * 4 + [_P] * 11 + [_E, _P, _P]
     lib.ssm_scan_fused_step.argtypes = [_P, _E] + [_I] * 3 + [_P] * 8 + [_E, _P, _P]
     _lib = lib
     return lib
@@ -106,7 +108,7 @@ def version() -> str:
 
 KERNEL_IDS = {"fwd_summary": 1, "fwd_carry": 2, "fwd_output": 3, "bwd_summary": 4,
               "bwd_carry": 5, "bwd_main": 6, "conv_bwd": 7, "rms_bwd": 8, "conv_fwd": 9,
-              "rms_fwd": 10, "scan_step": 11, "conv_step": 12}
+              "rms_fwd": 10, "scan_step": 11, "conv_step": 12, "decode_step": 13}
 
 
 def ssm_set_kernel_timer(kernel, start=None, stop=None):
@@ -481,6 +483,37 @@ def ssm_scan_fused_step(h, x_t, delta_t, A, B_t, C_t, Dv, delta_bias=None,
                                    1 if delta_softplus else 0,
                                    _ptr(z_t, "z_t", dt, (Bsz, D), dev),
                                    _ptr(out_t, "out_t", dt, (Bsz, D), dev)))
+    return out_t
+
+
+def ssm_decode_step(h, conv_state, x_t, W, conv_bias, delta_t, A, B_t, C_t, Dv,
+                    delta_bias=None, delta_softplus=False, z_t=None, out_t=None):
+    """One decode token of the block's scan branch in one launch: the conv step on x_t with
+    its SiLU, then the fused scan step.  Updates h [B, D, N] and conv_state [B, K-1, D] in
+    place; returns out_t [B, D]."""
+    lib = load()
+    Bsz, D, N = h.shape
+    K = W.shape[1]
+    dev = x_t.device
+    dt = x_t.dtype
+    code = _dtype_code(x_t)
+    f32 = torch.float32
+    out_t = torch.empty_like(x_t) if out_t is None else out_t
+    sp = _ptr(conv_state, "conv_state", dt, (Bsz, K - 1, D), dev) if K > 1 else None
+    _check(lib.ssm_decode_step(_stream(dev), code, Bsz, D, N, K,
+                               _ptr(h, "h", f32, (Bsz, D, N), dev), sp,
+                               _ptr(x_t, "x_t", dt, (Bsz, D), dev),
+                               _ptr(W, "W", f32, (D, K), dev),
+                               _ptr(conv_bias, "conv_bias", f32, (D,), dev),
+                               _ptr(delta_t, "delta_t", dt, (Bsz, D), dev),
+                               _ptr(A, "A", f32, (D, N), dev),
+                               _ptr(B_t, "B_t", dt, (Bsz, N), dev),
+                               _ptr(C_t, "C_t", dt, (Bsz, N), dev),
+                               _ptr(Dv, "Dv", f32, (D,), dev),
+                               _ptr(delta_bias, "delta_bias", f32, (D,), dev),
+                               1 if delta_softplus else 0,
+                               _ptr(z_t, "z_t", dt, (Bsz, D), dev),
+                               _ptr(out_t, "out_t", dt, (Bsz, D), dev)))
     return out_t
 
 

@@ -590,6 +590,36 @@ int ssm_scan_fused_step(void* stream, ssm_dtype_t dtype, int64_t B, int64_t D, i
                     "ssm_scan_fused_step");
 }
 
+int ssm_decode_step(void* stream, ssm_dtype_t dtype, int64_t B, int64_t D, int64_t N,
+                    int64_t K, float* h, void* conv_state, const void* x_t, const float* W,
+                    const float* conv_bias, const void* delta_t, const float* A,
+                    const void* B_t, const void* C_t, const float* Dv, const float* delta_bias,
+                    int delta_softplus, const void* z_t, void* out_t) {
+  int rc = check_scan_dims(dtype, B, 1, D, N);
+  if (rc) return rc;
+  if (K <= 0) return fail(SSM_ERR_ARG, "conv width must be positive (K=%lld)", (long long)K);
+  if (K > 8) return fail(SSM_ERR_UNSUPPORTED, "conv width K=%lld not supported (1..8)", (long long)K);
+  rc = K > 1 ? check_ptrs({{h, "h"}, {conv_state, "conv_state"}, {x_t, "x_t"}, {W, "W"},
+                           {delta_t, "delta_t"}, {A, "A"}, {B_t, "B_t"}, {C_t, "C_t"},
+                           {Dv, "Dv"}, {out_t, "out_t"}},
+                          {{conv_bias, "conv_bias"}, {delta_bias, "delta_bias"}, {z_t, "z_t"}})
+             : check_ptrs({{h, "h"}, {x_t, "x_t"}, {W, "W"}, {delta_t, "delta_t"}, {A, "A"},
+                           {B_t, "B_t"}, {C_t, "C_t"}, {Dv, "Dv"}, {out_t, "out_t"}},
+                          {{conv_state, "conv_state"}, {conv_bias, "conv_bias"},
+                           {delta_bias, "delta_bias"}, {z_t, "z_t"}});
+  if (rc) return rc;
+  if (delta_softplus != 0 && delta_softplus != 1)
+    return fail(SSM_ERR_ARG, "delta_softplus must be 0 or 1 (got %d)", delta_softplus);
+  ssm::DecodeArgs a{};
+  a.dtype = int(dtype);
+  a.B = B; a.D = D; a.N = N; a.K = K;
+  a.h = h; a.conv_state = conv_state; a.x_t = x_t; a.W = W; a.conv_bias = conv_bias;
+  a.delta_t = delta_t; a.A = A; a.B_t = B_t; a.C_t = C_t; a.Dv = Dv;
+  a.dt_bias = delta_bias; a.dt_softplus = delta_softplus != 0; a.z_t = z_t; a.out_t = out_t;
+  return hip_status(ssm::launch_decode_step(a, static_cast<hipStream_t>(stream)),
+                    "ssm_decode_step");
+}
+
 int conv1d_causal_step(void* stream, ssm_dtype_t dtype, int64_t B, int64_t D, int64_t K,
                        void* state, const void* x_t, const float* W, const float* bias,
                        ssm_act_t act, void* out_t) {

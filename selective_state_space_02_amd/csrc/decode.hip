@@ -17,7 +17,8 @@
 //
 // Fused forms, as the sequence kernels' (same functions, same order, so decoding stays
 // bit-identical to them): the scan step's time step softplus(delta_t + bias) (FZ) and
-// output gate y * silu(z_t); the conv step's SiLU (ACT).
+// output gate y * silu(z_t); the conv step's SiLU (ACT); and the decode token of the
+// block's scan branch, conv step -> SiLU -> fused scan step in one launch.
 //
 // Both are HBM-bound: the scan step reads and writes h (8 bytes per state), the conv
 // step reads and writes the window.
@@ -25,6 +26,76 @@
 #include "launch.hpp"
 
 namespace ssm {
+
+// One scan step for the channel (b, d) of a quad (lane q holds states q*NS .. q*NS+NS-1),
+// in two phases so that a caller can have every load in flight before it forms the
+// step's input xv: step_load issues the step's loads (raw values, no arithmetic, no
+// branch, so that no load waits for another), step_compute advances h and writes the
+// output.  Shared by the scan step and the decode token.
+template <typename T, int N>
+struct StepOperands {
+  static constexpr int NS = N / 4;
+  float hv[NS], Av[NS], Bv[NS], Cv[NS];
+  float bias, Dd;
+  T draw, zraw;
+};
+
+template <typename T, int N, bool FZ>
+__device__ __forceinline__ void step_load(StepOperands<T, N>& o, int64_t b, int64_t d,
+                                          int64_t D, int q, const float* __restrict__ h,
+                                          const T* __restrict__ delta_t,
+                                          const float* __restrict__ A,
+                                          const T* __restrict__ B_t, const T* __restrict__ C_t,
+                                          const float* __restrict__ Dv,
+                                          const float* __restrict__ dtb,
+                                          const T* __restrict__ z_t) {
+  constexpr int NS = N / 4;
+  const int64_t bd = b * D + d;
+  o.draw = delta_t[bd];
+  if constexpr (FZ) {
+    // absent operands read a valid stand-in address; the value is not used
+    o.bias = (dtb ? dtb : Dv)[d];
+    o.zraw = (z_t ? z_t : delta_t)[bd];
+  }
+  VecLoad<float, NS>::run(h + bd * N + q * NS, o.hv);
+  VecLoad<float, NS>::run(A + d * N + q * NS, o.Av);
+  load_vec<T, NS>(B_t + b * N + q * NS, o.Bv);
+  load_vec<T, NS>(C_t + b * N + q * NS, o.Cv);
+  o.Dd = Dv[d];
+}
+
+template <typename T, int N, bool FZ>
+__device__ __forceinline__ void step_compute(StepOperands<T, N>& o, int64_t b, int64_t d,
+                                             int64_t D, int q, float xv, float* __restrict__ h,
+                                             const float* __restrict__ dtb, bool sp,
+                                             const T* __restrict__ z_t, T* __restrict__ y_t) {
+  constexpr int NS = N / 4;
+  const int64_t bd = b * D + d;
+  float dl = to_f32(o.draw);
+  if constexpr (FZ) {
+    dl += dtb ? o.bias : 0.f;
+    if (sp) dl = softplus_f(dl);
+  }
+  const float u = dl * xv;
+  float yp;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const float a = __builtin_amdgcn_exp2f(dl * (o.Av[j] * kLog2e));
+    o.hv[j] = __builtin_fmaf(a, o.hv[j], u * o.Bv[j]);
+    yp = j ? __builtin_fmaf(o.Cv[j], o.hv[j], yp) : o.Cv[j] * o.hv[j];
+  }
+  yp = quad_sum(yp);
+  VecStore<float, NS>::run(h + bd * N + q * NS, o.hv);
+  // every lane forms y (the quad's lanes agree); the use below keeps the operand loads
+  // where step_load put them instead of inside the single-lane store
+  float yv = __builtin_fmaf(o.Dd, xv, yp);
+  if constexpr (FZ) {
+    const float zv = to_f32(o.zraw);
+    if (z_t) yv *= zv * sigmoid_f(zv);
+  }
+  asm volatile("" ::"v"(yv));
+  if (q == 0) y_t[bd] = from_f32<T>(yv);
+}
 
 template <typename T, int N, bool FZ>
 __global__ __launch_bounds__(256) void k_scan_step(int64_t D, float* __restrict__ h,
@@ -37,42 +108,72 @@ __global__ __launch_bounds__(256) void k_scan_step(int64_t D, float* __restrict_
                                                    const float* __restrict__ dtb, bool sp,
                                                    const T* __restrict__ z_t,
                                                    T* __restrict__ y_t) {
-  constexpr int NS = N / 4;
   const int tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
   const int64_t b = blockIdx.y, d = int64_t(blockIdx.x) * 64 + cl;
   if (d >= D) return;  // a channel's four lanes leave together; the quad sum stays in-quad
-  const int64_t bd = b * D + d;
-  const float xv = to_f32(x_t[bd]);
-  float dl = to_f32(delta_t[bd]);
-  float zv = 0.f;  // the gate input, loaded with the other inputs (not at the store)
-  if constexpr (FZ) {
-    const float bias = dtb ? dtb[d] : 0.f;
-    if (z_t) zv = to_f32(z_t[bd]);
-    dl += bias;
-    if (sp) dl = softplus_f(dl);
-  }
-  float hv[NS], Av[NS], Bv[NS], Cv[NS];
-  VecLoad<float, NS>::run(h + bd * N + q * NS, hv);
-  VecLoad<float, NS>::run(A + d * N + q * NS, Av);
-  load_vec<T, NS>(B_t + b * N + q * NS, Bv);
-  load_vec<T, NS>(C_t + b * N + q * NS, Cv);
-  const float u = dl * xv;
-  float yp;
+  StepOperands<T, N> o;
+  const T xr = x_t[b * D + d];
+  step_load<T, N, FZ>(o, b, d, D, q, h, delta_t, A, B_t, C_t, Dv, dtb, z_t);
+  step_compute<T, N, FZ>(o, b, d, D, q, to_f32(xr), h, dtb, sp, z_t, y_t);
+}
+
+// One decode token of the block's scan branch: the conv step on x_t (window [B][K-1][D]),
+// its SiLU, the result rounded to T as the two-call path stores it, then the fused scan
+// step on it.  The channel's four lanes share the window's loads and stores and all form
+// the conv output (same operations in the conv step's order, same value).
+template <typename T, int N, int K>
+__global__ __launch_bounds__(256) void k_decode_step(int64_t D, float* __restrict__ h,
+                                                     T* __restrict__ cstate,
+                                                     const T* __restrict__ x_t,
+                                                     const float* __restrict__ W,
+                                                     const float* __restrict__ cbias,
+                                                     const T* __restrict__ delta_t,
+                                                     const float* __restrict__ A,
+                                                     const T* __restrict__ B_t,
+                                                     const T* __restrict__ C_t,
+                                                     const float* __restrict__ Dv,
+                                                     const float* __restrict__ dtb, bool sp,
+                                                     const T* __restrict__ z_t,
+                                                     T* __restrict__ out_t) {
+  // The conv window of the group's 64 channels (K-1 stored rows, then x_t as tap K-1)
+  // is staged through LDS: thread t moves row t/64 of channel t%64, so each row is read
+  // and written as one contiguous run of 64 values.
+  __shared__ float sw[K][64];
+  const int tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
+  const int64_t b = blockIdx.y, d0 = int64_t(blockIdx.x) * 64, d = d0 + cl;
+  const int rc = tid & 63;
+  // every load is issued before the barrier; lanes past the last channel read the last
+  // channel's addresses (in bounds) and drop the values
+  const int64_t dc = d < D ? d : D - 1, rcol = d0 + rc < D ? d0 + rc : D - 1;
+  StepOperands<T, N> o;
+  step_load<T, N, true>(o, b, dc, D, q, h, delta_t, A, B_t, C_t, Dv, dtb, z_t);
+  float wk[K];
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    const float a = __builtin_amdgcn_exp2f(dl * (Av[j] * kLog2e));
-    hv[j] = __builtin_fmaf(a, hv[j], u * Bv[j]);
-    yp = j ? __builtin_fmaf(Cv[j], hv[j], yp) : Cv[j] * hv[j];
+  for (int k = 0; k < K; ++k) wk[k] = W[dc * K + k];
+  const float cb = cbias ? cbias[dc] : 0.f;
+  T raw[(K + 3) / 4];
+#pragma unroll
+  for (int i = 0; i < (K + 3) / 4; ++i) {
+    const int r = (tid >> 6) + 4 * i;  // uniform over the wavefront
+    if (r < K) raw[i] = (r < K - 1 ? cstate + (b * (K - 1) + r) * D : x_t + b * D)[rcol];
   }
-  yp = quad_sum(yp);
-  VecStore<float, NS>::run(h + bd * N + q * NS, hv);
-  if (q == 0) {
-    float yv = __builtin_fmaf(Dv[d], xv, yp);
-    if constexpr (FZ) {
-      if (z_t) yv *= zv * sigmoid_f(zv);
-    }
-    y_t[bd] = from_f32<T>(yv);
+#pragma unroll
+  for (int i = 0; i < (K + 3) / 4; ++i) {
+    const int r = (tid >> 6) + 4 * i;
+    if (r < K) sw[r][rc] = to_f32(raw[i]);
   }
+  __syncthreads();  // every read of the window is done before any row is rewritten
+  // the window moves up one row (the values came from T, so storing them back is exact)
+  if (d0 + rc < D)
+    for (int r = tid >> 6; r < K - 1; r += 4)
+      cstate[(b * (K - 1) + r) * D + d0 + rc] = from_f32<T>(sw[r + 1][rc]);
+  if (d >= D) return;  // a channel's four lanes leave together (the quad sum stays in-quad)
+  float acc = cb;
+#pragma unroll
+  for (int k = 0; k < K; ++k) acc = __builtin_fmaf(wk[k], sw[k][cl], acc);
+  acc *= sigmoid_f(acc);
+  const float xv = to_f32(from_f32<T>(acc));
+  step_compute<T, N, true>(o, b, d, D, q, xv, h, dtb, sp, z_t, out_t);
 }
 
 template <typename T, int K, int ACT>
@@ -164,6 +265,49 @@ static hipError_t conv_step_t(const ConvStepArgs& a, hipStream_t st) {
     case 8: return conv_step_k<T, 8>(a, st);
   }
   return hipErrorInvalidValue;
+}
+
+template <typename T, int N, int K>
+static void decode_step_nk(const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((k_decode_step<T, N, K>), dim3(unsigned((a.D + 63) / 64), unsigned(a.B)),
+                     dim3(256), 0, st, a.D, a.h, static_cast<T*>(a.conv_state),
+                     static_cast<const T*>(a.x_t), a.W, a.conv_bias,
+                     static_cast<const T*>(a.delta_t), a.A, static_cast<const T*>(a.B_t),
+                     static_cast<const T*>(a.C_t), a.Dv, a.dt_bias, a.dt_softplus,
+                     static_cast<const T*>(a.z_t), static_cast<T*>(a.out_t));
+}
+
+template <typename T, int N>
+static hipError_t decode_step_n(const DecodeArgs& a, hipStream_t st) {
+  switch (a.K) {
+    case 1: decode_step_nk<T, N, 1>(a, st); break;
+    case 2: decode_step_nk<T, N, 2>(a, st); break;
+    case 3: decode_step_nk<T, N, 3>(a, st); break;
+    case 4: decode_step_nk<T, N, 4>(a, st); break;
+    case 5: decode_step_nk<T, N, 5>(a, st); break;
+    case 6: decode_step_nk<T, N, 6>(a, st); break;
+    case 7: decode_step_nk<T, N, 7>(a, st); break;
+    case 8: decode_step_nk<T, N, 8>(a, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t decode_step_t(const DecodeArgs& a, hipStream_t st) {
+  hipError_t e = hipErrorInvalidValue;
+  timer_mark(kKDecodeStep, false, st);
+  switch (a.N) {
+    case 4: e = decode_step_n<T, 4>(a, st); break;
+    case 8: e = decode_step_n<T, 8>(a, st); break;
+    case 16: e = decode_step_n<T, 16>(a, st); break;
+  }
+  timer_mark(kKDecodeStep, true, st);
+  return e;
+}
+
+hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t st) {
+  return a.dtype == 0 ? decode_step_t<float>(a, st) : decode_step_t<bf16_t>(a, st);
 }
 
 hipError_t launch_conv1d_step(const ConvStepArgs& a, hipStream_t st) {

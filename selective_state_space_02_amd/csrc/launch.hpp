@@ -134,7 +134,8 @@ enum KernelId {
   kKRmsFwd = 10,
   kKScanStep = 11,
   kKConvStep = 12,
-  kKNumIds = 13
+  kKDecodeStep = 13,
+  kKNumIds = 14
 };
 
 // Records the caller's event for kernel `id` on stream st (stop = false: before the
@@ -201,6 +202,26 @@ struct ConvStepArgs {
   void* out_t;
 };
 hipError_t launch_conv1d_step(const ConvStepArgs& a, hipStream_t st);
+
+struct DecodeArgs {
+  int dtype;
+  int64_t B, D, N, K;
+  float* h;          // [B][D][N], in place
+  void* conv_state;  // [B][K-1][D], in place (unused when K == 1)
+  const void* x_t;   // the conv's input [B][D]
+  const float* W;
+  const float* conv_bias;  // nullable
+  const void* delta_t;
+  const float* A;
+  const void* B_t;
+  const void* C_t;
+  const float* Dv;
+  const float* dt_bias;  // nullable
+  bool dt_softplus;
+  const void* z_t;       // nullable
+  void* out_t;
+};
+hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_rmsnorm_bwd(const RmsArgs& a, const RmsPlan& p, hipStream_t st);
 // out[j] (+)= sum_{p < P} part[p*J + j] in a fixed order; tmp holds
 // reduce_tmp_floats(P, J) floats (may be null when that is 0).

@@ -332,6 +332,32 @@ def _fstep(lib, B=2, D=32, N=16, dtype=0, **kw):
                                    p["delta_softplus"], p["z_t"], p["out_t"])
 
 
+def _dstep(lib, B=2, D=32, N=16, K=4, dtype=0, **kw):
+    p = dict(h=FAKE, conv_state=FAKE, x_t=FAKE, W=FAKE, conv_bias=None, delta_t=FAKE, A=FAKE,
+             B_t=FAKE, C_t=FAKE, Dv=FAKE, delta_bias=None, delta_softplus=1, z_t=None,
+             out_t=FAKE)
+    p.update(kw)
+    return lib.ssm_decode_step(None, dtype, B, D, N, K, p["h"], p["conv_state"], p["x_t"], p["W"],
+                               p["conv_bias"], p["delta_t"], p["A"], p["B_t"], p["C_t"], p["Dv"],
+                               p["delta_bias"], p["delta_softplus"], p["z_t"], p["out_t"])
+
+
+def test_decode_step_validation():
+    lib = b.load()
+    assert _dstep(lib, N=5) == b.SSM_ERR_UNSUPPORTED
+    assert _dstep(lib, K=0) == b.SSM_ERR_ARG
+    assert _dstep(lib, K=9) == b.SSM_ERR_UNSUPPORTED
+    assert _dstep(lib, B=0) == b.SSM_ERR_ARG
+    assert _dstep(lib, delta_softplus=3) == b.SSM_ERR_ARG
+    for name in ("h", "conv_state", "x_t", "W", "delta_t", "A", "B_t", "C_t", "Dv", "out_t"):
+        assert _dstep(lib, **{name: None}) == b.SSM_ERR_ARG
+        assert name in b.last_error()
+    for name in ("conv_bias", "delta_bias", "z_t", "h"):
+        assert _dstep(lib, **{name: MIS}) == b.SSM_ERR_ALIGN
+    # a width-1 conv has no window: conv_state may be NULL
+    assert _dstep(lib, K=1, conv_state=MIS) == b.SSM_ERR_ALIGN
+
+
 def test_scan_fused_step_validation():
     lib = b.load()
     assert _fstep(lib, N=5) == b.SSM_ERR_UNSUPPORTED

@@ -210,3 +210,53 @@ def test_conv_step_with_silu_decodes_the_silu_conv_forward(w):
     compare({"out": out}, {"out": ref}, ("out",), label="conv step silu")
     assert torch.equal(out, full)
 
+
+# ---------------------------------------------------------------------------------
+# the decode token of the block's scan branch in one launch
+# ---------------------------------------------------------------------------------
+
+DECODE_CASES = [custom(B=3, L=12, D=20, N=16, K=4), custom(B=2, L=9, D=70, N=8, K=3, dtype="bf16"),
+                custom(B=2, L=6, D=33, N=4, K=1), custom(B=1, L=5, D=5120, N=16, K=4, dtype="bf16")]
+
+
+def _decode_inputs(w, seed=11):
+    p = _cuda(synth.scan_fused_inputs(w, seed=seed, with_h0=True))
+    c = _cuda(synth.conv_inputs(w, seed=seed))
+    return p, c, synth.conv_bias(w, seed=seed).cuda()
+
+
+@pytest.mark.parametrize("w", DECODE_CASES, ids=lambda w: f"B{w.B}D{w.D}N{w.N}K{w.K}{w.dtype}")
+def test_decode_step_is_the_two_calls_bit_for_bit_and_matches_the_oracle(w):
+    say(f"[decode step] B={w.B} L={w.L} D={w.D} N={w.N} K={w.K} {w.dtype}")
+    p, c, cb = _decode_inputs(w)
+    dt = c["x"].dtype
+    h1, h2 = p["h0"].clone(), p["h0"].clone()
+    s1 = torch.zeros((w.B, w.K - 1, w.D), dtype=dt, device="cuda")
+    s2 = s1.clone()
+    outs1, outs2 = [], []
+    for t in range(w.L):
+        sl = lambda k: p[k][:, t].contiguous()  # noqa: E731
+        kw = dict(delta_bias=p["delta_bias"], delta_softplus=True, z_t=sl("z"))
+        u = ssm.conv1d_causal_step(s1, c["x"][:, t].contiguous(), c["W"], cb, act="silu")
+        outs1.append(ssm.ssm_scan_fused_step(h1, u, sl("delta_raw"), p["A"], sl("Bm"), sl("Cm"),
+                                             p["Dv"], **kw))
+        outs2.append(ssm.ssm_decode_step(h2, s2, c["x"][:, t].contiguous(), c["W"], cb,
+                                         sl("delta_raw"), p["A"], sl("Bm"), sl("Cm"), p["Dv"],
+                                         **kw))
+    torch.cuda.synchronize()
+    o1, o2 = torch.stack(outs1, dim=1), torch.stack(outs2, dim=1)
+    assert torch.equal(o1, o2) and torch.equal(h1, h2) and torch.equal(s1, s2)
+    # the oracle's decode token, from the same inputs
+    q = {k: synth.as_f64(v.cpu()) for k, v in p.items()}
+    cq = {k: synth.as_f64(v.cpu()) for k, v in c.items()}
+    h, st = q["h0"], np.zeros((w.B, w.K - 1, w.D))
+    ref = []
+    for t in range(w.L):
+        h, st, o = oracle.decode_step(h, st, cq["x"][:, t], cq["W"], synth.as_f64(cb.cpu()),
+                                      q["delta_raw"][:, t], q["A"], q["Bm"][:, t], q["Cm"][:, t],
+                                      q["Dv"], delta_bias=q["delta_bias"], delta_softplus=True,
+                                      z_t=q["z"][:, t])
+        ref.append(o)
+    compare({"out": o2}, {"out": np.stack(ref, axis=1)}, ("out",), label="decode token")
+    assert rel_err(f64(h2), h) <= (TOL_F32 if w.dtype == "f32" else 2e-2)
+
