@@ -15,6 +15,9 @@ constexpr int kTc = 16;
 // register budget), so it needs the state at mid-tile too.
 constexpr int ckpt_per_tile(int64_t N) { return N == 16 ? 2 : 1; }
 
+// Chunk summaries the carry kernels load ahead of their sequential composition.
+constexpr int kCarryAhead = 16;
+
 struct ScanArgs {
   int dtype;  // 0 f32, 1 bf16
   int64_t B, L, D, N;

@@ -156,12 +156,30 @@ __global__ __launch_bounds__(256) void k_bwd_carry(
   const int64_t n = idx % N, bd = idx / N, d = bd % D, b = bd / D;
   const float A2 = A[d * N + n] * kLog2e;
   float gp = 0.f;
-  for (int c = nc - 1; c >= 0; --c) {
-    const int64_t o = (b * nc + c) * D + d;
-    gin[o * N + n] = gp;
-    if (c > 0) {
-      const float P = __builtin_amdgcn_exp2f(A2 * SD[o]);
-      gp = __builtin_fmaf(P, gp, GS[o * N + n]);
+  // sequential over chunks (last to first); a batch of kCarryAhead chunk summaries is
+  // loaded before it is composed
+  for (int c0 = nc - 1; c0 >= 0; c0 -= kCarryAhead) {
+    float sdv[kCarryAhead], gv[kCarryAhead];
+#pragma unroll
+    for (int i = 0; i < kCarryAhead; ++i) {
+      // (index clamped into [0, nc): before the start the value is loaded but not used;
+      // chunk 0's summary slot is never written nor used)
+      const int c = c0 - i >= 0 ? c0 - i : 0;
+      const int64_t o = (b * nc + c) * D + d;
+      sdv[i] = SD[o];
+      gv[i] = GS[o * N + n];
+    }
+#pragma unroll
+    for (int i = 0; i < kCarryAhead; ++i) {
+      const int c = c0 - i;
+      if (c >= 0) {
+        const int64_t o = (b * nc + c) * D + d;
+        gin[o * N + n] = gp;
+        if (c > 0) {
+          const float P = __builtin_amdgcn_exp2f(A2 * sdv[i]);
+          gp = __builtin_fmaf(P, gp, gv[i]);
+        }
+      }
     }
   }
 }

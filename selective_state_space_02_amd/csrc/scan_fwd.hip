@@ -124,12 +124,30 @@ __global__ __launch_bounds__(256) void k_fwd_carry(
   const int64_t n = idx % N, bd = idx / N, d = bd % D, b = bd / D;
   const float A2 = A[d * N + n] * kLog2e;
   float h = h0 ? h0[idx] : 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const int64_t o = (b * nc + c) * D + d;
-    hin[o * N + n] = h;
-    if (c + 1 < nc) {
-      const float P = __builtin_amdgcn_exp2f(A2 * SD[o]);
-      h = __builtin_fmaf(P, h, S[o * N + n]);
+  // the composition is sequential over chunks, the loads are not: a batch of kCarryAhead
+  // chunk summaries is loaded before it is composed (one memory latency per batch)
+  for (int c0 = 0; c0 < nc; c0 += kCarryAhead) {
+    float sdv[kCarryAhead], sv[kCarryAhead];
+#pragma unroll
+    for (int i = 0; i < kCarryAhead; ++i) {
+      // (index clamped into [0, nc): past the end the value is loaded but not used;
+      // chunk nc-1's summary slot is never written nor used)
+      const int c = c0 + i < nc ? c0 + i : nc - 1;
+      const int64_t o = (b * nc + c) * D + d;
+      sdv[i] = SD[o];
+      sv[i] = S[o * N + n];
+    }
+#pragma unroll
+    for (int i = 0; i < kCarryAhead; ++i) {
+      const int c = c0 + i;
+      if (c < nc) {
+        const int64_t o = (b * nc + c) * D + d;
+        hin[o * N + n] = h;
+        if (c + 1 < nc) {
+          const float P = __builtin_amdgcn_exp2f(A2 * sdv[i]);
+          h = __builtin_fmaf(P, h, sv[i]);
+        }
+      }
     }
   }
 }
