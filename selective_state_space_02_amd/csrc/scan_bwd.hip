@@ -285,14 +285,15 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
     fC.fetch(Cb + tt * N, tvalid, voff);
     pend_tv = tvalid;
     pend_tt = tt;
+    // Every load is issued unconditionally, straight into the registers the loop carries:
+    // an interval wholly past L, or the empty fetch past the chunk's first tile
+    // (tvalid 0), reads zeros through an empty descriptor.  (A load under a branch ends
+    // in a register copy at the join, whose wait would also cover the loads just issued.)
 #pragma unroll
     for (int hf = 0; hf < SPLIT; ++hf) {
-      if (hf == 0 || tt + hf * SL < L) {
-        buf_load_states<NS>(buf_rsrc(ckg + (tt / SL + hf) * D * N, ckbytes), ckoff, hk[hf]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < NS; ++j) hk[hf][j] = 0.f;  // an interval wholly past L
-      }
+      const bool has = tvalid > 0 && (hf == 0 || tt + hf * SL < L);
+      buf_load_states<NS>(buf_rsrc(ckg + (has ? tt / SL + hf : 0) * D * N, has ? ckbytes : 0u),
+                          ckoff, hk[hf]);
     }
   };
   // the gate's inputs of the pending tile (FZ with z), loaded just before its commit
@@ -339,7 +340,9 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
   fetch(tf, clamp_valid(L - tf), hcur);
   if constexpr (FZ) fetch_gate();
   commit(0);
-  if (ntile > 1) fetch(tf - kTc, kTc, hnxt);  // every tile but the last one is full
+  // every tile but the last one is full; past the first tile an empty fetch (at a valid
+  // address) keeps the loads unconditional
+  fetch(ntile > 1 ? tf - kTc : tf, ntile > 1 ? kTc : 0, hnxt);
   __syncthreads();
 
   float pv[V];  // channel-sum values of the step above the current one
@@ -484,10 +487,13 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
     if (it + 1 < ntile) {
       commit(buf ^ 1);
 #pragma unroll
-      for (int hf = 0; hf < SPLIT; ++hf)
+      for (int hf = 0; hf < SPLIT; ++hf) {
 #pragma unroll
         for (int j = 0; j < NS; ++j) hcur[hf][j] = hnxt[hf][j];
-      if (it + 2 < ntile) fetch(tf - 2 * kTc, kTc, hnxt);
+        step_fence_arr(hcur[hf]);  // moved before the loads below reuse hnxt's registers
+      }
+      step_fence();
+      fetch(it + 2 < ntile ? tf - 2 * kTc : tf, it + 2 < ntile ? kTc : 0, hnxt);
     }
     __syncthreads();
   }
