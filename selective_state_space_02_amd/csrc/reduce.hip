@@ -5,8 +5,9 @@
 // and LDS).
 //
 // One thread per output j sums a segment of partials with kAcc independent accumulators
-// (partial p goes to accumulator p mod kAcc; the accumulators are then added in index
-// order), so kAcc loads are in flight per thread.  When the outputs alone fill the GPU
+// (partial p goes to accumulator p mod kAcc, in increasing p; the accumulators are then
+// added in index order).  Loads are issued kBatch at a time before they are added, so a
+// thread waits one memory latency per kBatch partials (narrow outputs are latency-bound).  When the outputs alone fill the GPU
 // (at least kWideBlocks blocks of 256) or P <= kSeg, one launch sums all P partials.
 // Otherwise a first launch writes one sum per segment of kSeg partials to a temporary
 // buffer and the segments are summed the same way (reduce_tmp_floats() floats of
@@ -18,6 +19,7 @@ namespace ssm {
 
 constexpr int kSeg = 64;
 constexpr int kAcc = 4;
+constexpr int kBatch = 16;  // a multiple of kAcc
 constexpr int64_t kWideBlocks = 1024;
 
 __global__ __launch_bounds__(256) void k_reduce_seg(const float* __restrict__ part, int64_t P,
@@ -29,11 +31,21 @@ __global__ __launch_bounds__(256) void k_reduce_seg(const float* __restrict__ pa
   const int64_t p1 = (p0 + seg < P) ? p0 + seg : P;
   float acc[kAcc] = {0.f, 0.f, 0.f, 0.f};
   int64_t p = p0;
-  for (; p + kAcc <= p1; p += kAcc) {
+  for (; p + kBatch <= p1; p += kBatch) {
+    float v[kBatch];
 #pragma unroll
-    for (int k = 0; k < kAcc; ++k) acc[k] += part[(p + k) * J + j];
+    for (int k = 0; k < kBatch; ++k) v[k] = part[(p + k) * J + j];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) acc[k % kAcc] += v[k];
   }
-  for (int k = 0; p < p1; ++p, ++k) acc[k] += part[p * J + j];
+  if (p < p1) {  // the last, partial batch: loads clamped to the segment, extra values dropped
+    float v[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) v[k] = part[(p + k < p1 ? p + k : p1 - 1) * J + j];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (p + k < p1) acc[k % kAcc] += v[k];
+  }
   const float s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   float* o = out + int64_t(blockIdx.y) * J;  // one row per segment (a single row if P <= kSeg)
   o[j] = accumulate ? o[j] + s : s;
