@@ -215,8 +215,11 @@ def test_conv_step_with_silu_decodes_the_silu_conv_forward(w):
 # the decode token of the block's scan branch in one launch
 # ---------------------------------------------------------------------------------
 
+# K = 1 (no stored rows), K up to 8 (two window rows per thread of the staging), ragged
+# channel groups (D = 20, 70, 33, 130, 200), the three state sizes and both dtypes
 DECODE_CASES = [custom(B=3, L=12, D=20, N=16, K=4), custom(B=2, L=9, D=70, N=8, K=3, dtype="bf16"),
-                custom(B=2, L=6, D=33, N=4, K=1), custom(B=1, L=5, D=5120, N=16, K=4, dtype="bf16")]
+                custom(B=2, L=6, D=33, N=4, K=1), custom(B=1, L=5, D=5120, N=16, K=4, dtype="bf16"),
+                custom(B=2, L=7, D=130, N=4, K=8), custom(B=3, L=6, D=200, N=16, K=6, dtype="bf16")]
 
 
 def _decode_inputs(w, seed=11):
@@ -260,3 +263,25 @@ def test_decode_step_is_the_two_calls_bit_for_bit_and_matches_the_oracle(w):
     compare({"out": o2}, {"out": np.stack(ref, axis=1)}, ("out",), label="decode token")
     assert rel_err(f64(h2), h) <= (TOL_F32 if w.dtype == "f32" else 2e-2)
 
+
+def test_decode_step_without_optional_operands_is_the_two_calls():
+    """No conv bias, no time-step bias, no softplus, no gate: still the two calls bit for
+    bit.  (The time step is given positive, as it is without the softplus; a negative one
+    would grow the state past f32 within a few steps.)"""
+    w = custom(B=2, L=6, D=72, N=16, K=4, dtype="bf16")
+    say(f"[decode step, no optional operands] B={w.B} D={w.D} N={w.N} K={w.K} {w.dtype}")
+    p, c, _ = _decode_inputs(w, seed=12)
+    p["delta_raw"] = (p["delta_raw"].float().abs() * 0.05).to(p["delta_raw"].dtype)
+    h1, h2 = p["h0"].clone(), p["h0"].clone()
+    s1 = torch.zeros((w.B, w.K - 1, w.D), dtype=c["x"].dtype, device="cuda")
+    s2 = s1.clone()
+    for t in range(w.L):
+        sl = lambda k: p[k][:, t].contiguous()  # noqa: E731
+        u = ssm.conv1d_causal_step(s1, c["x"][:, t].contiguous(), c["W"], None, act="silu")
+        o1 = ssm.ssm_scan_fused_step(h1, u, sl("delta_raw"), p["A"], sl("Bm"), sl("Cm"), p["Dv"])
+        o2 = ssm.ssm_decode_step(h2, s2, c["x"][:, t].contiguous(), c["W"], None,
+                                 sl("delta_raw"), p["A"], sl("Bm"), sl("Cm"), p["Dv"])
+        assert torch.equal(o1, o2), t
+    torch.cuda.synchronize()
+    assert torch.isfinite(h1).all()
+    assert torch.equal(h1, h2) and torch.equal(s1, s2)
