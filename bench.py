@@ -27,7 +27,6 @@ if ROOT not in sys.path:
 METRIC = "scan fwd+bwd tokens·channels/sec and achieved HBM GB/s (% of peak), 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # published, counting packed f32 FMA (not used here)
-CLOCK_GHZ = 2.4
 
 # Algorithmic floating-point work per state update (b, t, d, n) of the backward main
 # kernel, counting FMA 2, mul/add 1, exp 1.  Recompute of a_t and h_t from the
@@ -111,26 +110,12 @@ def counter_traffic(workload_name):
     return rec.get("traffic_bytes_per_launch") if rec else None
 
 
-# VALU issue model of a gfx950 SIMD for wave64 f32 code without packed instructions: a
-# VALU instruction occupies the SIMD for 4 cycles, a transcendental one for 8 (the rate
-# the scan kernels' counters show at 87-97% VALU busy).
-SIMDS = 1024
-VALU_CYCLES, TRANS_CYCLES = 4, 8
-
-
-def valu_issue_frac(workload_name, launch_ms):
-    """Fraction of the SIMDs' cycles during one launch of the backward main kernel that
-    its VALU instructions (counted by SQ_INSTS_VALU / SQ_INSTS_VALU_TRANS_F32, which do
-    not vary from run to run) occupy under the issue model above; None without counters."""
+def counter_valu_busy(workload_name):
+    """Fraction of the SIMDs' cycles in which the backward main kernel's VALU was busy
+    (4 * SQ_ACTIVE_INST_VALU over SIMDs x dispatch cycles, in the counter run), or None
+    (see counter_record)."""
     rec = counter_record(workload_name)
-    if not rec or not launch_ms:
-        return None
-    sq = rec.get("sq", {})
-    valu, trans = sq.get("SQ_INSTS_VALU"), sq.get("SQ_INSTS_VALU_TRANS_F32")
-    if not valu or trans is None:
-        return None
-    busy = VALU_CYCLES * (valu - trans) + TRANS_CYCLES * trans
-    return busy / (SIMDS * launch_ms * 1e-3 * CLOCK_GHZ * 1e9)
+    return rec.get("valu_busy") if rec else None
 
 
 def algorithmic_bytes(w):
@@ -714,7 +699,7 @@ def main():
             "frac": achieved_tflops / FP32_VECTOR_PEAK_TFLOPS,
             "traffic": counter_traffic(w.name),
             "peak_without_packed_f32": FP32_VECTOR_PEAK_TFLOPS / 2,
-            "valu_issue_frac": valu_issue_frac(w.name, main_ms),
+            "valu_busy": counter_valu_busy(w.name),
             "avg_launch_ms": main_ms,
             "algorithmic_flops_per_launch": main_flops,
             "algorithmic_bytes_per_launch": bwd_main_bytes(w),
