@@ -155,7 +155,11 @@ __global__ __launch_bounds__(256) void k_decode_step(int64_t D, float* __restric
 #pragma unroll
   for (int i = 0; i < (K + 3) / 4; ++i) {
     const int r = (tid >> 6) + 4 * i;  // uniform over the wavefront
-    if (r < K) raw[i] = (r < K - 1 ? cstate + (b * (K - 1) + r) * D : x_t + b * D)[rcol];
+    const T* row = x_t + b * D;  // tap K-1; the stored rows (none when K = 1) before it
+    if constexpr (K > 1) {
+      if (r < K - 1) row = cstate + (b * (K - 1) + r) * D;
+    }
+    if (r < K) raw[i] = row[rcol];
   }
 #pragma unroll
   for (int i = 0; i < (K + 3) / 4; ++i) {
