@@ -270,6 +270,45 @@ __device__ __forceinline__ void chan_reduce_scatter(float (&v)[V], int) {
   }
 }
 
+// Permuted state order for four states per lane (N = 16), which lets every in-row
+// halving of the channel reduce-scatter below take one full-mask DPP add per pair.
+// Within a row of 16 lanes DPP pairs lanes by XOR only for the masks 8 (row_ror:8) and
+// 7 (row_half_mirror); a halving step with one add per pair also needs the partner to
+// hold, in the registers the lane keeps, the states the partner sends.  So lane l
+// (quad lane q = l & 3, lane bits b2, b3) holds the state quarter Q = q ^ (3*b2), and in
+// register r the state 4*Q + (r ^ m) with m = 2*b3 + b2: the partner across bit 3 (l ^ 8)
+// has the same Q and m ^ 2, the partner across bits 0..2 (l ^ 7) the same Q and m ^ 1.
+// A channel's four lanes still hold all 16 states (q -> q ^ 3*b2 is a permutation).
+__device__ __forceinline__ constexpr int perm_quarter(int lane) {
+  return (lane & 3) ^ (3 * ((lane >> 2) & 1));
+}
+__device__ __forceinline__ constexpr int perm_xor(int lane) {
+  return ((lane >> 2) & 1) | (((lane >> 3) & 1) << 1);
+}
+
+// Reduce-scatter over the 16 channels of a wavefront of the 8 values (index 2r + t:
+// register r's state, t = 0 for dB and 1 for dC) of the permuted order: halving across
+// lane bit 3 (row_ror:8, keeps r < 2), across lane bits 0..2 (row_half_mirror, keeps
+// r = 0), then across bit 4 (lane swap: bit 4 clear keeps t = 0).  On return v[0] of lane
+// l holds value t = bit 4 of l for state 4*perm_quarter(l) + perm_xor(l), summed over the
+// channels that agree with l's in channel bit 3 (lane bit 5): two partials per output, at
+// perm_partial_lane(t, n, 0 and 1).
+__device__ __forceinline__ void chan_reduce_scatter_perm(float (&v)[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v[k] += dpp<0x128>(v[k + 4]);  // row_ror:8 = lane ^ 8
+#pragma unroll
+  for (int k = 0; k < 2; ++k) v[k] += dpp<0x141>(v[k + 2]);  // row_half_mirror = lane ^ 7
+  float a = v[0], b = v[1];
+  swap16(a, b);
+  v[0] = a + b;
+}
+
+// Lane holding partial p (0 or 1) of output (t, n) after chan_reduce_scatter_perm.
+__device__ __forceinline__ constexpr int perm_partial_lane(int t, int n, int p) {
+  const int m = n & 3, b2 = m & 1, b3 = m >> 1, q = (n >> 2) ^ (3 * b2);
+  return q | (b2 << 2) | (b3 << 3) | (t << 4) | (p << 5);
+}
+
 // Lane that holds partial p (p < 16/V) of value index k for state quarter q after
 // chan_reduce_scatter<V>: k's bits (most significant first) at lane bits 3, 2, 4, p's
 // bits (least significant first) at the channel bits left over.

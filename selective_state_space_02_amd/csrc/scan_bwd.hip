@@ -219,8 +219,16 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
   constexpr int NP = 16 / V;      // partials per value left in LDS by chan_reduce_scatter
   constexpr int SL = kTc / SPLIT; // stashed steps = checkpoint interval
   static_assert(SPLIT == ckpt_per_tile(N), "stash split must match the checkpoints");
+  // Four states per lane take the permuted state order (perm_quarter / perm_xor), whose
+  // channel reduce-scatter costs one DPP add per pair.  B and C rows then take the
+  // two-copy layout of VecFetch::commit_perm, interleaved per step in sBC (B's row, then
+  // C's), so that the reverse step reads both with two LDS instructions.  The fused
+  // variant keeps the plain order: its LDS would no longer admit three workgroups per CU
+  // with the second copies.
+  constexpr bool PERM = NS == 4 && !FZ;
   __shared__ float sx[2][kTc][kTileCh], sd[2][kTc][kTileCh], sdy[2][kTc][kTileCh];
-  __shared__ float sB[2][kTc][N], sC[2][kTc][N];
+  __shared__ float sB[2][kTc][PERM ? 1 : N], sC[2][kTc][PERM ? 1 : N];
+  __shared__ float sBC[PERM ? 2 : 1][kTc][PERM ? 4 * N : 1];
   __shared__ float red[4][kTc][64];  // [wavefront][step][lane]
   // FZ: time-step bias, the time-step map's derivative for the current tile, and each
   // thread's running ddelta sums of its VEC channels
@@ -233,6 +241,9 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
   const bool act = d < D;
   const int D32 = int(D);
   const int dvalid = (D - d0 < kTileCh) ? int(D - d0) : kTileCh;
+  // register j of the lane holds state Qs*NS + (j ^ ms)
+  const int Qs = PERM ? perm_quarter(lane) : q, ms = PERM ? perm_xor(lane) : 0;
+  const uint32_t pa = uint32_t(16 * (ms & 1) + 4 * Qs + 2 * (ms >> 1)) * 4u;  // PERM reads
   const T* xb = x + int64_t(b) * L * D + d0;
   const T* db = delta + int64_t(b) * L * D + d0;
   const T* dyb = dy + int64_t(b) * L * D + d0;
@@ -242,7 +253,7 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
   T* ddb = ddelta + int64_t(b) * L * D + d0;
   // checkpoint f of this group: ckpt + ((b*nck + f)*D + d0)*N, lane at (cl*N + q*NS)
   const float* ckg = ckpt + (int64_t(b) * nck * D + d0) * N;
-  const uint32_t ckoff = act ? uint32_t(cl * N + q * NS) * 4u : kOffNone;
+  const uint32_t ckoff = act ? uint32_t(cl * N + Qs * NS) * 4u : kOffNone;
   const uint32_t ckbytes = uint32_t(dvalid * N) * 4u;
   float* pB = dBp + (int64_t(grp) * B + b) * L * N;
   float* pC = dCp + (int64_t(grp) * B + b) * L * N;
@@ -250,8 +261,8 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
   float A2[NS], gp[NS], dA_acc[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
-    A2[j] = act ? A[d * N + q * NS + j] * kLog2e : 0.f;
-    gp[j] = (act && gin) ? gin[((int64_t(b) * nc + c) * D + d) * N + q * NS + j] : 0.f;
+    A2[j] = act ? A[d * N + Qs * NS + (j ^ ms)] * kLog2e : 0.f;
+    gp[j] = (act && gin) ? gin[((int64_t(b) * nc + c) * D + d) * N + Qs * NS + (j ^ ms)] : 0.f;
     dA_acc[j] = 0.f;
   }
   const float Dd = act ? Dv[d] : 0.f;
@@ -292,8 +303,9 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
 #pragma unroll
     for (int hf = 0; hf < SPLIT; ++hf) {
       const bool has = tvalid > 0 && (hf == 0 || tt + hf * SL < L);
-      buf_load_states<NS>(buf_rsrc(ckg + (has ? tt / SL + hf : 0) * D * N, has ? ckbytes : 0u),
-                          ckoff, hk[hf]);
+      const auto rs = buf_rsrc(ckg + (has ? tt / SL + hf : 0) * D * N, has ? ckbytes : 0u);
+      if constexpr (PERM) buf_load_states_perm(rs, ckoff, ms, hk[hf]);
+      else buf_load_states<NS>(rs, ckoff, hk[hf]);
     }
   };
   // the gate's inputs of the pending tile (FZ with z), loaded just before its commit
@@ -332,8 +344,28 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
       fd.commit(gt, sd[bf]);
       fy.commit(gt, sdy[bf]);
     }
-    fB.commit(sB[bf], tid);
-    fC.commit(sC[bf], tid);
+    if constexpr (PERM) {
+      // (addresses rebuilt per tile from an opaque copy, not held across the compute)
+      const int ot = opaque(tid);
+      fB.commit_perm(&sBC[bf][0][0], 4 * N, ot);
+      fC.commit_perm(&sBC[bf][0][2 * N], 4 * N, ot);
+    } else {
+      fB.commit(sB[bf], tid);
+      fC.commit(sC[bf], tid);
+    }
+  };
+  // the lane's NS values of B, or of B and C, at step s of tile buffer bf
+  auto read_B = [&](int bf, int s, float (&o)[NS]) {
+    if constexpr (PERM) tile_read_perm(&sBC[bf][s][0], pa, o);
+    else tile_read_vec<N, NS>(sB[bf], s, q, o);
+  };
+  auto read_BC = [&](int bf, int s, float (&ob)[NS], float (&oc)[NS]) {
+    if constexpr (PERM) {
+      tile_read_perm2(&sBC[bf][s][0], pa, ob, oc);
+    } else {
+      tile_read_vec<N, NS>(sB[bf], s, q, ob);
+      tile_read_vec<N, NS>(sC[bf], s, q, oc);
+    }
   };
 
   int64_t tf = t0 + int64_t(ntile - 1) * kTc;  // first step of the current tile
@@ -357,7 +389,7 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
       // so the stash costs no register copies
       float as[SL][NS], hs[SL][NS];
       float ndl = sd[buf][s0][cl], nxv = sx[buf][s0][cl], nB[NS];
-      tile_read_vec<N, NS>(sB[buf], s0, q, nB);
+      read_B(buf, s0, nB);
 #pragma unroll
       for (int i = 0; i < SL; ++i) {
         const int s = s0 + i;
@@ -368,7 +400,7 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
         if (i + 1 < SL) {
           ndl = sd[buf][s + 1][cl];
           nxv = sx[buf][s + 1][cl];
-          tile_read_vec<N, NS>(sB[buf], s + 1, q, nB);
+          read_B(buf, s + 1, nB);
         }
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
@@ -388,8 +420,7 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
         rdl = sd[buf][s][cl];
         rxv = sx[buf][s][cl];
         rdy = sdy[buf][s][cl];
-        tile_read_vec<N, NS>(sB[buf], s, q, rB);
-        tile_read_vec<N, NS>(sC[buf], s, q, rC);
+        read_BC(buf, s, rB, rC);
       }
 #pragma unroll
       for (int i = SL - 1; i >= 0; --i) {
@@ -405,8 +436,7 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
           rdl = sd[buf][s - 1][cl];
           rxv = sx[buf][s - 1][cl];
           rdy = sdy[buf][s - 1][cl];
-          tile_read_vec<N, NS>(sB[buf], s - 1, q, rB);
-          tile_read_vec<N, NS>(sC[buf], s - 1, q, rC);
+          read_BC(buf, s - 1, rB, rC);
         }
         const float u = dl * xv;
         float sBg, sAq;
@@ -419,8 +449,9 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
           dA_acc[j] = __builtin_fmaf(gq, dl, dA_acc[j]);
           sAq = j ? __builtin_fmaf(gq, A2[j], sAq) : gq * A2[j];
           sBg = j ? __builtin_fmaf(g, Bv[j], sBg) : g * Bv[j];
-          vals[j] = g * u;
-          vals[NS + j] = dyv * hs[i][j];
+          // channel-sum values: dB then dC of each state (PERM), or all dB then all dC
+          vals[PERM ? 2 * j : j] = g * u;
+          vals[PERM ? 2 * j + 1 : NS + j] = dyv * hs[i][j];
           gp[j] = as[i][j] * g;
         }
         // identical in the channel's four lanes, which all write the same values
@@ -430,7 +461,8 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
         sd[buf][s][cl] = __builtin_fmaf(kLn2, sAq, xv * sBg);  // ddelta
         dD_acc = __builtin_fmaf(dyv, xv, dD_acc);
         if (s < kTc - 1) {
-          chan_reduce_scatter<V>(pv, lane);
+          if constexpr (PERM) chan_reduce_scatter_perm(pv);
+          else chan_reduce_scatter<V>(pv, lane);
           red[wave][s + 1][lane] = pv[0];
         }
 #pragma unroll
@@ -442,7 +474,8 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
         step_fence(dD_acc, rdl, rxv, rdy);
       }
     }
-    chan_reduce_scatter<V>(pv, lane);
+    if constexpr (PERM) chan_reduce_scatter_perm(pv);
+    else chan_reduce_scatter<V>(pv, lane);
     red[wave][0][lane] = pv[0];
     __syncthreads();
     if constexpr (FZ) {
@@ -474,9 +507,15 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
         float sum = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          float part = red[w][s][chan_partial_lane<V>(vi, 0, qr)];
+          float part;
+          if constexpr (PERM) {
+            part = red[w][s][perm_partial_lane(r / N, n, 0)] +
+                   red[w][s][perm_partial_lane(r / N, n, 1)];
+          } else {
+            part = red[w][s][chan_partial_lane<V>(vi, 0, qr)];
 #pragma unroll
-          for (int pi = 1; pi < NP; ++pi) part += red[w][s][chan_partial_lane<V>(vi, pi, qr)];
+            for (int pi = 1; pi < NP; ++pi) part += red[w][s][chan_partial_lane<V>(vi, pi, qr)];
+          }
           sum = w ? sum + part : part;
         }
         const int64_t o = (tf + s) * N;
@@ -511,11 +550,11 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
   if (act) {
     const int64_t o = (int64_t(b) * nc + c) * D + d;
 #pragma unroll
-    for (int j = 0; j < NS; ++j) dAp[o * N + q * NS + j] = dA_acc[j];
+    for (int j = 0; j < NS; ++j) dAp[o * N + Qs * NS + (j ^ ms)] = dA_acc[j];
     if (q == 0) dDp[o] = dD_acc;
     if (dh0 && c == 0) {
 #pragma unroll
-      for (int j = 0; j < NS; ++j) dh0[(int64_t(b) * D + d) * N + q * NS + j] = gp[j];
+      for (int j = 0; j < NS; ++j) dh0[(int64_t(b) * D + d) * N + Qs * NS + (j ^ ms)] = gp[j];
     }
   }
 }

@@ -272,6 +272,20 @@ struct VecFetch {
     BV::unpack(raw, v);
     if (tid < kTc * N) sm[tid / N][tid % N] = v[0];
   }
+  // Row layout of the permuted state order (N = 16): 2N floats, the step's vector (copy
+  // 0: state n at n) and the same vector with adjacent states swapped (copy 1: state n at
+  // N + (n ^ 1)); rows of consecutive steps start `stride` floats apart.
+  __device__ __forceinline__ void commit_perm(float* tile, int stride, int tid) const {
+    static_assert(N == 16, "the permuted state order is defined for four states per lane");
+    float v[1];
+    BV::unpack(raw, v);
+    if (tid < kTc * N) {
+      const int s = tid / N, n = tid % N;
+      float* r = tile + s * stride;
+      r[n] = v[0];
+      r[N + (n ^ 1)] = v[0];
+    }
+  }
 };
 
 // The NS state values of state group q (states q*NS .. q*NS+NS-1) at step s of an LDS
@@ -287,6 +301,30 @@ __device__ __forceinline__ void tile_read_vec(const float (*sm)[N], int s, int q
   } else {
     o[0] = sm[s][q];
   }
+}
+
+// A lane's four values of one step row of the permuted layout (VecFetch::commit_perm),
+// in the order of perm_quarter / perm_xor: register r gets state 4*Q + (r ^ m).  `a0` is
+// the lane's byte offset ((m & 1)*16 + 4*Q + 2*(m >> 1))*4: registers 0, 1 come from there
+// (copy m & 1 swaps the pair when m is odd) and 2, 3 from the quarter's other pair
+// (a0 ^ 8).  Each 8-byte read stays inside the row's 32 floats, one per LDS bank.
+__device__ __forceinline__ void tile_read_perm(const float* row, uint32_t a0, float (&o)[4]) {
+  const char* r = reinterpret_cast<const char*>(row);
+  const float2 lo = *reinterpret_cast<const float2*>(r + a0);
+  const float2 hi = *reinterpret_cast<const float2*>(r + (a0 ^ 8u));
+  o[0] = lo.x; o[1] = lo.y; o[2] = hi.x; o[3] = hi.y;
+}
+// The same for two rows 128 bytes apart (B's and C's rows of one step): the matching
+// reads of the two rows pair into one two-address LDS instruction each.
+__device__ __forceinline__ void tile_read_perm2(const float* row, uint32_t a0, float (&b)[4],
+                                                float (&c)[4]) {
+  const char* r = reinterpret_cast<const char*>(row);
+  const float2 b01 = *reinterpret_cast<const float2*>(r + a0);
+  const float2 c01 = *reinterpret_cast<const float2*>(r + a0 + 128);
+  const float2 b23 = *reinterpret_cast<const float2*>(r + (a0 ^ 8u));
+  const float2 c23 = *reinterpret_cast<const float2*>(r + (a0 ^ 8u) + 128);
+  b[0] = b01.x; b[1] = b01.y; b[2] = b23.x; b[3] = b23.y;
+  c[0] = c01.x; c[1] = c01.y; c[2] = c23.x; c[3] = c23.y;
 }
 
 // NS consecutive f32 state values of one lane through a descriptor (loads past it
@@ -305,6 +343,15 @@ __device__ __forceinline__ void buf_load_states(__amdgpu_buffer_rsrc_t r, uint32
   } else {
     o[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
   }
+}
+// Four f32 state values of one lane in the permuted order: register r gets the value at
+// byte offset off + 4*(r ^ m) (off = the lane's 16-byte state quarter, or kOffNone).
+__device__ __forceinline__ void buf_load_states_perm(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                     int m, float (&o)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(r, off + uint32_t((j ^ m) * 4), 0, 0));
 }
 template <int NS>
 __device__ __forceinline__ void buf_store_states(const float (&v)[NS], __amdgpu_buffer_rsrc_t r,

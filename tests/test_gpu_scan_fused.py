@@ -7,7 +7,9 @@ configurations, state sizes, dtypes, ragged L and D, with and without h0 and sto
 checkpoints.  The 2.8B-shaped layer runs in the benchmark's launch configuration and is
 checked on a sample of channels (every per-channel output) and on prefix / suffix
 windows (dC / dB, which sum over channels).  With every neighbour switched off the fused
-kernels must reproduce the plain scan bit for bit; repeated runs are bit-identical.
+kernels must reproduce the plain scan: bit for bit, except the sums that the plain
+backward adds in its permuted state order at N = 16 (equal there up to that rounding);
+repeated runs are bit-identical.
 """
 import hashlib
 
@@ -119,18 +121,32 @@ def test_scan_fused_recompute_matches_stored_checkpoints(w):
         assert torch.equal(a[k], b[k]), k
 
 
+@pytest.mark.parametrize("N", [8, 16])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_scan_fused_with_neighbours_off_is_the_plain_scan(dtype):
-    # no bias, no softplus, no gate: the fused kernels run the plain scan's arithmetic
-    w = custom(B=2, L=700, D=96, N=16, dtype=dtype)
-    say(f"[fused == plain] {dtype}")
+def test_scan_fused_with_neighbours_off_is_the_plain_scan(dtype, N):
+    # No bias, no softplus, no gate: the fused kernels run the plain scan's arithmetic.
+    # At N = 16 the plain backward holds a lane's four states in a lane-dependent order
+    # (its channel reduce-scatter needs it) and the fused one in the natural order, so
+    # the sums over states (dx, ddelta) and over channels (dB, dC) are added in another
+    # order there: equal up to that rounding.  Everything else is bit-identical.
+    w = custom(B=2, L=700, D=96, N=N, dtype=dtype)
+    say(f"[fused == plain] {dtype} N={N}")
     p = synth.scan_inputs(w, seed=4, with_h0=True)
     plain = scan_gpu(p, use_ckpt=True)
     q = dict(p, delta_raw=p["delta"], delta_bias=None, z=None)
     fused = fused_gpu(q, dict(softplus=False, bias=False, z=False))
     assert torch.equal(fused["out"], plain["y"])
+    order = ("dx", "ddelta", "dB", "dC") if N == 16 else ()
     for k in ("h_last", "dx", "ddelta", "dA", "dB", "dC", "dD", "dh0"):
-        assert torch.equal(fused[k], plain[k]), k
+        if k not in order:
+            assert torch.equal(fused[k], plain[k]), k
+            continue
+        a, b = fused[k].double(), plain[k].double()
+        # f32 sums of a few dozen terms in another order: a few ulps of the largest term;
+        # a bf16 output may in addition round to the neighbouring value (2^-8)
+        tol = 2.0 ** -8 if fused[k].dtype == torch.bfloat16 else 1e-6
+        err = float((a - b).abs().max() / b.abs().max())
+        assert err <= tol, (k, err)
 
 
 def test_scan_fused_accumulates_bias_grad():
