@@ -631,7 +631,7 @@ int conv1d_causal_step(void* stream, ssm_dtype_t dtype, int64_t B, int64_t D, in
   if (act != SSM_ACT_NONE && act != SSM_ACT_SILU)
     return fail(SSM_ERR_UNSUPPORTED, "activation %d not supported (0 none, 1 SiLU)", int(act));
   if (K > 8) return fail(SSM_ERR_UNSUPPORTED, "conv width K=%lld not supported (1..8)", (long long)K);
-  // one thread per (b, d): the grid's 2^31 - 1 blocks of 256 bound B*D
+  // element counts well inside int64 (the grid walks batch rows, so B itself is not bounded)
   if (B > kMaxElems / D || B * D > (int64_t(1) << 38))
     return fail(SSM_ERR_ARG, "tensor sizes overflow");
   int rc = K > 1 ? check_ptrs({{state, "state"}, {x_t, "x_t"}, {W, "W"}, {out_t, "out_t"}},

@@ -180,27 +180,62 @@ __global__ __launch_bounds__(256) void k_decode_step(int64_t D, float* __restric
   step_compute<T, N, true>(o, b, d, D, q, xv, h, dtb, sp, z_t, out_t);
 }
 
-template <typename T, int K, int ACT>
+// One token of the causal conv for VEC consecutive channels per thread (VEC = 4 when D is
+// a multiple of 4, moving 8 or 16 bytes per access, else 1).  blockIdx.x picks the channel
+// group; the batch rows are walked from blockIdx.y in steps of gridDim.y, which the host
+// sets to about B / kConvStepRows, so the grid needs no 64-bit index division, any B fits,
+// and the taps and bias of the thread's channels are read once for all its rows.
+constexpr int kConvStepRows = 4;
+template <typename T, int K, int ACT, int VEC>
 __global__ __launch_bounds__(256) void k_conv_step(int64_t B, int64_t D, T* __restrict__ state,
                                                    const T* __restrict__ x_t,
                                                    const float* __restrict__ W,
                                                    const float* __restrict__ bias,
                                                    T* __restrict__ out_t) {
-  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= B * D) return;
-  const int64_t b = i / D, d = i % D;
-  float win[K];
+  const int64_t d0 = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) * VEC;
+  if (d0 >= D) return;
+  // the VEC*K taps of the thread's channels are contiguous (and 16-byte aligned for VEC =
+  // 4, as W is): read them, and the biases, as 16-byte vectors
+  float w[VEC][K], bv[VEC];
+  if constexpr (VEC == 4) {
+    float wf[4 * K];
 #pragma unroll
-  for (int k = 0; k < K - 1; ++k) win[k] = to_f32(state[(b * (K - 1) + k) * D + d]);
-  win[K - 1] = to_f32(x_t[i]);
-  float acc = bias ? bias[d] : 0.f;
+    for (int i = 0; i < K; ++i) {
+      const float4 v = reinterpret_cast<const float4*>(W + d0 * K)[i];
+      wf[4 * i] = v.x; wf[4 * i + 1] = v.y; wf[4 * i + 2] = v.z; wf[4 * i + 3] = v.w;
+    }
 #pragma unroll
-  for (int k = 0; k < K; ++k) acc = __builtin_fmaf(W[d * K + k], win[k], acc);
-  if constexpr (ACT == kActSilu) acc *= sigmoid_f(acc);
-  out_t[i] = from_f32<T>(acc);
-  // the values came from T, so storing them back in T is exact
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-  for (int k = 0; k < K - 1; ++k) state[(b * (K - 1) + k) * D + d] = from_f32<T>(win[k + 1]);
+      for (int k = 0; k < K; ++k) w[c][k] = wf[c * K + k];
+    const float4 bb = bias ? *reinterpret_cast<const float4*>(bias + d0) : make_float4(0.f, 0.f, 0.f, 0.f);
+    bv[0] = bb.x; bv[1] = bb.y; bv[2] = bb.z; bv[3] = bb.w;
+  } else {
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) w[c][k] = W[(d0 + c) * K + k];
+      bv[c] = bias ? bias[d0 + c] : 0.f;
+    }
+  }
+  for (int64_t b = blockIdx.y; b < B; b += gridDim.y) {
+    float win[K][VEC];
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k) VecLoad<T, VEC>::run(state + (b * (K - 1) + k) * D + d0, win[k]);
+    VecLoad<T, VEC>::run(x_t + b * D + d0, win[K - 1]);
+    float acc[VEC];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) {
+      acc[c] = bv[c];
+#pragma unroll
+      for (int k = 0; k < K; ++k) acc[c] = __builtin_fmaf(w[c][k], win[k][c], acc[c]);
+      if constexpr (ACT == kActSilu) acc[c] *= sigmoid_f(acc[c]);
+    }
+    VecStore<T, VEC>::run(out_t + b * D + d0, acc);
+    // the window moves up one row (the values came from T, so storing them back is exact)
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k) VecStore<T, VEC>::run(state + (b * (K - 1) + k) * D + d0, win[k + 1]);
+  }
 }
 
 template <typename T, int N, bool FZ>
@@ -237,12 +272,20 @@ hipError_t launch_scan_step(const ScanStepArgs& a, hipStream_t st) {
   return a.dtype == 0 ? scan_step_t<float>(a, st) : scan_step_t<bf16_t>(a, st);
 }
 
+template <typename T, int K, int ACT, int VEC>
+static void conv_step_kav(const ConvStepArgs& a, hipStream_t st) {
+  const int64_t groups = (a.D + VEC - 1) / VEC;
+  const int64_t gy = (a.B + kConvStepRows - 1) / kConvStepRows;
+  const dim3 grid(unsigned((groups + 255) / 256), unsigned(gy < 65535 ? gy : 65535));
+  hipLaunchKernelGGL((k_conv_step<T, K, ACT, VEC>), grid, dim3(256), 0, st, a.B, a.D,
+                     static_cast<T*>(a.state), static_cast<const T*>(a.x_t), a.W, a.bias,
+                     static_cast<T*>(a.out_t));
+}
+
 template <typename T, int K, int ACT>
 static void conv_step_ka(const ConvStepArgs& a, hipStream_t st) {
-  const int64_t n = a.B * a.D;
-  hipLaunchKernelGGL((k_conv_step<T, K, ACT>), dim3(unsigned((n + 255) / 256)), dim3(256), 0, st,
-                     a.B, a.D, static_cast<T*>(a.state), static_cast<const T*>(a.x_t), a.W,
-                     a.bias, static_cast<T*>(a.out_t));
+  if (a.D % 4 == 0) conv_step_kav<T, K, ACT, 4>(a, st);
+  else conv_step_kav<T, K, ACT, 1>(a, st);
 }
 
 template <typename T, int K>

@@ -102,8 +102,11 @@ def test_scan_decode_is_bit_identical_to_single_chunk_scan(dtype):
     assert torch.equal(h, h_seq)
 
 
+# four channels per thread (D = 20, 5120) and one (D = 70, 33); B = 70000 is more batch rows
+# than one grid column of blocks, which the kernel walks in steps of the grid
 CONV_STEP_CASES = [custom(B=3, L=5, D=20, K=4), custom(B=2, L=9, D=70, K=8, dtype="bf16"),
-                   custom(B=4, L=2, D=33, K=1), custom(B=2, L=5, D=5120, K=4, dtype="bf16")]
+                   custom(B=4, L=2, D=33, K=1), custom(B=2, L=5, D=5120, K=4, dtype="bf16"),
+                   custom(B=70000, L=3, D=8, K=3, dtype="bf16")]
 
 
 @pytest.mark.parametrize("w", CONV_STEP_CASES, ids=lambda w: f"B{w.B}D{w.D}K{w.K}{w.dtype}")
