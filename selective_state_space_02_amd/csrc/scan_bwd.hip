@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
   const T* Cb = Cm + int64_t(b) * L * N;
   T* dxb = dx + int64_t(b) * L * D + d0;
   T* ddb = ddelta + int64_t(b) * L * D + d0;
-  // checkpoint f of this group: ckpt + ((b*nck + f)*D + d0)*N, lane at (cl*N + q*NS)
+  // checkpoint f of this group: ckpt + ((b*nck + f)*D + d0)*N, lane at (cl*N + Qs*NS)
   const float* ckg = ckpt + (int64_t(b) * nck * D + d0) * N;
   const uint32_t ckoff = act ? uint32_t(cl * N + Qs * NS) * 4u : kOffNone;
   const uint32_t ckbytes = uint32_t(dvalid * N) * 4u;
