@@ -36,6 +36,7 @@ __global__ __launch_bounds__(256, 4) void k_fwd_summary(
     const T* __restrict__ delta, const float* __restrict__ A, const T* __restrict__ Bm,
     const float* __restrict__ dtb, bool sp, float* __restrict__ S, float* __restrict__ SD) {
   constexpr int NS = N / 4;
+  // sx holds u = delta * x (commit_tile below)
   __shared__ float sx[2][kTc][kTileCh], sd[2][kTc][kTileCh], sB[2][kTc][N];
   __shared__ float sbias[FZ ? kTileCh : 1];
   const int c = blockIdx.z, b = blockIdx.y, tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
@@ -63,20 +64,27 @@ __global__ __launch_bounds__(256, 4) void k_fwd_summary(
     if (tid < kTileCh) sbias[tid] = (dtb && tid < dvalid) ? dtb[d0 + tid] : 0.f;
     __syncthreads();
   }
-  // chunks 0..nc-2 are full: every row is valid
-  auto commit_delta = [&](float (*sm)[kTileCh]) {
+  // chunks 0..nc-2 are full: every row is valid.  The tile's x is staged as the step's
+  // input u = delta * x (the only form the summary uses), formed once per element here
+  // from the delta this thread has just written, instead of in each of a channel's four
+  // lanes at every step.
+  auto commit_tile = [&](int bf) {
     if constexpr (FZ)
-      fd.commit_map(gt, sm, [&](int, float (&v)[VEC]) {
+      fd.commit_map(gt, sd[bf], [&](int, float (&v)[VEC]) {
         time_step_map<VEC>(v, &sbias[gt.c], gt.c < dvalid, sp, nullptr);
       });
     else
-      fd.commit(gt, sm);
+      fd.commit(gt, sd[bf]);
+    fx.commit_map(gt, sx[bf], [&](int k, float (&v)[VEC]) {
+      const float* dv = &sd[bf][gt.s_in + k * ChTile<T, VEC>::RPP][gt.c];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) v[i] *= dv[i];
+    });
   };
   fx.fetch(gt, xb + t0 * D, D32, kTc, dvalid);
   fd.fetch(gt, db + t0 * D, D32, kTc, dvalid);
   fB.fetch(Bb + t0 * N, kTc, voff);
-  fx.commit(gt, sx[0]);
-  commit_delta(sd[0]);
+  commit_tile(0);
   fB.commit(sB[0], tid);
   __syncthreads();
   for (int it = 0; it < ntile; ++it) {
@@ -90,7 +98,7 @@ __global__ __launch_bounds__(256, 4) void k_fwd_summary(
     }
 #pragma unroll 4
     for (int s = 0; s < kTc; ++s) {
-      const float dl = sd[buf][s][cl], u = dl * sx[buf][s][cl];
+      const float dl = sd[buf][s][cl], u = sx[buf][s][cl];
       float Bv[NS];
       tile_read_vec<N, NS>(sB[buf], s, q, Bv);
 #pragma unroll
@@ -101,8 +109,7 @@ __global__ __launch_bounds__(256, 4) void k_fwd_summary(
       sdl += dl;
     }
     if (more) {
-      fx.commit(gt, sx[buf ^ 1]);
-      commit_delta(sd[buf ^ 1]);
+      commit_tile(buf ^ 1);
       fB.commit(sB[buf ^ 1], tid);
     }
     __syncthreads();
