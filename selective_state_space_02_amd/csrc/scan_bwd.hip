@@ -62,7 +62,9 @@ __global__ __launch_bounds__(256, 4) void k_bwd_summary(
     A2[j] = act ? A[d * N + q * NS + j] * kLog2e : 0.f;
     gp[j] = 0.f;
   }
-  float sdl = 0.f;
+  // running sums of the delta this thread stages (ChTile placement): the chunk's sum of
+  // delta, accumulated once per value instead of in each of a channel's lanes per step
+  float dsum[VEC] = {};
   const int64_t t0 = int64_t(c) * Lc, t1 = (t0 + Lc < L) ? t0 + Lc : L;
   const int ntile = int((t1 - t0 + kTc - 1) / kTc);
   // tiles are walked from the last one backwards
@@ -84,11 +86,16 @@ __global__ __launch_bounds__(256, 4) void k_bwd_summary(
     pend_tv = tvalid;
   };
   auto commit = [&](int bf) {
-    if constexpr (FZ) {
-      fd.commit_map(gt, sd[bf], [&](int k, float (&v)[VEC]) {
+    // (rows past L were loaded as 0, and the time-step map zeroes them)
+    fd.commit_map(gt, sd[bf], [&](int k, float (&v)[VEC]) {
+      if constexpr (FZ) {
         const bool ok = gt.s_in + k * ChTile<T, VEC>::RPP < pend_tv && gt.c < dvalid;
         time_step_map<VEC>(v, &sbias[gt.c], ok, sp, nullptr);
-      });
+      }
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) dsum[i] += v[i];
+    });
+    if constexpr (FZ) {
       if (zb)
         fy.commit_map(gt, sdy[bf], [&](int k, float (&v)[VEC]) {
           float zv[VEC];
@@ -99,7 +106,6 @@ __global__ __launch_bounds__(256, 4) void k_bwd_summary(
       else
         fy.commit(gt, sdy[bf]);
     } else {
-      fd.commit(gt, sd[bf]);
       fy.commit(gt, sdy[bf]);
     }
     fC.commit(sC[bf], tid);
@@ -131,10 +137,9 @@ __global__ __launch_bounds__(256, 4) void k_bwd_summary(
         const float g = __builtin_fmaf(dyv, Cv[j], gp[j]);
         gp[j] = __builtin_amdgcn_exp2f(dl * A2[j]) * g;
       }
-      sdl += dl;
       step_fence_arr(gp);
       step_fence_arr(nC);
-      step_fence(sdl, ndl, ndy);
+      step_fence(ndl, ndy);
     }
     if (more) commit(buf ^ 1);
     __syncthreads();
@@ -143,8 +148,10 @@ __global__ __launch_bounds__(256, 4) void k_bwd_summary(
     const int64_t o = (int64_t(b) * nc + c) * D + d;
 #pragma unroll
     for (int j = 0; j < NS; ++j) GS[o * N + q * NS + j] = gp[j];
-    if (q == 0) SD[o] = sdl;
   }
+  // the tile buffers are free after the loop's last barrier
+  const float sdl = chan_rows_sum(gt, dsum, &sd[0][0][0], tid);
+  if (tid < dvalid) SD[(int64_t(b) * nc + c) * D + d0 + tid] = sdl;
 }
 
 template <int N>

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256, 4) void k_fwd_summary(
     A2[j] = act ? A[d * N + q * NS + j] * kLog2e : 0.f;
     h[j] = 0.f;
   }
-  float sdl = 0.f;
+  float dsum[VEC] = {};  // running sums of the delta this thread stages (ChTile placement)
   const int64_t t0 = int64_t(c) * Lc;  // chunks 0..nc-2 are full
   const int ntile = int(Lc / kTc);
   const ChTile<T, VEC> gt(D32, dvalid, tid);
@@ -68,13 +68,13 @@ __global__ __launch_bounds__(256, 4) void k_fwd_summary(
   // input u = delta * x (the only form the summary uses), formed once per element here
   // from the delta this thread has just written, instead of in each of a channel's four
   // lanes at every step.
+  // The chunk's sum of delta is accumulated here too, by the staging thread of each value.
   auto commit_tile = [&](int bf) {
-    if constexpr (FZ)
-      fd.commit_map(gt, sd[bf], [&](int, float (&v)[VEC]) {
-        time_step_map<VEC>(v, &sbias[gt.c], gt.c < dvalid, sp, nullptr);
-      });
-    else
-      fd.commit(gt, sd[bf]);
+    fd.commit_map(gt, sd[bf], [&](int, float (&v)[VEC]) {
+      if constexpr (FZ) time_step_map<VEC>(v, &sbias[gt.c], gt.c < dvalid, sp, nullptr);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) dsum[i] += v[i];
+    });
     fx.commit_map(gt, sx[bf], [&](int k, float (&v)[VEC]) {
       const float* dv = &sd[bf][gt.s_in + k * ChTile<T, VEC>::RPP][gt.c];
 #pragma unroll
@@ -106,7 +106,6 @@ __global__ __launch_bounds__(256, 4) void k_fwd_summary(
         const float a = __builtin_amdgcn_exp2f(dl * A2[j]);
         h[j] = __builtin_fmaf(a, h[j], u * Bv[j]);
       }
-      sdl += dl;
     }
     if (more) {
       commit_tile(buf ^ 1);
@@ -118,8 +117,10 @@ __global__ __launch_bounds__(256, 4) void k_fwd_summary(
     const int64_t o = (int64_t(b) * nc + c) * D + d;
 #pragma unroll
     for (int j = 0; j < NS; ++j) S[o * N + q * NS + j] = h[j];
-    if (q == 0) SD[o] = sdl;
   }
+  // the tile buffers are free after the loop's last barrier
+  const float sdl = chan_rows_sum(gt, dsum, &sx[0][0][0], tid);
+  if (tid < dvalid) SD[(int64_t(b) * nc + c) * D + d0 + tid] = sdl;
 }
 
 template <int N>

@@ -197,6 +197,26 @@ struct ChFetch {
   }
 };
 
+// Per-channel total of values the threads have accumulated in ChTile placement: each
+// thread holds running sums `part` of its VEC channels over its rows (s_in + k*RPP, every
+// tile), and the RPP threads that share a channel column are added in row order through
+// `scratch` (kTileThreads*VEC floats of LDS, free on entry).  Thread tid < kTileCh gets
+// the total of channel tid.  Contains a barrier: every thread of the block must call it.
+template <typename T, int VEC>
+__device__ __forceinline__ float chan_rows_sum(const ChTile<T, VEC>& g, const float (&part)[VEC],
+                                               float* scratch, int tid) {
+  using G = ChTile<T, VEC>;
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) scratch[tid * VEC + i] = part[i];
+  __syncthreads();
+  float t = 0.f;
+  if (tid < kTileCh) {
+    const int tc = tid / VEC, ci = tid % VEC;  // thread column and channel within it
+    for (int r = 0; r < G::RPP; ++r) t += scratch[(r * G::TPR + tc) * VEC + ci];
+  }
+  return t;
+}
+
 // Writes an LDS tile of per-channel outputs to a [.,L,D] tensor; tile = base + tf*D + d0;
 // rows >= tvalid and channels >= dvalid are not written.
 // tile_store_ch_map applies f(k, v) to pass k's values (rows g.s_in + k*RPP) before the
