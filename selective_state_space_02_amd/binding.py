@@ -49,7 +49,7 @@ def load():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
-                           "(run __graft_entry__.build() or selective_state_space_02_amd/build.py)")
+                           "(build it with: python selective_state_space_02_amd/build.py)")
     try:
         lib = ctypes.CDLL(LIB_PATH)
     except OSError as e:
