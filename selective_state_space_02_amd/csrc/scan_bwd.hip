@@ -484,6 +484,14 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
     if constexpr (PERM) chan_reduce_scatter_perm(pv);
     else chan_reduce_scatter<V>(pv, lane);
     red[wave][0][lane] = pv[0];
+    // The plain variant commits the next tile's inputs to the other buffer (free since
+    // the previous tile's second barrier) right after the wavefront's own compute, where
+    // it overlaps the workgroup's slower wavefronts, not between the barriers, where the
+    // whole workgroup waits.  The fused variant loads its gate inputs after the barrier
+    // (registers), so it commits after the stores.
+    if constexpr (!FZ) {
+      if (it + 1 < ntile) commit(buf ^ 1);
+    }
     __syncthreads();
     if constexpr (FZ) {
       if (it + 1 < ntile) fetch_gate();  // the next tile's, consumed by its commit below
@@ -531,7 +539,7 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
       }
     }
     if (it + 1 < ntile) {
-      commit(buf ^ 1);
+      if constexpr (FZ) commit(buf ^ 1);
 #pragma unroll
       for (int hf = 0; hf < SPLIT; ++hf) {
 #pragma unroll
