@@ -51,6 +51,7 @@ class HipEvents:
         self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventQuery.argtypes = [ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipGetLastError.argtypes = []
         self.made = []
 
     def pair(self):
@@ -67,7 +68,10 @@ class HipEvents:
         """None if the pair was never recorded (a kernel the workload did not launch)."""
         ms = self.c.c_float()
         rc = self.hip.hipEventElapsedTime(self.c.byref(ms), self.c.c_void_p(start), self.c.c_void_p(stop))
-        return ms.value if rc == 0 else None
+        if rc != 0:
+            self.hip.hipGetLastError()  # the query's own error, not left pending for later calls
+            return None
+        return ms.value
 
     def destroy(self):
         for e in self.made:

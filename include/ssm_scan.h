@@ -48,7 +48,10 @@
  * - Errors.  Arguments are validated on the host before any HIP call; a rejected
  *   call enqueues nothing and leaves every output untouched.  The return value is
  *   SSM_OK or a negative SSM_ERR_* code; ssm_last_error() then describes the
- *   problem.  Nothing aborts and no exception crosses the ABI.
+ *   problem.  Nothing aborts and no exception crosses the ABI.  SSM_ERR_HIP
+ *   reports only this call's launches: a HIP error still pending on the calling
+ *   thread from earlier runtime calls (hipGetLastError not yet called) is cleared
+ *   before they are enqueued.
  */
 #ifndef SSM_SCAN_H
 #define SSM_SCAN_H

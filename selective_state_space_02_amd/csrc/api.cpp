@@ -207,6 +207,11 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// A HIP error left pending on this thread by earlier runtime calls (the caller's, or any
+// other library's) would be read back by the launch check after this call's kernels and
+// reported as this call's failure; it is cleared just before the launches.
+void clear_pending_hip_error() { (void)hipGetLastError(); }
+
 // conv plan
 void conv_plan(int64_t B, int64_t L, int64_t D, int64_t K, ssm::ConvPlan* p) {
   // about 4096 workgroups; a workgroup spans 64 lanes of 4 channels (2 above width 4;
@@ -322,6 +327,7 @@ int ssm_scan_fwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t 
   a.x = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dv = Dv; a.h0 = h0;
   a.y = y; a.h_last = h_last;
   a.vec4 = D % 4 == 0;
+  clear_pending_hip_error();
   return hip_status(ssm::launch_scan_fwd(a, p, static_cast<hipStream_t>(stream)), "ssm_scan_fwd");
 }
 
@@ -360,10 +366,12 @@ int ssm_scan_bwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t 
     ssm::ScanArgs f = a;
     f.y = nullptr;
     f.h_last = nullptr;
+    clear_pending_hip_error();
     hipError_t e = ssm::launch_scan_fwd(f, fp, st);
     if (e != hipSuccess) return hip_status(e, "ssm_scan_bwd (forward recompute)");
     p.ckpt = own_ckpt;
   }
+  clear_pending_hip_error();
   return hip_status(ssm::launch_scan_bwd(a, p, st), "ssm_scan_bwd");
 }
 
@@ -396,6 +404,7 @@ int ssm_scan_fused_fwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, in
   a.fused = true;
   a.dt_bias = delta_bias; a.dt_softplus = delta_softplus != 0;
   a.z = z; a.ysave = y_save;
+  clear_pending_hip_error();
   return hip_status(ssm::launch_scan_fwd(a, p, static_cast<hipStream_t>(stream)),
                     "ssm_scan_fused_fwd");
 }
@@ -449,10 +458,12 @@ int ssm_scan_fused_bwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, in
     f.h_last = nullptr;
     f.z = nullptr;
     f.ysave = nullptr;
+    clear_pending_hip_error();
     hipError_t e = ssm::launch_scan_fwd(f, fp, st);
     if (e != hipSuccess) return hip_status(e, "ssm_scan_fused_bwd (forward recompute)");
     p.ckpt = own_ckpt;
   }
+  clear_pending_hip_error();
   return hip_status(ssm::launch_scan_bwd(a, p, st), "ssm_scan_fused_bwd");
 }
 
@@ -495,6 +506,7 @@ int conv1d_causal_bwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int
   a.act = int(act);
   a.x = x; a.W = W; a.bias = act == SSM_ACT_SILU ? bias : nullptr;
   a.dout = dout; a.dx = dx; a.dW = dW; a.db = db;
+  clear_pending_hip_error();
   return hip_status(ssm::launch_conv1d_bwd(a, p, static_cast<hipStream_t>(stream)),
                     "conv1d_causal_bwd");
 }
@@ -514,6 +526,7 @@ int conv1d_causal_fwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int
   a.Tb = p.Tb; a.nTb = p.nTb;
   a.act = int(act);
   a.x = x; a.W = W; a.bias = bias; a.out = out;
+  clear_pending_hip_error();
   return hip_status(ssm::launch_conv1d_fwd(a, static_cast<hipStream_t>(stream)),
                     "conv1d_causal_fwd");
 }
@@ -547,6 +560,7 @@ int rmsnorm_fwd(void* stream, ssm_dtype_t dtype, int64_t R, int64_t M, const voi
   a.eps = eps;
   a.x = x; a.residual = residual; a.scale = scale; a.y = y; a.rms = rms;
   a.residual_out = residual_out;
+  clear_pending_hip_error();
   return hip_status(ssm::launch_rmsnorm_fwd(a, static_cast<hipStream_t>(stream)), "rmsnorm_fwd");
 }
 
@@ -563,6 +577,7 @@ int ssm_scan_step(void* stream, ssm_dtype_t dtype, int64_t B, int64_t D, int64_t
   a.B = B; a.D = D; a.N = N;
   a.h = h; a.x_t = x_t; a.delta_t = delta_t; a.A = A; a.B_t = B_t; a.C_t = C_t; a.Dv = Dv;
   a.y_t = y_t;
+  clear_pending_hip_error();
   return hip_status(ssm::launch_scan_step(a, static_cast<hipStream_t>(stream)), "ssm_scan_step");
 }
 
@@ -586,6 +601,7 @@ int ssm_scan_fused_step(void* stream, ssm_dtype_t dtype, int64_t B, int64_t D, i
   a.y_t = out_t;
   a.fused = true;
   a.dt_bias = delta_bias; a.dt_softplus = delta_softplus != 0; a.z_t = z_t;
+  clear_pending_hip_error();
   return hip_status(ssm::launch_scan_step(a, static_cast<hipStream_t>(stream)),
                     "ssm_scan_fused_step");
 }
@@ -616,6 +632,7 @@ int ssm_decode_step(void* stream, ssm_dtype_t dtype, int64_t B, int64_t D, int64
   a.h = h; a.conv_state = conv_state; a.x_t = x_t; a.W = W; a.conv_bias = conv_bias;
   a.delta_t = delta_t; a.A = A; a.B_t = B_t; a.C_t = C_t; a.Dv = Dv;
   a.dt_bias = delta_bias; a.dt_softplus = delta_softplus != 0; a.z_t = z_t; a.out_t = out_t;
+  clear_pending_hip_error();
   return hip_status(ssm::launch_decode_step(a, static_cast<hipStream_t>(stream)),
                     "ssm_decode_step");
 }
@@ -644,6 +661,7 @@ int conv1d_causal_step(void* stream, ssm_dtype_t dtype, int64_t B, int64_t D, in
   a.B = B; a.D = D; a.K = K;
   a.act = int(act);
   a.state = state; a.x_t = x_t; a.W = W; a.bias = bias; a.out_t = out_t;
+  clear_pending_hip_error();
   return hip_status(ssm::launch_conv1d_step(a, static_cast<hipStream_t>(stream)),
                     "conv1d_causal_step");
 }
@@ -674,6 +692,7 @@ int rmsnorm_bwd(void* stream, ssm_dtype_t dtype, int64_t R, int64_t M, const voi
   a.dtype = int(dtype);
   a.R = R; a.M = M;
   a.dy = dy; a.x = x; a.scale = scale; a.rms = rms; a.dx = dx; a.dscale = dscale;
+  clear_pending_hip_error();
   return hip_status(ssm::launch_rmsnorm_bwd(a, p, static_cast<hipStream_t>(stream)), "rmsnorm_bwd");
 }
 
