@@ -12,7 +12,7 @@ step's algorithmic HBM bytes per second, a roofline entry for the dominant kerne
 f64 CPU oracle timed on a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-  python bench.py --gpus N        (N > 1 exits: this build runs on one GPU)
+  python bench.py --gpus N        (N > 1 exits: the scan library runs on one GPU)
 """
 import argparse
 import json
@@ -545,7 +545,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build runs on one GPU: every figure is one GPU's "
+        print(json.dumps({"error": "the scan library runs on one GPU: every figure is one GPU's "
                           "throughput; --gpus must be 1"}), flush=True)
         sys.exit(2)
 
