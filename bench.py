@@ -6,10 +6,14 @@ rmsnorm_bwd, each through the C ABI.  Default workload: the Mamba-2.8B-shaped la
 (B=2, L=16384, d_inner=5120, d_state=16, d_conv=4, bf16 activations, f32 state and
 arithmetic; RMSNorm backward over [32768, 2560]).
 
-Prints one JSON line: tokens*channels per second of the step (B*L*D / step time), the
-step's algorithmic HBM bytes per second, a roofline entry for the dominant kernel
-(measured live with HIP events recorded around that kernel on its own stream), and the
-f64 CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line.  `value` is the metric the workload is quoted on: tokens*channels
+per second of the scan forward+backward (B*L*D over the two calls' time, each timed with
+HIP events on the stream it runs on); the whole step's rate is reported beside it.  The
+`roofline` entry covers the dominant kernel (the backward main pass): its algorithmic
+HBM bytes per launch over its average launch time (HIP events recorded by the library
+around that kernel on its own stream) against the 8 TB/s HBM peak, and, beside that, its
+VALU issue time from the committed counter record against its measured time.  The f64
+CPU oracle is timed on a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
   python bench.py --gpus N        (N > 1 exits: the scan library runs on one GPU)
@@ -26,15 +30,25 @@ if ROOT not in sys.path:
 
 METRIC = "scan fwd+bwd tokens·channels/sec and achieved HBM GB/s (% of peak), 1 GPU"
 HBM_PEAK_GBPS = 8000.0
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # published, counting packed f32 FMA (not used here)
 
-# Algorithmic floating-point work per state update (b, t, d, n) of the backward main
-# kernel, counting FMA 2, mul/add 1, exp 1.  Recompute of a_t and h_t from the
-# checkpoint: delta*A 1, exp 1, delta*x*B 1, state FMA 2 -> 5.  Reverse: g = dy*C + g' 2,
-# a*h_{t-1} 1, dA term g*q*delta accumulated 3, ddelta term sum g*A*q 2, the shared
-# dx/ddelta term sum g*B 2, dB term g*delta*x and its channel sum 2, dC term dy*h and its
-# channel sum 2, carry a*g 1 -> 15.
-BWD_MAIN_FLOPS_PER_UPDATE = 20
+# MI355X VALU issue: 256 CUs x 4 SIMDs; a SIMD issues one wave64 VALU instruction per 4
+# cycles (16 lanes per cycle) at 2.4 GHz, and a transcendental one (v_exp_f32) occupies
+# it for 8 (the counter record's SQ_ACTIVE_INST_VALU equals 4 cycles per VALU instruction
+# plus 4 more per transcendental one to within 1.3%).  Without packed f32 (disabled in
+# every build) that is 3.93e13 lane-operations/s, or 78.6 TFLOP/s counting an FMA as 2.
+SIMDS = 256 * 4
+CLOCK_HZ = 2.4e9
+VALU_WAVE_INSTR_PER_S = SIMDS * CLOCK_HZ / 4
+LANE_OPS_PEAK = VALU_WAVE_INSTR_PER_S * 64
+FP32_NONPACKED_PEAK_TFLOPS = 2 * LANE_OPS_PEAK / 1e12
+
+# Operations the backward main pass must issue per state update (b, t, d, n), as the
+# method's cost model counts them: recompute of a_t and h_t (delta*A, exp, delta*x*B,
+# state FMA) and the reverse step (g = dy*C + g', a*h_{t-1}, g*q, the dA FMA, the
+# sum g*A*q, the sum g*B, the dB term g*delta*x, the dC term dy*h, the carry a*g):
+# 13 VALU operations and 1 exp.  The cross-lane channel sums come on top.
+BWD_MAIN_VALU_PER_UPDATE = 13
+BWD_MAIN_EXP_PER_UPDATE = 1
 
 
 class HipEvents:
@@ -114,12 +128,15 @@ def counter_traffic(workload_name):
     return rec.get("traffic_bytes_per_launch") if rec else None
 
 
-def counter_valu_busy(workload_name):
-    """Fraction of the SIMDs' cycles in which the backward main kernel's VALU was busy
-    (4 * SQ_ACTIVE_INST_VALU over SIMDs x dispatch cycles, in the counter run), or None
-    (see counter_record)."""
+def counter_valu_slots(workload_name):
+    """VALU issue slots per launch of the backward main kernel from the committed counter
+    record: wave64 VALU instructions, a transcendental one counting twice (SQ_INSTS_VALU
+    + SQ_INSTS_VALU_TRANS_F32), or None (see counter_record)."""
     rec = counter_record(workload_name)
-    return rec.get("valu_busy") if rec else None
+    if not rec:
+        return None
+    sq = rec["sq"]
+    return sq["SQ_INSTS_VALU"] + sq["SQ_INSTS_VALU_TRANS_F32"]
 
 
 def algorithmic_bytes(w):
@@ -643,14 +660,16 @@ def main():
     he.destroy()
 
     tokch = B * L * D
-    value = tokch / (ms_per_step * 1e-3)
     ab = algorithmic_bytes(w)
     step_bytes = sum(ab.values())
     scan_ms = call_ms["scan_fwd"] + call_ms["scan_bwd"]
+    value = tokch / (scan_ms * 1e-3)  # the metric: scan forward + backward
     main_ms = kern_ms["bwd_main"]
-    main_flops = BWD_MAIN_FLOPS_PER_UPDATE * B * L * D * N
-    achieved_tflops = main_flops / (main_ms * 1e-3) / 1e12
     main_gbps = bwd_main_bytes(w) / (main_ms * 1e-3) / 1e9
+    updates = B * L * D * N
+    main_ops = (BWD_MAIN_VALU_PER_UPDATE + BWD_MAIN_EXP_PER_UPDATE) * updates
+    slots = counter_valu_slots(w.name)
+    valu_floor_ms = slots / VALU_WAVE_INSTR_PER_S * 1e3 if slots else None
 
     layer_fwd = measure_layer_forward(w, c, r, args.seed, K_, dev)
     decode = measure_decode(w, args.seed, K_, dev)
@@ -679,10 +698,13 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "io_dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "L": L, "D": D, "N": N, "K": K,
                    "io_dtype": w.dtype, "rms_rows": w.rms_rows, "rms_dim": w.rms_dim,
                    "step": "ssm_scan_fwd + ssm_scan_bwd + conv1d_causal_bwd + rmsnorm_bwd"},
+        "scan_fwd_bwd_ms": scan_ms,
+        "step_tokens_channels_per_s": tokch / (ms_per_step * 1e-3),
         "hbm": {"algorithmic_bytes_per_step": step_bytes,
                 "GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
                 "frac_of_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
@@ -691,23 +713,31 @@ def main():
                 "rms_bwd_GBps": ab["rms_bwd"] / (call_ms["rms_bwd"] * 1e-3) / 1e9,
                 "copy_GBps": copy_gbps,
                 "frac_of_copy": step_bytes / (ms_per_step * 1e-3) / 1e9 / copy_gbps},
-        "scan_fwd_bwd_tokens_channels_per_s": tokch / (scan_ms * 1e-3),
         "call_ms": call_ms,
         "kernel_ms": kern_ms,
         "roofline": {
             "kernel": "k_bwd_main (scan backward main)",
-            "bound": "alu",
-            "achieved": achieved_tflops,
-            "peak": FP32_VECTOR_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": achieved_tflops / FP32_VECTOR_PEAK_TFLOPS,
+            "bound": "hbm",
+            "achieved": main_gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": main_gbps / HBM_PEAK_GBPS,
             "traffic": counter_traffic(w.name),
-            "peak_without_packed_f32": FP32_VECTOR_PEAK_TFLOPS / 2,
-            "valu_busy": counter_valu_busy(w.name),
             "avg_launch_ms": main_ms,
-            "algorithmic_flops_per_launch": main_flops,
             "algorithmic_bytes_per_launch": bwd_main_bytes(w),
-            "hbm_GBps_algorithmic": main_gbps,
+            # what actually binds the kernel: VALU issue.  Its issue time from the
+            # committed counter record (null once the kernel's sources changed since),
+            # and the method's own op count against the non-packed lane-op peak
+            "valu": {
+                "issue_slots_per_launch": slots,
+                "issue_floor_ms": valu_floor_ms,
+                "frac_of_issue_roof": valu_floor_ms / main_ms if valu_floor_ms else None,
+                "algorithmic_ops_per_update": BWD_MAIN_VALU_PER_UPDATE + BWD_MAIN_EXP_PER_UPDATE,
+                "algorithmic_lane_ops_per_s": main_ops / (main_ms * 1e-3),
+                "lane_ops_peak_per_s": LANE_OPS_PEAK,
+                "frac_of_lane_op_peak": main_ops / (main_ms * 1e-3) / LANE_OPS_PEAK,
+                "fp32_nonpacked_peak_tflops": FP32_NONPACKED_PEAK_TFLOPS,
+            },
         },
     }
     out["layer_forward"] = layer_fwd

@@ -49,9 +49,13 @@
  *   call enqueues nothing and leaves every output untouched.  The return value is
  *   SSM_OK or a negative SSM_ERR_* code; ssm_last_error() then describes the
  *   problem.  Nothing aborts and no exception crosses the ABI.  SSM_ERR_HIP
- *   reports only this call's launches: a HIP error still pending on the calling
- *   thread from earlier runtime calls (hipGetLastError not yet called) is cleared
- *   before they are enqueued.
+ *   reports only this call's launches, each taken from its own launch status: a HIP
+ *   error still pending on the calling thread from earlier runtime calls (the
+ *   caller's, or another library's) is neither reported as this call's failure nor
+ *   cleared; it stays pending for its owner.
+ * - Sizes.  Batch, sequence, channel and row counts are int64.  A size is refused
+ *   (SSM_ERR_UNSUPPORTED) only where one launch's grid (2^31 - 1 workgroups) could not
+ *   cover it, as stated per operation; element counts must stay below 2^46.
  */
 #ifndef SSM_SCAN_H
 #define SSM_SCAN_H
@@ -114,8 +118,10 @@ int ssm_set_kernel_timer(int kernel, void *start, void *stop);
  *
  * Shapes: x, delta, y, dy, dx, ddelta [B,L,D]; Bm, Cm [B,L,N] (shared by all
  * channels); A, dA [D,N]; Dv, dD [D]; h0, h_last, dh0 [B,D,N]; dB, dC [B,L,N] f32.
- * Supported: N in {4, 8, 16}; B <= 65535; 1 <= D <= 2^24; L >= 1 (tails
- * handled, no multiple required; D a multiple of 4 takes the vectorised path).
+ * Supported: N in {4, 8, 16}; 1 <= D <= 2^24 (a 16-step tile of one 64-channel
+ * group is addressed with 32-bit buffer offsets); any L >= 1 (tails handled, no
+ * multiple required; D a multiple of 4 takes the vectorised path); any B with
+ * B * ceil(D/64) and ceil(B * D * N / 256) below 2^31 (the 1-D grids).
  *
  * Checkpoints.  The forward can save the state before every 8th step (N = 16) or
  * every 16th step (N = 4, 8) into `ckpt`
@@ -124,6 +130,12 @@ int ssm_set_kernel_timer(int kernel, void *start, void *stop);
  * the forward itself into its workspace.
  * ------------------------------------------------------------------------------- */
 size_t ssm_scan_ckpt_bytes(int64_t B, int64_t L, int64_t D, int64_t N);
+/* Plan query (host only, no GPU work): the number of coarse chunks the forward and the
+ * backward split the sequence into for these sizes (chunks of whole 16-step tiles,
+ * lengths differing by at most one tile).  Either pointer may be NULL.  Returns SSM_OK,
+ * or SSM_ERR_ARG for non-positive sizes. */
+int ssm_scan_chunks(int64_t B, int64_t L, int64_t D, int64_t N, int *fwd_chunks,
+                    int *bwd_chunks);
 size_t ssm_scan_fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
                                     ssm_dtype_t dtype);
 /* with_ckpt = 1 if the backward will be given the forward's checkpoints */
@@ -218,8 +230,11 @@ int conv1d_causal_bwd(void *stream, ssm_dtype_t dtype, int64_t B, int64_t L, int
  *     dx[r,i]    = inv * (scale[i] dy[r,i] - x[r,i] * c)      (overwritten)
  *     dscale[i] += sum_r dy[r,i] * x[r,i] * inv              (accumulated)
  * Shapes: dy, x, dx [R,M] (dtype); scale, dscale [M] f32; rms [R] f32.
- * Supported: M <= 8192 when bf16 and M is a multiple of 8, M <= 4096 when f32 and M
- * is a multiple of 4, otherwise M <= 1024.
+ * Supported: any R and M (R * M < 2^46).  Rows of up to 16 column groups per lane
+ * (M <= 8192 bf16 with M a multiple of 8, M <= 4096 f32 with M a multiple of 4,
+ * otherwise M <= 1024) are read once or twice by one kernel; longer rows take two
+ * kernels (per-row coefficients, then column slabs of 8 groups per lane) that read
+ * the row twice; the slab grid must stay below 2^31 workgroups (M below about 2^31).
  * ------------------------------------------------------------------------------- */
 size_t rmsnorm_bwd_workspace_bytes(int64_t R, int64_t M, ssm_dtype_t dtype);
 int rmsnorm_bwd(void *stream, ssm_dtype_t dtype, int64_t R, int64_t M, const void *dy,

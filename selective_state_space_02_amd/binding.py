@@ -25,7 +25,7 @@ EXPORTS = ("ssm_last_error", "ssm_version", "ssm_set_kernel_timer", "ssm_scan_ck
            "ssm_scan_bwd", "conv1d_causal_bwd_workspace_bytes", "conv1d_causal_bwd",
            "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd", "conv1d_causal_fwd", "rmsnorm_fwd",
            "ssm_scan_step", "conv1d_causal_step", "ssm_scan_fused_fwd", "ssm_scan_fused_bwd",
-           "ssm_scan_fused_step", "ssm_decode_step")
+           "ssm_scan_fused_step", "ssm_decode_step", "ssm_scan_chunks")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -62,6 +62,8 @@ def load():
     lib.ssm_set_kernel_timer.argtypes = [_E, _P, _P]
     lib.ssm_scan_ckpt_bytes.restype = _S
     lib.ssm_scan_ckpt_bytes.argtypes = [_I] * 4
+    lib.ssm_scan_chunks.restype = _E
+    lib.ssm_scan_chunks.argtypes = [_I] * 4 + [ctypes.POINTER(ctypes.c_int)] * 2
     lib.ssm_scan_fwd_workspace_bytes.restype = _S
     lib.ssm_scan_fwd_workspace_bytes.argtypes = [_I] * 4 + [_E]
     lib.ssm_scan_bwd_workspace_bytes.restype = _S
@@ -334,6 +336,14 @@ def ssm_scan_fused_bwd(x, delta, A, Bm, Cm, Dv, dout, ckpt=None, h0=None, delta_
 # ----------------------------------------------------------------------------------
 # conv1d / RMSNorm
 # ----------------------------------------------------------------------------------
+
+def scan_chunks(B, L, D, N):
+    """(forward chunks, backward chunks) the library splits a sequence of these sizes
+    into (ssm_scan_chunks; a host-side plan query)."""
+    f, b = ctypes.c_int(0), ctypes.c_int(0)
+    _check(load().ssm_scan_chunks(B, L, D, N, ctypes.byref(f), ctypes.byref(b)))
+    return f.value, b.value
+
 
 def conv1d_causal_bwd_workspace_bytes(B, L, D, K, dtype_code) -> int:
     return int(load().conv1d_causal_bwd_workspace_bytes(B, L, D, K, dtype_code))

@@ -72,20 +72,19 @@ constexpr int64_t kCUs = 256;
 constexpr int64_t kFwdTargetWG = kCUs * 32;
 constexpr int64_t kBwdTargetWG = kCUs * 20;
 
-// Coarse chunking of the sequence: the chunk length is a multiple of the checkpoint
-// interval, the longest whose count reaches the target grid (nf / want intervals, so
-// the chunks come out even), but at least two intervals: below that the summary pass
-// costs as much as it saves.
+// Coarse chunking of the sequence: whole tiles per chunk, the longest chunks whose count
+// reaches the target grid (nf / want tiles each), but at least two tiles per chunk:
+// below that the summary pass costs as much as it saves.  The chunks then split the
+// tiles evenly (ssm::chunk_tile).
 ssm::Chunking choose_chunks(int64_t B, int64_t L, int64_t D, int64_t target) {
   ssm::Chunking c;
   c.nf = cdiv(L, ssm::kTc);
   const int64_t W = B * cdiv(D, 64);  // workgroups per chunk
   const int64_t want = cdiv(target, W);
-  int64_t tiles = want > 1 ? c.nf / want : c.nf;  // intervals per chunk
+  int64_t tiles = want > 1 ? c.nf / want : c.nf;  // tiles per chunk
   const int64_t tmin = c.nf < 2 ? c.nf : 2;
   if (tiles < tmin) tiles = tmin;
   c.nc = int(cdiv(c.nf, tiles));
-  c.Lc = tiles * ssm::kTc;
   return c;
 }
 
@@ -107,7 +106,6 @@ size_t fwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, ssm::FwdPlan* plan, vo
   Carver cv(ws);
   ssm::FwdPlan p{};
   p.nc = c.nc;
-  p.Lc = c.Lc;
   p.nf = c.nf;
   p.nck = ckpt_count(L, N);
   if (c.nc > 1) {
@@ -129,7 +127,6 @@ size_t bwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, bool with_ckpt, ssm::B
   Carver cv(ws);
   ssm::BwdPlan p{};
   p.nc = c.nc;
-  p.Lc = c.Lc;
   p.nf = c.nf;
   p.nck = ckpt_count(L, N);
   p.ng = cdiv(D, 64);
@@ -168,12 +165,16 @@ int check_scan_dims(ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D, int64_t 
     return fail(SSM_ERR_UNSUPPORTED, "dtype %d not supported (SSM_F32 or SSM_BF16)", int(dtype));
   if (N != 4 && N != 8 && N != 16)
     return fail(SSM_ERR_UNSUPPORTED, "state size N=%lld not supported (4, 8 or 16)", (long long)N);
-  if (B > 65535) return fail(SSM_ERR_UNSUPPORTED, "batch B=%lld exceeds 65535", (long long)B);
   // a 16-step tile of one channel group spans < 2^31 bytes (32-bit buffer offsets)
   if (D > (int64_t(1) << 24))
     return fail(SSM_ERR_UNSUPPORTED, "channels D=%lld exceed 2^24", (long long)D);
   if (B > kMaxElems / L || B * L > kMaxElems / D || B * L * D > kMaxElems / N)
     return fail(SSM_ERR_ARG, "tensor sizes overflow");
+  // one workgroup per (64-channel group, batch row) of a chunk, on a 1-D grid; the carry
+  // kernels take one thread per (batch row, channel, state)
+  if (B * cdiv(D, 64) > ssm::kMaxGridX || cdiv(B * D * N, 256) > ssm::kMaxGridX)
+    return fail(SSM_ERR_UNSUPPORTED, "B*D=%lld channels exceed one launch's grid",
+                (long long)(B * D));
   return SSM_OK;
 }
 
@@ -207,11 +208,6 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
-// A HIP error left pending on this thread by earlier runtime calls (the caller's, or any
-// other library's) would be read back by the launch check after this call's kernels and
-// reported as this call's failure; it is cleared just before the launches.
-void clear_pending_hip_error() { (void)hipGetLastError(); }
-
 // conv plan
 void conv_plan(int64_t B, int64_t L, int64_t D, int64_t K, ssm::ConvPlan* p) {
   // about 4096 workgroups; a workgroup spans 64 lanes of 4 channels (2 above width 4;
@@ -219,7 +215,7 @@ void conv_plan(int64_t B, int64_t L, int64_t D, int64_t K, ssm::ConvPlan* p) {
   // wavefronts x groups of 8 or 16 steps)
   const int64_t vec = (D % 4 != 0) ? 1 : (K <= 4 ? 4 : 2);
   const int64_t cgroups = cdiv(D, 64 * vec);
-  int64_t nTb = cdiv(4096, cgroups * B);
+  int64_t nTb = cdiv(4096, cgroups * B);  // (cgroups * B <= kMaxGridX, check_conv_dims)
   const int64_t maxTb = cdiv(L, 64);
   if (nTb > maxTb) nTb = maxTb;
   if (nTb < 1) nTb = 1;
@@ -239,28 +235,29 @@ size_t conv_ws(int64_t B, int64_t L, int64_t D, int64_t K, ssm_dtype_t dt, ssm::
   return cv.off;
 }
 
-// rms plan; returns false if M is not supported
-bool rms_plan(int64_t R, int64_t M, ssm_dtype_t dt, ssm::RmsPlan* p) {
+// rms plan (every R and M: rows of more than 16 column groups per lane take the looped
+// path, passes = 0)
+void rms_plan(int64_t R, int64_t M, ssm_dtype_t dt, ssm::RmsPlan* p) {
   const int64_t full = (dt == SSM_BF16) ? 8 : 4;
   p->vec = (M % full == 0) ? full : 1;
   const int64_t per_pass = 64 * p->vec;
   const int64_t need = cdiv(M, per_pass);
-  if (need > 16) return false;
-  p->passes = need <= 8 ? need : 16;  // rows of up to 8 passes stay in registers
+  // rows of up to 8 passes stay in registers, up to 16 are read twice
+  p->passes = need <= 8 ? need : (need <= 16 ? 16 : 0);
   // about 512 blocks of 4 wavefronts (each block leaves one dscale partial row; 2048
   // blocks measured no faster and cost a 4x larger reduce), at least 4 rows per block
   int64_t rpb = cdiv(R, 512);
   if (rpb < 4) rpb = 4;
   p->rows_per_block = rpb;
   p->nblk = cdiv(R, rpb);
-  return true;
 }
 
 size_t rms_ws(int64_t R, int64_t M, ssm_dtype_t dt, ssm::RmsPlan* plan, void* ws) {
   ssm::RmsPlan p{};
-  if (!rms_plan(R, M, dt, &p)) return 0;
+  rms_plan(R, M, dt, &p);
   Carver cv(ws);
   p.dsp = cv.take(size_t(p.nblk) * M);
+  if (p.passes == 0) p.crow = cv.take(size_t(R));
   p.rtmp = cv.take(size_t(ssm::reduce_tmp_floats(p.nblk, M)));
   if (plan) *plan = p;
   return cv.off;
@@ -296,6 +293,16 @@ size_t ssm_scan_ckpt_bytes(int64_t B, int64_t L, int64_t D, int64_t N) {
   return ckpt_floats(B, L, D, N) * sizeof(float);
 }
 
+int ssm_scan_chunks(int64_t B, int64_t L, int64_t D, int64_t N, int* fwd_chunks,
+                    int* bwd_chunks) {
+  if (B <= 0 || L <= 0 || D <= 0 || N <= 0)
+    return fail(SSM_ERR_ARG, "sizes must be positive (B=%lld L=%lld D=%lld N=%lld)",
+                (long long)B, (long long)L, (long long)D, (long long)N);
+  if (fwd_chunks) *fwd_chunks = choose_chunks(B, L, D, kFwdTargetWG).nc;
+  if (bwd_chunks) *bwd_chunks = choose_chunks(B, L, D, kBwdTargetWG).nc;
+  return ok();
+}
+
 size_t ssm_scan_fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype_t) {
   if (B <= 0 || L <= 0 || D <= 0 || N <= 0) return 0;
   return fwd_ws(B, L, D, N, nullptr, nullptr);
@@ -327,7 +334,6 @@ int ssm_scan_fwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t 
   a.x = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dv = Dv; a.h0 = h0;
   a.y = y; a.h_last = h_last;
   a.vec4 = D % 4 == 0;
-  clear_pending_hip_error();
   return hip_status(ssm::launch_scan_fwd(a, p, static_cast<hipStream_t>(stream)), "ssm_scan_fwd");
 }
 
@@ -366,12 +372,10 @@ int ssm_scan_bwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t 
     ssm::ScanArgs f = a;
     f.y = nullptr;
     f.h_last = nullptr;
-    clear_pending_hip_error();
-    hipError_t e = ssm::launch_scan_fwd(f, fp, st);
+      hipError_t e = ssm::launch_scan_fwd(f, fp, st);
     if (e != hipSuccess) return hip_status(e, "ssm_scan_bwd (forward recompute)");
     p.ckpt = own_ckpt;
   }
-  clear_pending_hip_error();
   return hip_status(ssm::launch_scan_bwd(a, p, st), "ssm_scan_bwd");
 }
 
@@ -404,7 +408,6 @@ int ssm_scan_fused_fwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, in
   a.fused = true;
   a.dt_bias = delta_bias; a.dt_softplus = delta_softplus != 0;
   a.z = z; a.ysave = y_save;
-  clear_pending_hip_error();
   return hip_status(ssm::launch_scan_fwd(a, p, static_cast<hipStream_t>(stream)),
                     "ssm_scan_fused_fwd");
 }
@@ -458,12 +461,10 @@ int ssm_scan_fused_bwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, in
     f.h_last = nullptr;
     f.z = nullptr;
     f.ysave = nullptr;
-    clear_pending_hip_error();
-    hipError_t e = ssm::launch_scan_fwd(f, fp, st);
+      hipError_t e = ssm::launch_scan_fwd(f, fp, st);
     if (e != hipSuccess) return hip_status(e, "ssm_scan_fused_bwd (forward recompute)");
     p.ckpt = own_ckpt;
   }
-  clear_pending_hip_error();
   return hip_status(ssm::launch_scan_bwd(a, p, st), "ssm_scan_fused_bwd");
 }
 
@@ -478,6 +479,11 @@ static int check_conv_dims(ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D, i
     return fail(SSM_ERR_UNSUPPORTED, "activation %d not supported (0 none, 1 SiLU)", int(act));
   if (K > 8) return fail(SSM_ERR_UNSUPPORTED, "conv width K=%lld not supported (1..8)", (long long)K);
   if (B > kMaxElems / L || B * L > kMaxElems / D) return fail(SSM_ERR_ARG, "tensor sizes overflow");
+  // one workgroup per (channel group, batch row, time block) on a 1-D grid, at least one
+  // time block; a channel group spans 64 lanes of 1 to 4 channels
+  if (B * cdiv(D, 64) > ssm::kMaxGridX)
+    return fail(SSM_ERR_UNSUPPORTED, "B*D=%lld channels exceed one launch's grid",
+                (long long)(B * D));
   return SSM_OK;
 }
 
@@ -506,7 +512,6 @@ int conv1d_causal_bwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int
   a.act = int(act);
   a.x = x; a.W = W; a.bias = act == SSM_ACT_SILU ? bias : nullptr;
   a.dout = dout; a.dx = dx; a.dW = dW; a.db = db;
-  clear_pending_hip_error();
   return hip_status(ssm::launch_conv1d_bwd(a, p, static_cast<hipStream_t>(stream)),
                     "conv1d_causal_bwd");
 }
@@ -526,7 +531,6 @@ int conv1d_causal_fwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int
   a.Tb = p.Tb; a.nTb = p.nTb;
   a.act = int(act);
   a.x = x; a.W = W; a.bias = bias; a.out = out;
-  clear_pending_hip_error();
   return hip_status(ssm::launch_conv1d_fwd(a, static_cast<hipStream_t>(stream)),
                     "conv1d_causal_fwd");
 }
@@ -542,8 +546,11 @@ int rmsnorm_fwd(void* stream, ssm_dtype_t dtype, int64_t R, int64_t M, const voi
     return fail(SSM_ERR_UNSUPPORTED, "dtype %d not supported", int(dtype));
   if (R > kMaxElems / M) return fail(SSM_ERR_ARG, "tensor sizes overflow");
   ssm::RmsPlan p{};
-  if (!rms_plan(R, M, dtype, &p))
-    return fail(SSM_ERR_UNSUPPORTED, "row length M=%lld not supported for this dtype", (long long)M);
+  rms_plan(R, M, dtype, &p);
+  // the looped backward runs one workgroup per (row block, column slab of 8 x 64 x vec
+  // columns) on a 1-D grid (at most 512 row blocks)
+  if (p.passes == 0 && p.nblk * cdiv(M, 8 * 64 * p.vec) > ssm::kMaxGridX)
+    return fail(SSM_ERR_UNSUPPORTED, "row length M=%lld exceeds one launch's grid", (long long)M);
   int rc = check_ptrs({{x, "x"}, {scale, "scale"}, {y, "y"}, {rms, "rms"}},
                       {{residual, "residual"}, {residual_out, "residual_out"}});
   if (rc) return rc;
@@ -560,7 +567,6 @@ int rmsnorm_fwd(void* stream, ssm_dtype_t dtype, int64_t R, int64_t M, const voi
   a.eps = eps;
   a.x = x; a.residual = residual; a.scale = scale; a.y = y; a.rms = rms;
   a.residual_out = residual_out;
-  clear_pending_hip_error();
   return hip_status(ssm::launch_rmsnorm_fwd(a, static_cast<hipStream_t>(stream)), "rmsnorm_fwd");
 }
 
@@ -577,7 +583,6 @@ int ssm_scan_step(void* stream, ssm_dtype_t dtype, int64_t B, int64_t D, int64_t
   a.B = B; a.D = D; a.N = N;
   a.h = h; a.x_t = x_t; a.delta_t = delta_t; a.A = A; a.B_t = B_t; a.C_t = C_t; a.Dv = Dv;
   a.y_t = y_t;
-  clear_pending_hip_error();
   return hip_status(ssm::launch_scan_step(a, static_cast<hipStream_t>(stream)), "ssm_scan_step");
 }
 
@@ -601,7 +606,6 @@ int ssm_scan_fused_step(void* stream, ssm_dtype_t dtype, int64_t B, int64_t D, i
   a.y_t = out_t;
   a.fused = true;
   a.dt_bias = delta_bias; a.dt_softplus = delta_softplus != 0; a.z_t = z_t;
-  clear_pending_hip_error();
   return hip_status(ssm::launch_scan_step(a, static_cast<hipStream_t>(stream)),
                     "ssm_scan_fused_step");
 }
@@ -632,7 +636,6 @@ int ssm_decode_step(void* stream, ssm_dtype_t dtype, int64_t B, int64_t D, int64
   a.h = h; a.conv_state = conv_state; a.x_t = x_t; a.W = W; a.conv_bias = conv_bias;
   a.delta_t = delta_t; a.A = A; a.B_t = B_t; a.C_t = C_t; a.Dv = Dv;
   a.dt_bias = delta_bias; a.dt_softplus = delta_softplus != 0; a.z_t = z_t; a.out_t = out_t;
-  clear_pending_hip_error();
   return hip_status(ssm::launch_decode_step(a, static_cast<hipStream_t>(stream)),
                     "ssm_decode_step");
 }
@@ -661,7 +664,6 @@ int conv1d_causal_step(void* stream, ssm_dtype_t dtype, int64_t B, int64_t D, in
   a.B = B; a.D = D; a.K = K;
   a.act = int(act);
   a.state = state; a.x_t = x_t; a.W = W; a.bias = bias; a.out_t = out_t;
-  clear_pending_hip_error();
   return hip_status(ssm::launch_conv1d_step(a, static_cast<hipStream_t>(stream)),
                     "conv1d_causal_step");
 }
@@ -680,8 +682,11 @@ int rmsnorm_bwd(void* stream, ssm_dtype_t dtype, int64_t R, int64_t M, const voi
     return fail(SSM_ERR_UNSUPPORTED, "dtype %d not supported", int(dtype));
   if (R > kMaxElems / M) return fail(SSM_ERR_ARG, "tensor sizes overflow");
   ssm::RmsPlan p{};
-  if (!rms_plan(R, M, dtype, &p))
-    return fail(SSM_ERR_UNSUPPORTED, "row length M=%lld not supported for this dtype", (long long)M);
+  rms_plan(R, M, dtype, &p);
+  // the looped backward runs one workgroup per (row block, column slab of 8 x 64 x vec
+  // columns) on a 1-D grid (at most 512 row blocks)
+  if (p.passes == 0 && p.nblk * cdiv(M, 8 * 64 * p.vec) > ssm::kMaxGridX)
+    return fail(SSM_ERR_UNSUPPORTED, "row length M=%lld exceeds one launch's grid", (long long)M);
   int rc = check_ptrs({{dy, "dy"}, {x, "x"}, {scale, "scale"}, {rms, "rms"}, {dx, "dx"},
                        {dscale, "dscale"}}, {});
   if (rc) return rc;
@@ -692,7 +697,6 @@ int rmsnorm_bwd(void* stream, ssm_dtype_t dtype, int64_t R, int64_t M, const voi
   a.dtype = int(dtype);
   a.R = R; a.M = M;
   a.dy = dy; a.x = x; a.scale = scale; a.rms = rms; a.dx = dx; a.dscale = dscale;
-  clear_pending_hip_error();
   return hip_status(ssm::launch_rmsnorm_bwd(a, p, static_cast<hipStream_t>(stream)), "rmsnorm_bwd");
 }
 

@@ -66,25 +66,23 @@ __global__ __launch_bounds__(256) void k_conv_bwd(
       dW[v][k] = 0.f;
     }
   }
-  const uint32_t rowb = uint32_t(D) * uint32_t(sizeof(T));  // bytes per timestep
+  // each row's descriptor spans the workgroup's valid channels of that row only (built
+  // from the row's 64-bit address), so no offset or size depends on D
+  const uint32_t rowv = uint32_t((D - c0 < CW) ? D - c0 : CW) * uint32_t(sizeof(T));
   const uint32_t loff = lc * uint32_t(sizeof(T));
   for (int64_t ts = t0 + int64_t(wave) * R; ts < t1; ts += 4 * R) {
-    // xr[i] = x[ts - K + 1 + i], gr[i] = g[ts + i]; rows outside [0, L) are zero.  One
-    // descriptor per tensor starting at the group's first valid row; rows are scalar
-    // offsets from it, lanes vector offsets.
-    const int64_t x0 = (ts - (K - 1) < 0) ? 0 : ts - (K - 1);
-    const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xg + x0 * D, uint32_t(HX) * rowb);
-    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gg + ts * D, uint32_t(H) * rowb);
+    // xr[i] = x[ts - K + 1 + i], gr[i] = g[ts + i]; rows outside [0, L) are zero
     typename BV::raw_t xraw[HX], graw[H];
 #pragma unroll
     for (int i = 0; i < HX; ++i) {
       const int64_t tx = ts - (K - 1) + i;
-      xraw[i] = (tx >= 0 && tx < L) ? BV::load(rx, loff, uint32_t(tx - x0) * rowb)
+      xraw[i] = (tx >= 0 && tx < L) ? BV::load(buf_rsrc(xg + tx * D, rowv), loff)
                                     : typename BV::raw_t{};
     }
 #pragma unroll
     for (int i = 0; i < H; ++i)
-      graw[i] = (ts + i < L) ? BV::load(rg, loff, uint32_t(i) * rowb) : typename BV::raw_t{};
+      graw[i] = (ts + i < L) ? BV::load(buf_rsrc(gg + (ts + i) * D, rowv), loff)
+                             : typename BV::raw_t{};
     // the conv output's gradient of every row the group touches; with SiLU fused, the
     // upstream value times silu'(pre), pre = bias + sum_k W x recomputed from the inputs
     float gf[H][VEC];
@@ -105,7 +103,6 @@ __global__ __launch_bounds__(256) void k_conv_bwd(
         }
       }
     }
-    const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dxg + ts * D, uint32_t(R) * rowb);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t t = ts + r;
@@ -124,7 +121,7 @@ __global__ __launch_bounds__(256) void k_conv_bwd(
 #pragma unroll
           for (int k = 0; k < K; ++k) dW[v][k] = __builtin_fmaf(gt, xv[k][v], dW[v][k]);
         }
-        if (act) BV::store(BV::pack(o), rd, loff, uint32_t(r) * rowb);
+        if (act) BV::store(BV::pack(o), buf_rsrc(dxg + t * D, rowv), loff);
       }
     }
   }
@@ -162,14 +159,14 @@ static hipError_t conv_ka(const ConvArgs& a, const ConvPlan& p, hipStream_t st) 
   const int64_t cgroups = (a.D + 64 * vec - 1) / (64 * vec);
   const dim3 grid(unsigned(cgroups * a.B * p.nTb));
   timer_mark(kKConvBwd, false, st);
+  hipError_t e;
   if (vec == VW)
-    hipLaunchKernelGGL((k_conv_bwd<T, K, VW, ACT>), grid, dim3(256), 0, st, a.L, a.D, p.Tb,
-                       p.nTb, cgroups, x, a.W, a.bias, g, dx, p.dWp, p.dbp);
+    e = launch(k_conv_bwd<T, K, VW, ACT>, grid, dim3(256), st, a.L, a.D, p.Tb, p.nTb, cgroups,
+               x, a.W, a.bias, g, dx, p.dWp, p.dbp);
   else
-    hipLaunchKernelGGL((k_conv_bwd<T, K, 1, ACT>), grid, dim3(256), 0, st, a.L, a.D, p.Tb,
-                       p.nTb, cgroups, x, a.W, a.bias, g, dx, p.dWp, p.dbp);
+    e = launch(k_conv_bwd<T, K, 1, ACT>, grid, dim3(256), st, a.L, a.D, p.Tb, p.nTb, cgroups, x,
+               a.W, a.bias, g, dx, p.dWp, p.dbp);
   timer_mark(kKConvBwd, true, st);
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t P = a.B * p.nTb;
   if ((e = launch_reduce(p.dWp, P, a.D * a.K, a.dW, true, p.rtmp, st)) != hipSuccess) return e;

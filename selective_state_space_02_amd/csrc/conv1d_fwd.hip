@@ -47,20 +47,19 @@ __global__ __launch_bounds__(256) void k_conv_fwd(int64_t L, int64_t D, int64_t 
 #pragma unroll
     for (int k = 0; k < K; ++k) w[v][k] = W[(c0 + lc + v) * K + k];
   }
-  const uint32_t rowb = uint32_t(D) * uint32_t(sizeof(T));  // bytes per timestep
+  // each row's descriptor spans the workgroup's valid channels of that row only (built
+  // from the row's 64-bit address), so no offset or size depends on D
+  const uint32_t rowv = uint32_t((D - c0 < CW) ? D - c0 : CW) * uint32_t(sizeof(T));
   const uint32_t loff = lc * uint32_t(sizeof(T));
   for (int64_t ts = t0 + int64_t(wave) * R; ts < t1; ts += 4 * R) {
     // xraw[i] = x[ts - K + 1 + i]; rows outside [0, L) are zero
-    const int64_t x0 = (ts - (K - 1) < 0) ? 0 : ts - (K - 1);
-    const __amdgpu_buffer_rsrc_t rx = buf_rsrc(xg + x0 * D, uint32_t(H) * rowb);
     typename BV::raw_t xraw[H];
 #pragma unroll
     for (int i = 0; i < H; ++i) {
       const int64_t tx = ts - (K - 1) + i;
-      xraw[i] = (tx >= 0 && tx < L) ? BV::load(rx, loff, uint32_t(tx - x0) * rowb)
+      xraw[i] = (tx >= 0 && tx < L) ? BV::load(buf_rsrc(xg + tx * D, rowv), loff)
                                     : typename BV::raw_t{};
     }
-    const __amdgpu_buffer_rsrc_t ro = buf_rsrc(og + ts * D, uint32_t(R) * rowb);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       if (ts + r < t1) {
@@ -75,7 +74,7 @@ __global__ __launch_bounds__(256) void k_conv_fwd(int64_t L, int64_t D, int64_t 
           if constexpr (ACT == kActSilu) acc *= sigmoid_f(acc);
           o[v] = acc;
         }
-        if (act) BV::store(BV::pack(o), ro, loff, uint32_t(r) * rowb);
+        if (act) BV::store(BV::pack(o), buf_rsrc(og + (ts + r) * D, rowv), loff);
       }
     }
   }
@@ -90,14 +89,15 @@ static hipError_t conv_fwd_ka(const ConvFwdArgs& a, hipStream_t st) {
   const T* x = static_cast<const T*>(a.x);
   T* out = static_cast<T*>(a.out);
   timer_mark(kKConvFwd, false, st);
+  hipError_t e;
   if (vec == VW)
-    hipLaunchKernelGGL((k_conv_fwd<T, K, VW, ACT>), grid, dim3(256), 0, st, a.L, a.D, a.Tb,
-                       a.nTb, cgroups, x, a.W, a.bias, out);
+    e = launch(k_conv_fwd<T, K, VW, ACT>, grid, dim3(256), st, a.L, a.D, a.Tb, a.nTb, cgroups,
+               x, a.W, a.bias, out);
   else
-    hipLaunchKernelGGL((k_conv_fwd<T, K, 1, ACT>), grid, dim3(256), 0, st, a.L, a.D, a.Tb,
-                       a.nTb, cgroups, x, a.W, a.bias, out);
+    e = launch(k_conv_fwd<T, K, 1, ACT>, grid, dim3(256), st, a.L, a.D, a.Tb, a.nTb, cgroups,
+               x, a.W, a.bias, out);
   timer_mark(kKConvFwd, true, st);
-  return hipGetLastError();
+  return e;
 }
 
 template <typename T, int K>

@@ -98,7 +98,7 @@ __device__ __forceinline__ void step_compute(StepOperands<T, N>& o, int64_t b, i
 }
 
 template <typename T, int N, bool FZ>
-__global__ __launch_bounds__(256) void k_scan_step(int64_t D, float* __restrict__ h,
+__global__ __launch_bounds__(256) void k_scan_step(int64_t B, int64_t D, float* __restrict__ h,
                                                    const T* __restrict__ x_t,
                                                    const T* __restrict__ delta_t,
                                                    const float* __restrict__ A,
@@ -109,7 +109,8 @@ __global__ __launch_bounds__(256) void k_scan_step(int64_t D, float* __restrict_
                                                    const T* __restrict__ z_t,
                                                    T* __restrict__ y_t) {
   const int tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
-  const int64_t b = blockIdx.y, d = int64_t(blockIdx.x) * 64 + cl;
+  const WgPos wp = wg_pos((D + 63) / 64, B);  // (channel group, batch row)
+  const int64_t b = wp.b, d = wp.grp * 64 + cl;
   if (d >= D) return;  // a channel's four lanes leave together; the quad sum stays in-quad
   StepOperands<T, N> o;
   const T xr = x_t[b * D + d];
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(256) void k_scan_step(int64_t D, float* __restrict_
 // step on it.  The channel's four lanes share the window's loads and stores and all form
 // the conv output (same operations in the conv step's order, same value).
 template <typename T, int N, int K>
-__global__ __launch_bounds__(256) void k_decode_step(int64_t D, float* __restrict__ h,
+__global__ __launch_bounds__(256) void k_decode_step(int64_t B, int64_t D, float* __restrict__ h,
                                                      T* __restrict__ cstate,
                                                      const T* __restrict__ x_t,
                                                      const float* __restrict__ W,
@@ -140,7 +141,8 @@ __global__ __launch_bounds__(256) void k_decode_step(int64_t D, float* __restric
   // and written as one contiguous run of 64 values.
   __shared__ float sw[K][64];
   const int tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
-  const int64_t b = blockIdx.y, d0 = int64_t(blockIdx.x) * 64, d = d0 + cl;
+  const WgPos wp = wg_pos((D + 63) / 64, B);  // (channel group, batch row)
+  const int64_t b = wp.b, d0 = wp.grp * 64, d = d0 + cl;
   const int rc = tid & 63;
   // every load is issued before the barrier; lanes past the last channel read the last
   // channel's addresses (in bounds) and drop the values
@@ -239,23 +241,19 @@ __global__ __launch_bounds__(256) void k_conv_step(int64_t B, int64_t D, T* __re
 }
 
 template <typename T, int N, bool FZ>
-static void scan_step_nf(const ScanStepArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((k_scan_step<T, N, FZ>), dim3(unsigned((a.D + 63) / 64), unsigned(a.B)),
-                     dim3(256), 0, st, a.D, a.h, static_cast<const T*>(a.x_t),
-                     static_cast<const T*>(a.delta_t), a.A, static_cast<const T*>(a.B_t),
-                     static_cast<const T*>(a.C_t), a.Dv, a.dt_bias, a.dt_softplus,
-                     static_cast<const T*>(a.z_t), static_cast<T*>(a.y_t));
+static hipError_t scan_step_nf(const ScanStepArgs& a, hipStream_t st) {
+  return launch(k_scan_step<T, N, FZ>, dim3(unsigned((a.D + 63) / 64 * a.B)), dim3(256), st,
+                a.B, a.D, a.h, static_cast<const T*>(a.x_t), static_cast<const T*>(a.delta_t),
+                a.A, static_cast<const T*>(a.B_t), static_cast<const T*>(a.C_t), a.Dv,
+                a.dt_bias, a.dt_softplus, static_cast<const T*>(a.z_t), static_cast<T*>(a.y_t));
 }
 
 template <typename T, int N>
 static hipError_t scan_step_n(const ScanStepArgs& a, hipStream_t st) {
   timer_mark(kKScanStep, false, st);
-  if (a.fused)
-    scan_step_nf<T, N, true>(a, st);
-  else
-    scan_step_nf<T, N, false>(a, st);
+  const hipError_t e = a.fused ? scan_step_nf<T, N, true>(a, st) : scan_step_nf<T, N, false>(a, st);
   timer_mark(kKScanStep, true, st);
-  return hipGetLastError();
+  return e;
 }
 
 template <typename T>
@@ -273,30 +271,27 @@ hipError_t launch_scan_step(const ScanStepArgs& a, hipStream_t st) {
 }
 
 template <typename T, int K, int ACT, int VEC>
-static void conv_step_kav(const ConvStepArgs& a, hipStream_t st) {
+static hipError_t conv_step_kav(const ConvStepArgs& a, hipStream_t st) {
   const int64_t groups = (a.D + VEC - 1) / VEC;
   const int64_t gy = (a.B + kConvStepRows - 1) / kConvStepRows;
   const dim3 grid(unsigned((groups + 255) / 256), unsigned(gy < 65535 ? gy : 65535));
-  hipLaunchKernelGGL((k_conv_step<T, K, ACT, VEC>), grid, dim3(256), 0, st, a.B, a.D,
-                     static_cast<T*>(a.state), static_cast<const T*>(a.x_t), a.W, a.bias,
-                     static_cast<T*>(a.out_t));
+  return launch(k_conv_step<T, K, ACT, VEC>, grid, dim3(256), st, a.B, a.D,
+                static_cast<T*>(a.state), static_cast<const T*>(a.x_t), a.W, a.bias,
+                static_cast<T*>(a.out_t));
 }
 
 template <typename T, int K, int ACT>
-static void conv_step_ka(const ConvStepArgs& a, hipStream_t st) {
-  if (a.D % 4 == 0) conv_step_kav<T, K, ACT, 4>(a, st);
-  else conv_step_kav<T, K, ACT, 1>(a, st);
+static hipError_t conv_step_ka(const ConvStepArgs& a, hipStream_t st) {
+  return a.D % 4 == 0 ? conv_step_kav<T, K, ACT, 4>(a, st) : conv_step_kav<T, K, ACT, 1>(a, st);
 }
 
 template <typename T, int K>
 static hipError_t conv_step_k(const ConvStepArgs& a, hipStream_t st) {
   timer_mark(kKConvStep, false, st);
-  if (a.act == kActSilu)
-    conv_step_ka<T, K, kActSilu>(a, st);
-  else
-    conv_step_ka<T, K, kActNone>(a, st);
+  const hipError_t e = a.act == kActSilu ? conv_step_ka<T, K, kActSilu>(a, st)
+                                         : conv_step_ka<T, K, kActNone>(a, st);
   timer_mark(kKConvStep, true, st);
-  return hipGetLastError();
+  return e;
 }
 
 template <typename T>
@@ -315,29 +310,27 @@ static hipError_t conv_step_t(const ConvStepArgs& a, hipStream_t st) {
 }
 
 template <typename T, int N, int K>
-static void decode_step_nk(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((k_decode_step<T, N, K>), dim3(unsigned((a.D + 63) / 64), unsigned(a.B)),
-                     dim3(256), 0, st, a.D, a.h, static_cast<T*>(a.conv_state),
-                     static_cast<const T*>(a.x_t), a.W, a.conv_bias,
-                     static_cast<const T*>(a.delta_t), a.A, static_cast<const T*>(a.B_t),
-                     static_cast<const T*>(a.C_t), a.Dv, a.dt_bias, a.dt_softplus,
-                     static_cast<const T*>(a.z_t), static_cast<T*>(a.out_t));
+static hipError_t decode_step_nk(const DecodeArgs& a, hipStream_t st) {
+  return launch(k_decode_step<T, N, K>, dim3(unsigned((a.D + 63) / 64 * a.B)), dim3(256), st,
+                a.B, a.D, a.h, static_cast<T*>(a.conv_state), static_cast<const T*>(a.x_t), a.W,
+                a.conv_bias, static_cast<const T*>(a.delta_t), a.A,
+                static_cast<const T*>(a.B_t), static_cast<const T*>(a.C_t), a.Dv, a.dt_bias,
+                a.dt_softplus, static_cast<const T*>(a.z_t), static_cast<T*>(a.out_t));
 }
 
 template <typename T, int N>
 static hipError_t decode_step_n(const DecodeArgs& a, hipStream_t st) {
   switch (a.K) {
-    case 1: decode_step_nk<T, N, 1>(a, st); break;
-    case 2: decode_step_nk<T, N, 2>(a, st); break;
-    case 3: decode_step_nk<T, N, 3>(a, st); break;
-    case 4: decode_step_nk<T, N, 4>(a, st); break;
-    case 5: decode_step_nk<T, N, 5>(a, st); break;
-    case 6: decode_step_nk<T, N, 6>(a, st); break;
-    case 7: decode_step_nk<T, N, 7>(a, st); break;
-    case 8: decode_step_nk<T, N, 8>(a, st); break;
-    default: return hipErrorInvalidValue;
+    case 1: return decode_step_nk<T, N, 1>(a, st);
+    case 2: return decode_step_nk<T, N, 2>(a, st);
+    case 3: return decode_step_nk<T, N, 3>(a, st);
+    case 4: return decode_step_nk<T, N, 4>(a, st);
+    case 5: return decode_step_nk<T, N, 5>(a, st);
+    case 6: return decode_step_nk<T, N, 6>(a, st);
+    case 7: return decode_step_nk<T, N, 7>(a, st);
+    case 8: return decode_step_nk<T, N, 8>(a, st);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 template <typename T>

@@ -5,7 +5,31 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 namespace ssm {
+
+// Kernel launch that returns the status of this launch alone: the arguments are
+// converted to the kernel's parameter types and passed to hipLaunchKernel, whose return
+// value is that launch's own status.  An error that an earlier runtime call left pending
+// on the calling thread (the caller's, or another library's) is neither returned nor
+// cleared, so it stays for its owner to read.
+template <typename... P, size_t... I>
+hipError_t launch_tuple(const void* fn, dim3 grid, dim3 block, hipStream_t st,
+                        std::tuple<P...>& args, std::index_sequence<I...>) {
+  void* argv[sizeof...(P) + 1] = {static_cast<void*>(&std::get<I>(args))..., nullptr};
+  return hipLaunchKernel(fn, grid, block, argv, 0, st);
+}
+template <typename... P, typename... A>
+hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t st, A&&... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  std::tuple<P...> vals(std::forward<A>(args)...);
+  return launch_tuple(reinterpret_cast<const void*>(kernel), grid, block, st, vals,
+                      std::index_sequence_for<P...>{});
+}
+// Largest grid dimension x a launch may use (hipLaunchKernel's limit for gridDim.x).
+constexpr int64_t kMaxGridX = 0x7fffffff;
 
 // Tile length of the scan kernels (steps staged through LDS at a time).
 constexpr int kTc = 16;
@@ -55,13 +79,32 @@ struct ScanArgs {
 // Coarse chunking of the sequence (shared rule for forward and backward).
 struct Chunking {
   int nc;       // number of coarse chunks
-  int64_t Lc;   // chunk length, a multiple of kTc
   int64_t nf;   // number of tiles, ceil(L / kTc)
 };
 
+// Chunk c of nc covers the tiles [chunk_tile(c), chunk_tile(c + 1)) of the nf tiles of
+// the sequence: an even split, chunk lengths differing by at most one tile.  Only the
+// last chunk can hold the sequence's partial tile, so chunks 0..nc-2 are full.
+__host__ __device__ __forceinline__ int64_t chunk_tile(int64_t c, int64_t nf, int64_t nc) {
+  return c * nf / nc;
+}
+
+// Position of a scan workgroup in its 1-D grid: the channel group varies fastest, then
+// the batch row, then the chunk (the order of the former 3-D grid), so the grid is not
+// bounded by the 65535 limit of a grid's y and z dimensions.  All three factors are
+// below 2^31 (the grid's x limit), so 32-bit division suffices.
+struct WgPos {
+  int64_t grp, b, c;
+};
+__device__ __forceinline__ WgPos wg_pos(int64_t groups, int64_t B) {
+  const uint32_t wg = blockIdx.x, g = uint32_t(groups), nb = uint32_t(B);
+  const uint32_t r = wg / g;
+  return {int64_t(wg - r * g), int64_t(r % nb), int64_t(r / nb)};
+}
+
 struct FwdPlan {
   int nc;
-  int64_t Lc, nf;
+  int64_t nf;
   int64_t nck;  // number of checkpoints, ceil(L / (kTc / ckpt_per_tile(N)))
   float* S;     // [B][nc][D][N]   (nc > 1)
   float* SD;    // [B][nc][D]      (nc > 1)
@@ -71,7 +114,7 @@ struct FwdPlan {
 
 struct BwdPlan {
   int nc;
-  int64_t Lc, nf, ng;
+  int64_t nf, ng;
   int64_t nck;        // number of checkpoints
   const float* ckpt;  // [B][nck][D][N]
   float* GS;          // [B][nc][D][N]  (nc > 1)
@@ -117,9 +160,12 @@ struct RmsArgs {
 };
 
 struct RmsPlan {
-  int64_t vec, passes, rows_per_block, nblk;
-  float* dsp;  // [nblk][M]
-  float* rtmp; // reduction scratch
+  int64_t vec;
+  int64_t passes;  // column groups per lane held at once; 0: the looped path (any M)
+  int64_t rows_per_block, nblk;
+  float* dsp;   // [nblk][M]
+  float* crow;  // [R] per-row coefficients (looped path only)
+  float* rtmp;  // reduction scratch
 };
 
 // Kernel identifiers of the timing hook (values are part of the C ABI, see

@@ -25,30 +25,36 @@ constexpr int64_t kWideBlocks = 1024;
 __global__ __launch_bounds__(256) void k_reduce_seg(const float* __restrict__ part, int64_t P,
                                                     int64_t J, int64_t seg,
                                                     float* __restrict__ out, int accumulate) {
-  const int64_t j = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (j >= J) return;
-  const int64_t p0 = int64_t(blockIdx.y) * seg;
-  const int64_t p1 = (p0 + seg < P) ? p0 + seg : P;
-  float acc[kAcc] = {0.f, 0.f, 0.f, 0.f};
-  int64_t p = p0;
-  for (; p + kBatch <= p1; p += kBatch) {
-    float v[kBatch];
+  // outputs and segments are strided over the grid (either count may exceed a grid
+  // dimension); each output's sum over its segment is formed in one thread, in order
+  const int64_t nseg = (P + seg - 1) / seg;
+  for (int64_t sg = blockIdx.y; sg < nseg; sg += gridDim.y) {
+    const int64_t p0 = sg * seg;
+    const int64_t p1 = (p0 + seg < P) ? p0 + seg : P;
+    float* o = out + sg * J;  // one row per segment (a single row if P <= seg)
+    for (int64_t j = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; j < J;
+         j += int64_t(gridDim.x) * blockDim.x) {
+      float acc[kAcc] = {0.f, 0.f, 0.f, 0.f};
+      int64_t p = p0;
+      for (; p + kBatch <= p1; p += kBatch) {
+        float v[kBatch];
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) v[k] = part[(p + k) * J + j];
+        for (int k = 0; k < kBatch; ++k) v[k] = part[(p + k) * J + j];
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) acc[k % kAcc] += v[k];
+        for (int k = 0; k < kBatch; ++k) acc[k % kAcc] += v[k];
+      }
+      if (p < p1) {  // the last, partial batch: loads clamped to the segment, extra values dropped
+        float v[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) v[k] = part[(p + k < p1 ? p + k : p1 - 1) * J + j];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k)
+          if (p + k < p1) acc[k % kAcc] += v[k];
+      }
+      const float s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      o[j] = accumulate ? o[j] + s : s;
+    }
   }
-  if (p < p1) {  // the last, partial batch: loads clamped to the segment, extra values dropped
-    float v[kBatch];
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) v[k] = part[(p + k < p1 ? p + k : p1 - 1) * J + j];
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k)
-      if (p + k < p1) acc[k % kAcc] += v[k];
-  }
-  const float s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  float* o = out + int64_t(blockIdx.y) * J;  // one row per segment (a single row if P <= kSeg)
-  o[j] = accumulate ? o[j] + s : s;
 }
 
 static bool single_pass(int64_t P, int64_t J) {
@@ -61,20 +67,26 @@ int64_t reduce_tmp_floats(int64_t P, int64_t J) {
   return S * J + reduce_tmp_floats(S, J);
 }
 
+// Grid limits of the strided loops above (x: blocks of 256 outputs, y: segments).
+constexpr int64_t kMaxReduceBlocksX = int64_t(1) << 20;
+constexpr int64_t kMaxReduceBlocksY = 65535;
+
+static dim3 reduce_grid(int64_t J, int64_t nseg) {
+  const int64_t gx = (J + 255) / 256;
+  return dim3(unsigned(gx < kMaxReduceBlocksX ? gx : kMaxReduceBlocksX),
+              unsigned(nseg < kMaxReduceBlocksY ? nseg : kMaxReduceBlocksY));
+}
+
 hipError_t launch_reduce(const float* part, int64_t P, int64_t J, float* out, bool accumulate,
                          float* tmp, hipStream_t st) {
   if (J <= 0) return hipSuccess;
   const dim3 block(256);
-  const int64_t gx = (J + 255) / 256;
-  if (single_pass(P, J)) {
-    hipLaunchKernelGGL(k_reduce_seg, dim3(gx, 1), block, 0, st, part, P, J, P, out,
-                       accumulate ? 1 : 0);
-    return hipGetLastError();
-  }
+  if (single_pass(P, J))
+    return launch(k_reduce_seg, reduce_grid(J, 1), block, st, part, P, J, P, out,
+                  accumulate ? 1 : 0);
   const int64_t S = (P + kSeg - 1) / kSeg;
-  hipLaunchKernelGGL(k_reduce_seg, dim3(gx, S), block, 0, st, part, P, J, int64_t(kSeg), tmp,
-                     0);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch(k_reduce_seg, reduce_grid(J, S), block, st, part, P, J, int64_t(kSeg),
+                        tmp, 0);
   if (e != hipSuccess) return e;
   return launch_reduce(tmp, S, J, out, accumulate, tmp + S * J, st);
 }

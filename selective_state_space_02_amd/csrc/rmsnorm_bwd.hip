@@ -8,10 +8,15 @@
 // rows); a lane owns PASSES groups of VEC consecutive columns.  Rows of at most eight
 // groups per lane (k_rms_bwd_res) are read once into registers: the dot product is
 // formed (wavefront DPP/shuffle sum), then dx is written from the same registers and
-// the scale-gradient terms accumulate in registers; scale is staged in LDS.  Longer
-// rows (k_rms_bwd) are read twice, the second time for dx.  At the end the four
-// wavefronts' column sums are added through LDS into one partial per block; k_reduce
-// sums the block partials in a fixed order.
+// the scale-gradient terms accumulate in registers; scale is staged in LDS.  Rows of up
+// to sixteen groups per lane (k_rms_bwd) are read twice, the second time for dx.  At the
+// end the four wavefronts' column sums are added through LDS into one partial per block;
+// k_reduce sums the block partials in a fixed order.
+//
+// Rows of any other length (the looped path) take two kernels: k_rms_bwd_rowc forms each
+// row's coefficient c[r] (one read of the row), then k_rms_bwd_slab covers the row in
+// column slabs of kSlabPasses groups per lane, one slab per workgroup column, writing dx
+// and each block's scale-gradient partials of its slab (a second read of the row).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -220,37 +225,140 @@ __global__ __launch_bounds__(256) void k_rms_bwd(
   }
 }
 
+// Looped path, first kernel: c[r] = inv^2 * (sum_i dy scale x) / M for every row, one
+// wavefront per row (four rows per workgroup at a time), columns strided over the lanes.
+template <typename T, int VEC>
+__global__ __launch_bounds__(256) void k_rms_bwd_rowc(
+    int64_t R, int64_t M, int64_t rows_per_block, const T* __restrict__ dy,
+    const T* __restrict__ x, const float* __restrict__ scale, const float* __restrict__ rms,
+    float* __restrict__ cr) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t r0 = int64_t(blockIdx.x) * rows_per_block;
+  const int64_t r1 = (r0 + rows_per_block < R) ? r0 + rows_per_block : R;
+  const float invM = 1.0f / float(M);
+  for (int64_t r = r0 + wave; r < r1; r += 4) {
+    const T* dyr = dy + r * M;
+    const T* xr = x + r * M;
+    float dot = 0.f;
+    for (int64_t col = int64_t(lane) * VEC; col < M; col += 64 * VEC) {
+      float a[VEC], b[VEC];
+      load_vec<T, VEC>(dyr + col, a);
+      load_vec<T, VEC>(xr + col, b);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) dot = __builtin_fmaf(a[v] * scale[col + v], b[v], dot);
+    }
+    dot = wave_sum(dot);
+    const float inv = 1.0f / rms[r];
+    if (lane == 0) cr[r] = dot * inv * inv * invM;
+  }
+}
+
+// Groups of VEC columns per lane in one column slab of the looped path.
+constexpr int kSlabPasses = 8;
+
+// Looped path, second kernel: workgroup (row block, column slab) writes dx of its slab
+// for its rows and the block's scale-gradient partial of the slab's columns.
+template <typename T, int VEC>
+__global__ __launch_bounds__(256) void k_rms_bwd_slab(
+    int64_t R, int64_t M, int64_t rows_per_block, int64_t nblk, const T* __restrict__ dy,
+    const T* __restrict__ x, const float* __restrict__ scale, const float* __restrict__ rms,
+    const float* __restrict__ cr, T* __restrict__ dx, float* __restrict__ dsp) {
+  constexpr int CP = 64 * VEC;  // columns per pass
+  __shared__ float part[4][CP];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t blk = int64_t(blockIdx.x) % nblk, slab = int64_t(blockIdx.x) / nblk;
+  const int64_t cs = slab * kSlabPasses * CP;  // first column of the slab
+  float acc[kSlabPasses][VEC], sc[kSlabPasses][VEC];
+#pragma unroll
+  for (int p = 0; p < kSlabPasses; ++p) {
+    const int64_t col = cs + (int64_t(p) * 64 + lane) * VEC;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      acc[p][v] = 0.f;
+      sc[p][v] = (col < M) ? scale[col + v] : 0.f;
+    }
+  }
+  const int64_t r0 = blk * rows_per_block;
+  const int64_t r1 = (r0 + rows_per_block < R) ? r0 + rows_per_block : R;
+  for (int64_t r = r0 + wave; r < r1; r += 4) {
+    const float inv = 1.0f / rms[r], c = cr[r];
+    const T* dyr = dy + r * M;
+    const T* xr = x + r * M;
+#pragma unroll
+    for (int p = 0; p < kSlabPasses; ++p) {
+      const int64_t col = cs + (int64_t(p) * 64 + lane) * VEC;
+      if (col < M) {
+        float a[VEC], b[VEC], o[VEC];
+        load_vec<T, VEC>(dyr + col, a);
+        load_vec<T, VEC>(xr + col, b);
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          o[v] = inv * __builtin_fmaf(sc[p][v], a[v], -b[v] * c);
+          acc[p][v] = __builtin_fmaf(a[v] * b[v], inv, acc[p][v]);
+        }
+        VecStore<T, VEC>::run(dx + r * M + col, o);
+      }
+    }
+  }
+  // sum the four wavefronts' column partials
+#pragma unroll
+  for (int p = 0; p < kSlabPasses; ++p) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) part[wave][lane * VEC + v] = acc[p][v];
+    __syncthreads();
+    for (int k = tid; k < CP; k += 256) {
+      const int64_t col = cs + int64_t(p) * CP + k;
+      if (col < M)
+        dsp[blk * M + col] = (part[0][k] + part[1][k]) + (part[2][k] + part[3][k]);
+    }
+    __syncthreads();
+  }
+}
+
 template <typename T, int VEC, int PASSES>
-static void rms_launch(const RmsArgs& a, const RmsPlan& p, hipStream_t st) {
+static hipError_t rms_launch(const RmsArgs& a, const RmsPlan& p, hipStream_t st) {
   const T* dy = static_cast<const T*>(a.dy);
   const T* x = static_cast<const T*>(a.x);
   T* dx = static_cast<T*>(a.dx);
+  hipError_t e;
   timer_mark(kKRmsBwd, false, st);
-  if constexpr (PASSES <= 8)
-    hipLaunchKernelGGL((k_rms_bwd_res<T, VEC, PASSES>), dim3(p.nblk), dim3(256), 0, st, a.R,
-                       a.M, p.rows_per_block, dy, x, a.scale, a.rms, dx, p.dsp);
-  else
-    hipLaunchKernelGGL((k_rms_bwd<T, VEC, PASSES>), dim3(p.nblk), dim3(256), 0, st, a.R, a.M,
-                       p.rows_per_block, dy, x, a.scale, a.rms, dx, p.dsp);
+  if constexpr (PASSES == 0) {  // the looped path
+    e = launch(k_rms_bwd_rowc<T, VEC>, dim3(unsigned(p.nblk)), dim3(256), st, a.R, a.M,
+               p.rows_per_block, dy, x, a.scale, a.rms, p.crow);
+    const int64_t nslab = (a.M + kSlabPasses * 64 * VEC - 1) / (kSlabPasses * 64 * VEC);
+    if (e == hipSuccess)
+      e = launch(k_rms_bwd_slab<T, VEC>, dim3(unsigned(p.nblk * nslab)), dim3(256), st, a.R,
+                 a.M, p.rows_per_block, p.nblk, dy, x, a.scale, a.rms, p.crow, dx, p.dsp);
+  } else if constexpr (PASSES <= 8) {
+    e = launch(k_rms_bwd_res<T, VEC, PASSES>, dim3(unsigned(p.nblk)), dim3(256), st, a.R, a.M,
+               p.rows_per_block, dy, x, a.scale, a.rms, dx, p.dsp);
+  } else {
+    e = launch(k_rms_bwd<T, VEC, PASSES>, dim3(unsigned(p.nblk)), dim3(256), st, a.R, a.M,
+               p.rows_per_block, dy, x, a.scale, a.rms, dx, p.dsp);
+  }
   timer_mark(kKRmsBwd, true, st);
+  return e;
 }
 
-// passes: exact count up to 8 (row resident in registers), else 16
+// passes: exact count up to 8 (row resident in registers), 16 (read twice), or 0 (the
+// looped path, any row length)
 template <typename T, int VEC>
 static hipError_t rms_v(const RmsArgs& a, const RmsPlan& p, hipStream_t st) {
   switch (p.passes) {
-    case 1: rms_launch<T, VEC, 1>(a, p, st); break;
-    case 2: rms_launch<T, VEC, 2>(a, p, st); break;
-    case 3: rms_launch<T, VEC, 3>(a, p, st); break;
-    case 4: rms_launch<T, VEC, 4>(a, p, st); break;
-    case 5: rms_launch<T, VEC, 5>(a, p, st); break;
-    case 6: rms_launch<T, VEC, 6>(a, p, st); break;
-    case 7: rms_launch<T, VEC, 7>(a, p, st); break;
-    case 8: rms_launch<T, VEC, 8>(a, p, st); break;
-    case 16: rms_launch<T, VEC, 16>(a, p, st); break;
-    default: return hipErrorInvalidValue;
+    case 0: return rms_launch<T, VEC, 0>(a, p, st);
+    case 1: return rms_launch<T, VEC, 1>(a, p, st);
+    case 2: return rms_launch<T, VEC, 2>(a, p, st);
+    case 3: return rms_launch<T, VEC, 3>(a, p, st);
+    case 4: return rms_launch<T, VEC, 4>(a, p, st);
+    case 5: return rms_launch<T, VEC, 5>(a, p, st);
+    case 6: return rms_launch<T, VEC, 6>(a, p, st);
+    case 7: return rms_launch<T, VEC, 7>(a, p, st);
+    case 8: return rms_launch<T, VEC, 8>(a, p, st);
+    case 16: return rms_launch<T, VEC, 16>(a, p, st);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_rmsnorm_bwd(const RmsArgs& a, const RmsPlan& p, hipStream_t st) {

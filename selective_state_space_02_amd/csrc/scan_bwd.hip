@@ -41,15 +41,17 @@ namespace ssm {
 // dy * silu(z) is formed at staging.
 template <typename T, int N, int VEC, bool FZ>
 __global__ __launch_bounds__(256, 4) void k_bwd_summary(
-    int64_t L, int64_t D, int64_t Lc, int nc, const T* __restrict__ delta,
-    const float* __restrict__ A, const T* __restrict__ Cm, const T* __restrict__ dy,
-    const float* __restrict__ dtb, bool sp, const T* __restrict__ z, float* __restrict__ GS,
-    float* __restrict__ SD) {
+    int64_t B, int64_t L, int64_t D, int64_t nf, int nc, int64_t groups,
+    const T* __restrict__ delta, const float* __restrict__ A, const T* __restrict__ Cm,
+    const T* __restrict__ dy, const float* __restrict__ dtb, bool sp, const T* __restrict__ z,
+    float* __restrict__ GS, float* __restrict__ SD) {
   constexpr int NS = N / 4;
   __shared__ float sd[2][kTc][kTileCh], sdy[2][kTc][kTileCh], sC[2][kTc][N];
   __shared__ float sbias[FZ ? kTileCh : 1];
-  const int c = blockIdx.z + 1, b = blockIdx.y, tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
-  const int64_t d0 = int64_t(blockIdx.x) * kTileCh, d = d0 + cl;
+  const WgPos wp = wg_pos(groups, B);
+  const int64_t c = wp.c + 1, b = wp.b;  // chunks 1..nc-1
+  const int tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
+  const int64_t d0 = wp.grp * kTileCh, d = d0 + cl;
   const bool act = d < D;
   const int D32 = int(D);
   const int dvalid = (D - d0 < kTileCh) ? int(D - d0) : kTileCh;
@@ -65,7 +67,8 @@ __global__ __launch_bounds__(256, 4) void k_bwd_summary(
   // running sums of the delta this thread stages (ChTile placement): the chunk's sum of
   // delta, accumulated once per value instead of in each of a channel's lanes per step
   float dsum[VEC] = {};
-  const int64_t t0 = int64_t(c) * Lc, t1 = (t0 + Lc < L) ? t0 + Lc : L;
+  const int64_t t0 = chunk_tile(c, nf, nc) * kTc, te = chunk_tile(c + 1, nf, nc) * kTc;
+  const int64_t t1 = te < L ? te : L;
   const int ntile = int((t1 - t0 + kTc - 1) / kTc);
   // tiles are walked from the last one backwards
   const ChTile<T, VEC> gt(D32, dvalid, tid);
@@ -145,13 +148,13 @@ __global__ __launch_bounds__(256, 4) void k_bwd_summary(
     __syncthreads();
   }
   if (act) {
-    const int64_t o = (int64_t(b) * nc + c) * D + d;
+    const int64_t o = (b * nc + c) * D + d;
 #pragma unroll
     for (int j = 0; j < NS; ++j) GS[o * N + q * NS + j] = gp[j];
   }
   // the tile buffers are free after the loop's last barrier
   const float sdl = chan_rows_sum(gt, dsum, &sd[0][0][0], tid);
-  if (tid < dvalid) SD[(int64_t(b) * nc + c) * D + d0 + tid] = sdl;
+  if (tid < dvalid) SD[(b * nc + c) * D + d0 + tid] = sdl;
 }
 
 template <int N>
@@ -212,7 +215,7 @@ __global__ __launch_bounds__(256) void k_bwd_carry(
 // previous tile's compute, so their registers are not held across it.
 template <typename T, int N, int VEC, int SPLIT, int WAVES, bool FZ>
 __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
-    int64_t B, int64_t L, int64_t D, int64_t Lc, int nc, int64_t nck,
+    int64_t B, int64_t L, int64_t D, int64_t nf, int nc, int64_t groups, int64_t nck,
     const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dv,
     const T* __restrict__ dy, const float* __restrict__ ckpt, const float* __restrict__ gin,
@@ -242,9 +245,10 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
   __shared__ float sbias[FZ ? kTileCh : 1], ssg[FZ ? kTc : 1][kTileCh];
   __shared__ float sdb[FZ ? kTileThreads * VEC : 1];
 
-  const int c = blockIdx.z, b = blockIdx.y, grp = blockIdx.x;
+  const WgPos wp = wg_pos(groups, B);
+  const int64_t c = wp.c, b = wp.b, grp = wp.grp;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = tid & 3, cl = tid >> 2;
-  const int64_t d0 = int64_t(grp) * kTileCh, d = d0 + cl;
+  const int64_t d0 = grp * kTileCh, d = d0 + cl;
   const bool act = d < D;
   const int D32 = int(D);
   const int dvalid = (D - d0 < kTileCh) ? int(D - d0) : kTileCh;
@@ -269,13 +273,14 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     A2[j] = act ? A[d * N + Qs * NS + (j ^ ms)] * kLog2e : 0.f;
-    gp[j] = (act && gin) ? gin[((int64_t(b) * nc + c) * D + d) * N + Qs * NS + (j ^ ms)] : 0.f;
+    gp[j] = (act && gin) ? gin[((b * nc + c) * D + d) * N + Qs * NS + (j ^ ms)] : 0.f;
     dA_acc[j] = 0.f;
   }
   const float Dd = act ? Dv[d] : 0.f;
   float dD_acc = 0.f;
 
-  const int64_t t0 = int64_t(c) * Lc, t1 = (t0 + Lc < L) ? t0 + Lc : L;
+  const int64_t t0 = chunk_tile(c, nf, nc) * kTc, te = chunk_tile(c + 1, nf, nc) * kTc;
+  const int64_t t1 = te < L ? te : L;
   const int ntile = int((t1 - t0 + kTc - 1) / kTc);
 
   const ChTile<T, VEC> gt(D32, dvalid, tid);
@@ -559,11 +564,11 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
       const int tc = tid / VEC, ci = tid % VEC;  // thread column and channel within it
       float sum = 0.f;
       for (int r = 0; r < G::RPP; ++r) sum += sdb[(r * G::TPR + tc) * VEC + ci];
-      dbp[(int64_t(b) * nc + c) * D + d0 + tid] = sum;
+      dbp[(b * nc + c) * D + d0 + tid] = sum;
     }
   }
   if (act) {
-    const int64_t o = (int64_t(b) * nc + c) * D + d;
+    const int64_t o = (b * nc + c) * D + d;
 #pragma unroll
     for (int j = 0; j < NS; ++j) dAp[o * N + Qs * NS + (j ^ ms)] = dA_acc[j];
     if (q == 0) dDp[o] = dD_acc;
@@ -595,29 +600,31 @@ static hipError_t bwd_impl(const ScanArgs& a, const BwdPlan& p, hipStream_t st) 
   const T* dy = static_cast<const T*>(a.dy);
   const dim3 block(256);
   const float* gin = nullptr;
+  hipError_t e;
   if (p.nc > 1) {
     timer_mark(kKBwdSummary, false, st);
-    hipLaunchKernelGGL((k_bwd_summary<T, N, VEC, FZ>), dim3(p.ng, a.B, p.nc - 1), block, 0, st,
-                       a.L, a.D, p.Lc, p.nc, delta, a.A, Cm, dy, a.dt_bias, a.dt_softplus,
-                       static_cast<const T*>(a.z), p.GS, p.SD);
+    e = launch(k_bwd_summary<T, N, VEC, FZ>, dim3(unsigned(p.ng * a.B * (p.nc - 1))), block, st,
+               a.B, a.L, a.D, p.nf, p.nc, p.ng, delta, a.A, Cm, dy, a.dt_bias, a.dt_softplus,
+               static_cast<const T*>(a.z), p.GS, p.SD);
     timer_mark(kKBwdSummary, true, st);
+    if (e != hipSuccess) return e;
     const int64_t tot = a.B * a.D * N;
     timer_mark(kKBwdCarry, false, st);
-    hipLaunchKernelGGL((k_bwd_carry<N>), dim3((tot + 255) / 256), block, 0, st, a.B, a.D,
-                       p.nc, a.A, p.GS, p.SD, p.gin);
+    e = launch(k_bwd_carry<N>, dim3(unsigned((tot + 255) / 256)), block, st, a.B, a.D, p.nc,
+               a.A, p.GS, p.SD, p.gin);
     timer_mark(kKBwdCarry, true, st);
+    if (e != hipSuccess) return e;
     gin = p.gin;
   }
   timer_mark(kKBwdMain, false, st);
   using Cfg = BwdMainCfg<N>;
-  hipLaunchKernelGGL((k_bwd_main<T, N, VEC, Cfg::kSplit, Cfg::kWaves, FZ>),
-                     dim3(p.ng, a.B, p.nc), block, 0, st, a.B, a.L, a.D, p.Lc, p.nc, p.nck, x,
-                     delta, a.A, Bm, Cm, a.Dv, dy, p.ckpt, gin, a.dt_bias, a.dt_softplus,
-                     static_cast<const T*>(a.z), static_cast<const T*>(a.ysave),
-                     static_cast<T*>(a.dx), static_cast<T*>(a.ddelta), static_cast<T*>(a.dz),
-                     p.dBp, p.dCp, p.dAp, p.dDp, a.ddt_bias ? p.dbp : nullptr, a.dh0);
+  e = launch(k_bwd_main<T, N, VEC, Cfg::kSplit, Cfg::kWaves, FZ>,
+             dim3(unsigned(p.ng * a.B * p.nc)), block, st, a.B, a.L, a.D, p.nf, p.nc, p.ng,
+             p.nck, x, delta, a.A, Bm, Cm, a.Dv, dy, p.ckpt, gin, a.dt_bias, a.dt_softplus,
+             static_cast<const T*>(a.z), static_cast<const T*>(a.ysave), static_cast<T*>(a.dx),
+             static_cast<T*>(a.ddelta), static_cast<T*>(a.dz), p.dBp, p.dCp, p.dAp, p.dDp,
+             a.ddt_bias ? p.dbp : nullptr, a.dh0);
   timer_mark(kKBwdMain, true, st);
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t BLN = a.B * a.L * N;
   if ((e = launch_reduce(p.dBp, p.ng, BLN, a.dB, false, p.rtmp, st)) != hipSuccess) return e;

@@ -7,8 +7,8 @@
 // and start it from a zero state (foxhunt ml-alpha forward-pass commit, forward
 // pipeline step 4).
 //
-// Parallel form.  The sequence is cut into nc coarse chunks of Lc steps (Lc a
-// multiple of the checkpoint interval kTc).  A chunk maps a start state h to
+// Parallel form.  The sequence is cut into nc coarse chunks of whole kTc-step tiles
+// (chunk_tile: an even split).  A chunk maps a start state h to
 //   h_end = P (.) h + S,   P[n] = prod_t a_t[n] = exp(A[d,n] * sum_t delta_t),
 // with S the chunk's end state from a zero start.  Three launches:
 //   1. k_fwd_summary: S and sum(delta) of chunks 0..nc-2 (skipped when nc == 1);
@@ -32,15 +32,18 @@ constexpr int kFwdOutputWaves = 6;
 // when sp).
 template <typename T, int N, int VEC, bool FZ>
 __global__ __launch_bounds__(256, 4) void k_fwd_summary(
-    int64_t L, int64_t D, int64_t Lc, int nc, const T* __restrict__ x,
-    const T* __restrict__ delta, const float* __restrict__ A, const T* __restrict__ Bm,
-    const float* __restrict__ dtb, bool sp, float* __restrict__ S, float* __restrict__ SD) {
+    int64_t B, int64_t L, int64_t D, int64_t nf, int nc, int64_t groups,
+    const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
+    const T* __restrict__ Bm, const float* __restrict__ dtb, bool sp, float* __restrict__ S,
+    float* __restrict__ SD) {
   constexpr int NS = N / 4;
   // sx holds u = delta * x (commit_tile below)
   __shared__ float sx[2][kTc][kTileCh], sd[2][kTc][kTileCh], sB[2][kTc][N];
   __shared__ float sbias[FZ ? kTileCh : 1];
-  const int c = blockIdx.z, b = blockIdx.y, tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
-  const int64_t d0 = int64_t(blockIdx.x) * kTileCh, d = d0 + cl;
+  const WgPos wp = wg_pos(groups, B);  // chunks 0..nc-2
+  const int64_t c = wp.c, b = wp.b;
+  const int tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
+  const int64_t d0 = wp.grp * kTileCh, d = d0 + cl;
   const bool act = d < D;
   const int D32 = int(D);
   const int dvalid = (D - d0 < kTileCh) ? int(D - d0) : kTileCh;
@@ -54,8 +57,9 @@ __global__ __launch_bounds__(256, 4) void k_fwd_summary(
     h[j] = 0.f;
   }
   float dsum[VEC] = {};  // running sums of the delta this thread stages (ChTile placement)
-  const int64_t t0 = int64_t(c) * Lc;  // chunks 0..nc-2 are full
-  const int ntile = int(Lc / kTc);
+  // chunks 0..nc-2 are full
+  const int64_t t0 = chunk_tile(c, nf, nc) * kTc;
+  const int ntile = int(chunk_tile(c + 1, nf, nc) - chunk_tile(c, nf, nc));
   const ChTile<T, VEC> gt(D32, dvalid, tid);
   const uint32_t voff = VecFetch<T, N>::offset(tid);
   ChFetch<T, VEC> fx, fd;
@@ -114,13 +118,13 @@ __global__ __launch_bounds__(256, 4) void k_fwd_summary(
     __syncthreads();
   }
   if (act) {
-    const int64_t o = (int64_t(b) * nc + c) * D + d;
+    const int64_t o = (b * nc + c) * D + d;
 #pragma unroll
     for (int j = 0; j < NS; ++j) S[o * N + q * NS + j] = h[j];
   }
   // the tile buffers are free after the loop's last barrier
   const float sdl = chan_rows_sum(gt, dsum, &sx[0][0][0], tid);
-  if (tid < dvalid) SD[(int64_t(b) * nc + c) * D + d0 + tid] = sdl;
+  if (tid < dvalid) SD[(b * nc + c) * D + d0 + tid] = sdl;
 }
 
 template <int N>
@@ -170,17 +174,20 @@ __global__ __launch_bounds__(256) void k_fwd_carry(
 // the stored output is y * silu(z), and ysave (nullable) receives y itself.
 template <typename T, int N, int VEC, bool FZ>
 __global__ __launch_bounds__(256, kFwdOutputWaves) void k_fwd_output(
-    int64_t L, int64_t D, int64_t Lc, int nc, int64_t nck, const T* __restrict__ x,
-    const T* __restrict__ delta, const float* __restrict__ A, const T* __restrict__ Bm,
-    const T* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ hin,
-    const float* __restrict__ dtb, bool sp, const T* __restrict__ z, T* __restrict__ y,
-    T* __restrict__ ysave, float* __restrict__ ckpt, float* __restrict__ h_last) {
+    int64_t B, int64_t L, int64_t D, int64_t nf, int nc, int64_t groups, int64_t nck,
+    const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
+    const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dv,
+    const float* __restrict__ hin, const float* __restrict__ dtb, bool sp,
+    const T* __restrict__ z, T* __restrict__ y, T* __restrict__ ysave,
+    float* __restrict__ ckpt, float* __restrict__ h_last) {
   constexpr int NS = N / 4;
   constexpr int CK = kTc / ckpt_per_tile(N);  // checkpoint interval
   __shared__ float sx[2][kTc][kTileCh], sd[2][kTc][kTileCh], sB[2][kTc][N], sC[2][kTc][N];
   __shared__ float sbias[FZ ? kTileCh : 1];
-  const int c = blockIdx.z, b = blockIdx.y, tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
-  const int64_t d0 = int64_t(blockIdx.x) * kTileCh, d = d0 + cl;
+  const WgPos wp = wg_pos(groups, B);
+  const int64_t c = wp.c, b = wp.b;
+  const int tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
+  const int64_t d0 = wp.grp * kTileCh, d = d0 + cl;
   const bool act = d < D;
   const int D32 = int(D);
   const int dvalid = (D - d0 < kTileCh) ? int(D - d0) : kTileCh;
@@ -205,8 +212,9 @@ __global__ __launch_bounds__(256, kFwdOutputWaves) void k_fwd_output(
   // loop over lanes
   zero(h);
   if (hin)
-    buf_load_states<NS>(buf_rsrc(hin + ((int64_t(b) * nc + c) * D + d0) * N, ckbytes), ckoff, h);
-  const int64_t t0 = int64_t(c) * Lc, t1 = (t0 + Lc < L) ? t0 + Lc : L;
+    buf_load_states<NS>(buf_rsrc(hin + ((b * nc + c) * D + d0) * N, ckbytes), ckoff, h);
+  const int64_t t0 = chunk_tile(c, nf, nc) * kTc, te = chunk_tile(c + 1, nf, nc) * kTc;
+  const int64_t t1 = te < L ? te : L;
   const int ntile = int((t1 - t0 + kTc - 1) / kTc);
   const ChTile<T, VEC> gt(D32, dvalid, tid);
   const uint32_t voff = VecFetch<T, N>::offset(tid);
@@ -307,7 +315,7 @@ __global__ __launch_bounds__(256, kFwdOutputWaves) void k_fwd_output(
   }
   if (h_last && act && c == nc - 1) {
 #pragma unroll
-    for (int j = 0; j < NS; ++j) h_last[(int64_t(b) * D + d) * N + q * NS + j] = h[j];
+    for (int j = 0; j < NS; ++j) h_last[(b * D + d) * N + q * NS + j] = h[j];
   }
 }
 
@@ -323,26 +331,29 @@ static hipError_t fwd_impl(const ScanArgs& a, const FwdPlan& p, hipStream_t st) 
   const dim3 block(256);
   const int64_t groups = (a.D + kTileCh - 1) / kTileCh;
   const float* hin = a.h0;  // [B][1][D][N] == [B][D][N] when nc == 1
+  hipError_t e;
   if (p.nc > 1) {
     timer_mark(kKFwdSummary, false, st);
-    hipLaunchKernelGGL((k_fwd_summary<T, N, VEC, FZ>), dim3(groups, a.B, p.nc - 1), block, 0, st,
-                       a.L, a.D, p.Lc, p.nc, x, delta, a.A, Bm, a.dt_bias, a.dt_softplus, p.S,
-                       p.SD);
+    e = launch(k_fwd_summary<T, N, VEC, FZ>, dim3(unsigned(groups * a.B * (p.nc - 1))), block,
+               st, a.B, a.L, a.D, p.nf, p.nc, groups, x, delta, a.A, Bm, a.dt_bias,
+               a.dt_softplus, p.S, p.SD);
     timer_mark(kKFwdSummary, true, st);
+    if (e != hipSuccess) return e;
     const int64_t tot = a.B * a.D * N;
     timer_mark(kKFwdCarry, false, st);
-    hipLaunchKernelGGL((k_fwd_carry<N>), dim3((tot + 255) / 256), block, 0, st, a.B, a.D,
-                       p.nc, a.A, a.h0, p.S, p.SD, p.hin);
+    e = launch(k_fwd_carry<N>, dim3(unsigned((tot + 255) / 256)), block, st, a.B, a.D, p.nc,
+               a.A, a.h0, p.S, p.SD, p.hin);
     timer_mark(kKFwdCarry, true, st);
+    if (e != hipSuccess) return e;
     hin = p.hin;
   }
   timer_mark(kKFwdOutput, false, st);
-  hipLaunchKernelGGL((k_fwd_output<T, N, VEC, FZ>), dim3(groups, a.B, p.nc), block, 0, st, a.L,
-                     a.D, p.Lc, p.nc, p.nck, x, delta, a.A, Bm, Cm, a.Dv, hin, a.dt_bias,
-                     a.dt_softplus, static_cast<const T*>(a.z), static_cast<T*>(a.y),
-                     static_cast<T*>(a.ysave), p.ckpt, a.h_last);
+  e = launch(k_fwd_output<T, N, VEC, FZ>, dim3(unsigned(groups * a.B * p.nc)), block, st, a.B,
+             a.L, a.D, p.nf, p.nc, groups, p.nck, x, delta, a.A, Bm, Cm, a.Dv, hin, a.dt_bias,
+             a.dt_softplus, static_cast<const T*>(a.z), static_cast<T*>(a.y),
+             static_cast<T*>(a.ysave), p.ckpt, a.h_last);
   timer_mark(kKFwdOutput, true, st);
-  return hipGetLastError();
+  return e;
 }
 
 template <typename T, int N>

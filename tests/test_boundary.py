@@ -137,10 +137,14 @@ def test_scan_rejects_unsupported_state_size(N):
     assert _bwd(lib, N=N) == b.SSM_ERR_UNSUPPORTED
 
 
-def test_scan_rejects_unsupported_dtype_and_batch():
+def test_scan_rejects_unsupported_dtype_and_grid():
     lib = b.load()
     assert _fwd(lib, dtype=2) == b.SSM_ERR_UNSUPPORTED
-    assert _fwd(lib, B=70000) == b.SSM_ERR_UNSUPPORTED
+    # the batch is not capped by a grid dimension of 65535 any more (the grid is 1-D); only
+    # (batch rows) x (64-channel groups) beyond one launch's 2^31 - 1 workgroups is refused
+    assert _fwd(lib, B=1 << 31, L=1, D=64) == b.SSM_ERR_UNSUPPORTED
+    assert "grid" in b.last_error()
+    assert _bwd(lib, B=1 << 31, L=1, D=64) == b.SSM_ERR_UNSUPPORTED
 
 
 def test_scan_rejects_overflowing_sizes():
@@ -241,9 +245,10 @@ def test_rms_validation():
     assert _rms(lib, R=0) == b.SSM_ERR_ARG
     assert _rms(lib, M=-3) == b.SSM_ERR_ARG
     assert _rms(lib, dtype=7) == b.SSM_ERR_UNSUPPORTED
-    assert _rms(lib, M=8192 + 8, dtype=1) == b.SSM_ERR_UNSUPPORTED
-    assert _rms(lib, M=4096 + 4, dtype=0) == b.SSM_ERR_UNSUPPORTED
-    assert _rms(lib, M=1025, dtype=0) == b.SSM_ERR_UNSUPPORTED       # not a multiple of 4
+    # rows of any length are supported (the looped path beyond 16 column groups per
+    # lane); only a row whose column slabs would exceed one launch's grid is refused
+    assert _rms(lib, R=1, M=(1 << 40) + 1, dtype=0) == b.SSM_ERR_UNSUPPORTED
+    assert "grid" in b.last_error()
     for name in ("dy", "x", "scale", "rms", "dx", "dscale"):
         assert _rms(lib, **{name: None}) == b.SSM_ERR_ARG
         assert _rms(lib, **{name: MIS}) == b.SSM_ERR_ALIGN
@@ -251,7 +256,10 @@ def test_rms_validation():
     assert need > 0
     assert _rms(lib, ws=FAKE, ws_bytes=need - 1) == b.SSM_ERR_WORKSPACE
     assert b.rmsnorm_bwd_workspace_bytes(10, 8192, 1) > 0
-    assert b.rmsnorm_bwd_workspace_bytes(10, 8193, 1) == 0
+    # the looped path (odd M, or M past 16 column groups per lane) also holds the per-row
+    # coefficients: R floats more than the block partials
+    for R, M, dt in ((10, 8193, 1), (10, 1500, 0), (10, 12288, 1), (10, 8192 * 4, 0)):
+        assert b.rmsnorm_bwd_workspace_bytes(R, M, dt) > 0
 
 
 def _conv_fwd(lib, B=2, L=64, D=32, K=4, dtype=0, x=FAKE, W=FAKE, bias=None, act=0, out=FAKE):
@@ -285,8 +293,6 @@ def test_rms_fwd_validation():
     assert _rms_fwd(lib, eps=float("nan")) == b.SSM_ERR_ARG
     assert _rms_fwd(lib, eps=float("inf")) == b.SSM_ERR_ARG
     assert _rms_fwd(lib, dtype=3) == b.SSM_ERR_UNSUPPORTED
-    assert _rms_fwd(lib, M=8192 + 8, dtype=1) == b.SSM_ERR_UNSUPPORTED
-    assert _rms_fwd(lib, M=1025, dtype=0) == b.SSM_ERR_UNSUPPORTED
     for name in ("x", "scale", "y", "rms"):
         assert _rms_fwd(lib, **{name: None}) == b.SSM_ERR_ARG
         assert _rms_fwd(lib, **{name: MIS}) == b.SSM_ERR_ALIGN
@@ -310,7 +316,7 @@ def test_scan_step_validation():
     assert _step(lib, N=3) == b.SSM_ERR_UNSUPPORTED
     assert _step(lib, B=0) == b.SSM_ERR_ARG
     assert _step(lib, D=-1) == b.SSM_ERR_ARG
-    assert _step(lib, B=65536) == b.SSM_ERR_UNSUPPORTED
+    assert _step(lib, B=1 << 31, D=64) == b.SSM_ERR_UNSUPPORTED  # beyond one launch's grid
     assert _step(lib, dtype=9) == b.SSM_ERR_UNSUPPORTED
     for name in ("h", "x_t", "delta_t", "A", "B_t", "C_t", "Dv", "y_t"):
         assert _step(lib, **{name: None}) == b.SSM_ERR_ARG

@@ -85,9 +85,16 @@ RMS_CASES = [custom(B=1, L=7, D=8), custom(B=3, L=11, D=100), custom(B=2, L=9, D
              custom(B=2, L=50, D=1000, dtype="bf16"), custom(B=1, L=33, D=4096),
              custom(B=1, L=17, D=8192, dtype="bf16"), custom(B=4, L=16, D=2),
              custom(B=2, L=5, D=203), custom(B=1, L=6, D=777, dtype="bf16")]
+# rows longer than 16 column groups per lane (the looped path: row coefficients, then
+# column slabs), with one column per lane group (M not a multiple of the vector width)
+# and with vectors; several row blocks and a ragged last slab
+RMS_LONG_CASES = [custom(B=20, L=30, D=1500, dtype="bf16"), custom(B=1, L=40, D=1501),
+                  custom(B=1, L=20, D=8192), custom(B=1, L=12, D=12288, dtype="bf16"),
+                  custom(B=3, L=7, D=40000, dtype="bf16"), custom(B=2, L=3, D=9001)]
 
 
-@pytest.mark.parametrize("w", RMS_CASES, ids=lambda w: f"R{w.rms_rows}M{w.rms_dim}{w.dtype}")
+@pytest.mark.parametrize("w", RMS_CASES + RMS_LONG_CASES,
+                         ids=lambda w: f"R{w.rms_rows}M{w.rms_dim}{w.dtype}")
 def test_rms_matches_oracle(w):
     say(f"[rms parity] R={w.rms_rows} M={w.rms_dim} {w.dtype}")
     p = with_saved_rms(synth.rms_inputs(w))

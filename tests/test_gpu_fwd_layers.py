@@ -79,7 +79,11 @@ RMS_CASES = [custom(B=1, L=7, D=8), custom(B=3, L=11, D=100), custom(B=2, L=9, D
              custom(B=2, L=50, D=1000, dtype="bf16"), custom(B=1, L=33, D=4096),
              custom(B=1, L=17, D=8192, dtype="bf16"), custom(B=4, L=16, D=2),
              custom(B=2, L=5, D=203), custom(B=1, L=6, D=777, dtype="bf16"),
-             custom(B=3, L=7, D=1536), custom(B=2, L=9, D=2560, dtype="bf16")]
+             custom(B=3, L=7, D=1536), custom(B=2, L=9, D=2560, dtype="bf16"),
+             # rows past 16 column groups per lane (the looped kernel, any row length)
+             custom(B=20, L=30, D=1500, dtype="bf16"), custom(B=1, L=40, D=1501),
+             custom(B=1, L=20, D=8192), custom(B=1, L=12, D=12288, dtype="bf16"),
+             custom(B=3, L=7, D=40000, dtype="bf16")]
 
 
 def rms_fwd_check(w, label):
@@ -117,7 +121,9 @@ def test_rms_fwd_rows_have_unit_mean_square_before_scale():
 
 RES_CASES = [custom(B=3, L=11, D=100), custom(B=2, L=9, D=96, dtype="bf16"),
              custom(B=1, L=17, D=8192, dtype="bf16"), custom(B=2, L=5, D=203),
-             custom(B=2, L=9, D=2560, dtype="bf16"), custom(B=1, L=33, D=4096)]
+             custom(B=2, L=9, D=2560, dtype="bf16"), custom(B=1, L=33, D=4096),
+             custom(B=2, L=10, D=1500, dtype="bf16"), custom(B=1, L=12, D=12288, dtype="bf16"),
+             custom(B=2, L=5, D=9001)]
 
 
 @pytest.mark.parametrize("w", RES_CASES + [WORKLOADS[-1]],

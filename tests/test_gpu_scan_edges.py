@@ -1,8 +1,10 @@
 """GPU parity of the scan at the edges of its supported sizes, and on degenerate inputs.
 
-- Sizes: 2^18 channels (4096 channel groups in one launch), the largest batch the grid
-  takes (65535 rows), and a long ragged sequence over one channel group (thousands of
-  coarse chunks and a long carry chain).  Every output is compared with the oracle.
+- Sizes: 2^18 channels (4096 channel groups in one launch), 65535 and 70000 batch rows
+  (past the 65535 limit of a grid's y dimension: the scan grids are 1-D), a batch wide
+  enough for several channel groups per row, and a long ragged sequence over one
+  channel group (thousands of coarse chunks and a long carry chain).  Every output is
+  compared with the oracle.
 - Degenerate inputs the method has closed forms for: a zero time step makes every step
   the identity (the state stays h0, y = C.h0 + Dv.x), and a zero upstream gradient gives
   exactly zero gradients.
@@ -23,6 +25,8 @@ ALL = ("y", "h_last", "dx", "ddelta", "dA", "dB", "dC", "dD", "dh0")
 EDGES = [
     ("many-channels-bf16", custom(B=1, L=40, D=1 << 18, N=16, dtype="bf16"), False),
     ("max-batch-f32", custom(B=65535, L=3, D=8, N=4), True),
+    ("batch-70000-bf16", custom(B=70000, L=5, D=8, N=16, dtype="bf16"), True),
+    ("batch-70000-groups-f32", custom(B=70000, L=2, D=130, N=8), False),
     ("long-ragged-f32", custom(B=1, L=100003, D=8, N=16), True),
 ]
 
