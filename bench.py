@@ -408,6 +408,69 @@ def measure_scan_fused(w, seed, steps, dev):
             "unfused_extra_ms_at_hbm_peak": extra / (HBM_PEAK_GBPS * 1e9) * 1e3}
 
 
+# Checkpoint intervals measured beside the step, with the slabs the sparse backward
+# regenerates its dense states in: (interval in steps, slabs); 0 is the default interval
+# (8 steps at N = 16), 512 the backward's chunk length on the 2.8B layer (a state at
+# each chunk start only).
+CKPT_INTERVALS = ((0, 1), (16, 4), (64, 2), (64, 8), (512, 4))
+
+
+def measure_ckpt_intervals(w, p, steps, dev):
+    """The scan forward and backward with the forward's states saved every `every` steps
+    (ssm_scan_fwd_every / ssm_scan_bwd_every; the backward regenerates the dense states of
+    one slab at a time), timed per call with events on the stream, against the checkpoint
+    memory and the backward's workspace.  Not part of the step and not in `value`."""
+    import torch
+    from selective_state_space_02_amd import binding as ssm
+    f32 = torch.float32
+    code = ssm.SSM_BF16 if w.dtype == "bf16" else ssm.SSM_F32
+    B, L, D, N = w.B, w.L, w.D, w.N
+    y = torch.empty_like(p["x"])
+    g = dict(dx=torch.empty_like(p["x"]), ddelta=torch.empty_like(p["x"]),
+             dA=torch.zeros((D, N), dtype=f32, device=dev), dB=torch.empty((B, L, N), dtype=f32, device=dev),
+             dC=torch.empty((B, L, N), dtype=f32, device=dev), dD=torch.zeros((D,), dtype=f32, device=dev))
+    ws_f = torch.empty(max(1, ssm.ssm_scan_fwd_workspace_bytes(B, L, D, N, code)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    out = {}
+    for every, slabs in CKPT_INTERVALS:
+        ck = ssm.new_ckpt(B, L, D, N, dev, ck_every=every)
+        wsb = ssm.ssm_scan_bwd_workspace_bytes_every(B, L, D, N, code, True, every, slabs)
+        ws_b = torch.empty(max(1, wsb), dtype=torch.uint8, device=dev)
+
+        def fwd():
+            ssm.ssm_scan_fwd_every(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], p["Dv"], every,
+                                   y=y, ckpt=ck, ws=ws_f)
+
+        def bwd():
+            ssm.ssm_scan_bwd_every(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], p["Dv"], p["dy"],
+                                   every, slabs, ckpt=ck, ws=ws_b, **g)
+        for _ in range(2):
+            fwd()
+            bwd()
+        torch.cuda.synchronize()
+        he = HipEvents()
+        ev = {k: [he.pair() for _ in range(steps)] for k in ("fwd", "bwd")}
+        kev = [he.pair() for _ in range(steps)]
+        for i in range(steps):
+            ssm.ssm_set_kernel_timer("fwd_output", *kev[i])
+            for k, f in (("fwd", fwd), ("bwd", bwd)):
+                he.record(ev[k][i][0], stream)
+                f()
+                he.record(ev[k][i][1], stream)
+        torch.cuda.synchronize()
+        ssm.ssm_set_kernel_timer("fwd_output", None, None)
+        ms = {k: sum(he.elapsed_ms(*pr) for pr in ev[k]) / steps for k in ev}
+        fo = sum(he.elapsed_ms(*pr) for pr in kev) / steps
+        he.destroy()
+        label = f"every {every} slabs {slabs}" if every else f"every {8 if N == 16 else 16} (default)"
+        out[label] = {"slabs": slabs, "ckpt_bytes": ck.numel() * 4, "bwd_workspace_bytes": wsb,
+                      "fwd_ms": ms["fwd"], "fwd_output_kernel_ms": fo, "bwd_ms": ms["bwd"],
+                      "fwd_bwd_ms": ms["fwd"] + ms["bwd"]}
+        del ck, ws_b
+        torch.cuda.empty_cache()
+    return out
+
+
 def measure_copy_GBps(dev, reps=5):
     """A plain 1 GiB device-to-device copy (torch's copy on the current stream), timed
     with events: the practical HBM rate the bandwidth fractions are also quoted against
@@ -678,6 +741,7 @@ def main():
     scan_fused["overhead_vs_plain_ms"] = (scan_fused["call_ms"]["fused_fwd"] +
                                           scan_fused["call_ms"]["fused_bwd"] - scan_ms)
 
+    ckpt_iv = measure_ckpt_intervals(w, p, K_, dev)
     copy_gbps = measure_copy_GBps(dev)
 
     if args.copy_calibration:
@@ -744,6 +808,7 @@ def main():
     out["conv_silu"] = conv_silu
     out["scan_fused"] = scan_fused
     out["decode"] = decode
+    out["ckpt_interval"] = ckpt_iv
     if not args.no_cpu_baseline:
         sample = args.cpu_sample_channels or max(16, min(w.D, 2048))
         print(f"[bench] cpu baseline: oracle on {sample} channels", file=sys.stderr, flush=True)

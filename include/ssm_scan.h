@@ -100,6 +100,9 @@ const char *ssm_version(void);
  *   9 conv1d forward               10 RMSNorm forward
  *  11 scan decode step             12 conv1d decode step
  *  13 decode token (conv step + SiLU + fused scan step)
+ *  14 scan-backward regeneration of dense states from sparse checkpoints
+ * (Kernels launched several times in one call -- the sparse-checkpoint backward's main
+ * pass and regeneration, once per slab -- leave the pair on their last launch.)
  * Returns SSM_ERR_ARG for an unknown id or a half-set pair.  Has no effect on results. */
 int ssm_set_kernel_timer(int kernel, void *start, void *stop);
 
@@ -160,6 +163,37 @@ int ssm_scan_bwd(void *stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t 
                  const void *Bm, const void *Cm, const float *Dv, const float *h0,
                  const void *dy, const float *ckpt, void *dx, void *ddelta, float *dA,
                  float *dB, float *dC, float *dD, float *dh0, void *ws, size_t ws_bytes);
+
+/* Checkpoint interval as a memory/compute trade (the forward cache the foxhunt ml-alpha
+ * backward-scratch commit keeps, against the forward recompute of the rustytorch
+ * backward_cuda commit).  ck_every = 0 is the default interval above (8 steps at N = 16,
+ * 16 below), which ssm_scan_fwd/ssm_scan_bwd use; any other value must be a positive
+ * multiple of 16 steps: the forward then saves the state before every ck_every-th step
+ * only (ssm_scan_ckpt_bytes_every() bytes, 1/m of the default for ck_every = m x the
+ * default), and the backward splits its coarse chunks (whole intervals) into `slabs`
+ * slabs, regenerating the default-interval states of one slab at a time from the saved
+ * ones into its workspace before its main pass over that slab: one more forward pass over
+ * the sequence, and a workspace holding one slab's states (about 1/slabs of the default
+ * checkpoints).  The same ck_every must be given to the forward and the backward;
+ * with ckpt == NULL the backward runs the forward at that interval into its workspace.
+ * Results are the default path's to within summation order (the chunks differ).
+ * Returns 0 (the byte queries) or SSM_ERR_ARG for another ck_every, or slabs < 1. */
+size_t ssm_scan_ckpt_bytes_every(int64_t B, int64_t L, int64_t D, int64_t N,
+                                 int64_t ck_every);
+size_t ssm_scan_bwd_workspace_bytes_every(int64_t B, int64_t L, int64_t D, int64_t N,
+                                          ssm_dtype_t dtype, int with_ckpt, int64_t ck_every,
+                                          int64_t slabs);
+int ssm_scan_fwd_every(void *stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D,
+                       int64_t N, const void *x, const void *delta, const float *A,
+                       const void *Bm, const void *Cm, const float *Dv, const float *h0,
+                       void *y, float *ckpt, float *h_last, int64_t ck_every, void *ws,
+                       size_t ws_bytes);
+int ssm_scan_bwd_every(void *stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D,
+                       int64_t N, const void *x, const void *delta, const float *A,
+                       const void *Bm, const void *Cm, const float *Dv, const float *h0,
+                       const void *dy, const float *ckpt, void *dx, void *ddelta, float *dA,
+                       float *dB, float *dC, float *dD, float *dh0, int64_t ck_every,
+                       int64_t slabs, void *ws, size_t ws_bytes);
 
 /* ---------------------------------------------------------------------------------
  * The scan between its neighbours in the Mamba block, fused into the scan's kernels.
@@ -240,7 +274,6 @@ size_t rmsnorm_bwd_workspace_bytes(int64_t R, int64_t M, ssm_dtype_t dtype);
 int rmsnorm_bwd(void *stream, ssm_dtype_t dtype, int64_t R, int64_t M, const void *dy,
                 const void *x, const float *scale, const float *rms, void *dx,
                 float *dscale, void *ws, size_t ws_bytes);
-
 /* ---------------------------------------------------------------------------------
  * Depthwise causal conv1d forward, the forward of conv1d_causal_bwd above (the window
  * of the mamba-rs backward_conv1d_step section holds the last K inputs, tap K-1 the

@@ -25,7 +25,9 @@ EXPORTS = ("ssm_last_error", "ssm_version", "ssm_set_kernel_timer", "ssm_scan_ck
            "ssm_scan_bwd", "conv1d_causal_bwd_workspace_bytes", "conv1d_causal_bwd",
            "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd", "conv1d_causal_fwd", "rmsnorm_fwd",
            "ssm_scan_step", "conv1d_causal_step", "ssm_scan_fused_fwd", "ssm_scan_fused_bwd",
-           "ssm_scan_fused_step", "ssm_decode_step", "ssm_scan_chunks")
+           "ssm_scan_fused_step", "ssm_decode_step", "ssm_scan_chunks",
+           "ssm_scan_ckpt_bytes_every", "ssm_scan_bwd_workspace_bytes_every",
+           "ssm_scan_fwd_every", "ssm_scan_bwd_every")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -72,6 +74,14 @@ def load():
     lib.ssm_scan_fwd.argtypes = [_P, _E] + [_I] * 4 + [_P] * 10 + [_P, _S]
     lib.ssm_scan_bwd.restype = _E
     lib.ssm_scan_bwd.argtypes = [_P, _E] + [_I] * 4 + [_P] * 16 + [_P, _S]
+    lib.ssm_scan_ckpt_bytes_every.restype = _S
+    lib.ssm_scan_ckpt_bytes_every.argtypes = [_I] * 5
+    lib.ssm_scan_bwd_workspace_bytes_every.restype = _S
+    lib.ssm_scan_bwd_workspace_bytes_every.argtypes = [_I] * 4 + [_E, _E, _I, _I]
+    lib.ssm_scan_fwd_every.restype = _E
+    lib.ssm_scan_fwd_every.argtypes = [_P, _E] + [_I] * 4 + [_P] * 10 + [_I] + [_P, _S]
+    lib.ssm_scan_bwd_every.restype = _E
+    lib.ssm_scan_bwd_every.argtypes = [_P, _E] + [_I] * 4 + [_P] * 16 + [_I, _I] + [_P, _S]
     lib.ssm_scan_fused_fwd.restype = _E
     lib.ssm_scan_fused_fwd.argtypes = [_P, _E] + [_I] * 4 + [_P] * 8 + [_E] + [_P] * 5 + [_P, _S]
     lib.ssm_scan_fused_bwd.restype = _E
@@ -110,7 +120,8 @@ def version() -> str:
 
 KERNEL_IDS = {"fwd_summary": 1, "fwd_carry": 2, "fwd_output": 3, "bwd_summary": 4,
               "bwd_carry": 5, "bwd_main": 6, "conv_bwd": 7, "rms_bwd": 8, "conv_fwd": 9,
-              "rms_fwd": 10, "scan_step": 11, "conv_step": 12, "decode_step": 13}
+              "rms_fwd": 10, "scan_step": 11, "conv_step": 12, "decode_step": 13,
+              "ckpt_regen": 14}
 
 
 def ssm_set_kernel_timer(kernel, start=None, stop=None):
@@ -176,6 +187,15 @@ def ssm_scan_ckpt_bytes(B, L, D, N) -> int:
     return int(load().ssm_scan_ckpt_bytes(B, L, D, N))
 
 
+def ssm_scan_ckpt_bytes_every(B, L, D, N, ck_every) -> int:
+    return int(load().ssm_scan_ckpt_bytes_every(B, L, D, N, ck_every))
+
+
+def ssm_scan_bwd_workspace_bytes_every(B, L, D, N, dtype_code, with_ckpt, ck_every, slabs) -> int:
+    return int(load().ssm_scan_bwd_workspace_bytes_every(B, L, D, N, dtype_code,
+                                                         int(bool(with_ckpt)), ck_every, slabs))
+
+
 def ssm_scan_fwd_workspace_bytes(B, L, D, N, dtype_code) -> int:
     return int(load().ssm_scan_fwd_workspace_bytes(B, L, D, N, dtype_code))
 
@@ -184,13 +204,25 @@ def ssm_scan_bwd_workspace_bytes(B, L, D, N, dtype_code, with_ckpt) -> int:
     return int(load().ssm_scan_bwd_workspace_bytes(B, L, D, N, dtype_code, int(bool(with_ckpt))))
 
 
-def new_ckpt(B, L, D, N, device) -> torch.Tensor:
-    """A buffer for the forward's checkpoints (f32, opaque layout)."""
-    return torch.empty(ssm_scan_ckpt_bytes(B, L, D, N) // 4, dtype=torch.float32, device=device)
+def new_ckpt(B, L, D, N, device, ck_every=0) -> torch.Tensor:
+    """A buffer for the forward's checkpoints (f32, opaque layout) at the given interval
+    (0: the default)."""
+    nbytes = ssm_scan_ckpt_bytes_every(B, L, D, N, ck_every)
+    if nbytes == 0:
+        raise ValueError(f"unsupported checkpoint interval {ck_every}")
+    return torch.empty(nbytes // 4, dtype=torch.float32, device=device)
 
 
 def ssm_scan_fwd(x, delta, A, Bm, Cm, Dv, h0=None, y=None, ckpt=None, h_last=None, ws=None):
     """y = scan(x, delta, A, Bm, Cm, Dv; h0).  Returns y (allocated if not given)."""
+    return ssm_scan_fwd_every(x, delta, A, Bm, Cm, Dv, 0, h0=h0, y=y, ckpt=ckpt, h_last=h_last,
+                              ws=ws)
+
+
+def ssm_scan_fwd_every(x, delta, A, Bm, Cm, Dv, ck_every, h0=None, y=None, ckpt=None,
+                       h_last=None, ws=None):
+    """ssm_scan_fwd saving its states every ck_every steps (0: the default interval, which
+    calls ssm_scan_fwd itself)."""
     lib = load()
     Bsz, L, D = x.shape
     N = A.shape[1]
@@ -207,12 +239,16 @@ def ssm_scan_fwd(x, delta, A, Bm, Cm, Dv, h0=None, y=None, ckpt=None, h_last=Non
         _ptr(ckpt, "ckpt", torch.float32, None, dev),
         _ptr(h_last, "h_last", torch.float32, (Bsz, D, N), dev),
     ]
-    if ckpt is not None and ckpt.numel() * 4 < ssm_scan_ckpt_bytes(Bsz, L, D, N):
+    if ckpt is not None and ckpt.numel() * 4 < ssm_scan_ckpt_bytes_every(Bsz, L, D, N, ck_every):
         raise ValueError("ckpt buffer too small (use new_ckpt)")
     need = ssm_scan_fwd_workspace_bytes(Bsz, L, D, N, code)
     ws, nbytes = _workspace(need, dev, ws)
-    _check(lib.ssm_scan_fwd(_stream(dev), code, Bsz, L, D, N, *args,
-                            _ptr(ws, "ws") if ws is not None else None, nbytes))
+    wsp = _ptr(ws, "ws") if ws is not None else None
+    if ck_every == 0:
+        _check(lib.ssm_scan_fwd(_stream(dev), code, Bsz, L, D, N, *args, wsp, nbytes))
+    else:
+        _check(lib.ssm_scan_fwd_every(_stream(dev), code, Bsz, L, D, N, *args, ck_every, wsp,
+                                      nbytes))
     return y
 
 
@@ -220,6 +256,14 @@ def ssm_scan_bwd(x, delta, A, Bm, Cm, Dv, dy, ckpt=None, h0=None, dx=None, ddelt
                  dA=None, dB=None, dC=None, dD=None, dh0=None, ws=None):
     """Backward.  dA and dD are accumulated into (zeros allocated if not given); every
     other gradient is overwritten.  Returns dict dx, ddelta, dA, dB, dC, dD, dh0."""
+    return ssm_scan_bwd_every(x, delta, A, Bm, Cm, Dv, dy, 0, 1, ckpt=ckpt, h0=h0, dx=dx,
+                              ddelta=ddelta, dA=dA, dB=dB, dC=dC, dD=dD, dh0=dh0, ws=ws)
+
+
+def ssm_scan_bwd_every(x, delta, A, Bm, Cm, Dv, dy, ck_every, slabs, ckpt=None, h0=None, dx=None,
+                       ddelta=None, dA=None, dB=None, dC=None, dD=None, dh0=None, ws=None):
+    """ssm_scan_bwd from checkpoints saved every ck_every steps, regenerating the dense
+    states slab by slab (ck_every = 0 and slabs = 1 call ssm_scan_bwd itself)."""
     lib = load()
     Bsz, L, D = x.shape
     N = A.shape[1]
@@ -233,7 +277,7 @@ def ssm_scan_bwd(x, delta, A, Bm, Cm, Dv, dy, ckpt=None, h0=None, dx=None, ddelt
     dB = torch.empty((Bsz, L, N), dtype=f32, device=dev) if dB is None else dB
     dC = torch.empty((Bsz, L, N), dtype=f32, device=dev) if dC is None else dC
     dD = torch.zeros((D,), dtype=f32, device=dev) if dD is None else dD
-    if ckpt is not None and ckpt.numel() * 4 < ssm_scan_ckpt_bytes(Bsz, L, D, N):
+    if ckpt is not None and ckpt.numel() * 4 < ssm_scan_ckpt_bytes_every(Bsz, L, D, N, ck_every):
         raise ValueError("ckpt buffer too small")
     args = [
         _ptr(x, "x", dt, (Bsz, L, D), dev), _ptr(delta, "delta", dt, (Bsz, L, D), dev),
@@ -246,10 +290,17 @@ def ssm_scan_bwd(x, delta, A, Bm, Cm, Dv, dy, ckpt=None, h0=None, dx=None, ddelt
         _ptr(dC, "dC", f32, (Bsz, L, N), dev), _ptr(dD, "dD", f32, (D,), dev),
         _ptr(dh0, "dh0", f32, (Bsz, D, N), dev),
     ]
-    need = ssm_scan_bwd_workspace_bytes(Bsz, L, D, N, code, ckpt is not None)
+    if ssm_scan_ckpt_bytes_every(Bsz, L, D, N, ck_every) == 0 or slabs < 1:
+        raise ValueError(f"unsupported checkpoint interval {ck_every} or slabs {slabs}")
+    need = ssm_scan_bwd_workspace_bytes_every(Bsz, L, D, N, code, ckpt is not None, ck_every,
+                                              slabs)
     ws, nbytes = _workspace(need, dev, ws)
-    _check(lib.ssm_scan_bwd(_stream(dev), code, Bsz, L, D, N, *args,
-                            _ptr(ws, "ws") if ws is not None else None, nbytes))
+    wsp = _ptr(ws, "ws") if ws is not None else None
+    if ck_every == 0 and slabs == 1:
+        _check(lib.ssm_scan_bwd(_stream(dev), code, Bsz, L, D, N, *args, wsp, nbytes))
+    else:
+        _check(lib.ssm_scan_bwd_every(_stream(dev), code, Bsz, L, D, N, *args, ck_every, slabs,
+                                      wsp, nbytes))
     return dict(dx=dx, ddelta=ddelta, dA=dA, dB=dB, dC=dC, dD=dD, dh0=dh0)
 
 

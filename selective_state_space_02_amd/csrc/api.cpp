@@ -72,24 +72,30 @@ constexpr int64_t kCUs = 256;
 constexpr int64_t kFwdTargetWG = kCUs * 32;
 constexpr int64_t kBwdTargetWG = kCUs * 20;
 
-// Coarse chunking of the sequence: whole tiles per chunk, the longest chunks whose count
-// reaches the target grid (nf / want tiles each), but at least two tiles per chunk:
-// below that the summary pass costs as much as it saves.  The chunks then split the
-// tiles evenly (ssm::chunk_tile).
-ssm::Chunking choose_chunks(int64_t B, int64_t L, int64_t D, int64_t target) {
+// Coarse chunking of the sequence: whole units of g tiles per chunk (g = 1, or the tiles
+// of one sparse-checkpoint interval), the longest chunks whose count reaches the target
+// grid (nu / want units each), but at least two tiles per chunk: below that the summary
+// pass costs as much as it saves.  The chunks then split the units evenly
+// (ssm::chunk_tile).
+ssm::Chunking choose_chunks(int64_t B, int64_t L, int64_t D, int64_t target, int64_t g = 1) {
   ssm::Chunking c;
   c.nf = cdiv(L, ssm::kTc);
+  const int64_t nu = cdiv(c.nf, g);   // units
   const int64_t W = B * cdiv(D, 64);  // workgroups per chunk
   const int64_t want = cdiv(target, W);
-  int64_t tiles = want > 1 ? c.nf / want : c.nf;  // tiles per chunk
-  const int64_t tmin = c.nf < 2 ? c.nf : 2;
-  if (tiles < tmin) tiles = tmin;
-  c.nc = int(cdiv(c.nf, tiles));
+  int64_t units = want > 1 ? nu / want : nu;  // units per chunk
+  const int64_t umin = g >= 2 ? 1 : (nu < 2 ? nu : 2);
+  if (units < umin) units = umin;
+  c.nc = int(cdiv(nu, units));
   return c;
 }
 
-// checkpoints: the state before every (kTc / ckpt_per_tile(N))-th step
-int64_t ckpt_count(int64_t L, int64_t N) { return cdiv(L, ssm::kTc / ssm::ckpt_per_tile(N)); }
+// The checkpoint interval a call uses: every = 0 selects the dense interval
+// (ssm::ckpt_base: 8 steps at N = 16, 16 below).
+int64_t ck_interval(int64_t N, int64_t every) { return every == 0 ? ssm::ckpt_base(N) : every; }
+
+// checkpoints: the state before every `every`-th step
+int64_t ckpt_count(int64_t L, int64_t every) { return cdiv(L, every); }
 
 // Largest reduction scratch (floats) over the (partials, outputs) pairs one call reduces.
 int64_t max_tmp(std::initializer_list<std::pair<int64_t, int64_t>> pj) {
@@ -101,13 +107,15 @@ int64_t max_tmp(std::initializer_list<std::pair<int64_t, int64_t>> pj) {
   return m;
 }
 
-size_t fwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, ssm::FwdPlan* plan, void* ws) {
+size_t fwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, int64_t every, ssm::FwdPlan* plan,
+              void* ws) {
   const ssm::Chunking c = choose_chunks(B, L, D, kFwdTargetWG);
   Carver cv(ws);
   ssm::FwdPlan p{};
   p.nc = c.nc;
   p.nf = c.nf;
-  p.nck = ckpt_count(L, N);
+  p.ck_every = ck_interval(N, every);
+  p.nck = ckpt_count(L, p.ck_every);
   if (c.nc > 1) {
     p.S = cv.take(size_t(B) * c.nc * D * N);
     p.SD = cv.take(size_t(B) * c.nc * D);
@@ -117,18 +125,34 @@ size_t fwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, ssm::FwdPlan* plan, vo
   return cv.off;
 }
 
-size_t ckpt_floats(int64_t B, int64_t L, int64_t D, int64_t N) {
-  return size_t(B) * size_t(ckpt_count(L, N)) * size_t(D) * size_t(N);
+size_t ckpt_floats(int64_t B, int64_t L, int64_t D, int64_t N, int64_t every) {
+  return size_t(B) * size_t(ckpt_count(L, ck_interval(N, every))) * size_t(D) * size_t(N);
 }
 
-size_t bwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, bool with_ckpt, ssm::BwdPlan* plan,
-              float** ckpt_out, ssm::FwdPlan* fplan, void* ws) {
-  const ssm::Chunking c = choose_chunks(B, L, D, kBwdTargetWG);
+// Backward plan.  With sparse checkpoints (every above the dense interval) the chunks are
+// whole checkpoint intervals (g = every / kTc tiles), and the main pass runs over slabs
+// of slab_chunks chunks, each after regenerating its dense states into ckd.  The chunk
+// target then also gives each slab's main launch about two rounds of resident
+// workgroups (three per CU): measured on the 2 x 16384 x 5120 layer, the backward's time
+// is flat in the chunk count (32 to 256 chunks within 2%) but drops when a slab's launch
+// would not fill the GPU (4 chunks of 160 workgroups per slab: +0.35 ms), while the
+// per-chunk buffers (carries, dA partials) grow with the count.
+size_t bwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, bool with_ckpt, int64_t every,
+              int64_t slabs, ssm::BwdPlan* plan, float** ckpt_out, ssm::FwdPlan* fplan,
+              void* ws) {
+  const int64_t ev = ck_interval(N, every);
+  const bool sparse = ev != ssm::ckpt_base(N);
+  const int64_t g = sparse ? ev / ssm::kTc : 1;
+  const int64_t slab_target = slabs * kCUs * 6;
+  const int64_t target = sparse && slab_target > kBwdTargetWG ? slab_target : kBwdTargetWG;
+  const ssm::Chunking c = choose_chunks(B, L, D, target, g);
   Carver cv(ws);
   ssm::BwdPlan p{};
   p.nc = c.nc;
   p.nf = c.nf;
-  p.nck = ckpt_count(L, N);
+  p.g = g;
+  p.ck_every = ev;
+  p.nck = ckpt_count(L, ev);
   p.ng = cdiv(D, 64);
   if (c.nc > 1) {
     p.GS = cv.take(size_t(B) * c.nc * D * N);
@@ -146,15 +170,40 @@ size_t bwd_ws(int64_t B, int64_t L, int64_t D, int64_t N, bool with_ckpt, ssm::B
     const int64_t t = max_tmp({{p.ng, B * L * N}, {B * c.nc, D * N}, {B * c.nc, D}});
     p.rtmp = cv.take(size_t(t));
   }
+  if (sparse) {
+    p.slab_chunks = int(cdiv(c.nc, slabs));
+    int64_t mx = 0;  // dense states of the longest slab
+    for (int64_t c0 = 0; c0 < c.nc; c0 += p.slab_chunks) {
+      const int64_t c1 = c0 + p.slab_chunks < c.nc ? c0 + p.slab_chunks : c.nc;
+      const int64_t ts = ssm::chunk_tile(c0, c.nf, c.nc, g) * ssm::kTc;
+      int64_t te = ssm::chunk_tile(c1, c.nf, c.nc, g) * ssm::kTc;
+      if (te > L) te = L;
+      const int64_t n = cdiv(te - ts, ssm::ckpt_base(N));
+      if (n > mx) mx = n;
+    }
+    p.nckd = mx;
+    p.ckd = cv.take(size_t(B) * size_t(mx) * size_t(D) * size_t(N));
+  }
   if (!with_ckpt) {
-    float* ck = cv.take(ckpt_floats(B, L, D, N));
+    float* ck = cv.take(ckpt_floats(B, L, D, N, every));
     if (ckpt_out) *ckpt_out = ck;
     // the forward's own workspace follows
     char* fbase = ws ? static_cast<char*>(ws) + cv.off : nullptr;
-    cv.off += fwd_ws(B, L, D, N, fplan, fbase);
+    cv.off += fwd_ws(B, L, D, N, every, fplan, fbase);
   }
   if (plan) *plan = p;
   return cv.off;
+}
+
+// every: 0 (the dense interval), the dense interval itself, or a positive multiple of
+// kTc; slabs >= 1
+int check_ckpt_every(int64_t N, int64_t every, int64_t slabs) {
+  if (every < 0 || (every != 0 && every != ssm::ckpt_base(N) && every % ssm::kTc != 0))
+    return fail(SSM_ERR_ARG,
+                "checkpoint interval %lld must be 0, %lld or a positive multiple of %d steps",
+                (long long)every, (long long)ssm::ckpt_base(N), ssm::kTc);
+  if (slabs < 1) return fail(SSM_ERR_ARG, "slabs must be >= 1 (got %lld)", (long long)slabs);
+  return SSM_OK;
 }
 
 int check_scan_dims(ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D, int64_t N) {
@@ -288,9 +337,14 @@ const char* ssm_last_error(void) { return g_err.c_str(); }
 
 const char* ssm_version(void) { return "ssmscan-gfx950 0.1.0"; }
 
-size_t ssm_scan_ckpt_bytes(int64_t B, int64_t L, int64_t D, int64_t N) {
+size_t ssm_scan_ckpt_bytes_every(int64_t B, int64_t L, int64_t D, int64_t N, int64_t every) {
   if (B <= 0 || L <= 0 || D <= 0 || N <= 0) return 0;
-  return ckpt_floats(B, L, D, N) * sizeof(float);
+  if (every < 0 || (every != 0 && every != ssm::ckpt_base(N) && every % ssm::kTc != 0)) return 0;
+  return ckpt_floats(B, L, D, N, every) * sizeof(float);
+}
+
+size_t ssm_scan_ckpt_bytes(int64_t B, int64_t L, int64_t D, int64_t N) {
+  return ssm_scan_ckpt_bytes_every(B, L, D, N, 0);
 }
 
 int ssm_scan_chunks(int64_t B, int64_t L, int64_t D, int64_t N, int* fwd_chunks,
@@ -305,28 +359,39 @@ int ssm_scan_chunks(int64_t B, int64_t L, int64_t D, int64_t N, int* fwd_chunks,
 
 size_t ssm_scan_fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype_t) {
   if (B <= 0 || L <= 0 || D <= 0 || N <= 0) return 0;
-  return fwd_ws(B, L, D, N, nullptr, nullptr);
+  return fwd_ws(B, L, D, N, 0, nullptr, nullptr);
 }
 
-size_t ssm_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype_t,
-                                    int with_ckpt) {
+size_t ssm_scan_bwd_workspace_bytes_every(int64_t B, int64_t L, int64_t D, int64_t N,
+                                          ssm_dtype_t, int with_ckpt, int64_t every,
+                                          int64_t slabs) {
   if (B <= 0 || L <= 0 || D <= 0 || N <= 0) return 0;
-  return bwd_ws(B, L, D, N, with_ckpt != 0, nullptr, nullptr, nullptr, nullptr);
+  if (every < 0 || (every != 0 && every != ssm::ckpt_base(N) && every % ssm::kTc != 0) ||
+      slabs < 1)
+    return 0;
+  return bwd_ws(B, L, D, N, with_ckpt != 0, every, slabs, nullptr, nullptr, nullptr, nullptr);
 }
 
-int ssm_scan_fwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D, int64_t N,
-                 const void* x, const void* delta, const float* A, const void* Bm,
-                 const void* Cm, const float* Dv, const float* h0, void* y, float* ckpt,
-                 float* h_last, void* ws, size_t ws_bytes) {
+size_t ssm_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
+                                    ssm_dtype_t dtype, int with_ckpt) {
+  return ssm_scan_bwd_workspace_bytes_every(B, L, D, N, dtype, with_ckpt, 0, 1);
+}
+
+int ssm_scan_fwd_every(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D,
+                       int64_t N, const void* x, const void* delta, const float* A,
+                       const void* Bm, const void* Cm, const float* Dv, const float* h0,
+                       void* y, float* ckpt, float* h_last, int64_t ck_every, void* ws,
+                       size_t ws_bytes) {
   int rc = check_scan_dims(dtype, B, L, D, N);
   if (rc) return rc;
+  if ((rc = check_ckpt_every(N, ck_every, 1))) return rc;
   rc = check_ptrs({{x, "x"}, {delta, "delta"}, {A, "A"}, {Bm, "Bm"}, {Cm, "Cm"}, {Dv, "Dv"}, {y, "y"}},
                   {{h0, "h0"}, {ckpt, "ckpt"}, {h_last, "h_last"}});
   if (rc) return rc;
   ssm::FwdPlan p{};
-  const size_t need = fwd_ws(B, L, D, N, &p, nullptr);
+  const size_t need = fwd_ws(B, L, D, N, ck_every, &p, nullptr);
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
-  fwd_ws(B, L, D, N, &p, ws);
+  fwd_ws(B, L, D, N, ck_every, &p, ws);
   p.ckpt = ckpt;
   ssm::ScanArgs a{};
   a.dtype = int(dtype);
@@ -337,13 +402,23 @@ int ssm_scan_fwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t 
   return hip_status(ssm::launch_scan_fwd(a, p, static_cast<hipStream_t>(stream)), "ssm_scan_fwd");
 }
 
-int ssm_scan_bwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D, int64_t N,
+int ssm_scan_fwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D, int64_t N,
                  const void* x, const void* delta, const float* A, const void* Bm,
-                 const void* Cm, const float* Dv, const float* h0, const void* dy,
-                 const float* ckpt, void* dx, void* ddelta, float* dA, float* dB, float* dC,
-                 float* dD, float* dh0, void* ws, size_t ws_bytes) {
+                 const void* Cm, const float* Dv, const float* h0, void* y, float* ckpt,
+                 float* h_last, void* ws, size_t ws_bytes) {
+  return ssm_scan_fwd_every(stream, dtype, B, L, D, N, x, delta, A, Bm, Cm, Dv, h0, y, ckpt,
+                            h_last, 0, ws, ws_bytes);
+}
+
+int ssm_scan_bwd_every(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D,
+                       int64_t N, const void* x, const void* delta, const float* A,
+                       const void* Bm, const void* Cm, const float* Dv, const float* h0,
+                       const void* dy, const float* ckpt, void* dx, void* ddelta, float* dA,
+                       float* dB, float* dC, float* dD, float* dh0, int64_t ck_every,
+                       int64_t slabs, void* ws, size_t ws_bytes) {
   int rc = check_scan_dims(dtype, B, L, D, N);
   if (rc) return rc;
+  if ((rc = check_ckpt_every(N, ck_every, slabs))) return rc;
   rc = check_ptrs({{x, "x"}, {delta, "delta"}, {A, "A"}, {Bm, "Bm"}, {Cm, "Cm"}, {Dv, "Dv"},
                    {dy, "dy"}, {dx, "dx"}, {ddelta, "ddelta"}, {dA, "dA"}, {dB, "dB"},
                    {dC, "dC"}, {dD, "dD"}},
@@ -353,9 +428,9 @@ int ssm_scan_bwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t 
   ssm::BwdPlan p{};
   ssm::FwdPlan fp{};
   float* own_ckpt = nullptr;
-  const size_t need = bwd_ws(B, L, D, N, with_ckpt, &p, &own_ckpt, &fp, nullptr);
+  const size_t need = bwd_ws(B, L, D, N, with_ckpt, ck_every, slabs, &p, &own_ckpt, &fp, nullptr);
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
-  bwd_ws(B, L, D, N, with_ckpt, &p, &own_ckpt, &fp, ws);
+  bwd_ws(B, L, D, N, with_ckpt, ck_every, slabs, &p, &own_ckpt, &fp, ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
   ssm::ScanArgs a{};
   a.dtype = int(dtype);
@@ -367,16 +442,25 @@ int ssm_scan_bwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t 
   if (with_ckpt) {
     p.ckpt = ckpt;
   } else {
-    // recompute the forward's checkpoints (y is not needed)
+    // recompute the forward's checkpoints (at the same interval; y is not needed)
     fp.ckpt = own_ckpt;
     ssm::ScanArgs f = a;
     f.y = nullptr;
     f.h_last = nullptr;
-      hipError_t e = ssm::launch_scan_fwd(f, fp, st);
+    hipError_t e = ssm::launch_scan_fwd(f, fp, st);
     if (e != hipSuccess) return hip_status(e, "ssm_scan_bwd (forward recompute)");
     p.ckpt = own_ckpt;
   }
   return hip_status(ssm::launch_scan_bwd(a, p, st), "ssm_scan_bwd");
+}
+
+int ssm_scan_bwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D, int64_t N,
+                 const void* x, const void* delta, const float* A, const void* Bm,
+                 const void* Cm, const float* Dv, const float* h0, const void* dy,
+                 const float* ckpt, void* dx, void* ddelta, float* dA, float* dB, float* dC,
+                 float* dD, float* dh0, void* ws, size_t ws_bytes) {
+  return ssm_scan_bwd_every(stream, dtype, B, L, D, N, x, delta, A, Bm, Cm, Dv, h0, dy, ckpt,
+                            dx, ddelta, dA, dB, dC, dD, dh0, 0, 1, ws, ws_bytes);
 }
 
 int ssm_scan_fused_fwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D,
@@ -395,9 +479,9 @@ int ssm_scan_fused_fwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, in
     return fail(SSM_ERR_ARG, "delta_softplus must be 0 or 1 (got %d)", delta_softplus);
   if (y_save && !z) return fail(SSM_ERR_ARG, "y_save is only written with the gate input z");
   ssm::FwdPlan p{};
-  const size_t need = fwd_ws(B, L, D, N, &p, nullptr);
+  const size_t need = fwd_ws(B, L, D, N, 0, &p, nullptr);
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
-  fwd_ws(B, L, D, N, &p, ws);
+  fwd_ws(B, L, D, N, 0, &p, ws);
   p.ckpt = ckpt;
   ssm::ScanArgs a{};
   a.dtype = int(dtype);
@@ -437,9 +521,9 @@ int ssm_scan_fused_bwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, in
   ssm::BwdPlan p{};
   ssm::FwdPlan fp{};
   float* own_ckpt = nullptr;
-  const size_t need = bwd_ws(B, L, D, N, with_ckpt, &p, &own_ckpt, &fp, nullptr);
+  const size_t need = bwd_ws(B, L, D, N, with_ckpt, 0, 1, &p, &own_ckpt, &fp, nullptr);
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
-  bwd_ws(B, L, D, N, with_ckpt, &p, &own_ckpt, &fp, ws);
+  bwd_ws(B, L, D, N, with_ckpt, 0, 1, &p, &own_ckpt, &fp, ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
   ssm::ScanArgs a{};
   a.dtype = int(dtype);

@@ -34,10 +34,14 @@ constexpr int64_t kMaxGridX = 0x7fffffff;
 // Tile length of the scan kernels (steps staged through LDS at a time).
 constexpr int kTc = 16;
 
-// Checkpoints per tile: the forward saves the state before every (kTc / ckpt_per_tile)-th
-// step for the backward.  At N = 16 the backward stashes half a tile at a time (its
-// register budget), so it needs the state at mid-tile too.
+// Checkpoints per tile: the backward recomputes states from the state before every
+// (kTc / ckpt_per_tile)-th step (the dense interval, ckpt_base).  At N = 16 the backward
+// stashes half a tile at a time (its register budget), so it needs the state at mid-tile
+// too.  The forward saves the states at the dense interval by default, or every
+// ck_every steps (a multiple of kTc); the backward then regenerates the dense states of
+// one slab of chunks at a time (k_ckpt_regen) before its main pass over that slab.
 constexpr int ckpt_per_tile(int64_t N) { return N == 16 ? 2 : 1; }
+constexpr int64_t ckpt_base(int64_t N) { return kTc / ckpt_per_tile(N); }
 
 // Chunk summaries the carry kernels load ahead of their sequential composition.
 constexpr int kCarryAhead = 16;
@@ -83,10 +87,15 @@ struct Chunking {
 };
 
 // Chunk c of nc covers the tiles [chunk_tile(c), chunk_tile(c + 1)) of the nf tiles of
-// the sequence: an even split, chunk lengths differing by at most one tile.  Only the
-// last chunk can hold the sequence's partial tile, so chunks 0..nc-2 are full.
-__host__ __device__ __forceinline__ int64_t chunk_tile(int64_t c, int64_t nf, int64_t nc) {
-  return c * nf / nc;
+// the sequence: an even split of units of g tiles (chunk lengths differing by at most
+// one unit; the last unit may be short), so every chunk boundary is a multiple of g
+// tiles.  Only the last chunk can hold the sequence's partial tile, so chunks 0..nc-2
+// are full.  nc must not exceed the unit count.
+__host__ __device__ __forceinline__ int64_t chunk_tile(int64_t c, int64_t nf, int64_t nc,
+                                                      int64_t g) {
+  const int64_t nu = (nf + g - 1) / g;
+  const int64_t t = g * (c * nu / nc);
+  return t < nf ? t : nf;
 }
 
 // Position of a scan workgroup in its 1-D grid: the channel group varies fastest, then
@@ -105,7 +114,8 @@ __device__ __forceinline__ WgPos wg_pos(int64_t groups, int64_t B) {
 struct FwdPlan {
   int nc;
   int64_t nf;
-  int64_t nck;  // number of checkpoints, ceil(L / (kTc / ckpt_per_tile(N)))
+  int64_t ck_every;  // steps between saved states: ckpt_base(N) or a multiple of kTc
+  int64_t nck;       // number of saved states, ceil(L / ck_every)
   float* S;     // [B][nc][D][N]   (nc > 1)
   float* SD;    // [B][nc][D]      (nc > 1)
   float* hin;   // [B][nc][D][N]   (nc > 1)
@@ -115,8 +125,16 @@ struct FwdPlan {
 struct BwdPlan {
   int nc;
   int64_t nf, ng;
+  int64_t g;          // chunk granularity in tiles (sparse checkpoints: every / kTc)
   int64_t nck;        // number of checkpoints
   const float* ckpt;  // [B][nck][D][N]
+  // sparse checkpoints (ck_every > ckpt_base(N)): the dense states of one slab of
+  // slab_chunks chunks at a time are regenerated into ckd ([B][nckd][D][N], the slab's
+  // states from its first step on) before the main pass over the slab
+  int64_t ck_every;
+  int slab_chunks;    // 0: dense checkpoints given, one main pass over every chunk
+  float* ckd;
+  int64_t nckd;
   float* GS;          // [B][nc][D][N]  (nc > 1)
   float* SD;          // [B][nc][D]     (nc > 1)
   float* gin;         // [B][nc][D][N]  (nc > 1)
@@ -184,7 +202,8 @@ enum KernelId {
   kKScanStep = 11,
   kKConvStep = 12,
   kKDecodeStep = 13,
-  kKNumIds = 14
+  kKCkptRegen = 14,
+  kKNumIds = 15
 };
 
 // Records the caller's event for kernel `id` on stream st (stop = false: before the

@@ -41,7 +41,7 @@ namespace ssm {
 // dy * silu(z) is formed at staging.
 template <typename T, int N, int VEC, bool FZ>
 __global__ __launch_bounds__(256, 4) void k_bwd_summary(
-    int64_t B, int64_t L, int64_t D, int64_t nf, int nc, int64_t groups,
+    int64_t B, int64_t L, int64_t D, int64_t nf, int nc, int64_t g, int64_t groups,
     const T* __restrict__ delta, const float* __restrict__ A, const T* __restrict__ Cm,
     const T* __restrict__ dy, const float* __restrict__ dtb, bool sp, const T* __restrict__ z,
     float* __restrict__ GS, float* __restrict__ SD) {
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256, 4) void k_bwd_summary(
   // running sums of the delta this thread stages (ChTile placement): the chunk's sum of
   // delta, accumulated once per value instead of in each of a channel's lanes per step
   float dsum[VEC] = {};
-  const int64_t t0 = chunk_tile(c, nf, nc) * kTc, te = chunk_tile(c + 1, nf, nc) * kTc;
+  const int64_t t0 = chunk_tile(c, nf, nc, g) * kTc, te = chunk_tile(c + 1, nf, nc, g) * kTc;
   const int64_t t1 = te < L ? te : L;
   const int ntile = int((t1 - t0 + kTc - 1) / kTc);
   // tiles are walked from the last one backwards
@@ -194,6 +194,94 @@ __global__ __launch_bounds__(256) void k_bwd_carry(
   }
 }
 
+// Regeneration of dense states for the sparse-checkpoint backward: workgroup (channel
+// group, batch row, run) runs the segments k = k0 + run*nrun .. (at most nrun of them,
+// below k1), each the steps [k*ck_every, min((k+1)*ck_every, L)) from the state the
+// forward saved before its first step (cks: [B][nck_s][D][N]), and stores the state
+// before every CK-th step (CK = ckpt_base(N), the dense interval the main pass
+// recomputes from) into ckd, whose batch rows hold nckd states from state index f0 on.
+// The recurrence is the forward's (the tile's x staged as u = delta * x); rows past L
+// are zero, the identity step.
+template <typename T, int N, int VEC>
+__global__ __launch_bounds__(256, 4) void k_ckpt_regen(
+    int64_t B, int64_t L, int64_t D, int64_t groups, int64_t ck_every, int64_t k0,
+    int64_t k1, int nrun, const T* __restrict__ x, const T* __restrict__ delta,
+    const float* __restrict__ A, const T* __restrict__ Bm, const float* __restrict__ cks,
+    int64_t nck_s, float* __restrict__ ckd, int64_t nckd, int64_t f0) {
+  constexpr int NS = N / 4;
+  constexpr int CK = int(ckpt_base(N));
+  __shared__ float sx[2][kTc][kTileCh], sd[2][kTc][kTileCh], sB[2][kTc][N];
+  const WgPos wp = wg_pos(groups, B);
+  const int64_t kr = k0 + wp.c * nrun, kre = kr + nrun < k1 ? kr + nrun : k1, b = wp.b;
+  const int tid = threadIdx.x, q = tid & 3, cl = tid >> 2;
+  const int64_t d0 = wp.grp * kTileCh, d = d0 + cl;
+  const bool act = d < D;
+  const int D32 = int(D);
+  const int dvalid = (D - d0 < kTileCh) ? int(D - d0) : kTileCh;
+  const T* xb = x + b * L * D + d0;
+  const T* db = delta + b * L * D + d0;
+  const T* Bb = Bm + b * L * N;
+  float A2[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) A2[j] = act ? A[d * N + q * NS + j] * kLog2e : 0.f;
+  const uint32_t ckoff = act ? uint32_t(cl * N + q * NS) * 4u : kOffNone;
+  const uint32_t ckbytes = uint32_t(dvalid * N) * 4u;
+  float h[NS];
+  float* ckg = ckd + (b * nckd * D + d0) * N;
+  const float* ckr = cks + (b * nck_s * D + d0) * N;
+  const int64_t t0 = kr * ck_every, te = kre * ck_every, t1 = te < L ? te : L;
+  const int ntile = int((t1 - t0 + kTc - 1) / kTc);
+  const int seg_tiles = int(ck_every / kTc);
+  const ChTile<T, VEC> gt(D32, dvalid, tid);
+  const uint32_t voff = VecFetch<T, N>::offset(tid);
+  ChFetch<T, VEC> fx, fd;
+  VecFetch<T, N> fB;
+  auto fetch = [&](int64_t tt) {
+    const int tv = clamp_valid(L - tt);
+    fx.fetch(gt, xb + tt * D, D32, tv, dvalid);
+    fd.fetch(gt, db + tt * D, D32, tv, dvalid);
+    fB.fetch(Bb + tt * N, tv, voff);
+  };
+  auto commit = [&](int bf) {
+    fd.commit(gt, sd[bf]);
+    fx.commit_map(gt, sx[bf], [&](int kk, float (&v)[VEC]) {
+      const float* dv = &sd[bf][gt.s_in + kk * ChTile<T, VEC>::RPP][gt.c];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) v[i] *= dv[i];
+    });
+    fB.commit(sB[bf], tid);
+  };
+  fetch(t0);
+  commit(0);
+  __syncthreads();
+  for (int it = 0; it < ntile; ++it) {
+    const int buf = it & 1;
+    const int64_t tf = t0 + int64_t(it) * kTc;
+    if (it + 1 < ntile) fetch(tf + kTc);
+    // each segment starts from the state the forward saved before it
+    if (it % seg_tiles == 0)
+      buf_load_states<NS>(buf_rsrc(ckr + (kr + it / seg_tiles) * D * N, ckbytes), ckoff, h);
+#pragma unroll
+    for (int part = 0; part < kTc / CK; ++part) {
+      const int64_t ts = tf + part * CK;
+      if (ts < L) buf_store_states<NS>(h, buf_rsrc(ckg + (ts / CK - f0) * D * N, ckbytes), ckoff);
+#pragma unroll 4
+      for (int s = part * CK; s < (part + 1) * CK; ++s) {
+        const float dl = sd[buf][s][cl], u = sx[buf][s][cl];
+        float Bv[NS];
+        tile_read_vec<N, NS>(sB[buf], s, q, Bv);
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          const float a = __builtin_amdgcn_exp2f(dl * A2[j]);
+          h[j] = __builtin_fmaf(a, h[j], u * Bv[j]);
+        }
+      }
+    }
+    if (it + 1 < ntile) commit(buf ^ 1);
+    __syncthreads();
+  }
+}
+
 // Main backward pass: one chunk of one batch row for 64 channels.  Tiles of kTc steps
 // are walked from the last one backwards.  A tile holds SPLIT checkpoint intervals
 // (SPLIT = ckpt_per_tile(N)); from the last interval to the first, the states of the
@@ -215,8 +303,8 @@ __global__ __launch_bounds__(256) void k_bwd_carry(
 // previous tile's compute, so their registers are not held across it.
 template <typename T, int N, int VEC, int SPLIT, int WAVES, bool FZ>
 __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
-    int64_t B, int64_t L, int64_t D, int64_t nf, int nc, int64_t groups, int64_t nck,
-    const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
+    int64_t B, int64_t L, int64_t D, int64_t nf, int nc, int64_t g, int64_t groups, int c_off,
+    int64_t nck, int64_t f0, const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dv,
     const T* __restrict__ dy, const float* __restrict__ ckpt, const float* __restrict__ gin,
     const float* __restrict__ dtb, bool sp, const T* __restrict__ z,
@@ -246,7 +334,7 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
   __shared__ float sdb[FZ ? kTileThreads * VEC : 1];
 
   const WgPos wp = wg_pos(groups, B);
-  const int64_t c = wp.c, b = wp.b, grp = wp.grp;
+  const int64_t c = wp.c + c_off, b = wp.b, grp = wp.grp;  // this launch's chunks from c_off
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = tid & 3, cl = tid >> 2;
   const int64_t d0 = grp * kTileCh, d = d0 + cl;
   const bool act = d < D;
@@ -262,7 +350,8 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
   const T* Cb = Cm + int64_t(b) * L * N;
   T* dxb = dx + int64_t(b) * L * D + d0;
   T* ddb = ddelta + int64_t(b) * L * D + d0;
-  // checkpoint f of this group: ckpt + ((b*nck + f)*D + d0)*N, lane at (cl*N + Qs*NS)
+  // checkpoint f (the state before step f*SL) of this group: ckpt + ((b*nck + f - f0)*D +
+  // d0)*N, lane at (cl*N + Qs*NS); the buffer holds the states from index f0 on
   const float* ckg = ckpt + (int64_t(b) * nck * D + d0) * N;
   const uint32_t ckoff = act ? uint32_t(cl * N + Qs * NS) * 4u : kOffNone;
   const uint32_t ckbytes = uint32_t(dvalid * N) * 4u;
@@ -279,7 +368,7 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
   const float Dd = act ? Dv[d] : 0.f;
   float dD_acc = 0.f;
 
-  const int64_t t0 = chunk_tile(c, nf, nc) * kTc, te = chunk_tile(c + 1, nf, nc) * kTc;
+  const int64_t t0 = chunk_tile(c, nf, nc, g) * kTc, te = chunk_tile(c + 1, nf, nc, g) * kTc;
   const int64_t t1 = te < L ? te : L;
   const int ntile = int((t1 - t0 + kTc - 1) / kTc);
 
@@ -315,7 +404,7 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
 #pragma unroll
     for (int hf = 0; hf < SPLIT; ++hf) {
       const bool has = tvalid > 0 && (hf == 0 || tt + hf * SL < L);
-      const auto rs = buf_rsrc(ckg + (has ? tt / SL + hf : 0) * D * N, has ? ckbytes : 0u);
+      const auto rs = buf_rsrc(ckg + (has ? tt / SL + hf - f0 : 0) * D * N, has ? ckbytes : 0u);
       if constexpr (PERM) buf_load_states_perm(rs, ckoff, ms, hk[hf]);
       else buf_load_states<NS>(rs, ckoff, hk[hf]);
     }
@@ -579,6 +668,9 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
   }
 }
 
+// Steps a regeneration workgroup covers at least (runs of short checkpoint intervals).
+constexpr int64_t kRegenSteps = 128;
+
 // Waves per SIMD of k_bwd_main.  Its LDS (41-45 KB) admits three workgroups per CU; at
 // N = 16 a full-tile stash does not fit the register budget of three waves per SIMD, a
 // half-tile one does, hence the mid-tile checkpoints at N = 16 (ckpt_per_tile).
@@ -604,8 +696,8 @@ static hipError_t bwd_impl(const ScanArgs& a, const BwdPlan& p, hipStream_t st) 
   if (p.nc > 1) {
     timer_mark(kKBwdSummary, false, st);
     e = launch(k_bwd_summary<T, N, VEC, FZ>, dim3(unsigned(p.ng * a.B * (p.nc - 1))), block, st,
-               a.B, a.L, a.D, p.nf, p.nc, p.ng, delta, a.A, Cm, dy, a.dt_bias, a.dt_softplus,
-               static_cast<const T*>(a.z), p.GS, p.SD);
+               a.B, a.L, a.D, p.nf, p.nc, p.g, p.ng, delta, a.A, Cm, dy, a.dt_bias,
+               a.dt_softplus, static_cast<const T*>(a.z), p.GS, p.SD);
     timer_mark(kKBwdSummary, true, st);
     if (e != hipSuccess) return e;
     const int64_t tot = a.B * a.D * N;
@@ -616,16 +708,43 @@ static hipError_t bwd_impl(const ScanArgs& a, const BwdPlan& p, hipStream_t st) 
     if (e != hipSuccess) return e;
     gin = p.gin;
   }
-  timer_mark(kKBwdMain, false, st);
   using Cfg = BwdMainCfg<N>;
-  e = launch(k_bwd_main<T, N, VEC, Cfg::kSplit, Cfg::kWaves, FZ>,
-             dim3(unsigned(p.ng * a.B * p.nc)), block, st, a.B, a.L, a.D, p.nf, p.nc, p.ng,
-             p.nck, x, delta, a.A, Bm, Cm, a.Dv, dy, p.ckpt, gin, a.dt_bias, a.dt_softplus,
-             static_cast<const T*>(a.z), static_cast<const T*>(a.ysave), static_cast<T*>(a.dx),
-             static_cast<T*>(a.ddelta), static_cast<T*>(a.dz), p.dBp, p.dCp, p.dAp, p.dDp,
-             a.ddt_bias ? p.dbp : nullptr, a.dh0);
-  timer_mark(kKBwdMain, true, st);
-  if (e != hipSuccess) return e;
+  // the main pass over chunks [c0, c1) with the dense states in ck (batch rows of nck
+  // states from index f0 on)
+  auto main_pass = [&](int c0, int c1, const float* ck, int64_t nck, int64_t f0) {
+    timer_mark(kKBwdMain, false, st);
+    const hipError_t r = launch(
+        k_bwd_main<T, N, VEC, Cfg::kSplit, Cfg::kWaves, FZ>, dim3(unsigned(p.ng * a.B * (c1 - c0))),
+        block, st, a.B, a.L, a.D, p.nf, p.nc, p.g, p.ng, c0, nck, f0, x, delta, a.A, Bm, Cm, a.Dv,
+        dy, ck, gin, a.dt_bias, a.dt_softplus, static_cast<const T*>(a.z),
+        static_cast<const T*>(a.ysave), static_cast<T*>(a.dx), static_cast<T*>(a.ddelta),
+        static_cast<T*>(a.dz), p.dBp, p.dCp, p.dAp, p.dDp, a.ddt_bias ? p.dbp : nullptr, a.dh0);
+    timer_mark(kKBwdMain, true, st);
+    return r;
+  };
+  if (p.slab_chunks == 0) {
+    if ((e = main_pass(0, p.nc, p.ckpt, p.nck, 0)) != hipSuccess) return e;
+  } else {
+    // sparse checkpoints: slab by slab, regenerate the dense states, then the main pass
+    // (the timing hook sees each kernel's last launch)
+    constexpr int64_t CK = ckpt_base(N);
+    for (int c0 = 0; c0 < p.nc; c0 += p.slab_chunks) {
+      const int c1 = c0 + p.slab_chunks < p.nc ? c0 + p.slab_chunks : p.nc;
+      const int64_t ts = chunk_tile(c0, p.nf, p.nc, p.g) * kTc;
+      const int64_t te0 = chunk_tile(c1, p.nf, p.nc, p.g) * kTc, te = te0 < a.L ? te0 : a.L;
+      const int64_t k0 = ts / p.ck_every, nseg = (te - ts + p.ck_every - 1) / p.ck_every;
+      // a workgroup regenerates runs of consecutive intervals, about kRegenSteps steps
+      const int nrun = int(p.ck_every >= kRegenSteps ? 1 : kRegenSteps / p.ck_every);
+      const int64_t nruns = (nseg + nrun - 1) / nrun;
+      timer_mark(kKCkptRegen, false, st);
+      e = launch(k_ckpt_regen<T, N, VEC>, dim3(unsigned(p.ng * a.B * nruns)), block, st, a.B,
+                 a.L, a.D, p.ng, p.ck_every, k0, k0 + nseg, nrun, x, delta, a.A, Bm, p.ckpt, p.nck,
+                 p.ckd, p.nckd, ts / CK);
+      timer_mark(kKCkptRegen, true, st);
+      if (e != hipSuccess) return e;
+      if ((e = main_pass(c0, c1, p.ckd, p.nckd, ts / CK)) != hipSuccess) return e;
+    }
+  }
   const int64_t BLN = a.B * a.L * N;
   if ((e = launch_reduce(p.dBp, p.ng, BLN, a.dB, false, p.rtmp, st)) != hipSuccess) return e;
   if ((e = launch_reduce(p.dCp, p.ng, BLN, a.dC, false, p.rtmp, st)) != hipSuccess) return e;

@@ -58,8 +58,8 @@ __global__ __launch_bounds__(256, 4) void k_fwd_summary(
   }
   float dsum[VEC] = {};  // running sums of the delta this thread stages (ChTile placement)
   // chunks 0..nc-2 are full
-  const int64_t t0 = chunk_tile(c, nf, nc) * kTc;
-  const int ntile = int(chunk_tile(c + 1, nf, nc) - chunk_tile(c, nf, nc));
+  const int64_t t0 = chunk_tile(c, nf, nc, 1) * kTc;
+  const int ntile = int(chunk_tile(c + 1, nf, nc, 1) - chunk_tile(c, nf, nc, 1));
   const ChTile<T, VEC> gt(D32, dvalid, tid);
   const uint32_t voff = VecFetch<T, N>::offset(tid);
   ChFetch<T, VEC> fx, fd;
@@ -166,7 +166,8 @@ __global__ __launch_bounds__(256) void k_fwd_carry(
 
 // hin: start state of each chunk, [B][nc][D][N]; may be null (zero start).
 // y (nullable: only the checkpoints are wanted); ckpt (nullable): [B][nck][D][N],
-// the state before step f*CK, CK = kTc / ckpt_per_tile(N).  y of a step overwrites the step's x in LDS (a
+// the state before step f*ck_every (ck_every: ckpt_base(N), or a multiple of kTc for
+// sparse checkpoints).  y of a step overwrites the step's x in LDS (a
 // channel's slots are read and written only by its four lanes, reads first) and is
 // stored after the tile; two barriers per tile: after the compute (y complete) and
 // after the next tile's inputs are committed.
@@ -175,9 +176,10 @@ __global__ __launch_bounds__(256) void k_fwd_carry(
 template <typename T, int N, int VEC, bool FZ>
 __global__ __launch_bounds__(256, kFwdOutputWaves) void k_fwd_output(
     int64_t B, int64_t L, int64_t D, int64_t nf, int nc, int64_t groups, int64_t nck,
-    const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
-    const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dv,
-    const float* __restrict__ hin, const float* __restrict__ dtb, bool sp,
+    int64_t ck_every, const T* __restrict__ x, const T* __restrict__ delta,
+    const float* __restrict__ A, const T* __restrict__ Bm, const T* __restrict__ Cm,
+    const float* __restrict__ Dv, const float* __restrict__ hin, const float* __restrict__ dtb,
+    bool sp,
     const T* __restrict__ z, T* __restrict__ y, T* __restrict__ ysave,
     float* __restrict__ ckpt, float* __restrict__ h_last) {
   constexpr int NS = N / 4;
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(256, kFwdOutputWaves) void k_fwd_output(
   zero(h);
   if (hin)
     buf_load_states<NS>(buf_rsrc(hin + ((b * nc + c) * D + d0) * N, ckbytes), ckoff, h);
-  const int64_t t0 = chunk_tile(c, nf, nc) * kTc, te = chunk_tile(c + 1, nf, nc) * kTc;
+  const int64_t t0 = chunk_tile(c, nf, nc, 1) * kTc, te = chunk_tile(c + 1, nf, nc, 1) * kTc;
   const int64_t t1 = te < L ? te : L;
   const int ntile = int((t1 - t0 + kTc - 1) / kTc);
   const ChTile<T, VEC> gt(D32, dvalid, tid);
@@ -244,6 +246,8 @@ __global__ __launch_bounds__(256, kFwdOutputWaves) void k_fwd_output(
     fB.commit(sB[bf], tid);
     fC.commit(sC[bf], tid);
   };
+  // the first sparse checkpoint position at or after the chunk's start, and its index
+  int64_t ck_idx = (t0 + ck_every - 1) / ck_every, ck_next = ck_idx * ck_every;
   if constexpr (FZ) __syncthreads();  // sbias
   fetch(t0);
   commit(0);
@@ -252,7 +256,17 @@ __global__ __launch_bounds__(256, kFwdOutputWaves) void k_fwd_output(
   for (int it = 0; it < ntile; ++it) {
     const int buf = it & 1;
     const int64_t tf = t0 + int64_t(it) * kTc;
-    if (ckg) buf_store_states<NS>(h, buf_rsrc(ckg + (tf / CK) * D * N, ckbytes), ckoff);
+    // (ck_every is CK -- every tile start, and mid-tile below -- or a multiple of kTc,
+    // whose positions are tile starts counted by ck_next; the conditions are uniform)
+    if (ckg) {
+      if (ck_every == CK) {
+        buf_store_states<NS>(h, buf_rsrc(ckg + (tf / CK) * D * N, ckbytes), ckoff);
+      } else if (tf == ck_next) {
+        buf_store_states<NS>(h, buf_rsrc(ckg + ck_idx * D * N, ckbytes), ckoff);
+        ck_next += ck_every;
+        ++ck_idx;
+      }
+    }
     // the gate input of this tile, used at its store
     if (FZ && zb) fz.fetch(gt, zb + tf * D, D32, clamp_valid(L - tf), dvalid);
     // the LDS operands of step s+1 are read during step s
@@ -284,7 +298,8 @@ __global__ __launch_bounds__(256, kFwdOutputWaves) void k_fwd_output(
       }
       yp = quad_sum(yp);  // identical in the channel's four lanes, which all write it
       sx[buf][s][cl] = __builtin_fmaf(Dd, xv, yp);  // y
-      if (CK < kTc && s % CK == CK - 1 && s + 1 < kTc && ckg && tf + s + 1 < L)  // mid-tile
+      if (CK < kTc && s % CK == CK - 1 && s + 1 < kTc && ckg && tf + s + 1 < L &&
+          ck_every == CK)  // mid-tile
         buf_store_states<NS>(h, buf_rsrc(ckg + ((tf + s + 1) / CK) * D * N, ckbytes), ckoff);
       step_fence_arr(h);
       step_fence_arr(nB);
@@ -349,7 +364,8 @@ static hipError_t fwd_impl(const ScanArgs& a, const FwdPlan& p, hipStream_t st) 
   }
   timer_mark(kKFwdOutput, false, st);
   e = launch(k_fwd_output<T, N, VEC, FZ>, dim3(unsigned(groups * a.B * p.nc)), block, st, a.B,
-             a.L, a.D, p.nf, p.nc, groups, p.nck, x, delta, a.A, Bm, Cm, a.Dv, hin, a.dt_bias,
+             a.L, a.D, p.nf, p.nc, groups, p.nck, p.ck_every, x, delta, a.A, Bm, Cm, a.Dv, hin,
+             a.dt_bias,
              a.dt_softplus, static_cast<const T*>(a.z), static_cast<T*>(a.y),
              static_cast<T*>(a.ysave), p.ckpt, a.h_last);
   timer_mark(kKFwdOutput, true, st);

@@ -434,3 +434,56 @@ def test_no_oracle_in_product_sources():
                 assert "liboracle" not in src, f
     csrc = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
     assert "ssm_scan.h" not in csrc and "common.hpp" not in csrc
+
+
+def _fwd_every(lib, every, B=2, L=64, D=32, N=16, ckpt=FAKE, **kw):
+    p = dict(x=FAKE, delta=FAKE, A=FAKE, Bm=FAKE, Cm=FAKE, Dv=FAKE, h0=None, y=FAKE, h_last=None)
+    p.update(kw)
+    return lib.ssm_scan_fwd_every(None, 0, B, L, D, N, p["x"], p["delta"], p["A"], p["Bm"],
+                                  p["Cm"], p["Dv"], p["h0"], p["y"], ckpt, p["h_last"], every,
+                                  None, 0)
+
+
+def _bwd_every(lib, every, slabs, B=2, L=64, D=32, N=16, ckpt=FAKE, ws=None, ws_bytes=0, **kw):
+    p = dict(x=FAKE, delta=FAKE, A=FAKE, Bm=FAKE, Cm=FAKE, Dv=FAKE, h0=None, dy=FAKE,
+             dx=FAKE, ddelta=FAKE, dA=FAKE, dB=FAKE, dC=FAKE, dD=FAKE, dh0=None)
+    p.update(kw)
+    return lib.ssm_scan_bwd_every(None, 0, B, L, D, N, p["x"], p["delta"], p["A"], p["Bm"],
+                                  p["Cm"], p["Dv"], p["h0"], p["dy"], ckpt, p["dx"],
+                                  p["ddelta"], p["dA"], p["dB"], p["dC"], p["dD"], p["dh0"],
+                                  every, slabs, ws, ws_bytes)
+
+
+@pytest.mark.parametrize("every,N", [(-16, 16), (24, 16), (8, 4), (8, 8), (4, 16), (17, 16)])
+def test_checkpoint_interval_validation(every, N):
+    # the interval is 0 (default), the default itself, or a positive multiple of 16 steps
+    lib = b.load()
+    assert _fwd_every(lib, every, N=N) == b.SSM_ERR_ARG
+    assert "checkpoint interval" in b.last_error()
+    assert _bwd_every(lib, every, 1, N=N) == b.SSM_ERR_ARG
+    assert b.ssm_scan_ckpt_bytes_every(2, 64, 32, N, every) == 0
+    assert b.ssm_scan_bwd_workspace_bytes_every(2, 64, 32, N, 0, 1, every, 1) == 0
+
+
+def test_checkpoint_interval_slabs_and_sizes():
+    lib = b.load()
+    assert _bwd_every(lib, 64, 0) == b.SSM_ERR_ARG
+    assert "slabs" in b.last_error()
+    assert b.ssm_scan_bwd_workspace_bytes_every(2, 64, 32, 16, 0, 1, 64, 0) == 0
+    # the default interval through the new entry points is the plain call's plan
+    assert b.ssm_scan_ckpt_bytes_every(2, 1000, 32, 16, 0) == b.ssm_scan_ckpt_bytes(2, 1000, 32, 16)
+    assert b.ssm_scan_ckpt_bytes_every(2, 1000, 32, 16, 8) == b.ssm_scan_ckpt_bytes(2, 1000, 32, 16)
+    assert b.ssm_scan_bwd_workspace_bytes_every(2, 1000, 32, 16, 0, 1, 0, 1) == \
+        b.ssm_scan_bwd_workspace_bytes(2, 1000, 32, 16, 0, 1)
+    # checkpoints shrink with the interval; the backward's workspace holds one slab's
+    # regenerated states, so more slabs take less of it
+    B, L, D, N = 2, 16384, 5120, 16
+    dense = b.ssm_scan_ckpt_bytes(B, L, D, N)
+    for every in (16, 64, 512):
+        assert b.ssm_scan_ckpt_bytes_every(B, L, D, N, every) * (every // 8) == dense
+    w1 = b.ssm_scan_bwd_workspace_bytes_every(B, L, D, N, 1, 1, 64, 1)
+    w8 = b.ssm_scan_bwd_workspace_bytes_every(B, L, D, N, 1, 1, 64, 8)
+    assert w8 < w1
+    # a too-small workspace is refused before any launch
+    assert _bwd_every(lib, 64, 8, B=B, L=L, D=D, N=N, ws=FAKE, ws_bytes=w8 - 1) == \
+        b.SSM_ERR_WORKSPACE
