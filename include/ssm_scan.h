@@ -274,6 +274,22 @@ size_t rmsnorm_bwd_workspace_bytes(int64_t R, int64_t M, ssm_dtype_t dtype);
 int rmsnorm_bwd(void *stream, ssm_dtype_t dtype, int64_t R, int64_t M, const void *dy,
                 const void *x, const float *scale, const float *rms, void *dx,
                 float *dscale, void *ws, size_t ws_bytes);
+
+/* rmsnorm_bwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops, harnesses that forbid hipMalloc.  Same operation, arguments
+ * and results as rmsnorm_bwd (bit for bit), without a workspace: its scratch (block
+ * partials of dscale, reduction temporaries, per-row coefficients) lives in a static
+ * device array of 16 MiB, one per GPU, held until the process ends.  The call allocates
+ * nothing (no hipMalloc, no hipFree).  It uses the current device's array: `stream`
+ * must belong to the current device.  Calls on one GPU share its array, so calls whose
+ * work overlaps on one GPU (other threads, other streams) race; serialize them.
+ * Returns SSM_ERR_UNSUPPORTED when the plan's scratch exceeds 16 MiB (about
+ * 512 x M + R floats: M up to about 8000 for long batches), SSM_ERR_HIP if the array's
+ * address cannot be taken; otherwise as rmsnorm_bwd. */
+int rmsnorm_bwd_noalloc(void *stream, ssm_dtype_t dtype, int64_t R, int64_t M,
+                        const void *dy, const void *x, const float *scale, const float *rms,
+                        void *dx, float *dscale);
+
 /* ---------------------------------------------------------------------------------
  * Depthwise causal conv1d forward, the forward of conv1d_causal_bwd above (the window
  * of the mamba-rs backward_conv1d_step section holds the last K inputs, tap K-1 the

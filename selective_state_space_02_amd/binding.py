@@ -27,7 +27,7 @@ EXPORTS = ("ssm_last_error", "ssm_version", "ssm_set_kernel_timer", "ssm_scan_ck
            "ssm_scan_step", "conv1d_causal_step", "ssm_scan_fused_fwd", "ssm_scan_fused_bwd",
            "ssm_scan_fused_step", "ssm_decode_step", "ssm_scan_chunks",
            "ssm_scan_ckpt_bytes_every", "ssm_scan_bwd_workspace_bytes_every",
-           "ssm_scan_fwd_every", "ssm_scan_bwd_every")
+           "ssm_scan_fwd_every", "ssm_scan_bwd_every", "rmsnorm_bwd_noalloc")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -94,6 +94,8 @@ def load():
     lib.rmsnorm_bwd_workspace_bytes.argtypes = [_I] * 2 + [_E]
     lib.rmsnorm_bwd.restype = _E
     lib.rmsnorm_bwd.argtypes = [_P, _E] + [_I] * 2 + [_P] * 6 + [_P, _S]
+    lib.rmsnorm_bwd_noalloc.restype = _E
+    lib.rmsnorm_bwd_noalloc.argtypes = [_P, _E] + [_I] * 2 + [_P] * 6
     lib.conv1d_causal_fwd.restype = _E
     lib.conv1d_causal_fwd.argtypes = [_P, _E] + [_I] * 4 + [_P] * 3 + [_E, _P]
     lib.rmsnorm_fwd.restype = _E
@@ -458,6 +460,23 @@ def rmsnorm_bwd(dy, x, scale, rms, dx=None, dscale=None, ws=None):
     ws, nbytes = _workspace(need, dev, ws)
     _check(lib.rmsnorm_bwd(_stream(dev), code, R, M, *args,
                            _ptr(ws, "ws") if ws is not None else None, nbytes))
+    return dict(dx=dx, dscale=dscale)
+
+
+def rmsnorm_bwd_noalloc(dy, x, scale, rms, dx, dscale):
+    """rmsnorm_bwd without a workspace (the library's static scratch); the caller passes
+    the outputs, so nothing is allocated here either.  dx is overwritten, dscale
+    accumulated.  Returns dict dx, dscale."""
+    lib = load()
+    R, M = x.shape
+    dev = x.device
+    dt = x.dtype
+    code = _dtype_code(x)
+    f32 = torch.float32
+    args = [_ptr(dy, "dy", dt, (R, M), dev), _ptr(x, "x", dt, (R, M), dev),
+            _ptr(scale, "scale", f32, (M,), dev), _ptr(rms, "rms", f32, (R,), dev),
+            _ptr(dx, "dx", dt, (R, M), dev), _ptr(dscale, "dscale", f32, (M,), dev)]
+    _check(lib.rmsnorm_bwd_noalloc(_stream(dev), code, R, M, *args))
     return dict(dx=dx, dscale=dscale)
 
 

@@ -784,4 +784,38 @@ int rmsnorm_bwd(void* stream, ssm_dtype_t dtype, int64_t R, int64_t M, const voi
   return hip_status(ssm::launch_rmsnorm_bwd(a, p, static_cast<hipStream_t>(stream)), "rmsnorm_bwd");
 }
 
+int rmsnorm_bwd_noalloc(void* stream, ssm_dtype_t dtype, int64_t R, int64_t M, const void* dy,
+                        const void* x, const float* scale, const float* rms, void* dx,
+                        float* dscale) {
+  if (R <= 0 || M <= 0)
+    return fail(SSM_ERR_ARG, "sizes must be positive (R=%lld M=%lld)", (long long)R, (long long)M);
+  if (dtype != SSM_F32 && dtype != SSM_BF16)
+    return fail(SSM_ERR_UNSUPPORTED, "dtype %d not supported", int(dtype));
+  if (R > kMaxElems / M) return fail(SSM_ERR_ARG, "tensor sizes overflow");
+  ssm::RmsPlan p{};
+  rms_plan(R, M, dtype, &p);
+  if (p.passes == 0 && p.nblk * cdiv(M, 8 * 64 * p.vec) > ssm::kMaxGridX)
+    return fail(SSM_ERR_UNSUPPORTED, "row length M=%lld exceeds one launch's grid", (long long)M);
+  int rc = check_ptrs({{dy, "dy"}, {x, "x"}, {scale, "scale"}, {rms, "rms"}, {dx, "dx"},
+                       {dscale, "dscale"}}, {});
+  if (rc) return rc;
+  // the same plan as rmsnorm_bwd, carved out of the static scratch instead of a workspace
+  const size_t need = rms_ws(R, M, dtype, &p, nullptr);
+  if (need > ssm::kNoAllocScratchBytes)
+    return fail(SSM_ERR_UNSUPPORTED,
+                "rmsnorm_bwd_noalloc: R=%lld M=%lld needs %zu bytes of scratch, above the static "
+                "buffer's %zu (use rmsnorm_bwd with a workspace)",
+                (long long)R, (long long)M, need, ssm::kNoAllocScratchBytes);
+  void* ws = nullptr;
+  hipError_t e = ssm::noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e, "rmsnorm_bwd_noalloc (scratch address)");
+  rms_ws(R, M, dtype, &p, ws);
+  ssm::RmsArgs a{};
+  a.dtype = int(dtype);
+  a.R = R; a.M = M;
+  a.dy = dy; a.x = x; a.scale = scale; a.rms = rms; a.dx = dx; a.dscale = dscale;
+  return hip_status(ssm::launch_rmsnorm_bwd(a, p, static_cast<hipStream_t>(stream)),
+                    "rmsnorm_bwd_noalloc");
+}
+
 }  // extern "C"

@@ -291,6 +291,10 @@ struct DecodeArgs {
 };
 hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_rmsnorm_bwd(const RmsArgs& a, const RmsPlan& p, hipStream_t st);
+// The static scratch of rmsnorm_bwd_noalloc: its size, and the device address of the
+// current device's copy (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+hipError_t noalloc_scratch(void** ptr);
 // out[j] (+)= sum_{p < P} part[p*J + j] in a fixed order; tmp holds
 // reduce_tmp_floats(P, J) floats (may be null when that is 0).
 hipError_t launch_reduce(const float* part, int64_t P, int64_t J, float* out, bool accumulate,

@@ -17,6 +17,8 @@
 // row's coefficient c[r] (one read of the row), then k_rms_bwd_slab covers the row in
 // column slabs of kSlabPasses groups per lane, one slab per workgroup column, writing dx
 // and each block's scale-gradient partials of its slab (a second read of the row).
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -359,6 +361,36 @@ static hipError_t rms_v(const RmsArgs& a, const RmsPlan& p, hipStream_t st) {
     case 16: return rms_launch<T, VEC, 16>(a, p, st);
   }
   return hipErrorInvalidValue;
+}
+
+// Scratch of rmsnorm_bwd_noalloc, for callers that cannot allocate (code under HIP graph
+// capture, serving loops, harnesses that forbid hipMalloc): a static device array of
+// kNoAllocScratchBytes, one copy per GPU for the life of the process.  Host code never
+// uses the array's name as an address: the device address of each GPU's copy is taken
+// once per device with hipGetSymbolAddress (with that device current) and kept in
+// g_scratch_ptr; that pointer is what reaches the kernels.  Calls on one GPU share its
+// copy, so calls that overlap on one GPU race.  Nothing in it needs clearing: every
+// partial the kernels read was written by the same call.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* q = g_scratch_ptr[dev].load();
+  if (!q) {
+    e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev].store(q);
+  }
+  *ptr = q;
+  return hipSuccess;
 }
 
 hipError_t launch_rmsnorm_bwd(const RmsArgs& a, const RmsPlan& p, hipStream_t st) {
