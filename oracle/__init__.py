@@ -10,7 +10,11 @@ section it follows, is stated in ``oracle.c``.
 
 Parity status: every function here is pinned by the CPU tests (closed forms, finite
 differences, the unrolled form, step/split equivalence, invariants, page formulas and
-hand-derived worked examples under ``tests/golden``); none is "parity unpinned".
+hand-derived worked examples under ``tests/golden``).  One exception: the sigmoid-gated
+scan (alpha_scan_fwd/bwd) is "parity unpinned" against the pages -- they name the
+operation without printing its recurrence, so its forward is a stated reading; that
+reading's implementation is pinned (closed forms, the unrolled form, limits) and its
+backward is pinned to its forward by central differences and exact identities.
 """
 import ctypes
 import os
@@ -47,6 +51,8 @@ def _load():
             "oracle_silu": [_I] + [_D] * 2,
             "oracle_silu_grad": [_I] + [_D] * 3,
             "oracle_softplus": [_I] + [_D] * 2,
+            "oracle_alpha_scan_fwd": [_I] * 4 + [_D] * 6,
+            "oracle_alpha_scan_bwd": [_I] * 4 + [_D] * 8,
         }
         for name, args in sigs.items():
             fn = getattr(lib, name)
@@ -309,3 +315,30 @@ def decode_step(h, conv_state, x_t, W, conv_bias, delta_t, A, B_t, C_t, Dv, delt
                               delta_softplus=delta_softplus, z_t=z_t)
     return h2, state2, out
 
+
+# ----------------------------------------------------------------------------------
+# sigmoid-gated scan (foxhunt ml-alpha forward-pass commit; parity unpinned, see oracle.c)
+# ----------------------------------------------------------------------------------
+
+def alpha_scan_fwd(a, b, Wc, h0=None):
+    """a, b [Bn,K,S]; Wc [H,S]; h0 [Bn,H] or None.  Returns (h [Bn,H], x_last [Bn,S])."""
+    a, b, Wc, h0 = map(_f64, (a, b, Wc, h0))
+    Bn, K, S = a.shape
+    H = Wc.shape[0]
+    h = np.empty((Bn, H))
+    xl = np.empty((Bn, S))
+    _load().oracle_alpha_scan_fwd(Bn, K, S, H, _p(a), _p(b), _p(Wc), _p(h0), _p(h), _p(xl))
+    return h, xl
+
+
+def alpha_scan_bwd(a, b, Wc, dh):
+    """Exact adjoint for upstream gradient dh [Bn,H].  Returns dict da, db, dWc (from
+    zero), dh0."""
+    a, b, Wc, dh = map(_f64, (a, b, Wc, dh))
+    Bn, K, S = a.shape
+    H = Wc.shape[0]
+    out = dict(da=np.empty((Bn, K, S)), db=np.empty((Bn, K, S)), dWc=np.zeros((H, S)),
+               dh0=np.empty((Bn, H)))
+    _load().oracle_alpha_scan_bwd(Bn, K, S, H, _p(a), _p(b), _p(Wc), _p(dh), _p(out["da"]),
+                                  _p(out["db"]), _p(out["dWc"]), _p(out["dh0"]))
+    return out

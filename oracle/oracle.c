@@ -488,3 +488,86 @@ void oracle_rmsnorm_bwd(int64_t R, int64_t M, const double *dy, const double *x,
         dscale[i] += acc;
     }
 }
+
+/* ---------------------------------------------------------------------------------
+ * Sigmoid-gated scan of the foxhunt ml-alpha forward-pass commit
+ * ("mamba2_alpha_scan_fwd -- selective SSM scan over K timesteps with sigmoid-gated
+ * state update"; forward pipeline steps 4-5: zero-initialised h_s2, then the scan
+ * (a_proj, b_proj, W_c, h_s2) -> h_enriched).  The page does not print the recurrence;
+ * PARITY UNPINNED against the pages: this is one reading, chosen to agree with every
+ * fact the backward-scratch commit states about its gradients (d_a and d_b summed over
+ * the hidden channels j, d_W_c summed over the batch, d_h_s2 an identity passthrough):
+ *   per batch row i and state s, x_{-1}[i,s] = 0 and for k = 0..K-1
+ *     g_k = sigmoid(a[i,k,s]),   x_k[i,s] = g_k x_{k-1}[i,s] + (1 - g_k) b[i,k,s]
+ *   h[i,j] = h0[i,j] + sum_s Wc[j,s] x_{K-1}[i,s]
+ * Layouts: a, b [Bn][K][S]; Wc [H][S]; h0, h [Bn][H] (h0 NULL = 0); x_last [Bn][S]
+ * (NULL to skip).
+ * ------------------------------------------------------------------------------- */
+void oracle_alpha_scan_fwd(int64_t Bn, int64_t K, int64_t S, int64_t H, const double *a,
+                           const double *b, const double *Wc, const double *h0, double *h,
+                           double *x_last)
+{
+    double *xl = (double *)malloc(sizeof(double) * (size_t)(Bn * S));
+    for (int64_t i = 0; i < Bn; ++i) {
+        for (int64_t s = 0; s < S; ++s) {
+            double x = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double g = sigmoid(a[(i * K + k) * S + s]);
+                x = g * x + (1.0 - g) * b[(i * K + k) * S + s];
+            }
+            xl[i * S + s] = x;
+            if (x_last) x_last[i * S + s] = x;
+        }
+        for (int64_t j = 0; j < H; ++j) {
+            double acc = h0 ? h0[i * H + j] : 0.0;
+            for (int64_t s = 0; s < S; ++s) acc += Wc[j * S + s] * xl[i * S + s];
+            h[i * H + j] = acc;
+        }
+    }
+    free(xl);
+}
+
+/* Its exact adjoint for the upstream gradient dh [Bn][H]:
+ *   dh0[i,j] = dh[i,j]                                  (overwritten; NULL to skip)
+ *   dWc[j,s] += sum_i dh[i,j] x_{K-1}[i,s]              (accumulated)
+ *   lambda_{K-1}[i,s] = sum_j Wc[j,s] dh[i,j], and for k = K-1..0:
+ *     da[i,k,s] = lambda_k (x_{k-1} - b_k) g_k (1 - g_k)
+ *     db[i,k,s] = lambda_k (1 - g_k)                    (both overwritten)
+ *     lambda_{k-1} = lambda_k g_k
+ * The forward states x_k are recomputed per (i, s) and kept for the reverse loop. */
+void oracle_alpha_scan_bwd(int64_t Bn, int64_t K, int64_t S, int64_t H, const double *a,
+                           const double *b, const double *Wc, const double *dh, double *da,
+                           double *db, double *dWc, double *dh0)
+{
+    double *xs = (double *)malloc(sizeof(double) * (size_t)(K + 1));
+    double *xl = (double *)malloc(sizeof(double) * (size_t)(Bn * S));
+    for (int64_t i = 0; i < Bn; ++i) {
+        for (int64_t s = 0; s < S; ++s) {
+            xs[0] = 0.0;  /* xs[k + 1] = x_k */
+            for (int64_t k = 0; k < K; ++k) {
+                const double g = sigmoid(a[(i * K + k) * S + s]);
+                xs[k + 1] = g * xs[k] + (1.0 - g) * b[(i * K + k) * S + s];
+            }
+            xl[i * S + s] = xs[K];
+            double lam = 0.0;
+            for (int64_t j = 0; j < H; ++j) lam += Wc[j * S + s] * dh[i * H + j];
+            for (int64_t k = K - 1; k >= 0; --k) {
+                const int64_t o = (i * K + k) * S + s;
+                const double g = sigmoid(a[o]);
+                da[o] = lam * (xs[k] - b[o]) * g * (1.0 - g);
+                db[o] = lam * (1.0 - g);
+                lam *= g;
+            }
+        }
+        if (dh0)
+            for (int64_t j = 0; j < H; ++j) dh0[i * H + j] = dh[i * H + j];
+    }
+    for (int64_t j = 0; j < H; ++j)
+        for (int64_t s = 0; s < S; ++s) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < Bn; ++i) acc += dh[i * H + j] * xl[i * S + s];
+            dWc[j * S + s] += acc;
+        }
+    free(xs);
+    free(xl);
+}

@@ -21,7 +21,7 @@ from .workloads import Workload
 
 # tensor ids (fixed order)
 (_X, _DELTA, _B, _C, _DV, _DY, _CX, _CW, _CDOUT, _RX, _RDY, _RSCALE, _H0, _CBIAS, _DRAW, _DBIAS,
- _Z, _RRES) = range(1, 19)
+ _Z, _RRES, _GA, _GB, _GWC, _GH0, _GDH) = range(1, 24)
 
 RMS_EPS = 1e-5  # the RMSNorm eps of every workload
 
@@ -117,3 +117,17 @@ def rms_residual(w: Workload, seed: int = 0) -> torch.Tensor:
 def as_f64(t: torch.Tensor):
     """Exact f64 copy (numpy) of a stored tensor, for the oracle."""
     return t.to(torch.float64).numpy()
+
+
+def alpha_inputs(w: Workload, seed: int = 0, with_h0: bool = False) -> dict:
+    """Inputs of the sigmoid-gated scan on a workload's shape: batch rows B, steps L,
+    state S = N, hidden channels H = D.  The gate and input projections a, b [B,L,N] and
+    the upstream gradient dh [B,D] ~ N(0,1), W_c [D,N] ~ U(-0.5, 0.5), and the initial
+    hidden state h0 [B,D] zero (the page's zero-initialised h_s2) unless with_h0 (N(0,1)).
+    f32 throughout (the page's kernel is f32)."""
+    B, L, S, H = w.B, w.L, w.N, w.D
+    out = dict(a=_normal((B, L, S), seed, _GA), b=_normal((B, L, S), seed, _GB),
+               Wc=torch.rand((H, S), generator=_gen(seed, _GWC), dtype=torch.float32) - 0.5,
+               dh=_normal((B, H), seed, _GDH))
+    out["h0"] = _normal((B, H), seed, _GH0) if with_h0 else torch.zeros((B, H))
+    return out
