@@ -471,6 +471,52 @@ def measure_ckpt_intervals(w, p, steps, dev):
     return out
 
 
+def measure_alpha_scan(seed, steps, dev):
+    """The sigmoid-gated scan (ssm_alpha_scan_fwd/bwd) on the shape of the pages' alpha
+    stack (256 sequences of 32 steps, state 16, hidden 64), each call timed with events on
+    its stream.  Not part of the step and not in `value`.  Algorithmic bytes: the forward
+    reads a, b, W_c, h0 and writes h; the backward reads a, b, W_c, dh and writes da, db,
+    dh0 and dW_c (read and written)."""
+    import torch
+    from selective_state_space_02_amd import binding as ssm
+    from selective_state_space_02_amd import synth
+    from selective_state_space_02_amd.workloads import BY_NAME
+    w = BY_NAME["alpha-stack"]
+    Bn, K, S, H = w.B, w.L, w.N, w.D
+    p = {k: v.to(dev) for k, v in synth.alpha_inputs(w, seed).items()}
+    h = torch.empty((Bn, H), device=dev)
+    g = dict(da=torch.empty_like(p["a"]), db=torch.empty_like(p["b"]),
+             dWc=torch.zeros_like(p["Wc"]), dh0=torch.empty((Bn, H), device=dev))
+    ws = torch.empty(max(1, int(ssm.load().ssm_alpha_scan_bwd_workspace_bytes(Bn, K, S, H))),
+                     dtype=torch.uint8, device=dev)
+
+    def fwd():
+        ssm.ssm_alpha_scan_fwd(p["a"], p["b"], p["Wc"], h0=p["h0"], h=h)
+
+    def bwd():
+        ssm.ssm_alpha_scan_bwd(p["a"], p["b"], p["Wc"], p["dh"], ws=ws, **g)
+    for _ in range(3):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    he = HipEvents()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ev = {k: [he.pair() for _ in range(steps)] for k in ("fwd", "bwd")}
+    for i in range(steps):
+        for k, f in (("fwd", fwd), ("bwd", bwd)):
+            he.record(ev[k][i][0], stream)
+            f()
+            he.record(ev[k][i][1], stream)
+    torch.cuda.synchronize()
+    ms = {k: sum(he.elapsed_ms(*pr) for pr in ev[k]) / steps for k in ev}
+    he.destroy()
+    P, Hb, W = Bn * K * S * 4, Bn * H * 4, H * S * 4
+    nbytes = {"fwd": 2 * P + W + 2 * Hb, "bwd": 4 * P + 2 * W + 2 * Hb + 2 * W}
+    return {"shape": {"Bn": Bn, "K": K, "S": S, "H": H}, "fwd_ms": ms["fwd"], "bwd_ms": ms["bwd"],
+            "algorithmic_bytes": nbytes,
+            "GBps": {k: nbytes[k] / (ms[k] * 1e-3) / 1e9 for k in ms}}
+
+
 def measure_copy_GBps(dev, reps=5):
     """A plain 1 GiB device-to-device copy (torch's copy on the current stream), timed
     with events: the practical HBM rate the bandwidth fractions are also quoted against
@@ -742,6 +788,7 @@ def main():
                                           scan_fused["call_ms"]["fused_bwd"] - scan_ms)
 
     ckpt_iv = measure_ckpt_intervals(w, p, K_, dev)
+    alpha = measure_alpha_scan(args.seed, K_, dev)
     copy_gbps = measure_copy_GBps(dev)
 
     if args.copy_calibration:
@@ -809,6 +856,7 @@ def main():
     out["scan_fused"] = scan_fused
     out["decode"] = decode
     out["ckpt_interval"] = ckpt_iv
+    out["alpha_scan"] = alpha
     if not args.no_cpu_baseline:
         sample = args.cpu_sample_channels or max(16, min(w.D, 2048))
         print(f"[bench] cpu baseline: oracle on {sample} channels", file=sys.stderr, flush=True)

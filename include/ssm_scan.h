@@ -17,6 +17,11 @@
  *   ssm_scan_fused_step one-token decode step of the fused scan
  *   ssm_decode_step    one decode token of the block's scan branch (conv step, SiLU,
  *                      fused scan step) in one launch
+ *   ssm_scan_fwd_every / ssm_scan_bwd_every
+ *                      the scan with sparse checkpoints (states regenerated per slab)
+ *   ssm_alpha_scan_fwd / ssm_alpha_scan_bwd
+ *                      the sigmoid-gated scan of the ml-alpha kernel (one reading)
+ *   rmsnorm_bwd_noalloc  rmsnorm_bwd without a workspace (static scratch)
  *
  * Common conventions
  * ------------------
@@ -274,6 +279,32 @@ size_t rmsnorm_bwd_workspace_bytes(int64_t R, int64_t M, ssm_dtype_t dtype);
 int rmsnorm_bwd(void *stream, ssm_dtype_t dtype, int64_t R, int64_t M, const void *dy,
                 const void *x, const float *scale, const float *rms, void *dx,
                 float *dscale, void *ws, size_t ws_bytes);
+
+/* ---------------------------------------------------------------------------------
+ * Sigmoid-gated scan: the foxhunt ml-alpha forward-pass commit's "selective SSM scan
+ * over K timesteps with sigmoid-gated state update" (a_proj, b_proj, W_c and the
+ * zero-initialised h_s2 in, h_enriched out).  The page does not print the recurrence;
+ * this library computes the reading below (its results are not pinned to the pages),
+ * per batch row i and state s:
+ *     g_k = sigmoid(a[i,k,s]),   x_k[i,s] = g_k x_{k-1}[i,s] + (1 - g_k) b[i,k,s]
+ *     h[i,j] = h0[i,j] + sum_s Wc[j,s] x_{K-1}[i,s]          (x_{-1} = 0)
+ * and its exact adjoint for dh = dL/dh, with the gradient structure the backward-scratch
+ * commit states (d_a and d_b summed over the hidden channels, d_W_c over the batch, d_h_s2
+ * passed through):
+ *     da[i,k,s], db[i,k,s] (overwritten);  dWc[j,s] += sum_i dh[i,j] x_{K-1}[i,s];
+ *     dh0 = dh (overwritten; NULL to skip)
+ * Shapes (f32, row-major): a, b, da, db [Bn,K,S]; Wc, dWc [H,S]; h0, h, dh, dh0 [Bn,H].
+ * Supported: 1 <= S <= 1024 (states staged in LDS), any Bn, K, H.  The backward's
+ * workspace (ssm_alpha_scan_bwd_workspace_bytes) holds the recomputed states.
+ * ------------------------------------------------------------------------------- */
+size_t ssm_alpha_scan_bwd_workspace_bytes(int64_t Bn, int64_t K, int64_t S, int64_t H);
+int ssm_alpha_scan_fwd(void *stream, int64_t Bn, int64_t K, int64_t S, int64_t H,
+                       const float *a, const float *b, const float *Wc, const float *h0,
+                       float *h);
+int ssm_alpha_scan_bwd(void *stream, int64_t Bn, int64_t K, int64_t S, int64_t H,
+                       const float *a, const float *b, const float *Wc, const float *dh,
+                       float *da, float *db, float *dWc, float *dh0, void *ws,
+                       size_t ws_bytes);
 
 /* rmsnorm_bwd for callers that cannot allocate device memory: code under HIP graph
  * capture, serving loops, harnesses that forbid hipMalloc.  Same operation, arguments

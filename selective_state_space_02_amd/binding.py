@@ -27,7 +27,8 @@ EXPORTS = ("ssm_last_error", "ssm_version", "ssm_set_kernel_timer", "ssm_scan_ck
            "ssm_scan_step", "conv1d_causal_step", "ssm_scan_fused_fwd", "ssm_scan_fused_bwd",
            "ssm_scan_fused_step", "ssm_decode_step", "ssm_scan_chunks",
            "ssm_scan_ckpt_bytes_every", "ssm_scan_bwd_workspace_bytes_every",
-           "ssm_scan_fwd_every", "ssm_scan_bwd_every", "rmsnorm_bwd_noalloc")
+           "ssm_scan_fwd_every", "ssm_scan_bwd_every", "rmsnorm_bwd_noalloc",
+           "ssm_alpha_scan_bwd_workspace_bytes", "ssm_alpha_scan_fwd", "ssm_alpha_scan_bwd")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -96,6 +97,12 @@ def load():
     lib.rmsnorm_bwd.argtypes = [_P, _E] + [_I] * 2 + [_P] * 6 + [_P, _S]
     lib.rmsnorm_bwd_noalloc.restype = _E
     lib.rmsnorm_bwd_noalloc.argtypes = [_P, _E] + [_I] * 2 + [_P] * 6
+    lib.ssm_alpha_scan_bwd_workspace_bytes.restype = _S
+    lib.ssm_alpha_scan_bwd_workspace_bytes.argtypes = [_I] * 4
+    lib.ssm_alpha_scan_fwd.restype = _E
+    lib.ssm_alpha_scan_fwd.argtypes = [_P] + [_I] * 4 + [_P] * 5
+    lib.ssm_alpha_scan_bwd.restype = _E
+    lib.ssm_alpha_scan_bwd.argtypes = [_P] + [_I] * 4 + [_P] * 8 + [_P, _S]
     lib.conv1d_causal_fwd.restype = _E
     lib.conv1d_causal_fwd.argtypes = [_P, _E] + [_I] * 4 + [_P] * 3 + [_E, _P]
     lib.rmsnorm_fwd.restype = _E
@@ -616,3 +623,46 @@ def conv1d_causal_step(state, x_t, W, bias=None, act="none", out_t=None):
                                   _ptr(W, "W", f32, (D, K), dev), bp, ac,
                                   _ptr(out_t, "out_t", dt, (Bsz, D), dev)))
     return out_t
+
+
+# ----------------------------------------------------------------------------------
+# sigmoid-gated scan
+# ----------------------------------------------------------------------------------
+
+def ssm_alpha_scan_fwd(a, b, Wc, h0=None, h=None):
+    """h [Bn, H] = h0 + Wc x_{K-1} of the sigmoid-gated scan over a, b [Bn, K, S] (f32).
+    Returns h (allocated if not given)."""
+    lib = load()
+    Bn, K, S = a.shape
+    H = Wc.shape[0]
+    dev = a.device
+    f32 = torch.float32
+    h = torch.empty((Bn, H), dtype=f32, device=dev) if h is None else h
+    args = [_ptr(a, "a", f32, (Bn, K, S), dev), _ptr(b, "b", f32, (Bn, K, S), dev),
+            _ptr(Wc, "Wc", f32, (H, S), dev), _ptr(h0, "h0", f32, (Bn, H), dev),
+            _ptr(h, "h", f32, (Bn, H), dev)]
+    _check(lib.ssm_alpha_scan_fwd(_stream(dev), Bn, K, S, H, *args))
+    return h
+
+
+def ssm_alpha_scan_bwd(a, b, Wc, dh, da=None, db=None, dWc=None, dh0=None, ws=None):
+    """Backward of ssm_alpha_scan_fwd for dh [Bn, H].  dWc is accumulated into (zeros if
+    not given); da, db, dh0 are overwritten.  Returns dict da, db, dWc, dh0."""
+    lib = load()
+    Bn, K, S = a.shape
+    H = Wc.shape[0]
+    dev = a.device
+    f32 = torch.float32
+    da = torch.empty_like(a) if da is None else da
+    db = torch.empty_like(b) if db is None else db
+    dWc = torch.zeros((H, S), dtype=f32, device=dev) if dWc is None else dWc
+    dh0 = torch.empty((Bn, H), dtype=f32, device=dev) if dh0 is None else dh0
+    args = [_ptr(a, "a", f32, (Bn, K, S), dev), _ptr(b, "b", f32, (Bn, K, S), dev),
+            _ptr(Wc, "Wc", f32, (H, S), dev), _ptr(dh, "dh", f32, (Bn, H), dev),
+            _ptr(da, "da", f32, (Bn, K, S), dev), _ptr(db, "db", f32, (Bn, K, S), dev),
+            _ptr(dWc, "dWc", f32, (H, S), dev), _ptr(dh0, "dh0", f32, (Bn, H), dev)]
+    need = int(lib.ssm_alpha_scan_bwd_workspace_bytes(Bn, K, S, H))
+    ws, nbytes = _workspace(need, dev, ws)
+    _check(lib.ssm_alpha_scan_bwd(_stream(dev), Bn, K, S, H, *args,
+                                  _ptr(ws, "ws") if ws is not None else None, nbytes))
+    return dict(da=da, db=db, dWc=dWc, dh0=dh0)

@@ -19,7 +19,7 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-command-line-argument"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 SOURCES = ["scan_fwd.hip", "scan_bwd.hip", "reduce.hip", "conv1d_bwd.hip", "rmsnorm_bwd.hip",
-           "conv1d_fwd.hip", "rmsnorm_fwd.hip", "decode.hip",
+           "conv1d_fwd.hip", "rmsnorm_fwd.hip", "decode.hip", "alpha_scan.hip",
            "api.cpp"]
 
 

@@ -784,6 +784,61 @@ int rmsnorm_bwd(void* stream, ssm_dtype_t dtype, int64_t R, int64_t M, const voi
   return hip_status(ssm::launch_rmsnorm_bwd(a, p, static_cast<hipStream_t>(stream)), "rmsnorm_bwd");
 }
 
+static int check_alpha_dims(int64_t Bn, int64_t K, int64_t S, int64_t H) {
+  if (Bn <= 0 || K <= 0 || S <= 0 || H <= 0)
+    return fail(SSM_ERR_ARG, "sizes must be positive (Bn=%lld K=%lld S=%lld H=%lld)",
+                (long long)Bn, (long long)K, (long long)S, (long long)H);
+  if (S > ssm::kAlphaMaxS)
+    return fail(SSM_ERR_UNSUPPORTED, "state size S=%lld exceeds %lld", (long long)S,
+                (long long)ssm::kAlphaMaxS);
+  if (Bn > kMaxElems / K || Bn * K > kMaxElems / S || Bn > kMaxElems / H || H * S > kMaxElems)
+    return fail(SSM_ERR_ARG, "tensor sizes overflow");
+  return SSM_OK;
+}
+
+size_t ssm_alpha_scan_bwd_workspace_bytes(int64_t Bn, int64_t K, int64_t S, int64_t H) {
+  if (Bn <= 0 || K <= 0 || S <= 0 || H <= 0) return 0;
+  Carver cv(nullptr);
+  cv.take(size_t(Bn) * size_t(K) * size_t(S));
+  cv.take(size_t(Bn) * size_t(S));
+  return cv.off;
+}
+
+int ssm_alpha_scan_fwd(void* stream, int64_t Bn, int64_t K, int64_t S, int64_t H,
+                       const float* a, const float* b, const float* Wc, const float* h0,
+                       float* h) {
+  int rc = check_alpha_dims(Bn, K, S, H);
+  if (rc) return rc;
+  rc = check_ptrs({{a, "a"}, {b, "b"}, {Wc, "Wc"}, {h, "h"}}, {{h0, "h0"}});
+  if (rc) return rc;
+  ssm::AlphaArgs x{};
+  x.Bn = Bn; x.K = K; x.S = S; x.H = H;
+  x.a = a; x.b = b; x.Wc = Wc; x.h0 = h0; x.h = h;
+  return hip_status(ssm::launch_alpha_fwd(x, static_cast<hipStream_t>(stream)),
+                    "ssm_alpha_scan_fwd");
+}
+
+int ssm_alpha_scan_bwd(void* stream, int64_t Bn, int64_t K, int64_t S, int64_t H,
+                       const float* a, const float* b, const float* Wc, const float* dh,
+                       float* da, float* db, float* dWc, float* dh0, void* ws, size_t ws_bytes) {
+  int rc = check_alpha_dims(Bn, K, S, H);
+  if (rc) return rc;
+  rc = check_ptrs({{a, "a"}, {b, "b"}, {Wc, "Wc"}, {dh, "dh"}, {da, "da"}, {db, "db"},
+                   {dWc, "dWc"}},
+                  {{dh0, "dh0"}});
+  if (rc) return rc;
+  const size_t need = ssm_alpha_scan_bwd_workspace_bytes(Bn, K, S, H);
+  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  Carver cv(ws);
+  float* xh = cv.take(size_t(Bn) * size_t(K) * size_t(S));
+  float* xl = cv.take(size_t(Bn) * size_t(S));
+  ssm::AlphaArgs x{};
+  x.Bn = Bn; x.K = K; x.S = S; x.H = H;
+  x.a = a; x.b = b; x.Wc = Wc; x.dh = dh; x.da = da; x.db = db; x.dWc = dWc; x.dh0 = dh0;
+  return hip_status(ssm::launch_alpha_bwd(x, xh, xl, static_cast<hipStream_t>(stream)),
+                    "ssm_alpha_scan_bwd");
+}
+
 int rmsnorm_bwd_noalloc(void* stream, ssm_dtype_t dtype, int64_t R, int64_t M, const void* dy,
                         const void* x, const float* scale, const float* rms, void* dx,
                         float* dscale) {

@@ -291,6 +291,26 @@ struct DecodeArgs {
 };
 hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_rmsnorm_bwd(const RmsArgs& a, const RmsPlan& p, hipStream_t st);
+
+// The sigmoid-gated scan (alpha_scan.hip): a, b, da, db [Bn][K][S]; Wc, dWc [H][S];
+// h0, h, dh, dh0 [Bn][H]; f32.
+constexpr int64_t kAlphaMaxS = 1024;
+struct AlphaArgs {
+  int64_t Bn, K, S, H;
+  const float* a;
+  const float* b;
+  const float* Wc;
+  const float* h0;  // nullable (zero)
+  float* h;
+  const float* dh;
+  float* da;
+  float* db;
+  float* dWc;  // accumulated
+  float* dh0;  // nullable
+};
+hipError_t launch_alpha_fwd(const AlphaArgs& a, hipStream_t st);
+// xh: Bn*K*S floats, xl: Bn*S floats of workspace
+hipError_t launch_alpha_bwd(const AlphaArgs& a, float* xh, float* xl, hipStream_t st);
 // The static scratch of rmsnorm_bwd_noalloc: its size, and the device address of the
 // current device's copy (looked up once per device).
 constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;

@@ -487,3 +487,32 @@ def test_checkpoint_interval_slabs_and_sizes():
     # a too-small workspace is refused before any launch
     assert _bwd_every(lib, 64, 8, B=B, L=L, D=D, N=N, ws=FAKE, ws_bytes=w8 - 1) == \
         b.SSM_ERR_WORKSPACE
+
+
+def test_alpha_scan_validation():
+    lib = b.load()
+
+    def fwd(Bn=4, K=8, S=4, H=8, **kw):
+        p = dict(a=FAKE, b=FAKE, Wc=FAKE, h0=None, h=FAKE)
+        p.update(kw)
+        return lib.ssm_alpha_scan_fwd(None, Bn, K, S, H, p["a"], p["b"], p["Wc"], p["h0"], p["h"])
+
+    def bwd(Bn=4, K=8, S=4, H=8, ws=None, ws_bytes=0, **kw):
+        p = dict(a=FAKE, b=FAKE, Wc=FAKE, dh=FAKE, da=FAKE, db=FAKE, dWc=FAKE, dh0=None)
+        p.update(kw)
+        return lib.ssm_alpha_scan_bwd(None, Bn, K, S, H, p["a"], p["b"], p["Wc"], p["dh"],
+                                      p["da"], p["db"], p["dWc"], p["dh0"], ws, ws_bytes)
+    for dims in ((0, 8, 4, 8), (4, 0, 4, 8), (4, 8, 0, 8), (4, 8, 4, -1)):
+        assert fwd(*dims) == b.SSM_ERR_ARG
+        assert bwd(*dims) == b.SSM_ERR_ARG
+    assert fwd(S=1025) == b.SSM_ERR_UNSUPPORTED and "state size" in b.last_error()
+    assert bwd(S=1025) == b.SSM_ERR_UNSUPPORTED
+    for name in ("a", "b", "Wc", "h"):
+        assert fwd(**{name: None}) == b.SSM_ERR_ARG and name in b.last_error()
+        assert fwd(**{name: MIS}) == b.SSM_ERR_ALIGN
+    assert fwd(h0=MIS) == b.SSM_ERR_ALIGN
+    for name in ("a", "b", "Wc", "dh", "da", "db", "dWc"):
+        assert bwd(**{name: None}) == b.SSM_ERR_ARG and name in b.last_error()
+    need = b.load().ssm_alpha_scan_bwd_workspace_bytes(4, 8, 4, 8)
+    assert need >= 4 * 8 * 4 * 4 + 4 * 4 * 4
+    assert bwd(ws=FAKE, ws_bytes=need - 1) == b.SSM_ERR_WORKSPACE
