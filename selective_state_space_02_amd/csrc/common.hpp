@@ -207,6 +207,14 @@ __device__ __forceinline__ T opaque(T v) {
   asm volatile("" : "+v"(v));
   return v;
 }
+// An explicit register move into a register other than src's.  Where a loop hands a
+// loop-carried value over (the next tile's checkpoint becoming the current one) right
+// before src's register is reloaded, this keeps the reload landing in src's own
+// register: a plain assignment may leave the loads in temporaries that are copied back
+// at the loop edge, and that copy waits for every load in flight.
+__device__ __forceinline__ void reg_move(float& dst, float src) {
+  asm volatile("v_mov_b32 %0, %1" : "=&v"(dst) : "v"(src));
+}
 template <int K>
 __device__ __forceinline__ void step_fence_arr(float (&v)[K]) {
 #pragma unroll

@@ -637,8 +637,7 @@ __global__ __launch_bounds__(256, WAVES) void k_bwd_main(
 #pragma unroll
       for (int hf = 0; hf < SPLIT; ++hf) {
 #pragma unroll
-        for (int j = 0; j < NS; ++j) hcur[hf][j] = hnxt[hf][j];
-        step_fence_arr(hcur[hf]);  // moved before the loads below reuse hnxt's registers
+        for (int j = 0; j < NS; ++j) reg_move(hcur[hf][j], hnxt[hf][j]);
       }
       step_fence();
       fetch(it + 2 < ntile ? tf - 2 * kTc : tf, it + 2 < ntile ? kTc : 0, hnxt);
