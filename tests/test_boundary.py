@@ -233,6 +233,11 @@ def test_conv_validation():
     need = b.conv1d_causal_bwd_workspace_bytes(2, 64, 32, 4, 0)
     assert need > 0
     assert _conv(lib, ws=FAKE, ws_bytes=need - 1) == b.SSM_ERR_WORKSPACE
+    # no 32-bit size limit on D (per-row descriptors); only a grid of more than 2^31 - 1
+    # workgroups (batch rows x channel groups) is refused
+    assert _conv(lib, B=1 << 31, L=1, D=64) == b.SSM_ERR_UNSUPPORTED
+    assert "grid" in b.last_error()
+    assert b.conv1d_causal_bwd_workspace_bytes(1, 2, 1 << 27, 4, 1) > 0
 
 
 def _rms(lib, R=64, M=128, dtype=0, dy=FAKE, x=FAKE, scale=FAKE, rms=FAKE, dx=FAKE,
@@ -278,6 +283,8 @@ def test_conv_fwd_validation():
         assert name in b.last_error()
         assert _conv_fwd(lib, **{name: MIS}) == b.SSM_ERR_ALIGN
     assert _conv_fwd(lib, bias=MIS) == b.SSM_ERR_ALIGN     # optional, but aligned if given
+    assert _conv_fwd(lib, B=1 << 31, L=1, D=64) == b.SSM_ERR_UNSUPPORTED
+    assert "grid" in b.last_error()
 
 
 def _rms_fwd(lib, R=64, M=128, dtype=0, x=FAKE, residual=None, scale=FAKE, eps=1e-5, y=FAKE,

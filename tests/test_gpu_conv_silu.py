@@ -109,3 +109,26 @@ def test_fused_equals_unfused_chain():
         e = rel_err(f64(fused[k]), f64(chain[k]))
         say("fused vs chain", k, f"{e:.2e}")
         assert e <= 1e-5, (k, e)
+
+
+def test_conv_silu_rows_past_32bit_sizes():
+    # D = 50,000,001 f32 channels with K = 8 and SiLU: the rows a workgroup touches span
+    # 22 * D * 4 > 2^32 bytes, where a single 32-bit buffer size over all of them would
+    # wrap.  Channels are independent, so a sample (first, last, the group boundaries
+    # near the end, random ones) is compared with the oracle.
+    w = custom(B=1, L=3, D=50_000_001, K=8)
+    say(f"[conv silu wide] B={w.B} L={w.L} D={w.D} K={w.K} {w.dtype}")
+    p = synth.conv_inputs(w)
+    bias = synth.conv_bias(w)
+    got = gpu_both(p, bias)
+    rng = np.random.default_rng(7)
+    idx = np.unique(np.concatenate([[0, 1, 255, 256, w.D - 257, w.D - 256, w.D - 2, w.D - 1],
+                                    rng.choice(w.D, 24, replace=False)]))
+    t = torch.from_numpy(idx)
+    q = dict(x=p["x"][:, :, t].contiguous(), W=p["W"][t].contiguous(),
+             dout=p["dout"][:, :, t].contiguous())
+    bq = bias[t].contiguous()
+    sub = dict(dx=got["dx"][:, :, t.cuda()], dW=got["dW"][t.cuda()], db=got["db"][t.cuda()],
+               out=got["out"][:, :, t.cuda()])
+    compare(sub, {"out": ref_fwd(q, bq)}, ("out",), label="conv silu fwd wide")
+    compare(sub, ref_bwd(q, bq), ("dx", "dW", "db"), label="conv silu bwd wide")
