@@ -294,8 +294,10 @@ int rmsnorm_bwd(void *stream, ssm_dtype_t dtype, int64_t R, int64_t M, const voi
  *     da[i,k,s], db[i,k,s] (overwritten);  dWc[j,s] += sum_i dh[i,j] x_{K-1}[i,s];
  *     dh0 = dh (overwritten; NULL to skip)
  * Shapes (f32, row-major): a, b, da, db [Bn,K,S]; Wc, dWc [H,S]; h0, h, dh, dh0 [Bn,H].
- * Supported: 1 <= S <= 1024 (states staged in LDS), any Bn, K, H.  The backward's
- * workspace (ssm_alpha_scan_bwd_workspace_bytes) holds the recomputed states.
+ * Supported: 1 <= S <= 1024 (states staged in LDS), any Bn, K, H whose grids fit one
+ * launch (ceil(Bn / max(1, 64/S)) and ceil(H*S/256) workgroups below 2^31).  The
+ * backward's workspace (ssm_alpha_scan_bwd_workspace_bytes) holds the recomputed states
+ * and the dWc partial sums of batch segments (added in segment order: deterministic).
  * ------------------------------------------------------------------------------- */
 size_t ssm_alpha_scan_bwd_workspace_bytes(int64_t Bn, int64_t K, int64_t S, int64_t H);
 int ssm_alpha_scan_fwd(void *stream, int64_t Bn, int64_t K, int64_t S, int64_t H,

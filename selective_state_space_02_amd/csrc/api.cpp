@@ -793,14 +793,21 @@ static int check_alpha_dims(int64_t Bn, int64_t K, int64_t S, int64_t H) {
                 (long long)ssm::kAlphaMaxS);
   if (Bn > kMaxElems / K || Bn * K > kMaxElems / S || Bn > kMaxElems / H || H * S > kMaxElems)
     return fail(SSM_ERR_ARG, "tensor sizes overflow");
+  const ssm::AlphaPlan p = ssm::alpha_plan(Bn, S, H);
+  if (p.nblk > ssm::kMaxGridX || p.ncb * p.nseg > ssm::kMaxGridX)
+    return fail(SSM_ERR_UNSUPPORTED, "sizes exceed one launch's grid (Bn=%lld H*S=%lld)",
+                (long long)Bn, (long long)(H * S));
   return SSM_OK;
 }
 
 size_t ssm_alpha_scan_bwd_workspace_bytes(int64_t Bn, int64_t K, int64_t S, int64_t H) {
   if (Bn <= 0 || K <= 0 || S <= 0 || H <= 0) return 0;
+  const ssm::AlphaPlan p = ssm::alpha_plan(Bn, S, H);
   Carver cv(nullptr);
   cv.take(size_t(Bn) * size_t(K) * size_t(S));
   cv.take(size_t(Bn) * size_t(S));
+  cv.take(size_t(p.nseg) * size_t(H) * size_t(S));
+  cv.take(size_t(ssm::reduce_tmp_floats(p.nseg, H * S)));
   return cv.off;
 }
 
@@ -830,12 +837,15 @@ int ssm_alpha_scan_bwd(void* stream, int64_t Bn, int64_t K, int64_t S, int64_t H
   const size_t need = ssm_alpha_scan_bwd_workspace_bytes(Bn, K, S, H);
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
   Carver cv(ws);
+  const ssm::AlphaPlan p = ssm::alpha_plan(Bn, S, H);
   float* xh = cv.take(size_t(Bn) * size_t(K) * size_t(S));
   float* xl = cv.take(size_t(Bn) * size_t(S));
+  float* part = cv.take(size_t(p.nseg) * size_t(H) * size_t(S));
+  float* tmp = cv.take(size_t(ssm::reduce_tmp_floats(p.nseg, H * S)));
   ssm::AlphaArgs x{};
   x.Bn = Bn; x.K = K; x.S = S; x.H = H;
   x.a = a; x.b = b; x.Wc = Wc; x.dh = dh; x.da = da; x.db = db; x.dWc = dWc; x.dh0 = dh0;
-  return hip_status(ssm::launch_alpha_bwd(x, xh, xl, static_cast<hipStream_t>(stream)),
+  return hip_status(ssm::launch_alpha_bwd(x, xh, xl, part, tmp, static_cast<hipStream_t>(stream)),
                     "ssm_alpha_scan_bwd");
 }
 

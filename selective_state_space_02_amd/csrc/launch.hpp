@@ -308,9 +308,16 @@ struct AlphaArgs {
   float* dWc;  // accumulated
   float* dh0;  // nullable
 };
+// Launch plan of the sigmoid-gated scan: rpb batch rows per workgroup (nblk workgroups);
+// dWc summed over nseg segments of `rows` batch rows, ncb column blocks of 256 (j, s).
+struct AlphaPlan {
+  int64_t rpb, nblk, rows, nseg, ncb;
+};
+AlphaPlan alpha_plan(int64_t Bn, int64_t S, int64_t H);
 hipError_t launch_alpha_fwd(const AlphaArgs& a, hipStream_t st);
-// xh: Bn*K*S floats, xl: Bn*S floats of workspace
-hipError_t launch_alpha_bwd(const AlphaArgs& a, float* xh, float* xl, hipStream_t st);
+// Workspace: xh Bn*K*S floats, xl Bn*S, part nseg*H*S, tmp reduce_tmp_floats(nseg, H*S).
+hipError_t launch_alpha_bwd(const AlphaArgs& a, float* xh, float* xl, float* part, float* tmp,
+                            hipStream_t st);
 // The static scratch of rmsnorm_bwd_noalloc: its size, and the device address of the
 // current device's copy (looked up once per device).
 constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;

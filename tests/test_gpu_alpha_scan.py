@@ -4,8 +4,9 @@ the oracle's (one stated reading of the ml-alpha kernel's scan; see oracle.c).
 Every output (h, da, db, dWc, dh0) is compared on: the page's training-test shape (4
 sequences of 8 steps, hidden 8, state 4), the alpha-stack workload's shape, single
 steps and states, state counts that leave a workgroup's rows ragged, one row per
-workgroup (S >= 256), hidden sizes past a workgroup, a given initial state, and a batch
-wider than a grid dimension of 65535.  dWc accumulates; repeated runs are bit-identical.
+workgroup (S >= 64), step and hidden counts that are not multiples of the 8 loads issued
+at a time, a given initial state, and a batch wider than a grid dimension of 65535 (whose
+dWc is summed over 3182 segments of 22 rows).  dWc accumulates; repeated runs are bit-identical.
 """
 import numpy as np
 import pytest
