@@ -287,10 +287,10 @@ __device__ __forceinline__ void chan_reduce_scatter(float (&v)[V], int) {
 // register r the state 4*Q + (r ^ m) with m = 2*b3 + b2: the partner across bit 3 (l ^ 8)
 // has the same Q and m ^ 2, the partner across bits 0..2 (l ^ 7) the same Q and m ^ 1.
 // A channel's four lanes still hold all 16 states (q -> q ^ 3*b2 is a permutation).
-__device__ __forceinline__ constexpr int perm_quarter(int lane) {
+__host__ __device__ __forceinline__ constexpr int perm_quarter(int lane) {
   return (lane & 3) ^ (3 * ((lane >> 2) & 1));
 }
-__device__ __forceinline__ constexpr int perm_xor(int lane) {
+__host__ __device__ __forceinline__ constexpr int perm_xor(int lane) {
   return ((lane >> 2) & 1) | (((lane >> 3) & 1) << 1);
 }
 
@@ -312,7 +312,7 @@ __device__ __forceinline__ void chan_reduce_scatter_perm(float (&v)[8]) {
 }
 
 // Lane holding partial p (0 or 1) of output (t, n) after chan_reduce_scatter_perm.
-__device__ __forceinline__ constexpr int perm_partial_lane(int t, int n, int p) {
+__host__ __device__ __forceinline__ constexpr int perm_partial_lane(int t, int n, int p) {
   const int m = n & 3, b2 = m & 1, b3 = m >> 1, q = (n >> 2) ^ (3 * b2);
   return q | (b2 << 2) | (b3 << 3) | (t << 4) | (p << 5);
 }
@@ -321,7 +321,7 @@ __device__ __forceinline__ constexpr int perm_partial_lane(int t, int n, int p) 
 // chan_reduce_scatter<V>: k's bits (most significant first) at lane bits 3, 2, 4, p's
 // bits (least significant first) at the channel bits left over.
 template <int V>
-__device__ __forceinline__ constexpr int chan_partial_lane(int k, int p, int q) {
+__host__ __device__ __forceinline__ constexpr int chan_partial_lane(int k, int p, int q) {
   constexpr int S = V == 8 ? 3 : (V == 4 ? 2 : 1);
   constexpr int sb[3] = {3, 2, 4};
   int l = q;
