@@ -71,12 +71,21 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 constexpr int64_t kCUs = 256;
 constexpr int64_t kFwdTargetWG = kCUs * 32;
 constexpr int64_t kBwdTargetWG = kCUs * 20;
+// Every chunk costs a fixed prologue and epilogue in each pass (addressing, the first
+// tiles' loads, the carried state, its dA/dD partials), so chunks shorter than about 16
+// tiles pay for themselves only where the grid would otherwise be too small.  Measured on
+// 8 x 2048 x 1536 (f32): 64 + 32 chunks (2 and 4 tiles) 0.620 ms, 8 + 8 chunks 0.558 ms;
+// on 4 x 8192 x 2560 (bf16) 57 + 32 chunks 1.563 ms, 32 + 32 1.548 ms; on 2 x 16384 x
+// 5120 the plan is unchanged.
+constexpr int64_t kLongChunkTiles = 16;
+constexpr int64_t kMinChunkWG = kCUs * 4;
 
 // Coarse chunking of the sequence: whole units of g tiles per chunk (g = 1, or the tiles
 // of one sparse-checkpoint interval), the longest chunks whose count reaches the target
 // grid (nu / want units each), but at least two tiles per chunk: below that the summary
-// pass costs as much as it saves.  The chunks then split the units evenly
-// (ssm::chunk_tile).
+// pass costs as much as it saves.  Chunks are then lengthened towards kLongChunkTiles
+// tiles as far as the grid keeps kMinChunkWG workgroups.  The chunks split the units
+// evenly (ssm::chunk_tile).
 ssm::Chunking choose_chunks(int64_t B, int64_t L, int64_t D, int64_t target, int64_t g = 1) {
   ssm::Chunking c;
   c.nf = cdiv(L, ssm::kTc);
@@ -86,6 +95,14 @@ ssm::Chunking choose_chunks(int64_t B, int64_t L, int64_t D, int64_t target, int
   int64_t units = want > 1 ? nu / want : nu;  // units per chunk
   const int64_t umin = g >= 2 ? 1 : (nu < 2 ? nu : 2);
   if (units < umin) units = umin;
+  const int64_t ulong = cdiv(kLongChunkTiles, g);
+  if (units < ulong) {
+    // the longest units up to ulong whose chunk count still gives kMinChunkWG workgroups
+    const int64_t nc_min = cdiv(kMinChunkWG, W);
+    int64_t u = nc_min <= 1 ? nu : nu / nc_min;
+    if (u > ulong) u = ulong;
+    if (u > units) units = u;
+  }
   c.nc = int(cdiv(nu, units));
   return c;
 }
