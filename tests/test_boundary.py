@@ -523,3 +523,15 @@ def test_alpha_scan_validation():
     need = b.load().ssm_alpha_scan_bwd_workspace_bytes(4, 8, 4, 8)
     assert need >= 4 * 8 * 4 * 4 + 4 * 4 * 4
     assert bwd(ws=FAKE, ws_bytes=need - 1) == b.SSM_ERR_WORKSPACE
+
+
+def test_chunk_plan_prefers_long_chunks_while_the_grid_stays_full():
+    # (forward, backward) coarse chunks.  The 2 x 16384 x 5120 layer keeps its
+    # grid-target plan; where that plan would cut chunks of 2-4 tiles, chunks grow
+    # towards 16 tiles (256 steps) as long as 1024 workgroups remain; narrow problems
+    # keep short chunks to fill the GPU; one tile is one chunk.
+    assert b.scan_chunks(2, 16384, 5120, 16) == (54, 32)
+    assert b.scan_chunks(8, 2048, 1536, 16) == (8, 8)
+    assert b.scan_chunks(4, 1000, 4100, 16) == (5, 5)
+    assert b.scan_chunks(1, 16384, 64, 16) == (512, 512)
+    assert b.scan_chunks(2, 8, 8, 4) == (1, 1)

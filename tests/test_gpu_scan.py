@@ -38,6 +38,10 @@ CASES = [
     ("one-step", custom(B=2, L=1, D=17, N=16), True),
     ("d-below-quad-group", custom(B=1, L=50, D=3, N=16), False),
     ("long-memory", custom(B=2, L=1500, D=64, N=16, delta_mu=-4.0, delta_sigma=1.0), False),
+    # the long-chunk plan (5 forward and 5 backward chunks of 12-13 tiles) with ragged
+    # tails in L (1000 = 62 tiles + 8 steps) and D (4100: 64 full channel groups + 4
+    # channels, one channel per thread)
+    ("long-chunk-plan-ragged-bf16", custom(B=4, L=1000, D=4100, N=16, dtype="bf16"), False),
 ]
 
 
