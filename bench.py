@@ -7,8 +7,11 @@ rmsnorm_bwd, each through the C ABI.  Default workload: the Mamba-2.8B-shaped la
 arithmetic; RMSNorm backward over [32768, 2560]).
 
 Prints one JSON line.  `value` is the metric the workload is quoted on: tokens*channels
-per second of the scan forward+backward (B*L*D over the two calls' time, each timed with
-HIP events on the stream it runs on); the whole step's rate is reported beside it.  The
+per second of the scan forward+backward: B*L*D over the time per (forward, backward)
+pair, the pairs called back to back with one HIP event pair around them all on the stream
+they run on.  The whole step's rate, and a per-call and per-kernel breakdown from an
+instrumented loop (events around every call and around the timed kernels), are reported
+beside it.  The
 `roofline` entry covers the dominant kernel (the backward main pass): its algorithmic
 HBM bytes per launch over its average launch time (HIP events recorded by the library
 around that kernel on its own stream) against the 8 TB/s HBM peak, and, beside that, its
@@ -517,6 +520,65 @@ def measure_alpha_scan(seed, steps, dev):
             "GBps": {k: nbytes[k] / (ms[k] * 1e-3) / 1e9 for k in ms}}
 
 
+def measure_scan_back_to_back(call_fwd, call_bwd, steps):
+    """The scan forward and backward called back to back `steps` times with one event
+    pair around them all, on the stream the calls launch on: the metric's time.  No event
+    sits between the kernels (each one recorded there leaves the GPU idle for a few
+    microseconds; the instrumented loop that gives the per-call and per-kernel breakdown
+    records about ten per scan step)."""
+    import torch
+    for _ in range(2):
+        call_fwd()
+        call_bwd()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        call_fwd()
+        call_bwd()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def measure_graph_step(calls, steps, dev):
+    """The step's library calls captured once into a HIP graph (torch.cuda.graph; the
+    calls only launch kernels on the caller's stream) and replayed: the time per step
+    of `steps` replays against `steps` eager steps, both bracketed by events on the
+    current stream.  The difference, if any, is what the launch path costs the eager
+    steps.  Not part of `value`."""
+    import torch
+
+    def step():
+        for _, f in calls:
+            f()
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm-up on a side stream before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    g.replay()
+    eager_ms = timed(step)
+    graph_ms = timed(g.replay)
+    return {"eager_ms": eager_ms, "graph_ms": graph_ms, "steps": steps}
+
+
 def measure_copy_GBps(dev, reps=5):
     """A plain 1 GiB device-to-device copy (torch's copy on the current stream), timed
     with events: the practical HBM rate the bandwidth fractions are also quoted against
@@ -771,7 +833,10 @@ def main():
     tokch = B * L * D
     ab = algorithmic_bytes(w)
     step_bytes = sum(ab.values())
-    scan_ms = call_ms["scan_fwd"] + call_ms["scan_bwd"]
+    scan_call_ms = call_ms["scan_fwd"] + call_ms["scan_bwd"]  # instrumented loop
+    print(f"[bench] timing {K_} scan forward+backward pairs back to back", file=sys.stderr,
+          flush=True)
+    scan_ms = measure_scan_back_to_back(call_fwd, call_bwd, K_)
     value = tokch / (scan_ms * 1e-3)  # the metric: scan forward + backward
     main_ms = kern_ms["bwd_main"]
     main_gbps = bwd_main_bytes(w) / (main_ms * 1e-3) / 1e9
@@ -785,10 +850,11 @@ def main():
     conv_silu = measure_conv_silu(w, c, args.seed, K_, dev)
     scan_fused = measure_scan_fused(w, args.seed, K_, dev)
     scan_fused["overhead_vs_plain_ms"] = (scan_fused["call_ms"]["fused_fwd"] +
-                                          scan_fused["call_ms"]["fused_bwd"] - scan_ms)
+                                          scan_fused["call_ms"]["fused_bwd"] - scan_call_ms)
 
     ckpt_iv = measure_ckpt_intervals(w, p, K_, dev)
     alpha = measure_alpha_scan(args.seed, K_, dev)
+    graph_step = measure_graph_step(calls, K_, dev)
     copy_gbps = measure_copy_GBps(dev)
 
     if args.copy_calibration:
@@ -815,6 +881,7 @@ def main():
                    "io_dtype": w.dtype, "rms_rows": w.rms_rows, "rms_dim": w.rms_dim,
                    "step": "ssm_scan_fwd + ssm_scan_bwd + conv1d_causal_bwd + rmsnorm_bwd"},
         "scan_fwd_bwd_ms": scan_ms,
+        "scan_fwd_bwd_instrumented_ms": scan_call_ms,
         "step_tokens_channels_per_s": tokch / (ms_per_step * 1e-3),
         "hbm": {"algorithmic_bytes_per_step": step_bytes,
                 "GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
@@ -857,6 +924,7 @@ def main():
     out["decode"] = decode
     out["ckpt_interval"] = ckpt_iv
     out["alpha_scan"] = alpha
+    out["graph_step"] = graph_step
     if not args.no_cpu_baseline:
         sample = args.cpu_sample_channels or max(16, min(w.D, 2048))
         print(f"[bench] cpu baseline: oracle on {sample} channels", file=sys.stderr, flush=True)
