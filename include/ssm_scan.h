@@ -182,7 +182,13 @@ int ssm_scan_bwd(void *stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t 
  * checkpoints).  The same ck_every must be given to the forward and the backward;
  * with ckpt == NULL the backward runs the forward at that interval into its workspace.
  * Results are the default path's to within summation order (the chunks differ).
- * Returns 0 (the byte queries) or SSM_ERR_ARG for another ck_every, or slabs < 1. */
+ * Returns 0 (the byte queries) or SSM_ERR_ARG for another ck_every, or slabs < 1.
+ *
+ * The backward also takes dh_last (nullable [B,D,N] f32): the gradient arriving at the
+ * final state h_{L-1} from outside the sequence, added to that state's adjoint (NULL:
+ * zero).  With it a sequence cut into consecutive pieces runs piece by piece: the forward
+ * of piece k + 1 starts from the h_last of piece k (h0), and the backward of piece k
+ * takes as dh_last the dh0 of piece k + 1; dA and dD then accumulate over the pieces. */
 size_t ssm_scan_ckpt_bytes_every(int64_t B, int64_t L, int64_t D, int64_t N,
                                  int64_t ck_every);
 size_t ssm_scan_bwd_workspace_bytes_every(int64_t B, int64_t L, int64_t D, int64_t N,
@@ -197,8 +203,8 @@ int ssm_scan_bwd_every(void *stream, ssm_dtype_t dtype, int64_t B, int64_t L, in
                        int64_t N, const void *x, const void *delta, const float *A,
                        const void *Bm, const void *Cm, const float *Dv, const float *h0,
                        const void *dy, const float *ckpt, void *dx, void *ddelta, float *dA,
-                       float *dB, float *dC, float *dD, float *dh0, int64_t ck_every,
-                       int64_t slabs, void *ws, size_t ws_bytes);
+                       float *dB, float *dC, float *dD, float *dh0, const float *dh_last,
+                       int64_t ck_every, int64_t slabs, void *ws, size_t ws_bytes);
 
 /* ---------------------------------------------------------------------------------
  * The scan between its neighbours in the Mamba block, fused into the scan's kernels.

@@ -82,7 +82,7 @@ def load():
     lib.ssm_scan_fwd_every.restype = _E
     lib.ssm_scan_fwd_every.argtypes = [_P, _E] + [_I] * 4 + [_P] * 10 + [_I] + [_P, _S]
     lib.ssm_scan_bwd_every.restype = _E
-    lib.ssm_scan_bwd_every.argtypes = [_P, _E] + [_I] * 4 + [_P] * 16 + [_I, _I] + [_P, _S]
+    lib.ssm_scan_bwd_every.argtypes = [_P, _E] + [_I] * 4 + [_P] * 17 + [_I, _I] + [_P, _S]
     lib.ssm_scan_fused_fwd.restype = _E
     lib.ssm_scan_fused_fwd.argtypes = [_P, _E] + [_I] * 4 + [_P] * 8 + [_E] + [_P] * 5 + [_P, _S]
     lib.ssm_scan_fused_bwd.restype = _E
@@ -270,9 +270,11 @@ def ssm_scan_bwd(x, delta, A, Bm, Cm, Dv, dy, ckpt=None, h0=None, dx=None, ddelt
 
 
 def ssm_scan_bwd_every(x, delta, A, Bm, Cm, Dv, dy, ck_every, slabs, ckpt=None, h0=None, dx=None,
-                       ddelta=None, dA=None, dB=None, dC=None, dD=None, dh0=None, ws=None):
+                       ddelta=None, dA=None, dB=None, dC=None, dD=None, dh0=None, dh_last=None,
+                       ws=None):
     """ssm_scan_bwd from checkpoints saved every ck_every steps, regenerating the dense
-    states slab by slab (ck_every = 0 and slabs = 1 call ssm_scan_bwd itself)."""
+    states slab by slab (ck_every = 0 and slabs = 1 call ssm_scan_bwd itself, unless
+    dh_last, the gradient arriving at the final state [B, D, N] f32, is given)."""
     lib = load()
     Bsz, L, D = x.shape
     N = A.shape[1]
@@ -299,17 +301,18 @@ def ssm_scan_bwd_every(x, delta, A, Bm, Cm, Dv, dy, ck_every, slabs, ckpt=None, 
         _ptr(dC, "dC", f32, (Bsz, L, N), dev), _ptr(dD, "dD", f32, (D,), dev),
         _ptr(dh0, "dh0", f32, (Bsz, D, N), dev),
     ]
+    dhl = _ptr(dh_last, "dh_last", f32, (Bsz, D, N), dev)
     if ssm_scan_ckpt_bytes_every(Bsz, L, D, N, ck_every) == 0 or slabs < 1:
         raise ValueError(f"unsupported checkpoint interval {ck_every} or slabs {slabs}")
     need = ssm_scan_bwd_workspace_bytes_every(Bsz, L, D, N, code, ckpt is not None, ck_every,
                                               slabs)
     ws, nbytes = _workspace(need, dev, ws)
     wsp = _ptr(ws, "ws") if ws is not None else None
-    if ck_every == 0 and slabs == 1:
+    if ck_every == 0 and slabs == 1 and dh_last is None:
         _check(lib.ssm_scan_bwd(_stream(dev), code, Bsz, L, D, N, *args, wsp, nbytes))
     else:
-        _check(lib.ssm_scan_bwd_every(_stream(dev), code, Bsz, L, D, N, *args, ck_every, slabs,
-                                      wsp, nbytes))
+        _check(lib.ssm_scan_bwd_every(_stream(dev), code, Bsz, L, D, N, *args, dhl, ck_every,
+                                      slabs, wsp, nbytes))
     return dict(dx=dx, ddelta=ddelta, dA=dA, dB=dB, dC=dC, dD=dD, dh0=dh0)
 
 

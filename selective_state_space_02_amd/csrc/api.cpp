@@ -431,15 +431,15 @@ int ssm_scan_bwd_every(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, in
                        int64_t N, const void* x, const void* delta, const float* A,
                        const void* Bm, const void* Cm, const float* Dv, const float* h0,
                        const void* dy, const float* ckpt, void* dx, void* ddelta, float* dA,
-                       float* dB, float* dC, float* dD, float* dh0, int64_t ck_every,
-                       int64_t slabs, void* ws, size_t ws_bytes) {
+                       float* dB, float* dC, float* dD, float* dh0, const float* dh_last,
+                       int64_t ck_every, int64_t slabs, void* ws, size_t ws_bytes) {
   int rc = check_scan_dims(dtype, B, L, D, N);
   if (rc) return rc;
   if ((rc = check_ckpt_every(N, ck_every, slabs))) return rc;
   rc = check_ptrs({{x, "x"}, {delta, "delta"}, {A, "A"}, {Bm, "Bm"}, {Cm, "Cm"}, {Dv, "Dv"},
                    {dy, "dy"}, {dx, "dx"}, {ddelta, "ddelta"}, {dA, "dA"}, {dB, "dB"},
                    {dC, "dC"}, {dD, "dD"}},
-                  {{h0, "h0"}, {ckpt, "ckpt"}, {dh0, "dh0"}});
+                  {{h0, "h0"}, {ckpt, "ckpt"}, {dh0, "dh0"}, {dh_last, "dh_last"}});
   if (rc) return rc;
   const bool with_ckpt = ckpt != nullptr;
   ssm::BwdPlan p{};
@@ -455,6 +455,7 @@ int ssm_scan_bwd_every(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, in
   a.x = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dv = Dv; a.h0 = h0;
   a.dy = dy; a.dx = dx; a.ddelta = ddelta; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD;
   a.dh0 = dh0;
+  a.dh_last = dh_last;
   a.vec4 = D % 4 == 0;
   if (with_ckpt) {
     p.ckpt = ckpt;
@@ -477,7 +478,7 @@ int ssm_scan_bwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t 
                  const float* ckpt, void* dx, void* ddelta, float* dA, float* dB, float* dC,
                  float* dD, float* dh0, void* ws, size_t ws_bytes) {
   return ssm_scan_bwd_every(stream, dtype, B, L, D, N, x, delta, A, Bm, Cm, Dv, h0, dy, ckpt,
-                            dx, ddelta, dA, dB, dC, dD, dh0, 0, 1, ws, ws_bytes);
+                            dx, ddelta, dA, dB, dC, dD, dh0, nullptr, 0, 1, ws, ws_bytes);
 }
 
 int ssm_scan_fused_fwd(void* stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t D,

@@ -68,6 +68,7 @@ struct ScanArgs {
   float* dC;
   float* dD;
   float* dh0;  // nullable
+  const float* dh_last;  // nullable [B][D][N]: gradient arriving at h_{L-1} (zero if null)
   // The scan's Mamba-block neighbours (fused entry points only).  The delta input is
   // then the raw time step: delta_eff = dt_softplus ? softplus(delta + dt_bias[d])
   // : delta + dt_bias[d]; with z the output is y * silu(z).

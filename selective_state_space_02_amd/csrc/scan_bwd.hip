@@ -160,12 +160,13 @@ __global__ __launch_bounds__(256, 4) void k_bwd_summary(
 template <int N>
 __global__ __launch_bounds__(256) void k_bwd_carry(
     int64_t B, int64_t D, int nc, const float* __restrict__ A, const float* __restrict__ GS,
-    const float* __restrict__ SD, float* __restrict__ gin) {
+    const float* __restrict__ SD, const float* __restrict__ dh_last, float* __restrict__ gin) {
   const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= B * D * N) return;
   const int64_t n = idx % N, bd = idx / N, d = bd % D, b = bd / D;
   const float A2 = A[d * N + n] * kLog2e;
-  float gp = 0.f;
+  // what arrives at the end of the last chunk: the final state's own gradient, if given
+  float gp = dh_last ? dh_last[idx] : 0.f;
   // sequential over chunks (last to first); a batch of kCarryAhead chunk summaries is
   // loaded before it is composed
   for (int c0 = nc - 1; c0 >= 0; c0 -= kCarryAhead) {
@@ -690,7 +691,9 @@ static hipError_t bwd_impl(const ScanArgs& a, const BwdPlan& p, hipStream_t st) 
   const T* Cm = static_cast<const T*>(a.Cm);
   const T* dy = static_cast<const T*>(a.dy);
   const dim3 block(256);
-  const float* gin = nullptr;
+  // the adjoint arriving at each chunk's end, [B][nc][D][N]: with one chunk that is the
+  // final state's gradient alone, whose [B][D][N] layout is the same array
+  const float* gin = a.dh_last;
   hipError_t e;
   if (p.nc > 1) {
     timer_mark(kKBwdSummary, false, st);
@@ -702,7 +705,7 @@ static hipError_t bwd_impl(const ScanArgs& a, const BwdPlan& p, hipStream_t st) 
     const int64_t tot = a.B * a.D * N;
     timer_mark(kKBwdCarry, false, st);
     e = launch(k_bwd_carry<N>, dim3(unsigned((tot + 255) / 256)), block, st, a.B, a.D, p.nc,
-               a.A, p.GS, p.SD, p.gin);
+               a.A, p.GS, p.SD, a.dh_last, p.gin);
     timer_mark(kKBwdCarry, true, st);
     if (e != hipSuccess) return e;
     gin = p.gin;

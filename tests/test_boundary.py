@@ -453,12 +453,12 @@ def _fwd_every(lib, every, B=2, L=64, D=32, N=16, ckpt=FAKE, **kw):
 
 def _bwd_every(lib, every, slabs, B=2, L=64, D=32, N=16, ckpt=FAKE, ws=None, ws_bytes=0, **kw):
     p = dict(x=FAKE, delta=FAKE, A=FAKE, Bm=FAKE, Cm=FAKE, Dv=FAKE, h0=None, dy=FAKE,
-             dx=FAKE, ddelta=FAKE, dA=FAKE, dB=FAKE, dC=FAKE, dD=FAKE, dh0=None)
+             dx=FAKE, ddelta=FAKE, dA=FAKE, dB=FAKE, dC=FAKE, dD=FAKE, dh0=None, dh_last=None)
     p.update(kw)
     return lib.ssm_scan_bwd_every(None, 0, B, L, D, N, p["x"], p["delta"], p["A"], p["Bm"],
                                   p["Cm"], p["Dv"], p["h0"], p["dy"], ckpt, p["dx"],
                                   p["ddelta"], p["dA"], p["dB"], p["dC"], p["dD"], p["dh0"],
-                                  every, slabs, ws, ws_bytes)
+                                  p["dh_last"], every, slabs, ws, ws_bytes)
 
 
 @pytest.mark.parametrize("every,N", [(-16, 16), (24, 16), (8, 4), (8, 8), (4, 16), (17, 16)])
@@ -494,6 +494,9 @@ def test_checkpoint_interval_slabs_and_sizes():
     # a too-small workspace is refused before any launch
     assert _bwd_every(lib, 64, 8, B=B, L=L, D=D, N=N, ws=FAKE, ws_bytes=w8 - 1) == \
         b.SSM_ERR_WORKSPACE
+    # the final state's gradient is optional, but aligned if given
+    assert _bwd_every(lib, 0, 1, dh_last=MIS) == b.SSM_ERR_ALIGN
+    assert "dh_last" in b.last_error()
 
 
 def test_alpha_scan_validation():
