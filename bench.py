@@ -903,6 +903,9 @@ def main():
             "traffic": counter_traffic(w.name),
             "avg_launch_ms": main_ms,
             "algorithmic_bytes_per_launch": bwd_main_bytes(w),
+            # `bound` names the roof `frac` is taken against (the metric's: HBM); the
+            # resource that limits the kernel is its VALU issue rate
+            "limited_by": "valu_issue",
             # what actually binds the kernel: VALU issue.  Its issue time from the
             # committed counter record (null once the kernel's sources changed since),
             # and the method's own op count against the non-packed lane-op peak
