@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libssmscan.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-command-line-argument"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Werror", "-Wno-unused-command-line-argument"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 SOURCES = ["scan_fwd.hip", "scan_bwd.hip", "reduce.hip", "conv1d_bwd.hip", "rmsnorm_bwd.hip",
            "conv1d_fwd.hip", "rmsnorm_fwd.hip", "decode.hip", "alpha_scan.hip",
