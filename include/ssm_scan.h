@@ -182,7 +182,8 @@ int ssm_scan_bwd(void *stream, ssm_dtype_t dtype, int64_t B, int64_t L, int64_t 
  * checkpoints).  The same ck_every must be given to the forward and the backward;
  * with ckpt == NULL the backward runs the forward at that interval into its workspace.
  * Results are the default path's to within summation order (the chunks differ).
- * Returns 0 (the byte queries) or SSM_ERR_ARG for another ck_every, or slabs < 1.
+ * Returns 0 (the byte queries) or SSM_ERR_ARG for another ck_every, or slabs outside
+ * [1, 65536].
  *
  * The backward also takes dh_last (nullable [B,D,N] f32): the gradient arriving at the
  * final state h_{L-1} from outside the sequence, added to that state's adjoint (NULL:

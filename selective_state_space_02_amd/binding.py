@@ -302,7 +302,7 @@ def ssm_scan_bwd_every(x, delta, A, Bm, Cm, Dv, dy, ck_every, slabs, ckpt=None, 
         _ptr(dh0, "dh0", f32, (Bsz, D, N), dev),
     ]
     dhl = _ptr(dh_last, "dh_last", f32, (Bsz, D, N), dev)
-    if ssm_scan_ckpt_bytes_every(Bsz, L, D, N, ck_every) == 0 or slabs < 1:
+    if ssm_scan_ckpt_bytes_every(Bsz, L, D, N, ck_every) == 0 or not 1 <= slabs <= 65536:
         raise ValueError(f"unsupported checkpoint interval {ck_every} or slabs {slabs}")
     need = ssm_scan_bwd_workspace_bytes_every(Bsz, L, D, N, code, ckpt is not None, ck_every,
                                               slabs)

@@ -219,7 +219,9 @@ int check_ckpt_every(int64_t N, int64_t every, int64_t slabs) {
     return fail(SSM_ERR_ARG,
                 "checkpoint interval %lld must be 0, %lld or a positive multiple of %d steps",
                 (long long)every, (long long)ssm::ckpt_base(N), ssm::kTc);
-  if (slabs < 1) return fail(SSM_ERR_ARG, "slabs must be >= 1 (got %lld)", (long long)slabs);
+  if (slabs < 1 || slabs > ssm::kMaxSlabs)
+    return fail(SSM_ERR_ARG, "slabs must be in [1, %lld] (got %lld)", (long long)ssm::kMaxSlabs,
+                (long long)slabs);
   return SSM_OK;
 }
 
@@ -384,7 +386,7 @@ size_t ssm_scan_bwd_workspace_bytes_every(int64_t B, int64_t L, int64_t D, int64
                                           int64_t slabs) {
   if (B <= 0 || L <= 0 || D <= 0 || N <= 0) return 0;
   if (every < 0 || (every != 0 && every != ssm::ckpt_base(N) && every % ssm::kTc != 0) ||
-      slabs < 1)
+      slabs < 1 || slabs > ssm::kMaxSlabs)
     return 0;
   return bwd_ws(B, L, D, N, with_ckpt != 0, every, slabs, nullptr, nullptr, nullptr, nullptr);
 }

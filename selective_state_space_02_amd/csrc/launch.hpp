@@ -91,13 +91,20 @@ struct Chunking {
 // the sequence: an even split of units of g tiles (chunk lengths differing by at most
 // one unit; the last unit may be short), so every chunk boundary is a multiple of g
 // tiles.  Only the last chunk can hold the sequence's partial tile, so chunks 0..nc-2
-// are full.  nc must not exceed the unit count.
+// are full.  nc must not exceed the unit count.  floor(c * nu / nc) is formed as
+// c * q + floor(c * r / nc) with nu = q * nc + r, exact without the c * nu product, which
+// could pass 2^63 for sequences near the size limit cut into very many chunks.
 __host__ __device__ __forceinline__ int64_t chunk_tile(int64_t c, int64_t nf, int64_t nc,
                                                       int64_t g) {
   const int64_t nu = (nf + g - 1) / g;
-  const int64_t t = g * (c * nu / nc);
+  const int64_t q = nu / nc, r = nu % nc;
+  const int64_t t = g * (c * q + c * r / nc);
   return t < nf ? t : nf;
 }
+
+// Most slabs a sparse-checkpoint backward may split its chunks into (it keeps the chunk
+// count, and every grid the backward launches, far from the 32-bit and grid limits).
+constexpr int64_t kMaxSlabs = 65536;
 
 // Position of a scan workgroup in its 1-D grid: the channel group varies fastest, then
 // the batch row, then the chunk (the order of the former 3-D grid), so the grid is not

@@ -476,6 +476,9 @@ def test_checkpoint_interval_slabs_and_sizes():
     lib = b.load()
     assert _bwd_every(lib, 64, 0) == b.SSM_ERR_ARG
     assert "slabs" in b.last_error()
+    assert _bwd_every(lib, 64, 65537) == b.SSM_ERR_ARG
+    assert b.ssm_scan_bwd_workspace_bytes_every(2, 64, 32, 16, 0, 1, 64, 65537) == 0
+    assert b.ssm_scan_bwd_workspace_bytes_every(2, 64, 32, 16, 0, 1, 64, 65536) > 0
     assert b.ssm_scan_bwd_workspace_bytes_every(2, 64, 32, 16, 0, 1, 64, 0) == 0
     # the default interval through the new entry points is the plain call's plan
     assert b.ssm_scan_ckpt_bytes_every(2, 1000, 32, 16, 0) == b.ssm_scan_ckpt_bytes(2, 1000, 32, 16)
