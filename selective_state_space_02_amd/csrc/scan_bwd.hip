@@ -735,13 +735,17 @@ static hipError_t bwd_impl(const ScanArgs& a, const BwdPlan& p, hipStream_t st) 
       const int64_t ts = chunk_tile(c0, p.nf, p.nc, p.g) * kTc;
       const int64_t te0 = chunk_tile(c1, p.nf, p.nc, p.g) * kTc, te = te0 < a.L ? te0 : a.L;
       const int64_t k0 = ts / p.ck_every, nseg = (te - ts + p.ck_every - 1) / p.ck_every;
-      // a workgroup regenerates runs of consecutive intervals, about kRegenSteps steps
-      const int nrun = int(p.ck_every >= kRegenSteps ? 1 : kRegenSteps / p.ck_every);
+      // a workgroup regenerates runs of consecutive intervals, about kRegenSteps steps,
+      // longer where the grid would pass one launch's limit (every interval restarts from
+      // its saved state, so the run length does not change the states)
+      int64_t nrun = p.ck_every >= kRegenSteps ? 1 : kRegenSteps / p.ck_every;
+      const int64_t cap = kMaxGridX / (p.ng * a.B);
+      if ((nseg + nrun - 1) / nrun > cap) nrun = (nseg + cap - 1) / cap;
       const int64_t nruns = (nseg + nrun - 1) / nrun;
       timer_mark(kKCkptRegen, false, st);
       e = launch(k_ckpt_regen<T, N, VEC>, dim3(unsigned(p.ng * a.B * nruns)), block, st, a.B,
-                 a.L, a.D, p.ng, p.ck_every, k0, k0 + nseg, nrun, x, delta, a.A, Bm, p.ckpt, p.nck,
-                 p.ckd, p.nckd, ts / CK);
+                 a.L, a.D, p.ng, p.ck_every, k0, k0 + nseg, int(nrun), x, delta, a.A, Bm, p.ckpt,
+                 p.nck, p.ckd, p.nckd, ts / CK);
       timer_mark(kKCkptRegen, true, st);
       if (e != hipSuccess) return e;
       if ((e = main_pass(c0, c1, p.ckd, p.nckd, ts / CK)) != hipSuccess) return e;
