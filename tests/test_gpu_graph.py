@@ -92,3 +92,58 @@ def test_step_replays_from_a_graph_bit_identically():
         for k in out:
             assert torch.equal(out[k], ref[k]), (rep, k)
         say(f"[graph] replay {rep} bit-identical ({float(junk):.3f})")
+
+
+def test_sparse_checkpoint_scan_replays_from_a_graph_bit_identically():
+    # the sparse-checkpoint path launches per slab (regeneration, then the main pass);
+    # the forward, and the backward with a final-state gradient, are captured together
+    w = custom(B=2, L=700, D=130, N=16, dtype="bf16")
+    dev = torch.device("cuda")
+    p = {k: v.to(dev) for k, v in synth.scan_inputs(w, seed=8).items()}
+    B, L, D, N = w.B, w.L, w.D, w.N
+    f32 = torch.float32
+    every, slabs = 64, 3
+    code = ssm.SSM_BF16
+    u8 = torch.uint8
+    ckpt = ssm.new_ckpt(B, L, D, N, dev, ck_every=every)
+    ws_f = torch.empty(max(1, ssm.ssm_scan_fwd_workspace_bytes(B, L, D, N, code)), dtype=u8, device=dev)
+    ws_b = torch.empty(max(1, ssm.ssm_scan_bwd_workspace_bytes_every(B, L, D, N, code, True, every, slabs)),
+                       dtype=u8, device=dev)
+    dh_last = torch.randn((B, D, N), dtype=f32, device=dev)
+    out = dict(y=torch.empty_like(p["x"]), dx=torch.empty_like(p["x"]), ddelta=torch.empty_like(p["x"]),
+               dA=torch.zeros((D, N), dtype=f32, device=dev), dB=torch.empty((B, L, N), dtype=f32, device=dev),
+               dC=torch.empty((B, L, N), dtype=f32, device=dev), dD=torch.zeros((D,), dtype=f32, device=dev),
+               dh0=torch.empty((B, D, N), dtype=f32, device=dev))
+    a = (p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], p["Dv"])
+
+    def run():
+        out["dA"].zero_()
+        out["dD"].zero_()
+        ssm.ssm_scan_fwd_every(*a, every, y=out["y"], ckpt=ckpt, ws=ws_f)
+        ssm.ssm_scan_bwd_every(*a, p["dy"], every, slabs, ckpt=ckpt, dx=out["dx"],
+                               ddelta=out["ddelta"], dA=out["dA"], dB=out["dB"], dC=out["dC"],
+                               dD=out["dD"], dh0=out["dh0"], dh_last=dh_last, ws=ws_b)
+
+    run()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in out.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        junk = torch.randn(1 << 20, device=dev).sum()
+        for k in out:
+            out[k].fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in out:
+            assert torch.equal(out[k], ref[k]), (rep, k)
+        say(f"[graph sparse] replay {rep} bit-identical ({float(junk):.3f})")
