@@ -18,7 +18,9 @@
  *   ssm_decode_step    one decode token of the block's scan branch (conv step, SiLU,
  *                      fused scan step) in one launch
  *   ssm_scan_fwd_every / ssm_scan_bwd_every
- *                      the scan with sparse checkpoints (states regenerated per slab)
+ *                      the scan with sparse checkpoints (states regenerated per slab);
+ *                      the backward also takes the gradient arriving at the final state
+ *   ssm_scan_chunks    the coarse chunk counts the scan plans (host query)
  *   ssm_alpha_scan_fwd / ssm_alpha_scan_bwd
  *                      the sigmoid-gated scan of the ml-alpha kernel (one reading)
  *   rmsnorm_bwd_noalloc  rmsnorm_bwd without a workspace (static scratch)
