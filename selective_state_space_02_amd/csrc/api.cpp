@@ -251,14 +251,18 @@ struct Ptr {
   const char* name;
 };
 
+constexpr const char* kAlignHint =
+    " (a view at an offset into a larger buffer keeps the offset: pass a copy)";
+
 int check_ptrs(std::initializer_list<Ptr> required, std::initializer_list<Ptr> optional) {
   for (const Ptr& q : required)
     if (!q.p) return fail(SSM_ERR_ARG, "required pointer '%s' is NULL", q.name);
   for (const Ptr& q : required)
-    if (!aligned16(q.p)) return fail(SSM_ERR_ALIGN, "pointer '%s' is not 16-byte aligned", q.name);
+    if (!aligned16(q.p))
+      return fail(SSM_ERR_ALIGN, "pointer '%s' is not 16-byte aligned%s", q.name, kAlignHint);
   for (const Ptr& q : optional)
     if (q.p && !aligned16(q.p))
-      return fail(SSM_ERR_ALIGN, "pointer '%s' is not 16-byte aligned", q.name);
+      return fail(SSM_ERR_ALIGN, "pointer '%s' is not 16-byte aligned%s", q.name, kAlignHint);
   return SSM_OK;
 }
 
